@@ -1,0 +1,310 @@
+"""Benchmark of the Lightning Attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+
+A timed step is one la_prefill over the workload B=1, H=64, N=8192, d=128,
+bf16 Q/K/V ~ N(0,1)/sqrt(d), per-head decay exp(-U[0.001, 0.1]) (the
+MiniMax-Text-01 lightning-layer shape at its 8192-token pretraining length).
+Inputs are resident in HBM before timing starts; two input sets alternate
+(1.08 GB together, four times the 256 MB Infinity Cache) so no step reads
+inputs left in cache by the step before.  W untimed warmup steps, then K
+timed steps bracketed by torch.cuda.synchronize().
+
+One JSON line is printed with the contract fields plus:
+  roofline      the prefill kernel's algorithmic HBM bytes per launch over
+                its average launch time (HIP events on its stream), against
+                8 TB/s; `traffic` is the counter-measured bytes per launch
+                from profiles/ if it was taken on the current kernel source.
+  cpu_baseline  the fp64 oracle (blockwise, beta=64) timed on the host cores
+                over heads of the same workload.
+  mfma          algorithmic TFLOP/s at beta=64 against 2.5 PFLOP/s bf16.
+  decode        la_decode alone on 256 sequences x 64 heads: GB/s vs 8 TB/s.
+  mixed         decode on one stream concurrent with a packed prefill of 8
+                sequences (lengths U[1K, 32K]) on another.
+  sweep         cold tokens/s at N = 1K ... 1M and for a packed varlen batch.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s + MFMA TFLOP/s (H=64,d=128,N=8K..1M); decode HBM GB/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+H, D, BETA = 64, 128, 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n8k_traffic.json")
+KERNEL_SOURCES = ["linear_attention_la_amd/csrc/la_prefill_bf16.hip",
+                  "linear_attention_la_amd/csrc/la_device.h",
+                  "linear_attention_la_amd/csrc/la_internal.h"]
+
+
+def prefill_bytes(tokens, seqs, heads=H, d=D):
+    """Algorithmic HBM bytes: Q, K, V read and O written once (2 B each), plus
+    the fp32 final state."""
+    return tokens * heads * d * 8 + seqs * heads * d * d * 4
+
+
+def prefill_flops(tokens, heads=H, d=D, beta=BETA):
+    """Algorithmic flops at block size beta: 4 d^2 (Q S and K^T V) plus
+    2 d (beta + 1) (causal halves of Q K^T and P V) per token per head."""
+    return tokens * heads * (4 * d * d + 2 * d * (beta + 1))
+
+
+def decode_bytes(batch, heads=H, d=D):
+    """fp32 state read and written, q/k/v read and o written in bf16."""
+    return batch * heads * (8 * d * d + 8 * d)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(algorithmic):
+    """Counter-measured HBM bytes per launch, if taken on this kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def timed_launches(fn, reps, stream, flush=None):
+    """Average duration (s) of `fn` over `reps` launches, by HIP events on
+    `stream`; `flush` runs between launches, outside the events."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        for i in range(reps):
+            if flush is not None:
+                flush()
+            starts[i].record(stream)
+            fn(i)
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps / 1e3
+
+
+def cpu_baseline(budget_s=12.0):
+    """fp64 oracle over heads of the N=8192 workload (host inputs of the same
+    distribution), until budget_s of compute has been spent."""
+    import oracle
+    from la_inputs import decay_from_seed, host_qkv
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    N = 8192
+    decay = decay_from_seed(H)
+    heads_done, elapsed = 0, 0.0
+    chunk = 8
+    while elapsed < budget_s and heads_done < 4 * H:
+        q, k, v = host_qkv(N, chunk, D, 5000 + heads_done)
+        t0 = time.perf_counter()
+        for j in range(chunk):
+            oracle.blockwise(q[:, j], k[:, j], v[:, j], float(decay[(heads_done + j) % H]), BETA)
+        elapsed += time.perf_counter() - t0
+        heads_done += chunk
+    tokens_equiv = N * heads_done / H
+    return {"value": tokens_equiv / elapsed, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 blockwise oracle (beta={BETA}) on {heads_done} (sequence, head) "
+                      f"chains of N={N}, d={D} ({heads_done / H:.2f}x the 64-head workload), "
+                      f"{elapsed:.1f} s of compute on {len(os.sched_getaffinity(0))} "
+                      f"visible host cores",
+            "seconds": round(elapsed, 2)}
+
+
+def bench_decode(dev, reps=20):
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states, workload
+
+    w = workload("mixed_decode")
+    B = w["batch"]
+    kv = device_states(B, H, D, w["seed"], dev, scale=0.5)
+    q, k, v = (x.view(B, H, D) for x in device_qkv(B, H, D, w["seed"] + 1, dev))
+    out = torch.empty_like(q)
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        la.decode(q, k, v, kv, w["decay"], out=out)
+    t = timed_launches(lambda i: la.decode(q, k, v, kv, w["decay"], out=out), reps, s)
+    gbs = decode_bytes(B) / t / 1e9
+    return {"batch": B, "heads": H, "head_dim": D, "us": round(t * 1e6, 2),
+            "GB_per_s": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": decode_bytes(B)}, (q, k, v, kv, out, w)
+
+
+def bench_mixed(dev, dec_state, reps=10):
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import cu_seqlens, device_qkv, workload
+
+    q, k, v, kv, out, wd = dec_state
+    B = wd["batch"]
+    wp = workload("mixed_prefill")
+    cu = cu_seqlens(wp["lengths"])
+    T = int(cu[-1])
+    qp, kp, vp = device_qkv(T, H, D, wp["seed"], dev)
+    cu_dev = torch.from_numpy(cu).to(dev)
+    op = torch.empty_like(qp)
+    kvp = torch.empty((len(wp["lengths"]), H, D, D), dtype=torch.float32, device=dev)
+    sp, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+          for n in ("p0", "p1", "d0", "d1")}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(reps):
+        ev["p0"][i].record(sp)
+        la.prefill(qp, kp, vp, cu_dev, wp["decay"], stream=sp, out=op, kv_final=kvp)
+        ev["p1"][i].record(sp)
+        ev["d0"][i].record(sd)
+        la.decode(q, k, v, kv, wd["decay"], stream=sd, out=out)
+        ev["d1"][i].record(sd)
+        torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    tp = sum(a.elapsed_time(b) for a, b in zip(ev["p0"], ev["p1"])) / reps / 1e3
+    td = sum(a.elapsed_time(b) for a, b in zip(ev["d0"], ev["d1"])) / reps / 1e3
+    return {"prefill_seqs": len(wp["lengths"]), "prefill_tokens": T, "decode_batch": B,
+            "prefill_us": round(tp * 1e6, 1), "decode_us_under_load": round(td * 1e6, 1),
+            "decode_GB_per_s_under_load": round(decode_bytes(B) / td / 1e9, 1),
+            "prefill_tokens_per_s_under_load": round(T / tp, 0),
+            "step_wall_us": round(wall * 1e6, 1)}
+
+
+def bench_sweep(dev, reps=5):
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import cu_seqlens, device_qkv, workload
+
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB cache flush
+    res = {}
+    s = torch.cuda.current_stream()
+    for name in ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodecay",
+                 "n1m", "varlen64"):
+        w = workload(name)
+        cu = cu_seqlens(w["lengths"])
+        T = int(cu[-1])
+        q, k, v = device_qkv(T, H, D, w["seed"], dev)
+        cu_dev = torch.from_numpy(cu).to(dev)
+        o = torch.empty_like(q)
+        kvf = torch.empty((len(w["lengths"]), H, D, D), dtype=torch.float32, device=dev)
+        run = lambda i: la.prefill(q, k, v, cu_dev, w["decay"], out=o, kv_final=kvf)  # noqa
+        run(0)
+        t = timed_launches(run, reps, s, flush=lambda: scratch.zero_())
+        by = prefill_bytes(T, len(w["lengths"]))
+        res[name] = {"tokens": T, "seqs": len(w["lengths"]), "us": round(t * 1e6, 1),
+                     "tokens_per_s": round(T / t, 0), "GB_per_s": round(by / t / 1e9, 1),
+                     "frac_of_8TBs": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "tflops_beta64": round(prefill_flops(T) / t / 1e12, 1)}
+        del q, k, v, o, kvf
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="skip decode/mixed/sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import decay_from_seed, device_qkv, workload
+
+    dev = torch.device("cuda:0")
+    la.lib()
+    w = workload("n8k")
+    N = w["lengths"][0]
+    decay = w["decay"]
+    sets = [device_qkv(N, H, D, w["seed"] + i, dev) for i in range(2)]
+    cu_dev = torch.tensor([0, N], dtype=torch.int32, device=dev)
+    cu_host = [0, N]
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+    kvf = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, k, v = sets[i & 1]
+        la.prefill(q, k, v, cu_dev, decay, out=o, kv_final=kvf)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev0[i].record(stream)
+        step(i)
+        ev1[i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern_s = sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / args.steps / 1e3
+
+    tokens_per_s = N * args.steps / elapsed
+    by = prefill_bytes(N, 1)
+    achieved = by / kern_s / 1e9
+    tflops = prefill_flops(N) / kern_s / 1e12
+    traffic = measured_traffic(by)
+    line = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "la_prefill B=1 H=64 N=8192 d=128 bf16 in/out, fp32 state, "
+                               "seeded per-head decay", "global_batch": 1, "seq_len": N,
+                   "heads": H, "head_dim": D, "beta": BETA, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "prefill_bf16_kernel<128,false>",
+                     "kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes": by},
+        "mfma": {"tflops_algorithmic_beta64": round(tflops, 2),
+                 "frac_of_2500": round(tflops / BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_extra:
+        dec, dec_state = bench_decode(dev)
+        line["decode"] = dec
+        line["mixed"] = bench_mixed(dev, dec_state)
+        del dec_state
+        torch.cuda.empty_cache()
+        line["sweep"] = bench_sweep(dev)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline()
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

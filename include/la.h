@@ -1,0 +1,148 @@
+/*
+ * la.h -- C ABI of libla: Lightning Attention prefill and decode for AMD
+ * MI355X (gfx950).
+ *
+ * What is computed.  Lightning Attention is causal linear attention in which
+ * an element-wise product takes the place of softmax (emonzhong.com,
+ * "MiniMax-01: Scaling Foundation Models with Lightning Attention", section
+ * 方法要点), evaluated with the right-product kernel trick and split into
+ * intra-block and inter-block work so that the cumsum of causal linear
+ * attention is avoided (CSDN, "【AI论文】MiniMax-01:利用闪电注意力机制扩展基础
+ * 模型", §2.1; jvyan.cn news article, 一、模型架构; mizuki blog,
+ * "MiniMax-01：4M 上下文破局", 关键概念清单).  The pages print no formula.
+ * This library reads the element-wise product as a causal decay mask: for
+ * one sequence and one head h with decay lambda = decay[h],
+ *
+ *     S_t = lambda * S_{t-1} + k_t^T v_t,     o_t = q_t S_t,
+ *
+ * i.e. O = [(Q K^T) .* M] V + diag(lambda^(t+1)) Q S_init with
+ * M[t][j] = lambda^(t-j) for t >= j and 0 otherwise, and the final state
+ * S_L = lambda^L S_init + sum_j lambda^(L-1-j) k_j^T v_j.  There is no
+ * softmax, no 1/sqrt(d) scale and no normaliser in this core.  The state
+ * S is d x d, rows indexed by the key dimension r and columns by the value
+ * dimension c.
+ *
+ * Layouts.  q, k, v, o are contiguous [T, H, d] (token-major): element
+ * (t, h, c) sits at ((int64)t * H + h) * d + c.  Sequences are packed along
+ * the token axis (data packing, CSDN §3.2; jvyan.cn 二、计算优化) and
+ * delimited by cu_seqlens[S+1] (cu[0] = 0, cu[S] = T, non-decreasing).
+ * States are contiguous fp32 [S, H, d, d]; element (s, h, r, c) sits at
+ * (((int64)s * H + h) * d + r) * d + c.
+ *
+ * Ownership.  The caller allocates and owns every buffer.  The library
+ * allocates no device memory, keeps no pointer after a call returns and
+ * holds no global state; calls on different streams with disjoint outputs
+ * may run concurrently.  Work is enqueued on `stream` (a hipStream_t passed
+ * as void*, NULL = the default stream) and is asynchronous: device buffers
+ * must stay valid until the stream has passed the kernel.  Host arrays
+ * (decay, cu_seqlens_host) are read only during the call.  The device that
+ * owns the buffers must be the calling thread's current HIP device.
+ *
+ * Errors.  Every entry point returns la_status and never aborts or prints.
+ * Argument errors are detected on the host before anything is enqueued:
+ * LA_ERR_INVALID_ARG, nothing runs, outputs are untouched.  Valid but
+ * unsupported shapes or dtypes: LA_ERR_UNSUPPORTED.  A failed kernel launch:
+ * LA_ERR_HIP.  A fault inside a kernel surfaces at the caller's next
+ * synchronisation; the library never synchronises.  la_last_error() gives a
+ * thread-local description of the last non-OK return.
+ */
+#ifndef LA_H_
+#define LA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum la_status {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1,
+  LA_ERR_UNSUPPORTED = 2,
+  LA_ERR_HIP = 3
+} la_status;
+
+typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
+
+/* Largest number of heads one call accepts (per-head decay travels in the
+ * kernel arguments). */
+#define LA_MAX_HEADS 256
+
+/*
+ * la_prefill -- blockwise causal linear attention with per-head decay over
+ * packed variable-length sequences; writes O and the final state.
+ *
+ * Follows the intra-block / inter-block split (emonzhong.com 方法要点;
+ * mizuki blog 关键概念清单: intra-block left product, inter-block right
+ * product) over packed sequences (CSDN §3.2).  Blocks never straddle two
+ * sequences; each (sequence, head) pair is an independent chain.
+ *
+ *   q, k, v          device, [T, H, d] of in_dtype (not written).
+ *   cu_seqlens_dev   device int32 [S+1]; same contents as cu_seqlens_host.
+ *   cu_seqlens_host  host int32 [S+1]; validated (cu[0] = 0, non-decreasing,
+ *                    cu[S] = T) and used for scheduling.
+ *   num_seqs         S >= 0.  S = 0 is a no-op returning LA_OK.
+ *   total_tokens     T >= 0, < 2^31.
+ *   num_heads        H in [1, LA_MAX_HEADS].
+ *   head_dim         d: 64 or 128 (d_k = d_v = d).
+ *   in_dtype         LA_BF16 or LA_FP32.
+ *   out_dtype        dtype of o: LA_BF16 or LA_FP32 (bf16 output needs bf16
+ *                    input).  fp32 results are rounded to bf16 with
+ *                    round-to-nearest-even.
+ *   decay            host float [H], 0 < decay[h] <= 1 (1 = no decay).
+ *   kv_init          device fp32 [S, H, d, d] initial states, or NULL for
+ *                    zero states.
+ *   o                device [T, H, d] of out_dtype (written); must not
+ *                    overlap q, k, v, kv_init or kv_final.
+ *   kv_final         device fp32 [S, H, d, d] final states (written), or
+ *                    NULL to skip.  May be exactly kv_init (in-place
+ *                    continuation); any other overlap with an input is an
+ *                    error.
+ *   stream           hipStream_t or NULL.
+ *
+ * Zero-length sequences produce no rows; their final state is kv_init's (or
+ * zero).
+ */
+la_status la_prefill(const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                     int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                     int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                     const float* decay, const float* kv_init, void* o, float* kv_final,
+                     void* stream);
+
+/*
+ * la_decode -- one decode token per sequence, updating fp32 states in place.
+ *
+ * The length-1 step that serving runs in its own kernel, apart from the
+ * length > 1 prefill, so that both can run on two streams in parallel
+ * (jvyan.cn 二、计算优化; CSDN §3.2).  For every (b, h):
+ *     kv[b,h] <- decay[h] * kv[b,h] + k[b,h]^T v[b,h]      (update first)
+ *     o[b,h]  <- q[b,h] kv[b,h]                            (then read out)
+ *
+ *   q, k, v    device [B, H, d] of in_dtype (not written).
+ *   kv         device fp32 [B, H, d, d], read and written in place.
+ *   decay      host float [H], 0 < decay[h] <= 1.
+ *   batch      B >= 0 (0 is a no-op).
+ *   num_heads  H in [1, LA_MAX_HEADS].
+ *   head_dim   d: 64 or 128.
+ *   in_dtype   LA_BF16 or LA_FP32; o has the same dtype (bf16 rounded to
+ *              nearest-even).
+ *   o          device [B, H, d] (written); must not overlap q, k, v or kv.
+ *   stream     hipStream_t or NULL.
+ */
+la_status la_decode(const void* q, const void* k, const void* v, float* kv,
+                    const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                    la_dtype in_dtype, void* o, void* stream);
+
+/* Static, never-NULL name of a status code. */
+const char* la_status_str(la_status s);
+
+/* Thread-local description of the last non-OK return on this thread
+ * ("" if none).  Valid until the next library call on the same thread. */
+const char* la_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H_ */

@@ -1,0 +1,29 @@
+"""Lightning Attention prefill and decode for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libla.so`` (include/la.h).  It only
+marshals arguments: torch supplies device memory and streams, every step of
+the computation runs in the HIP kernels.  There is no CPU fallback: if the
+library is missing, every call raises.
+
+    o, kv = prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None)
+    o = decode(q, k, v, kv, decay)          # kv updated in place
+"""
+
+from ._binding import (  # noqa: F401
+    LAError,
+    LA_OK,
+    LA_ERR_INVALID_ARG,
+    LA_ERR_UNSUPPORTED,
+    LA_ERR_HIP,
+    LA_BF16,
+    LA_FP32,
+    LA_MAX_HEADS,
+    lib,
+    lib_path,
+    la_prefill,
+    la_decode,
+    la_status_str,
+    la_last_error,
+    prefill,
+    decode,
+)

@@ -1,0 +1,199 @@
+"""ctypes binding of libla's C ABI (include/la.h).
+
+Two layers:
+
+* ``la_prefill`` / ``la_decode`` / ``la_status_str`` / ``la_last_error``:
+  the C entry points with the same names and plain integer pointers.
+* ``prefill`` / ``decode``: torch-facing wrappers that check shapes, allocate
+  outputs with torch on the inputs' device and pass ``data_ptr()`` and the
+  current (or given) stream handle.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
+LA_BF16, LA_FP32 = 0, 1
+LA_MAX_HEADS = 256
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_DEFAULT_LIB = os.path.join(_HERE, "_lib", "libla.so")
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_status_name(status)}: {msg}")
+        self.status = status
+
+
+def _status_name(s):
+    return {0: "LA_OK", 1: "LA_ERR_INVALID_ARG", 2: "LA_ERR_UNSUPPORTED", 3: "LA_ERR_HIP"}.get(
+        s, f"status {s}")
+
+
+def lib_path():
+    return os.environ.get("LA_LIB", _DEFAULT_LIB)
+
+
+def lib():
+    """Load libla.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libla.so not found at {path}; build it with "
+            "`python -m linear_attention_la_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.la_prefill.restype = ctypes.c_int
+    L.la_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int, ctypes.c_int,
+                             vp, vp, vp, vp, vp]
+    L.la_decode.restype = ctypes.c_int
+    L.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
+    L.la_status_str.restype = ctypes.c_char_p
+    L.la_status_str.argtypes = [ctypes.c_int]
+    L.la_last_error.restype = ctypes.c_char_p
+    L.la_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+# ---- raw C entry points (plain integer pointers) ----
+
+def la_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens, num_heads,
+               head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final, stream):
+    return lib().la_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                            num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o,
+                            kv_final, stream)
+
+
+def la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream):
+    return lib().la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream)
+
+
+def la_status_str(s):
+    return lib().la_status_str(s).decode()
+
+
+def la_last_error():
+    return lib().la_last_error().decode()
+
+
+def _check(status):
+    if status != LA_OK:
+        raise LAError(status, la_last_error())
+
+
+# ---- torch-facing wrappers ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _host_decay(decay, num_heads):
+    torch = _torch()
+    if isinstance(decay, torch.Tensor):
+        decay = decay.detach().cpu().numpy()
+    d = np.ascontiguousarray(np.asarray(decay, dtype=np.float32).reshape(-1))
+    if d.shape[0] != num_heads:
+        raise ValueError(f"decay has {d.shape[0]} entries, expected {num_heads}")
+    return d
+
+
+def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=None,
+            final_state=True, out=None, kv_final=None):
+    """Packed varlen prefill.  q, k, v: device [T, H, d] (bf16 or fp32, same
+    dtype, contiguous).  cu_seqlens: [S+1] int (host or device).  decay: host
+    [H] floats in (0, 1].  kv_init: device fp32 [S, H, d, d] or None.
+
+    Returns (o [T, H, d], kv_final [S, H, d, d] or None).  ``out`` and
+    ``kv_final`` may supply preallocated outputs; ``kv_final`` may be
+    ``kv_init`` itself (in-place continuation)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a device tensor")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T, H, d] tensor")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share shape and dtype")
+    T, H, d = q.shape
+    dev = q.device
+    in_code = _dtype_code(q)
+    if out_dtype is None:
+        out_dtype = q.dtype
+    out_code = LA_BF16 if out_dtype == torch.bfloat16 else LA_FP32
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens if (cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32
+                                and cu_seqlens.is_contiguous()) else cu_host.to(dev)
+    else:
+        cu_host = torch.from_numpy(np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32)))
+        cu_dev = cu_host.to(dev)
+    if stream is not None and cu_dev is not cu_seqlens:
+        cu_dev.record_stream(stream)  # temporary read by a kernel on another stream
+    S = cu_host.numel() - 1
+    if S < 0:
+        raise ValueError("cu_seqlens must have at least one entry")
+    dec = _host_decay(decay, H)
+    if kv_init is not None:
+        if (not kv_init.is_cuda or kv_init.dtype != torch.float32 or not kv_init.is_contiguous()
+                or tuple(kv_init.shape) != (S, H, d, d)):
+            raise ValueError("kv_init must be a contiguous fp32 device tensor [S, H, d, d]")
+    if out is None:
+        out = torch.empty((T, H, d), dtype=out_dtype, device=dev)
+    if final_state and kv_final is None:
+        kv_final = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    if not final_state:
+        kv_final = None
+    st = la_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_dev.data_ptr(),
+                    cu_host.data_ptr(), S, T, H, d, in_code, out_code,
+                    dec.ctypes.data, None if kv_init is None else kv_init.data_ptr(),
+                    out.data_ptr(), None if kv_final is None else kv_final.data_ptr(),
+                    _stream_handle(stream, dev))
+    _check(st)
+    return out, kv_final
+
+
+def decode(q, k, v, kv, decay, stream=None, out=None):
+    """One decode token per sequence.  q, k, v: device [B, H, d]; kv: device
+    fp32 [B, H, d, d], updated in place.  Returns o [B, H, d] (q's dtype)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("kv", kv)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype \
+            or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share shape [B, H, d] and dtype")
+    B, H, d = q.shape
+    if kv.dtype != torch.float32 or tuple(kv.shape) != (B, H, d, d):
+        raise ValueError("kv must be fp32 [B, H, d, d]")
+    dec = _host_decay(decay, H)
+    if out is None:
+        out = torch.empty_like(q)
+    st = la_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(), dec.ctypes.data,
+                   B, H, d, _dtype_code(q), out.data_ptr(), _stream_handle(stream, q.device))
+    _check(st)
+    return out

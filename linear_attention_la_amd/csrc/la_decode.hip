@@ -1,0 +1,122 @@
+// Decode kernel: one token per sequence, fp32 state updated in place.
+//
+// The length-1 step that serving keeps in its own kernel, apart from the
+// length > 1 prefill, so the two can run on separate streams (jvyan.cn news
+// article on MiniMax-01, 二、计算优化; CSDN "【AI论文】MiniMax-01:利用闪电注意力
+// 机制扩展基础模型" §3.2).  For each (b, h):
+//   S <- lambda S + k^T v        (update first)
+//   o <- q S                     (read out the updated state)
+// Decay, update and read-out are fused into one pass over the state, so each
+// 64 KiB fp32 state (d = 128) is read once and written once: the kernel is a
+// pure HBM stream (0.5 flop per byte).
+//
+// Layout: one workgroup per (b, h).  Thread t owns the column quad
+// 4*(t % (d/4)) and rows r = t / (d/4) + RP*n; each row of the state is read
+// with float4 loads by d/4 consecutive lanes (coalesced 512 B rows for
+// d = 128).  Row partial sums of o are combined through LDS.
+
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename InT>
+__device__ __forceinline__ float load_in(const InT* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_in<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_in<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+template <typename InT>
+__device__ __forceinline__ void store_o(InT* p, int64_t i, floatx4 x);
+template <>
+__device__ __forceinline__ void store_o<float>(float* p, int64_t i, floatx4 x) {
+  *reinterpret_cast<float4*>(p + i) = make_float4(x[0], x[1], x[2], x[3]);
+}
+template <>
+__device__ __forceinline__ void store_o<uint16_t>(uint16_t* p, int64_t i, floatx4 x) {
+  *reinterpret_cast<uint2*>(p + i) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+}
+
+template <int D, typename InT>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+  constexpr int CQ = D / 4;         // column quads per row
+  constexpr int RP = kThreads / CQ;  // rows handled concurrently
+  constexpr int NR = D / RP;         // rows per thread
+  __shared__ float qs[D], ks[D];
+  __shared__ floatx4 red[RP][CQ];
+
+  const int bh = blockIdx.x;
+  const int h = bh % a.num_heads;
+  const int t = threadIdx.x;
+  const int cq = t % CQ;
+  const int rp = t / CQ;
+  const int64_t vec_off = (int64_t)bh * D;
+  const InT* __restrict__ q = static_cast<const InT*>(a.q);
+  const InT* __restrict__ k = static_cast<const InT*>(a.k);
+  const InT* __restrict__ v = static_cast<const InT*>(a.v);
+  floatx4* __restrict__ S = reinterpret_cast<floatx4*>(a.kv + (int64_t)bh * D * D);
+
+  // Issue the whole state stream first (NR independent 16 B loads/thread).
+  floatx4 sv[NR];
+#pragma unroll
+  for (int n = 0; n < NR; ++n)
+    sv[n] = __builtin_nontemporal_load(&S[(rp + RP * n) * CQ + cq]);
+
+  if (t < D) {
+    qs[t] = load_in(q, vec_off + t);
+    ks[t] = load_in(k, vec_off + t);
+  }
+  floatx4 vv;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vv[m] = load_in(v, vec_off + 4 * cq + m);
+  const float lam = a.decay[h];
+  __syncthreads();
+
+  floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int r = rp + RP * n;
+    const float kr = ks[r], qr = qs[r];
+    floatx4 s;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      s[m] = fmaf(lam, sv[n][m], kr * vv[m]);
+      acc[m] = fmaf(qr, s[m], acc[m]);
+    }
+    __builtin_nontemporal_store(s, &S[r * CQ + cq]);
+  }
+  red[rp][cq] = acc;
+  __syncthreads();
+  if (t < CQ) {
+    floatx4 o = red[0][t];
+#pragma unroll
+    for (int p = 1; p < RP; ++p) o += red[p][t];
+    store_o(static_cast<InT*>(a.o), vec_off + 4 * t, o);
+  }
+}
+
+template <int D>
+hipError_t launch_d(const DecodeArgs& a, la_dtype in_dtype, hipStream_t stream) {
+  const dim3 grid((unsigned)a.batch * (unsigned)a.num_heads), block(kThreads);
+  if (in_dtype == LA_FP32)
+    hipLaunchKernelGGL((decode_kernel<D, float>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, uint16_t>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, la_dtype in_dtype,
+                         hipStream_t stream) {
+  if (head_dim == 64) return launch_d<64>(a, in_dtype, stream);
+  return launch_d<128>(a, in_dtype, stream);
+}
+
+}  // namespace la

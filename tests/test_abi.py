@@ -1,0 +1,165 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+the public header declares, and rejects bad arguments on the host (before
+any HIP call) with the documented status codes."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import linear_attention_la_amd as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            src = open(os.path.join(inc, fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(la_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for n in ("la_prefill", "la_decode", "la_status_str", "la_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = la.lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libla.so does not export {name}"
+
+
+def test_status_strings():
+    assert la.la_status_str(la.LA_OK) == "LA_OK"
+    assert la.la_status_str(la.LA_ERR_INVALID_ARG) == "LA_ERR_INVALID_ARG"
+    assert la.la_status_str(la.LA_ERR_UNSUPPORTED) == "LA_ERR_UNSUPPORTED"
+    assert la.la_status_str(la.LA_ERR_HIP) == "LA_ERR_HIP"
+    assert la.la_status_str(77) == "LA_STATUS_UNKNOWN"
+
+
+# Fake, never-dereferenced device addresses: validation runs on the host only
+# and must reject every case below before touching them.
+Q, K, V, O, KVF, KVI, CUD = (0x10000000 * (i + 1) for i in range(7))
+T, H, D = 100, 4, 128
+BIG = T * H * D * 4  # bytes of one fp32 [T,H,d] tensor
+
+
+def _prefill(**kw):
+    args = dict(q=Q, k=K, v=V, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2, T=T,
+                H=H, d=D, in_dt=la.LA_BF16, out_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), kv_init=None, o=O, kv_final=KVF)
+    args.update(kw)
+    cu = args["cu_host"]
+    dec = args["decay"]
+    st = la.la_prefill(args["q"], args["k"], args["v"], args["cu_dev"],
+                       None if cu is None else cu.ctypes.data, args["S"], args["T"], args["H"],
+                       args["d"], args["in_dt"], args["out_dt"],
+                       None if dec is None else dec.ctypes.data, args["kv_init"], args["o"],
+                       args["kv_final"], None)
+    return st, la.la_last_error()
+
+
+BAD_PREFILL = [
+    ("negative_seqs", dict(S=-1), la.LA_ERR_INVALID_ARG),
+    ("negative_tokens", dict(T=-5), la.LA_ERR_INVALID_ARG),
+    ("tokens_over_int32", dict(T=1 << 31), la.LA_ERR_INVALID_ARG),
+    ("zero_heads", dict(H=0), la.LA_ERR_INVALID_ARG),
+    ("too_many_heads", dict(H=257, decay=np.full(257, 0.9, np.float32)), la.LA_ERR_UNSUPPORTED),
+    ("head_dim_96", dict(d=96), la.LA_ERR_UNSUPPORTED),
+    ("head_dim_zero", dict(d=0), la.LA_ERR_INVALID_ARG),
+    ("bad_in_dtype", dict(in_dt=7), la.LA_ERR_INVALID_ARG),
+    ("bad_out_dtype", dict(out_dt=-1), la.LA_ERR_INVALID_ARG),
+    ("fp32_in_bf16_out", dict(in_dt=la.LA_FP32, out_dt=la.LA_BF16), la.LA_ERR_UNSUPPORTED),
+    ("decay_null", dict(decay=None), la.LA_ERR_INVALID_ARG),
+    ("decay_zero", dict(decay=np.array([0.9, 0.0, 0.9, 0.9], np.float32)), la.LA_ERR_INVALID_ARG),
+    ("decay_above_one", dict(decay=np.array([0.9, 1.0001, 0.9, 0.9], np.float32)),
+     la.LA_ERR_INVALID_ARG),
+    ("decay_nan", dict(decay=np.array([0.9, np.nan, 0.9, 0.9], np.float32)), la.LA_ERR_INVALID_ARG),
+    ("decay_negative", dict(decay=np.array([-0.5, 0.9, 0.9, 0.9], np.float32)),
+     la.LA_ERR_INVALID_ARG),
+    ("cu_host_null", dict(cu_host=None), la.LA_ERR_INVALID_ARG),
+    ("cu_first_nonzero", dict(cu_host=np.array([1, 40, 100], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("cu_decreasing", dict(cu_host=np.array([0, 60, 50], np.int32), T=50), la.LA_ERR_INVALID_ARG),
+    ("cu_last_mismatch", dict(cu_host=np.array([0, 40, 99], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("cu_dev_null", dict(cu_dev=None), la.LA_ERR_INVALID_ARG),
+    ("q_null", dict(q=None), la.LA_ERR_INVALID_ARG),
+    ("o_null", dict(o=None), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_q", dict(o=Q + 64), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_v", dict(o=V - 64), la.LA_ERR_INVALID_ARG),
+    ("kv_final_overlaps_k", dict(kv_final=K + 2), la.LA_ERR_INVALID_ARG),
+    ("kv_final_overlaps_o", dict(kv_final=O + 2), la.LA_ERR_INVALID_ARG),
+    ("kv_final_overlaps_kv_init_partially", dict(kv_init=KVI, kv_final=KVI + 4),
+     la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_kv_init", dict(kv_init=KVI, o=KVI + 16), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_PREFILL, ids=[b[0] for b in BAD_PREFILL])
+def test_prefill_rejects(name, kw, code):
+    st, msg = _prefill(**kw)
+    assert st == code, (st, msg)
+    assert msg, "la_last_error must describe the failure"
+
+
+def test_prefill_zero_sequences_is_noop():
+    st, msg = _prefill(S=0, T=0, cu_host=np.array([0], np.int32), q=None, k=None, v=None, o=None,
+                       kv_final=None, cu_dev=None)
+    assert st == la.LA_OK, msg
+    assert msg == ""
+
+
+def _decode(**kw):
+    args = dict(q=Q, k=K, v=V, kv=KVF, decay=np.full(H, 0.9, np.float32), B=3, H=H, d=D,
+                dt=la.LA_BF16, o=O)
+    args.update(kw)
+    dec = args["decay"]
+    st = la.la_decode(args["q"], args["k"], args["v"], args["kv"],
+                      None if dec is None else dec.ctypes.data, args["B"], args["H"], args["d"],
+                      args["dt"], args["o"], None)
+    return st, la.la_last_error()
+
+
+BAD_DECODE = [
+    ("negative_batch", dict(B=-1), la.LA_ERR_INVALID_ARG),
+    ("zero_heads", dict(H=0), la.LA_ERR_INVALID_ARG),
+    ("head_dim_32", dict(d=32), la.LA_ERR_UNSUPPORTED),
+    ("bad_dtype", dict(dt=3), la.LA_ERR_INVALID_ARG),
+    ("decay_null", dict(decay=None), la.LA_ERR_INVALID_ARG),
+    ("decay_zero", dict(decay=np.array([0.9, 0.9, 0.0, 0.9], np.float32)), la.LA_ERR_INVALID_ARG),
+    ("kv_null", dict(kv=None), la.LA_ERR_INVALID_ARG),
+    ("o_null", dict(o=None), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_kv", dict(o=KVF + 8), la.LA_ERR_INVALID_ARG),
+    ("kv_overlaps_q", dict(kv=Q - 16), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_k", dict(o=K + 2), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_DECODE, ids=[b[0] for b in BAD_DECODE])
+def test_decode_rejects(name, kw, code):
+    st, msg = _decode(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_decode_zero_batch_is_noop():
+    st, msg = _decode(B=0, q=None, k=None, v=None, kv=None, o=None)
+    assert st == la.LA_OK, msg
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """No CPU fallback: a missing library is an error, not a silent path."""
+    from linear_attention_la_amd import _binding
+
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setenv("LA_LIB", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not found"):
+        _binding.lib()
+    monkeypatch.setattr(_binding, "_lib", None)

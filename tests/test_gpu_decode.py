@@ -1,0 +1,137 @@
+"""GPU parity of la_decode, prefill->decode consistency, and the two-stream
+mixed serving step (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import (cu_seqlens, device_qkv, device_states, host_qkv, random_states,
+                       workload)
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_random_states(dev, d, dtype):
+    """Three successive decode steps on random states against the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    B, H = 5, 3
+    decay = np.array([1.0, 0.97, 0.5], np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kv = random_states(B, H, d, 41 + d)
+    kvd = to_dev(kv, torch.float32, dev)
+    kv_ref = kv.astype(np.float64)
+    for step in range(3):
+        say(f"decode d={d} dtype={dtype} step={step}")
+        q, k, v = (x[:B * H].reshape(B, H, d)
+                   for x in host_qkv(B * H, 1, d, 100 * step + d, dtype))
+        o = la.decode(to_dev(q, tdt, dev), to_dev(k, tdt, dev), to_dev(v, tdt, dev), kvd, decay)
+        torch.cuda.synchronize()
+        # the oracle continues from the GPU's fp32 state of the previous step
+        # only through values it computed itself: kv_ref is its own chain
+        o_ref, kv_ref = oracle.decode_batch(q, k, v, kv_ref, decay)
+        tol = 1e-5 if dtype == "fp32" else 1e-2
+        parity.check(to_np(o), o_ref, 1, tol, out_bf16=(dtype == "bf16"), what="decode o")
+        parity.check(to_np(kvd), kv_ref, 1, 1e-5, what="decode kv")
+
+
+def test_prefill_then_decode(dev):
+    """prefill(x[:L]) then decode(x[L]) matches the last row and state of the
+    oracle's prefill over x[:L+1]; the GPU state is carried in place."""
+    import torch
+    import linear_attention_la_amd as la
+
+    H, d = 4, 128
+    lengths = [130, 64, 1, 257]
+    decay = np.array([1.0, 0.99, 0.9, 0.6], np.float32)
+    S = len(lengths)
+    Ls = np.array(lengths)
+    q, k, v = host_qkv(int(Ls.sum() + S), H, d, 77)
+    # sequence s occupies rows [off_s, off_s + L_s + 1): prefix then one decode token
+    offs = np.concatenate([[0], np.cumsum(Ls + 1)])[:-1]
+    pre_idx = np.concatenate([np.arange(o, o + L) for o, L in zip(offs, Ls)])
+    dec_idx = offs + Ls
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    _, kv = la.prefill(qd[pre_idx].contiguous(), kd[pre_idx].contiguous(),
+                       vd[pre_idx].contiguous(), cu_seqlens(lengths), decay)
+    o = la.decode(qd[dec_idx].contiguous(), kd[dec_idx].contiguous(), vd[dec_idx].contiguous(),
+                  kv, decay)
+    torch.cuda.synchronize()
+    full = cu_seqlens(Ls + 1)
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, full, decay, beta=64)
+    parity.check(to_np(o), o_ref[full[1:] - 1], 1, 1e-2, out_bf16=True, what="prefill+decode o")
+    parity.check(to_np(kv), kv_ref, 1, 1e-2, what="prefill+decode kv")
+
+
+def test_decode_full_batch_sampled(dev):
+    """256 sequences x 64 heads x d=128 (the serving batch): sampled
+    (sequence, head) pairs checked one by one against the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload("mixed_decode")
+    B, H, d = w["batch"], w["H"], w["d"]
+    kvd = device_states(B, H, d, w["seed"], dev, scale=0.5)
+    kv0 = kvd.clone()
+    qd, kd, vd = (x.view(B, H, d) for x in device_qkv(B, H, d, w["seed"] + 1, dev))
+    o = la.decode(qd, kd, vd, kvd, w["decay"])
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(9))
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 48), rng.integers(0, H, 48))]
+    pairs += [(0, 0), (B - 1, H - 1)]
+    for b, h in pairs:
+        o_ref, s_ref = oracle.decode_step(to_np(qd[b, h]), to_np(kd[b, h]), to_np(vd[b, h]),
+                                          to_np(kv0[b, h]), w["decay"][h])
+        parity.check(to_np(o[b, h])[None], o_ref[None], 0, 1e-2, out_bf16=True,
+                     what=f"decode ({b},{h}) o")
+        parity.check(to_np(kvd[b, h])[None], s_ref[None], 0, 1e-5, what=f"decode ({b},{h}) kv")
+
+
+def test_two_streams_bitwise(dev):
+    """Decode on one stream concurrently with a packed prefill on another
+    gives exactly the results each gives alone."""
+    import torch
+    import linear_attention_la_amd as la
+
+    wp = workload("mixed_prefill")
+    wd = workload("mixed_decode")
+    B, H, d = wd["batch"], wd["H"], wd["d"]
+    cu = cu_seqlens(wp["lengths"])
+    T = int(cu[-1])
+    say(f"two streams: prefill T={T}, decode B={B}")
+    qp, kp, vp = device_qkv(T, H, d, wp["seed"], dev)
+    qd, kd, vd = (x.view(B, H, d) for x in device_qkv(B, H, d, wd["seed"] + 1, dev))
+    kv_init = device_states(B, H, d, wd["seed"], dev, scale=0.5)
+    cu_dev = torch.from_numpy(cu).to(dev)
+
+    kv_a = kv_init.clone()
+    o_dec_a = la.decode(qd, kd, vd, kv_a, wd["decay"])
+    o_pre_a, kv_pre_a = la.prefill(qp, kp, vp, cu_dev, wp["decay"])
+    torch.cuda.synchronize()
+
+    sp, sd = torch.cuda.Stream(), torch.cuda.Stream()
+    kv_b = kv_init.clone()
+    o_pre_b = torch.empty_like(o_pre_a)
+    kv_pre_b = torch.empty_like(kv_pre_a)
+    o_dec_b = torch.empty_like(o_dec_a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        kv_b.copy_(kv_init)
+        torch.cuda.synchronize()
+        la.prefill(qp, kp, vp, cu_dev, wp["decay"], stream=sp, out=o_pre_b, kv_final=kv_pre_b)
+        la.decode(qd, kd, vd, kv_b, wd["decay"], stream=sd, out=o_dec_b)
+        torch.cuda.synchronize()
+        assert torch.equal(o_dec_a, o_dec_b)
+        assert torch.equal(kv_a, kv_b)
+        assert torch.equal(o_pre_a, o_pre_b)
+        assert torch.equal(kv_pre_a, kv_pre_b)

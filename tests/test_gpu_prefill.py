@@ -1,0 +1,231 @@
+"""GPU parity of la_prefill against the fp64 oracle (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import (cu_seqlens, decay_from_seed, device_qkv, host_int_qkv, host_qkv,
+                       random_states, rne_bf16, workload)
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _run(dev, lengths, H, d, dtype, decay, seed, kv_init=False, out_f32=False, beta=64):
+    import torch
+    import linear_attention_la_amd as la
+
+    say(f"case lengths={list(lengths)[:8]}{'...' if len(lengths) > 8 else ''} H={H} d={d} "
+        f"dtype={dtype} kv_init={kv_init} out_f32={out_f32}")
+    T = int(sum(lengths))
+    q, k, v = host_qkv(T, H, d, seed, dtype)
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(len(lengths), H, d, seed + 7, scale=0.1) if kv_init else None
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd, kd, vd = (to_dev(x, tdt, dev) for x in (q, k, v))
+    kv0d = to_dev(kv0, torch.float32, dev) if kv_init else None
+    o, kv = la.prefill(qd, kd, vd, cu, decay, kv_init=kv0d,
+                       out_dtype=torch.float32 if out_f32 else None)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0, beta=beta)
+    return to_np(o), to_np(kv), o_ref, kv_ref
+
+
+def test_tiny_workload_fp32(dev):
+    """N=256, H=2, d=64, fp32, decay {1.0, 0.9}: relative L2 <= 1e-5."""
+    w = workload("tiny")
+    o, kv, o_ref, kv_ref = _run(dev, w["lengths"], w["H"], w["d"], "fp32", w["decay"], w["seed"],
+                                out_f32=True, beta=32)
+    s1 = parity.check(o, o_ref, 1, 1e-5, what="tiny o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-5, what="tiny kv")
+    say("tiny", s1, s2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kv_init", [False, True])
+def test_fp32_ragged(dev, d, kv_init):
+    lengths = [1, 31, 32, 33, 100, 0, 7]
+    decay = np.array([1.0, 0.95, 0.5], np.float32)
+    o, kv, o_ref, kv_ref = _run(dev, lengths, 3, d, "fp32", decay, 11 + d, kv_init=kv_init,
+                                out_f32=True)
+    parity.check(o, o_ref, 1, 1e-5, what="fp32 ragged o")
+    parity.check(kv, kv_ref, 1, 1e-5, what="fp32 ragged kv")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("out_f32", [False, True])
+@pytest.mark.parametrize("kv_init", [False, True])
+def test_bf16_ragged(dev, d, out_f32, kv_init):
+    """Ragged lengths around the 64-token block (empty, 1, 63..65, several
+    blocks plus a tail), decays from none to strong."""
+    lengths = [1, 63, 64, 65, 129, 0, 300, 17]
+    decay = np.array([1.0, 0.99, 0.9, 0.5], np.float32)
+    o, kv, o_ref, kv_ref = _run(dev, lengths, 4, d, "bf16", decay, 21 + d, kv_init=kv_init,
+                                out_f32=out_f32)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=not out_f32, what="bf16 ragged o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="bf16 ragged kv")
+    say("bf16 ragged", s1, s2)
+
+
+def test_bf16_n8k_all_heads(dev):
+    """B=1, H=64, N=8192, d=128, bf16, seeded decay: every head checked."""
+    w = workload("n8k")
+    o, kv, o_ref, kv_ref = _run(dev, w["lengths"], w["H"], w["d"], "bf16", w["decay"], w["seed"])
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="n8k o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="n8k kv")
+    say("n8k", s1, s2)
+
+
+def test_exact_integer_inputs_bitwise(dev):
+    """Entries in {-1, 0, 1} with decay 1 (sequences up to 256 tokens) or 0.5
+    (up to 12 tokens) keep every intermediate exactly representable, so the
+    GPU must equal the exact result bit for bit (fp32 output) and its
+    round-to-nearest-even bf16 value (bf16 output)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    for lengths, decay in (([256, 100, 37, 0, 1, 64], np.array([1.0, 1.0], np.float32)),
+                           ([12, 5, 1, 9], np.array([0.5, 0.5], np.float32))):
+        say(f"exact case lengths={lengths} decay={decay.tolist()}")
+        T = sum(lengths)
+        q, k, v = host_int_qkv(T, 2, 128, 5)
+        cu = cu_seqlens(lengths)
+        qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+        o32, kv = la.prefill(qd, kd, vd, cu, decay, out_dtype=torch.float32)
+        o16, _ = la.prefill(qd, kd, vd, cu, decay)
+        torch.cuda.synchronize()
+        o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, beta=64)
+        assert np.array_equal(to_np(o32), o_ref)
+        assert np.array_equal(to_np(kv), kv_ref)
+        assert np.array_equal(to_np(o16), rne_bf16(o_ref.astype(np.float32)).astype(np.float64))
+
+
+def test_zero_length_sequences(dev):
+    """All sequences empty: no rows, final state = initial state (or zero)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    H, d = 2, 128
+    kv0 = random_states(3, H, d, 3)
+    kv0d = to_dev(kv0, torch.float32, dev)
+    qd = torch.empty((0, H, d), dtype=torch.bfloat16, device=dev)
+    o, kv = la.prefill(qd, qd.clone(), qd.clone(), [0, 0, 0, 0], [0.9, 1.0], kv_init=kv0d)
+    o2, kv2 = la.prefill(qd, qd.clone(), qd.clone(), [0, 0, 0, 0], [0.9, 1.0])
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, d)
+    assert np.array_equal(to_np(kv), kv0.astype(np.float64))
+    assert np.all(to_np(kv2) == 0.0)
+
+
+def test_continuation_in_place(dev):
+    """Prefill A, then B from A's state (kv_final aliasing kv_init), equals
+    one prefill of A||B within tolerance; both match the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    H, d, L, cut = 4, 128, 1000, 321
+    decay = np.array([1.0, 0.99, 0.9, 0.7], np.float32)
+    q, k, v = host_qkv(L, H, d, 31)
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    o_full, kv_full = la.prefill(qd, kd, vd, [0, L], decay)
+    o_a, kv = la.prefill(qd[:cut].contiguous(), kd[:cut].contiguous(), vd[:cut].contiguous(),
+                         [0, cut], decay)
+    o_b, kv_b = la.prefill(qd[cut:].contiguous(), kd[cut:].contiguous(), vd[cut:].contiguous(),
+                           [0, L - cut], decay, kv_init=kv, kv_final=kv)
+    torch.cuda.synchronize()
+    assert kv_b.data_ptr() == kv.data_ptr()
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, np.array([0, L]), decay, beta=64)
+    o_split = np.concatenate([to_np(o_a), to_np(o_b)])
+    parity.check(o_split, o_ref, 1, 1e-2, out_bf16=True, what="continuation o")
+    parity.check(to_np(kv), kv_ref, 1, 1e-2, what="continuation kv")
+    parity.check(o_split, to_np(o_full), 1, 1e-2, out_bf16=True, what="split vs full")
+
+
+def test_determinism_bitwise(dev):
+    """Two runs of the same launch agree bit for bit (no atomics)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload("n8k")
+    qd, kd, vd = device_qkv(8192, 64, 128, w["seed"], dev)
+    o1, kv1 = la.prefill(qd, kd, vd, [0, 8192], w["decay"])
+    o2, kv2 = la.prefill(qd, kd, vd, [0, 8192], w["decay"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(kv1, kv2)
+
+
+def _check_heads(dev, qd, kd, vd, cu, decay, o, kv, heads, beta=256, what=""):
+    """Full oracle check of the listed heads of a large device-resident run."""
+    for h in heads:
+        q = to_np(qd[:, h, :])[:, None, :]
+        k = to_np(kd[:, h, :])[:, None, :]
+        v = to_np(vd[:, h, :])[:, None, :]
+        o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, np.array([decay[h]]), beta=beta)
+        s1 = parity.check(to_np(o[:, h, :])[:, None, :], o_ref, 1, 1e-2, out_bf16=True,
+                          what=f"{what} o head {h}")
+        s2 = parity.check(to_np(kv[:, h])[:, None], kv_ref, 1, 1e-2, what=f"{what} kv head {h}")
+        say(what, "head", h, s1, s2)
+
+
+@pytest.mark.parametrize("name", ["sweep1024", "sweep4096", "sweep16384", "sweep65536",
+                                  "sweep65536_nodecay"])
+def test_length_sweep(dev, name):
+    """B=1, H=64, d=128, N in {1K, 4K, 16K, 64K} (+ no decay at 64K): a spread
+    of heads checked against the oracle over the whole sequence."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload(name)
+    N = w["lengths"][0]
+    say(f"sweep {name} N={N}")
+    qd, kd, vd = device_qkv(N, 64, 128, w["seed"], dev)
+    o, kv = la.prefill(qd, kd, vd, [0, N], w["decay"])
+    torch.cuda.synchronize()
+    _check_heads(dev, qd, kd, vd, np.array([0, N]), w["decay"], o, kv, [0, 21, 42, 63],
+                 what=name)
+
+
+def test_one_million_tokens(dev):
+    """B=1, H=64, N=1,048,576, d=128 in the benchmark's launch configuration;
+    two heads (strongest and weakest decay) checked over all 1M tokens."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload("n1m")
+    N = w["lengths"][0]
+    say("n1m: generating inputs")
+    qd, kd, vd = device_qkv(N, 64, 128, w["seed"], dev)
+    o, kv = la.prefill(qd, kd, vd, [0, N], w["decay"])
+    torch.cuda.synchronize()
+    say("n1m: kernel done, checking")
+    assert torch.isfinite(o).all()
+    heads = [int(np.argmin(w["decay"])), int(np.argmax(w["decay"]))]
+    _check_heads(dev, qd, kd, vd, np.array([0, N]), w["decay"], o, kv, heads, beta=256,
+                 what="n1m")
+    del qd, kd, vd, o, kv
+    torch.cuda.empty_cache()
+
+
+def test_varlen_64_sequences(dev):
+    """64 sequences, lengths log-uniform in [512, 131072], packed: every
+    sequence of two heads checked."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload("varlen64")
+    cu = cu_seqlens(w["lengths"])
+    T = int(cu[-1])
+    say(f"varlen64 T={T}")
+    qd, kd, vd = device_qkv(T, 64, 128, w["seed"] + 1, dev)
+    o, kv = la.prefill(qd, kd, vd, cu, w["decay"])
+    torch.cuda.synchronize()
+    _check_heads(dev, qd, kd, vd, cu, w["decay"], o, kv, [5, 50], beta=256, what="varlen64")
+    del qd, kd, vd, o, kv
+    torch.cuda.empty_cache()
