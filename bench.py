@@ -27,7 +27,6 @@ One JSON line is printed with the contract fields plus:
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -176,7 +175,8 @@ def bench_mixed(dev, dec_state, reps=10):
     t0 = time.perf_counter()
     for i in range(reps):
         ev["p0"][i].record(sp)
-        la.prefill(qp, kp, vp, cu_dev, wp["decay"], stream=sp, out=op, kv_final=kvp)
+        la.prefill(qp, kp, vp, cu_dev, wp["decay"], stream=sp, out=op, kv_final=kvp,
+                   cu_seqlens_host=cu)
         ev["p1"][i].record(sp)
         ev["d0"][i].record(sd)
         la.decode(q, k, v, kv, wd["decay"], stream=sd, out=out)
@@ -210,7 +210,8 @@ def bench_sweep(dev, reps=5):
         cu_dev = torch.from_numpy(cu).to(dev)
         o = torch.empty_like(q)
         kvf = torch.empty((len(w["lengths"]), H, D, D), dtype=torch.float32, device=dev)
-        run = lambda i: la.prefill(q, k, v, cu_dev, w["decay"], out=o, kv_final=kvf)  # noqa
+        run = lambda i: la.prefill(q, k, v, cu_dev, w["decay"], out=o, kv_final=kvf,  # noqa
+                                   cu_seqlens_host=cu)
         run(0)
         t = timed_launches(run, reps, s, flush=lambda: scratch.zero_())
         by = prefill_bytes(T, len(w["lengths"]))
@@ -230,6 +231,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip decode/mixed/sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -239,9 +242,17 @@ def main():
     import torch
 
     import linear_attention_la_amd as la
-    from la_inputs import decay_from_seed, device_qkv, workload
+    from la_inputs import device_qkv, workload
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}))
+        return
     la.lib()
     w = workload("n8k")
     N = w["lengths"][0]
@@ -255,7 +266,7 @@ def main():
 
     def step(i):
         q, k, v = sets[i & 1]
-        la.prefill(q, k, v, cu_dev, decay, out=o, kv_final=kvf)
+        la.prefill(q, k, v, cu_dev, decay, out=o, kv_final=kvf, cu_seqlens_host=cu_host)
 
     for i in range(args.warmup):
         step(i)

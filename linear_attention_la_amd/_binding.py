@@ -123,14 +123,17 @@ def _host_decay(decay, num_heads):
 
 
 def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=None,
-            final_state=True, out=None, kv_final=None):
+            final_state=True, out=None, kv_final=None, cu_seqlens_host=None):
     """Packed varlen prefill.  q, k, v: device [T, H, d] (bf16 or fp32, same
     dtype, contiguous).  cu_seqlens: [S+1] int (host or device).  decay: host
     [H] floats in (0, 1].  kv_init: device fp32 [S, H, d, d] or None.
 
     Returns (o [T, H, d], kv_final [S, H, d, d] or None).  ``out`` and
     ``kv_final`` may supply preallocated outputs; ``kv_final`` may be
-    ``kv_init`` itself (in-place continuation)."""
+    ``kv_init`` itself (in-place continuation).  When cu_seqlens is a device
+    tensor, passing its host copy as ``cu_seqlens_host`` (a CPU int32 tensor or
+    array with the same contents) avoids a device-to-host copy, which would
+    synchronise the stream on every call."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -145,7 +148,15 @@ def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=Non
     if out_dtype is None:
         out_dtype = q.dtype
     out_code = LA_BF16 if out_dtype == torch.bfloat16 else LA_FP32
-    if isinstance(cu_seqlens, torch.Tensor):
+    if cu_seqlens_host is not None:
+        cu_host = torch.as_tensor(np.ascontiguousarray(
+            cu_seqlens_host.cpu().numpy() if isinstance(cu_seqlens_host, torch.Tensor)
+            else cu_seqlens_host, dtype=np.int32))
+        if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda
+                and cu_seqlens.dtype == torch.int32 and cu_seqlens.is_contiguous()):
+            raise ValueError("cu_seqlens_host needs cu_seqlens as a contiguous int32 device tensor")
+        cu_dev = cu_seqlens
+    elif isinstance(cu_seqlens, torch.Tensor):
         cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
         cu_dev = cu_seqlens if (cu_seqlens.is_cuda and cu_seqlens.dtype == torch.int32
                                 and cu_seqlens.is_contiguous()) else cu_host.to(dev)

@@ -12,18 +12,25 @@
 //   S_b+1  = lambda^ell S_b + K_b^T diag(lambda^(ell-1-j)) V_b
 // The per-token cumsum is replaced by this per-block state chain.
 //
-// Decomposition.  One workgroup (4 waves) owns one (sequence, head, 32-column
+// Decomposition.  One workgroup (8 waves) owns one (sequence, head, 32-column
 // slice of the value dimension) chain; the d x d state is split by value
 // columns over d/32 workgroups, each of which recomputes Q K^T for its block
-// so that no cross-workgroup exchange exists.  Inside a block, wave w owns
-// the query strip i in [16w, 16w+16): it forms its strip of scores
-// S^T = K Q^T, applies the mask and decay in registers, and feeds them
-// straight back into the MFMA as the B operand of O^T = V^T P^T (the score
-// tile's accumulator layout -- 4 consecutive keys per lane -- is a valid
-// operand layout when the value operand uses the same key order), then adds
-// diag(lambda^(i+1)) (S^T Q^T).  The state's 16x16 tiles are spread over the
-// four waves (more tiles to the waves with shorter causal strips) and stay in
-// fp32 accumulators for the whole chain.
+// so that no cross-workgroup exchange exists.  Within the workgroup:
+//  * strip waves 0..3: wave k owns query rows i in [16k, 16k+16).  It forms
+//    its strip of scores S^T = K Q^T, applies mask and decay in registers and
+//    feeds them straight back into the MFMA as the B operand of O^T = V^T P^T
+//    (the score tile's accumulator layout -- 4 consecutive keys per lane -- is
+//    a valid operand layout when the value operand uses the same key order),
+//    adds diag(lambda^(i+1)) S^T Q^T and writes its rows of O;
+//  * state waves 4..7: own 16-row tiles of the 32-column state slice in fp32
+//    accumulators for the whole chain and advance them by K^T Vd; they also
+//    move Q, K and V from HBM into LDS, one block ahead.
+// Wave k and wave k+4 share a SIMD; state rows are dealt so that the MFMA
+// work per SIMD is nearly even (strips near the diagonal are shorter).
+// LDS stages are double-buffered: block b+1 is loaded from HBM while block b
+// is computed, so each block needs one workgroup barrier.  Only the state
+// waves load and only the strip waves store, and the barrier waits for LDS
+// traffic alone, so no wave ever waits for its own stores to reach HBM.
 //
 // Precision.  The three intermediate operands that are not inputs -- P, the
 // state as the operand of Q S, and the decayed V rows -- are each carried as
@@ -31,18 +38,23 @@
 // two MFMAs, so they enter the products with ~16 significant bits; inputs
 // are bf16 already and every sum is fp32.  The state is stored in fp32.
 //
-// LDS (bf16 bits unless noted):
-//   Qs, Ks  [64][d+16]   row-major; K is also read transposed by
-//                        ds_read_b64_tr_b16 for the K^T operand
-//   Vs      [64][32+16]  the slice of V (row-major, read transposed)
-//   Vh, Vl  [64][32+16]  lambda^(ell-1-j)-scaled V rows, hi/lo
-//   Sh, Sl  [2][32][d+8] state^T hi/lo for the Q S product, double-buffered
+// LDS (bf16 bits):
+//   Qs, Ks  [2][64][d]    rows with 16 B chunks XOR-swizzled per row, so that
+//                         16 consecutive rows of one chunk (MFMA operand
+//                         reads) and 8 consecutive rows of two chunks
+//                         (transposed reads of K) hit distinct banks
+//   Vs, Vh, Vl [2][64][48] the value slice, and its lambda^(ell-1-j)-scaled
+//                         rows as hi/lo (row stride 96 B: conflict-free
+//                         transposed reads)
+//   Sh, Sl  [2][32][d+8]  state^T hi/lo for the Q S product
 // MFMA operand layout (16x16x32 bf16): lane l supplies row (l % 16) of A and
 // column (l % 16) of B, 8 k-values per lane in lane group g = l / 16; the 4
 // results of lane l sit at rows 4g + m, column l % 16.  The order of the 8
 // k-values is free as long as A and B agree.
 // ds_read_b64_tr_b16: in each 16-lane group, lane 4r + a gives the address
 // of 4 elements of row r; lane i receives element i of each of the 4 rows.
+
+#include <type_traits>
 
 #include "la_device.h"
 #include "la_internal.h"
@@ -51,8 +63,9 @@ namespace la {
 namespace {
 
 constexpr int kBeta = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kDV = kBf16Cols;  // 32 value columns per workgroup
+constexpr int kVS = 48;         // V row stride (elements)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -98,40 +111,70 @@ __device__ __forceinline__ bf16x8 cat2(uint2 a, uint2 b) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// State tiles (16x16, index n -> row tile n/2, column tile n%2) owned by each
-// wave.  Waves with long causal strips get fewer tiles so the MFMA work per
-// wave is even.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Swizzle of the 16 B chunks of a Q/K row.  The LDS serves 128 B per clock
+// (32 banks): a 16 B read is served 8 lanes at a time, an 8 B read 16 lanes
+// at a time.  Chunk c of row r is stored at chunk c ^ swz(r), which keeps
+//  * 8 consecutive rows of one chunk (MFMA operand reads, 16 B/lane) and
+//  * 4 consecutive rows of an aligned chunk pair (transposed reads of K,
+//    8 B/lane, 16 lanes)
+// on distinct banks.  Every row is a multiple of 128 B long.
 template <int D>
-struct TileSplit;
+__device__ __forceinline__ int swz(int r) {
+  return 2 * (r & 3) + ((r >> 2) & 1);
+}
+// Element offset of 16 B chunk c of row r.
+template <int D>
+__device__ __forceinline__ int qk_off(int r, int c) {
+  return r * D + 8 * (c ^ swz<D>(r));
+}
+
+// State row tiles (16 rows x both 16-column tiles) owned by state wave k.
+// The strip wave on the same SIMD has a causal strip of k+1 score tiles, so
+// state waves beside long strips get fewer row tiles.
+template <int D>
+struct RowSplit;
 template <>
-struct TileSplit<128> {
-  static constexpr int kMax = 6;
-  __device__ static int begin(int w) { return w == 0 ? 0 : w == 1 ? 6 : w == 2 ? 11 : 14; }
-  __device__ static int end(int w) { return w == 0 ? 6 : w == 1 ? 11 : w == 2 ? 14 : 16; }
-};
-template <>
-struct TileSplit<64> {
+struct RowSplit<128> {  // 8 row tiles: 3, 3, 1, 1
   static constexpr int kMax = 3;
-  __device__ static int begin(int w) { return w == 0 ? 0 : w == 1 ? 3 : w == 2 ? 6 : 7; }
-  __device__ static int end(int w) { return w == 0 ? 3 : w == 1 ? 6 : w == 2 ? 7 : 8; }
+  __device__ static int begin(int k) { return k == 0 ? 0 : k == 1 ? 3 : k == 2 ? 6 : 7; }
+  __device__ static int end(int k) { return k == 0 ? 3 : k == 1 ? 6 : k == 2 ? 7 : 8; }
 };
+template <>
+struct RowSplit<64> {  // 4 row tiles: 2, 1, 1, 0
+  static constexpr int kMax = 2;
+  __device__ static int begin(int k) { return k == 0 ? 0 : k == 1 ? 2 : k == 2 ? 3 : 4; }
+  __device__ static int end(int k) { return k == 0 ? 2 : k == 1 ? 3 : 4; }
+};
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every outstanding global store and load of the wave (vmcnt(0)); here the
+// waves that store O never need to wait for those stores, and the waves that
+// prefetch the next block wait for their loads only where they use them.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int N>
+using IC = std::integral_constant<int, N>;
 
 template <int D, bool kOutF32>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NDV = D / kDV;
-  constexpr int KS = D + 16;      // Qs/Ks row stride
-  constexpr int VS = kDV + 16;    // V row stride
-  constexpr int SS = D + 8;       // state^T row stride
-  constexpr int NK = D / 32;      // k-steps over d
-  constexpr int CH = D / 8;       // 16 B chunks per Q/K row
-  constexpr int NQC = CH / 4;     // Q (and K) chunks staged per thread
-  constexpr int MAXT = TileSplit<D>::kMax;
+  constexpr int SS = D + 8;        // state^T row stride
+  constexpr int NK = D / 32;       // k-steps over d
+  constexpr int CH = D / 8;        // 16 B chunks per Q/K row
+  constexpr int NQC = CH / 4;      // Q (and K) chunks staged per state thread
+  constexpr int MAXR = RowSplit<D>::kMax;
+  constexpr int QKSZ = kBeta * D;
+  constexpr int VSZ = kBeta * kVS;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBeta * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBeta * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBeta * VS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vh[kBeta * VS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vl[kBeta * VS];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][QKSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][QKSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][VSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Vh[2][VSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Vl[2][VSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Sh[2][kDV * SS];
   __shared__ __attribute__((aligned(16))) uint16_t Sl[2][kDV * SS];
 
@@ -143,181 +186,203 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   const int s = sh / H;
   const int c0 = cs * kDV;
   const int t = threadIdx.x;
-  const int w = t >> 6;
+  const int wid = uniform(t >> 6);
+  const bool strip = wid < 4;
+  const int k = wid & 3;      // strip index, or state-wave index
   const int l = t & 63;
   const int li = l & 15;
   const int g = l >> 4;
-  const int tr_r = li >> 2;  // row supplied to a transposed read
-  const int tr_a = li & 3;   // 4-element chunk supplied to a transposed read
+  const int tr_r = li >> 2;   // row supplied to a transposed read
+  const int tr_a = li & 3;    // 4-element piece supplied to a transposed read
 
   const int64_t start = a.cu_seqlens[s];
   const int64_t end = a.cu_seqlens[s + 1];
+  const int nblocks = (int)((end - start + kBeta - 1) / kBeta);
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* __restrict__ k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ v = static_cast<const uint16_t*>(a.v);
   const int64_t state_off = ((int64_t)s * H + h) * D * D;
-  const int64_t row_stride = (int64_t)H * D;  // elements between tokens
+  const int row_stride = H * D;  // elements between tokens (< 2^15)
   const float l2 = a.log2_decay[h];
+  const float lam_beta = exp2f((float)kBeta * l2);
 
-  // Per-lane decay factors of the score strip.  Element (i, j) of tile
-  // (ti = w, tj) has i - j = 16 (w - tj) + (li - 4g - m).
+  // ---- per-lane decay factors (strip waves) ----
+  // Element (i, j) of score tile (k, tj) has i - j = 16 (k - tj) + (li-4g-m):
   //   diagonal tile:     lambda^(li-4g-m) if >= 0, else 0
-  //   tile with w > tj:  lambda^(16 (w-tj-1)) * lambda^(16 + li - 4g - m)
+  //   tile with k > tj:  lambda^(16 (k-tj-1)) * lambda^(16 + li - 4g - m)
   // (no negative exponents, so no overflow for small lambda).
-  floatx4 fdiag, foff;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int x = li - 4 * g - m;
-    fdiag[m] = x >= 0 ? exp2f((float)x * l2) : 0.0f;
-    foff[m] = exp2f((float)(16 + x) * l2);
-  }
-  const float f16 = exp2f(16.0f * l2);
-  const float qdecay = exp2f((float)(16 * w + li + 1) * l2);  // lambda^(i+1)
-
-  // State tiles of this wave, fp32, in accumulator layout.
-  const int tb = TileSplit<D>::begin(w);
-  const int te = TileSplit<D>::end(w);
-  floatx4 st[MAXT];
-#pragma unroll
-  for (int n = 0; n < MAXT; ++n) {
-    const int tile = tb + n;
-    const int tr = tile >> 1, tc = tile & 1;
+  floatx4 fdiag, foff[3];
+  {
+    const float f16 = exp2f(16.0f * l2);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const int r = 16 * tr + 4 * g + m;
-      st[n][m] = (tile < te && a.kv_init)
-                     ? a.kv_init[state_off + (int64_t)r * D + c0 + 16 * tc + li]
-                     : 0.0f;
+      const int x = li - 4 * g - m;
+      fdiag[m] = x >= 0 ? exp2f((float)x * l2) : 0.0f;
+      foff[0][m] = exp2f((float)(16 + x) * l2);
+      foff[1][m] = foff[0][m] * f16;
+      foff[2][m] = foff[1][m] * f16;
     }
-    if (tile < te) {
-      uint2 hi, lo;
-      split4(st[n], hi, lo);
-      *reinterpret_cast<uint2*>(&Sh[0][(16 * tc + li) * SS + 16 * tr + 4 * g]) = hi;
-      *reinterpret_cast<uint2*>(&Sl[0][(16 * tc + li) * SS + 16 * tr + 4 * g]) = lo;
+  }
+  const float qdecay = exp2f((float)(16 * k + li + 1) * l2);  // lambda^(i+1)
+
+  // ---- state row tiles (state waves), fp32 accumulator layout ----
+  // st[n][tc]: rows 16 (rb + n) + 4g + m, column 16 tc + li of the slice.
+  const int rb = RowSplit<D>::begin(k);
+  const int re = strip ? rb : RowSplit<D>::end(k);
+  floatx4 st[MAXR][2];
+#pragma unroll
+  for (int n = 0; n < MAXR; ++n) {
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc) {
+      st[n][tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int tr = rb + n;
+      if (tr < re) {
+        if (a.kv_init) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            st[n][tc][m] =
+                a.kv_init[state_off + (int64_t)(16 * tr + 4 * g + m) * D + c0 + 16 * tc + li];
+        }
+        uint2 hi, lo;
+        split4(st[n][tc], hi, lo);
+        const int so = (16 * tc + li) * SS + 16 * tr + 4 * g;
+        *reinterpret_cast<uint2*>(&Sh[0][so]) = hi;
+        *reinterpret_cast<uint2*>(&Sl[0][so]) = lo;
+      }
     }
   }
 
-  // Staging roles.  Q/K chunk p of thread t: id = t + 256 p, row id / CH,
-  // 16 B chunk id % CH (a wave covers whole rows: coalesced).  V: row t / 4,
-  // chunk t % 4 of the 32-column slice.
-  const int vrow = t >> 2;
-  const int vch = t & 3;
+  // ---- staging: the state waves move Q, K and V; strip waves only store O ----
+  // State thread u = t - 256: Q/K chunk p has id = u + 256 p, row id / CH,
+  // chunk id % CH (a wave reads whole rows: coalesced); V: row u / 4, chunk
+  // u % 4 of the 32-column value slice.
+  const int u = t - 256;
+  const int vrow = u >> 2;
+  const int vch = u & 3;
   uint4 qreg[NQC], kreg[NQC], vreg;
 
   auto load_block = [&](int64_t b0, int ell) {
+    const uint16_t* qb0 = q + b0 * row_stride + (int64_t)h * D;
+    const uint16_t* kb0 = kp + b0 * row_stride + (int64_t)h * D;
+    const uint16_t* vb0 = v + b0 * row_stride + (int64_t)h * D + c0;
 #pragma unroll
     for (int p = 0; p < NQC; ++p) {
-      const int id = t + kThreads * p;
+      const int id = u + 256 * p;
       const int row = id / CH;
+      const int off = row * row_stride + 8 * (id % CH);
       if (row < ell) {
-        const int64_t off = (b0 + row) * row_stride + (int64_t)h * D + 8 * (id % CH);
-        qreg[p] = *reinterpret_cast<const uint4*>(q + off);
-        kreg[p] = *reinterpret_cast<const uint4*>(k + off);
+        qreg[p] = *reinterpret_cast<const uint4*>(qb0 + off);
+        kreg[p] = *reinterpret_cast<const uint4*>(kb0 + off);
       } else {
         qreg[p] = make_uint4(0, 0, 0, 0);
         kreg[p] = make_uint4(0, 0, 0, 0);
       }
     }
-    vreg = vrow < ell ? *reinterpret_cast<const uint4*>(v + (b0 + vrow) * row_stride +
-                                                         (int64_t)h * D + c0 + 8 * vch)
+    vreg = vrow < ell ? *reinterpret_cast<const uint4*>(vb0 + vrow * row_stride + 8 * vch)
                       : make_uint4(0, 0, 0, 0);
   };
 
-  int64_t b0 = start;
-  int ell = (int)((end - b0) < kBeta ? (end - b0) : kBeta);
-  if (b0 < end) load_block(b0, ell);
-
-  for (int bi = 0; b0 < end; ++bi) {
-    const int cur = bi & 1;
-    const bool full = ell == kBeta;
-    __syncthreads();  // the previous block is done with every staged tile
-
-    // ---- stage the block ----
+  auto store_block = [&](int buf, int ell) {
 #pragma unroll
     for (int p = 0; p < NQC; ++p) {
-      const int id = t + kThreads * p;
-      const int row = id / CH, col = 8 * (id % CH);
-      *reinterpret_cast<uint4*>(&Qs[row * KS + col]) = qreg[p];
-      *reinterpret_cast<uint4*>(&Ks[row * KS + col]) = kreg[p];
+      const int id = u + 256 * p;
+      const int o = qk_off<D>(id / CH, id % CH);
+      *reinterpret_cast<uint4*>(&Qs[buf][o]) = qreg[p];
+      *reinterpret_cast<uint4*>(&Ks[buf][o]) = kreg[p];
     }
-    {
-      *reinterpret_cast<uint4*>(&Vs[vrow * VS + 8 * vch]) = vreg;
-      // V row scaled by lambda^(ell-1-j), split hi/lo.
-      const float wv = vrow < ell ? exp2f((float)(ell - 1 - vrow) * l2) : 0.0f;
-      const uint32_t wds[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
-      uint32_t hp[4], lp[4];
+    const int o = vrow * kVS + 8 * vch;
+    *reinterpret_cast<uint4*>(&Vs[buf][o]) = vreg;
+    // value row scaled by lambda^(ell-1-j), split hi/lo
+    const float wv = vrow < ell ? exp2f((float)(ell - 1 - vrow) * l2) : 0.0f;
+    const uint32_t wd[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
+    uint32_t hp[4], lp[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = bf16_lo(wds[e]) * wv, x1 = bf16_hi(wds[e]) * wv;
-        const uint32_t hh = cvt2(x0, x1);
-        hp[e] = hh;
-        lp[e] = cvt2(x0 - bf16_lo(hh), x1 - bf16_hi(hh));
-      }
-      *reinterpret_cast<uint4*>(&Vh[vrow * VS + 8 * vch]) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
-      *reinterpret_cast<uint4*>(&Vl[vrow * VS + 8 * vch]) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = bf16_lo(wd[e]) * wv, x1 = bf16_hi(wd[e]) * wv;
+      const uint32_t hh = cvt2(x0, x1);
+      hp[e] = hh;
+      lp[e] = cvt2(x0 - bf16_lo(hh), x1 - bf16_hi(hh));
     }
+    *reinterpret_cast<uint4*>(&Vh[buf][o]) = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+    *reinterpret_cast<uint4*>(&Vl[buf][o]) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+  };
 
-    // ---- prefetch the next block ----
-    const int64_t nb0 = b0 + kBeta;
-    const int nell = nb0 < end ? (int)((end - nb0) < kBeta ? (end - nb0) : kBeta) : 0;
-    if (nb0 < end) load_block(nb0, nell);
-    __syncthreads();
+  auto block_len = [&](int b) -> int {
+    const int64_t rem = end - (start + (int64_t)b * kBeta);
+    return rem < kBeta ? (int)rem : kBeta;
+  };
 
-    // ---- query strip operands ----
+  // ---- one block of a strip wave (strip index KS fixed at compile time) ----
+  auto strip_body = [&](auto KS_, int cur, int64_t b0, int ell) {
+    constexpr int KS = decltype(KS_)::value;
+    const uint16_t* Qc = Qs[cur];
+    const uint16_t* Kc = Ks[cur];
+    const uint16_t* Vc = Vs[cur];
     bf16x8 qb[NK];
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qb[kk] = ld8(&Qs[(16 * w + li) * KS + 32 * kk + 8 * g]);
+    for (int kk = 0; kk < NK; ++kk) qb[kk] = ld8(&Qc[qk_off<D>(16 * KS + li, 4 * kk + g)]);
 
-    // ---- scores S^T = K Q^T for tiles tj <= w; mask, decay, hi/lo ----
+    // scores S^T = K Q^T for tiles tj <= KS (independent chains interleaved)
+    floatx4 sc[KS + 1];
+#pragma unroll
+    for (int tj = 0; tj <= KS; ++tj) sc[tj] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+      for (int tj = 0; tj <= KS; ++tj)
+        sc[tj] = mfma(ld8(&Kc[qk_off<D>(16 * tj + li, 4 * kk + g)]), qb[kk], sc[tj]);
+    // mask, decay, hi/lo
     uint2 ph[4], pl[4];
 #pragma unroll
     for (int tj = 0; tj < 4; ++tj) {
-      ph[tj] = make_uint2(0, 0);
-      pl[tj] = make_uint2(0, 0);
-      if (tj <= w) {
-        floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk)
-          acc = mfma(ld8(&Ks[(16 * tj + li) * KS + 32 * kk + 8 * g]), qb[kk], acc);
-        floatx4 f;
-        if (tj == w) {
-          f = fdiag;
-        } else {
-          const int dd = w - tj - 1;  // 0, 1, 2
-          const float sc = dd == 0 ? 1.0f : dd == 1 ? f16 : f16 * f16;
-          f = foff * sc;
-        }
-        split4(acc * f, ph[tj], pl[tj]);
+      if (tj <= KS) {
+        const floatx4 f = tj == KS ? fdiag : foff[KS - tj - 1 < 0 ? 0 : KS - tj - 1];
+        split4(sc[tj] * f, ph[tj], pl[tj]);
+      } else {
+        ph[tj] = make_uint2(0, 0);
+        pl[tj] = make_uint2(0, 0);
       }
     }
 
-    // ---- O^T = V^T P^T + lambda^(i+1) S^T Q^T, two value-column tiles ----
+    // O^T = V^T P^T + lambda^(i+1) S^T Q^T for the two value-column tiles
+    constexpr int NJ = KS / 2 + 1;  // 32-key chunks with nonzero scores
+    floatx4 oi[2], oe[2];
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc) {
-      floatx4 oi = {0.0f, 0.0f, 0.0f, 0.0f};
-      floatx4 oe = {0.0f, 0.0f, 0.0f, 0.0f};
+      oi[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      oe[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
-      for (int kk2 = 0; kk2 < 2; ++kk2) {
-        if (2 * kk2 <= w) {
-          const int j0 = 32 * kk2 + 4 * g;
-          const bf16x8 va = cat(ld_tr(&Vs[(j0 + tr_r) * VS + 16 * tc + 4 * tr_a]),
-                                ld_tr(&Vs[(j0 + 16 + tr_r) * VS + 16 * tc + 4 * tr_a]));
-          oi = mfma(va, cat2(ph[2 * kk2], ph[2 * kk2 + 1]), oi);
-          oi = mfma(va, cat2(pl[2 * kk2], pl[2 * kk2 + 1]), oi);
-        }
-      }
+    for (int kk2 = 0; kk2 < NJ; ++kk2) {
+      const int j0 = 32 * kk2 + 4 * g + tr_r;
+      const bf16x8 p_h = cat2(ph[2 * kk2], ph[2 * kk2 + 1]);
+      const bf16x8 p_l = cat2(pl[2 * kk2], pl[2 * kk2 + 1]);
 #pragma unroll
-      for (int kk = 0; kk < NK; ++kk) {
-        const int off = (16 * tc + li) * SS + 32 * kk + 8 * g;
-        oe = mfma(ld8(&Sh[cur][off]), qb[kk], oe);
-        oe = mfma(ld8(&Sl[cur][off]), qb[kk], oe);
+      for (int tc = 0; tc < 2; ++tc) {
+        const bf16x8 va = cat(ld_tr(&Vc[j0 * kVS + 16 * tc + 4 * tr_a]),
+                              ld_tr(&Vc[(j0 + 16) * kVS + 16 * tc + 4 * tr_a]));
+        oi[tc] = mfma(va, p_h, oi[tc]);
+        oi[tc] = mfma(va, p_l, oi[tc]);
       }
-      const int i = 16 * w + li;
-      if (i < ell) {
+    }
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        const int so = (16 * tc + li) * SS + 32 * kk + 8 * g;
+        oe[tc] = mfma(ld8(&Sh[cur][so]), qb[kk], oe[tc]);
+        oe[tc] = mfma(ld8(&Sl[cur][so]), qb[kk], oe[tc]);
+      }
+    }
+    const int i = 16 * KS + li;
+    if (i < ell) {
+      const int64_t orow = (b0 + i) * (int64_t)row_stride + (int64_t)h * D + c0;
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
         float out[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) out[m] = fmaf(qdecay, oe[m], oi[m]);
-        const int64_t off = (b0 + i) * row_stride + (int64_t)h * D + c0 + 16 * tc + 4 * g;
+        for (int m = 0; m < 4; ++m) out[m] = fmaf(qdecay, oe[tc][m], oi[tc][m]);
+        const int64_t off = orow + 16 * tc + 4 * g;
         if constexpr (kOutF32) {
           *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off) =
               make_float4(out[0], out[1], out[2], out[3]);
@@ -327,52 +392,113 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         }
       }
     }
+  };
 
-    // ---- state: S <- lambda^ell S + K^T Vd, then its bf16 hi/lo copy ----
-    const float fl = full ? exp2f(64.0f * l2) : exp2f((float)ell * l2);
+  // ---- one block of a state wave (NR row tiles fixed at compile time) ----
+  auto state_body = [&](auto NR_, int cur, int ell) {
+    constexpr int NR = decltype(NR_)::value;
+    const uint16_t* Kc = Ks[cur];
+    const uint16_t* Hc = Vh[cur];
+    const uint16_t* Lc = Vl[cur];
+    const float fl = ell == kBeta ? lam_beta : exp2f((float)ell * l2);
+    // decayed-V operands of both column tiles and both key halves
+    bf16x8 vh[2][2], vl[2][2];
 #pragma unroll
-    for (int n = 0; n < MAXT; ++n) {
-      const int tile = tb + n;
-      if (tile < te) {
-        const int tr = tile >> 1, tc = tile & 1;
-        floatx4 acc = st[n] * fl;
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
 #pragma unroll
-        for (int kk2 = 0; kk2 < 2; ++kk2) {
-          const int j0 = 32 * kk2 + 8 * g;
-          const int ko = 16 * tr + 4 * tr_a;
-          const int vo = 16 * tc + 4 * tr_a;
-          const bf16x8 ka = cat(ld_tr(&Ks[(j0 + tr_r) * KS + ko]),
-                                ld_tr(&Ks[(j0 + 4 + tr_r) * KS + ko]));
-          const bf16x8 vh = cat(ld_tr(&Vh[(j0 + tr_r) * VS + vo]),
-                                ld_tr(&Vh[(j0 + 4 + tr_r) * VS + vo]));
-          const bf16x8 vl = cat(ld_tr(&Vl[(j0 + tr_r) * VS + vo]),
-                                ld_tr(&Vl[(j0 + 4 + tr_r) * VS + vo]));
-          acc = mfma(ka, vh, acc);
-          acc = mfma(ka, vl, acc);
-        }
-        st[n] = acc;
-        uint2 hi, lo;
-        split4(acc, hi, lo);
-        *reinterpret_cast<uint2*>(&Sh[cur ^ 1][(16 * tc + li) * SS + 16 * tr + 4 * g]) = hi;
-        *reinterpret_cast<uint2*>(&Sl[cur ^ 1][(16 * tc + li) * SS + 16 * tr + 4 * g]) = lo;
+      for (int tc = 0; tc < 2; ++tc) {
+        const int j0 = 32 * kk2 + 4 * g + tr_r;
+        const int vo = 16 * tc + 4 * tr_a;
+        vh[kk2][tc] = cat(ld_tr(&Hc[j0 * kVS + vo]), ld_tr(&Hc[(j0 + 16) * kVS + vo]));
+        vl[kk2][tc] = cat(ld_tr(&Lc[j0 * kVS + vo]), ld_tr(&Lc[(j0 + 16) * kVS + vo]));
       }
     }
+    bf16x8 ka[NR > 0 ? NR : 1][2];
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+      const int tr = rb + n;
+#pragma unroll
+      for (int kk2 = 0; kk2 < 2; ++kk2) {
+        const int j0 = 32 * kk2 + 4 * g + tr_r;
+        const int kc = 2 * tr + (tr_a >> 1);
+        const int kh = 4 * (tr_a & 1);
+        ka[n][kk2] = cat(ld_tr(&Kc[qk_off<D>(j0, kc) + kh]),
+                         ld_tr(&Kc[qk_off<D>(j0 + 16, kc) + kh]));
+      }
+    }
+    floatx4 acc[NR > 0 ? NR : 1][2];
+#pragma unroll
+    for (int n = 0; n < NR; ++n)
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) acc[n][tc] = st[n][tc] * fl;
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+#pragma unroll
+      for (int n = 0; n < NR; ++n)
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) acc[n][tc] = mfma(ka[n][kk2], vh[kk2][tc], acc[n][tc]);
+#pragma unroll
+      for (int n = 0; n < NR; ++n)
+#pragma unroll
+        for (int tc = 0; tc < 2; ++tc) acc[n][tc] = mfma(ka[n][kk2], vl[kk2][tc], acc[n][tc]);
+    }
+#pragma unroll
+    for (int n = 0; n < NR; ++n) {
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        st[n][tc] = acc[n][tc];
+        uint2 hi, lo;
+        split4(acc[n][tc], hi, lo);
+        const int so = (16 * tc + li) * SS + 16 * (rb + n) + 4 * g;
+        *reinterpret_cast<uint2*>(&Sh[cur ^ 1][so]) = hi;
+        *reinterpret_cast<uint2*>(&Sl[cur ^ 1][so]) = lo;
+      }
+    }
+  };
 
-    b0 = nb0;
-    ell = nell;
+  if (!strip && nblocks > 0) {
+    load_block(start, block_len(0));
+    store_block(0, block_len(0));
+  }
+  lds_barrier();
+
+  for (int b = 0; b < nblocks; ++b) {
+    const int cur = b & 1;
+    const int64_t b0 = start + (int64_t)b * kBeta;
+    const int ell = block_len(b);
+    if (strip) {
+      switch (k) {
+        case 0: strip_body(IC<0>{}, cur, b0, ell); break;
+        case 1: strip_body(IC<1>{}, cur, b0, ell); break;
+        case 2: strip_body(IC<2>{}, cur, b0, ell); break;
+        default: strip_body(IC<3>{}, cur, b0, ell); break;
+      }
+    } else {
+      const bool more = b + 1 < nblocks;
+      const int nell = more ? block_len(b + 1) : 0;
+      if (more) load_block(b0 + kBeta, nell);
+      switch (re - rb) {
+        case 3: state_body(IC<3>{}, cur, ell); break;
+        case 2: state_body(IC<2>{}, cur, ell); break;
+        case 1: state_body(IC<1>{}, cur, ell); break;
+        default: break;
+      }
+      if (more) store_block(cur ^ 1, nell);
+    }
+    lds_barrier();
   }
 
   if (a.kv_final) {
 #pragma unroll
-    for (int n = 0; n < MAXT; ++n) {
-      const int tile = tb + n;
-      if (tile < te) {
-        const int tr = tile >> 1, tc = tile & 1;
+    for (int n = 0; n < MAXR; ++n) {
+      const int tr = rb + n;
+      if (tr < re) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int r = 16 * tr + 4 * g + m;
-          a.kv_final[state_off + (int64_t)r * D + c0 + 16 * tc + li] = st[n][m];
-        }
+        for (int tc = 0; tc < 2; ++tc)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            a.kv_final[state_off + (int64_t)(16 * tr + 4 * g + m) * D + c0 + 16 * tc + li] =
+                st[n][tc][m];
       }
     }
   }
