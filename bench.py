@@ -40,7 +40,7 @@ METRIC = "prefill tokens/s + MFMA TFLOP/s (H=64,d=128,N=8K..1M); decode HBM GB/s
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 H, D, BETA = 64, 128, 64
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n8k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n8k_hbm_traffic.txt")
 KERNEL_SOURCES = ["linear_attention_la_amd/csrc/la_prefill_bf16.hip",
                   "linear_attention_la_amd/csrc/la_device.h",
                   "linear_attention_la_amd/csrc/la_internal.h"]
@@ -70,15 +70,21 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(algorithmic):
-    """Counter-measured HBM bytes per launch, if taken on this kernel source."""
+def measured_traffic():
+    """Counter-measured HBM bytes per launch of the prefill kernel, if the
+    counters were taken on the current kernel source (else None)."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().splitlines()
+                   if ":" in line and not line.startswith("#"))
     except (OSError, ValueError):
         return None
+    rec = {k_.strip(): v_.strip() for k_, v_ in rec.items()}
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return int(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def timed_launches(fn, reps, stream, flush=None):
@@ -115,7 +121,7 @@ def cpu_baseline(budget_s=12.0):
     decay = decay_from_seed(H)
     heads_done, elapsed = 0, 0.0
     chunk = 8
-    while elapsed < budget_s and heads_done < 4 * H:
+    while elapsed < budget_s and heads_done < 32 * H:
         q, k, v = host_qkv(N, chunk, D, 5000 + heads_done)
         t0 = time.perf_counter()
         for j in range(chunk):
@@ -233,6 +239,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time la_decode on the 256 x 64-head serving batch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -252,6 +260,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}))
+        return
+    if args.decode_only:
+        la.lib()
+        dec, _ = bench_decode(dev, reps=max(args.steps, 1))
+        print(json.dumps({"decode": dec}))
         return
     la.lib()
     w = workload("n8k")
@@ -287,7 +300,7 @@ def main():
     by = prefill_bytes(N, 1)
     achieved = by / kern_s / 1e9
     tflops = prefill_flops(N) / kern_s / 1e12
-    traffic = measured_traffic(by)
+    traffic = measured_traffic()
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
