@@ -38,6 +38,9 @@
  * (decay, cu_seqlens_host) are read only during the call.  The device that
  * owns the buffers must be the calling thread's current HIP device.
  *
+ * Alignment.  Every device pointer must be 16-byte aligned (the kernels use
+ * 16 B vector accesses); a misaligned pointer is LA_ERR_INVALID_ARG.
+ *
  * Errors.  Every entry point returns la_status and never aborts or prints.
  * Argument errors are detected on the host before anything is enqueued:
  * LA_ERR_INVALID_ARG, nothing runs, outputs are untouched.  Valid but

@@ -29,6 +29,8 @@ la_status ok() {
 }
 
 bool valid_dtype(la_dtype d) { return d == LA_BF16 || d == LA_FP32; }
+// Kernels use 16 B vector loads and stores at row granularity.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t dtype_size(la_dtype d) { return d == LA_BF16 ? 2 : 4; }
 
 struct Range {
@@ -122,6 +124,12 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   if (total_tokens > 0 && (!q || !k || !v || !o))
     return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL when total_tokens > 0");
 
+  const void* ptrs[] = {q, k, v, o, kv_init, kv_final};
+  const char* names[] = {"q", "k", "v", "o", "kv_init", "kv_final"};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+
   const int cols = in_dtype == LA_BF16 ? la::kBf16Cols : la::kF32Cols;
   const int64_t items = (int64_t)num_seqs * num_heads * (head_dim / cols);
   if (items >= ((int64_t)1 << 31))
@@ -176,6 +184,11 @@ la_status la_decode(const void* q, const void* k, const void* v, float* kv,
   if (batch == 0) return ok();
   if (!q || !k || !v || !kv || !o)
     return fail(LA_ERR_INVALID_ARG, "q, k, v, kv and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, kv, o};
+  const char* names[] = {"q", "k", "v", "kv", "o"};
+  for (int i = 0; i < 5; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
   if ((int64_t)batch * num_heads >= ((int64_t)1 << 31))
     return fail(LA_ERR_UNSUPPORTED, "batch * num_heads exceeds the grid limit");
 

@@ -16,7 +16,8 @@
 // slice of the value dimension) chain; the d x d state is split by value
 // columns over d/32 workgroups, each of which recomputes Q K^T for its block
 // so that no cross-workgroup exchange exists.  Within the workgroup:
-//  * strip waves 0..3: wave k owns query rows i in [16k, 16k+16).  It forms
+//  * strip waves 0..3: wave k owns query rows i in [16k, 16k+16), whose Q rows
+//    it loads from HBM straight into its MFMA operand registers.  It forms
 //    its strip of scores S^T = K Q^T, applies mask and decay in registers and
 //    feeds them straight back into the MFMA as the B operand of O^T = V^T P^T
 //    (the score tile's accumulator layout -- 4 consecutive keys per lane -- is
@@ -24,7 +25,7 @@
 //    adds diag(lambda^(i+1)) S^T Q^T and writes its rows of O;
 //  * state waves 4..7: own 16-row tiles of the 32-column state slice in fp32
 //    accumulators for the whole chain and advance them by K^T Vd; they also
-//    move Q, K and V from HBM into LDS, one block ahead.
+//    move K and V from HBM into LDS, two blocks ahead.
 // Wave k and wave k+4 share a SIMD; state rows are dealt so that the MFMA
 // work per SIMD is nearly even (strips near the diagonal are shorter).
 // LDS stages are double-buffered: block b+1 is loaded from HBM while block b
@@ -39,10 +40,9 @@
 // are bf16 already and every sum is fp32.  The state is stored in fp32.
 //
 // LDS (bf16 bits):
-//   Qs, Ks  [2][64][d]    rows with 16 B chunks XOR-swizzled per row, so that
-//                         16 consecutive rows of one chunk (MFMA operand
-//                         reads) and 8 consecutive rows of two chunks
-//                         (transposed reads of K) hit distinct banks
+//   Ks      [2][64][d]    rows with 16 B chunks XOR-swizzled per row (see
+//                         swz): operand reads and transposed reads of K are
+//                         bank-conflict free
 //   Vs, Vh, Vl [2][64][48] the value slice, and its lambda^(ell-1-j)-scaled
 //                         rows as hi/lo (row stride 96 B: conflict-free
 //                         transposed reads)
@@ -113,6 +113,19 @@ __device__ __forceinline__ bf16x8 cat2(uint2 a, uint2 b) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over [base, base + bytes).  Buffer loads outside the
+// range return zero and stores outside it are dropped, so every memory
+// instruction of a block is issued unconditionally: rows past the end of a
+// sequence need no branch, and the number of outstanding vector-memory
+// operations is the same on every path, which lets each wait count only
+// the operations it needs (a data-dependent count forces waiting for all).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
 // Swizzle of the 16 B chunks of a Q/K row.  The LDS serves 128 B per clock
 // (32 banks): a 16 B read is served 8 lanes at a time, an 8 B read 16 lanes
 // at a time.  Chunk c of row r is stored at chunk c ^ swz(r), which keeps
@@ -164,14 +177,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NDV = D / kDV;
   constexpr int SS = D + 8;        // state^T row stride
   constexpr int NK = D / 32;       // k-steps over d
-  constexpr int CH = D / 8;        // 16 B chunks per Q/K row
-  constexpr int NQC = CH / 4;      // Q (and K) chunks staged per state thread
+  constexpr int CH = D / 8;        // 16 B chunks per K row
+  constexpr int NKC = CH / 4;      // K chunks staged per state thread
   constexpr int MAXR = RowSplit<D>::kMax;
-  constexpr int QKSZ = kBeta * D;
+  constexpr int KSZ = kBeta * D;
   constexpr int VSZ = kBeta * kVS;
 
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][QKSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][QKSZ];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][VSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Vh[2][VSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[2][VSZ];
@@ -252,49 +264,67 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- staging: the state waves move Q, K and V; strip waves only store O ----
-  // State thread u = t - 256: Q/K chunk p has id = u + 256 p, row id / CH,
+  // Valid rows of block b (0 past the end of the sequence).
+  auto block_len = [&](int b) -> int {
+    const int64_t rem = end - (start + (int64_t)b * kBeta);
+    return rem <= 0 ? 0 : rem < kBeta ? (int)rem : kBeta;
+  };
+  // Buffer resource over the valid rows (all heads) of block b of a [T, H, d]
+  // tensor with elements of `esize` bytes.
+  auto block_rsrc = [&](const void* base, int b, int esize) {
+    const char* p = static_cast<const char*>(base) +
+                    (start + (int64_t)b * kBeta) * row_stride * (int64_t)esize;
+    return buf_rsrc(p, block_len(b) * row_stride * esize);
+  };
+
+  // ---- strip waves: their 16 query rows go straight from HBM into the
+  // MFMA operand registers (lane (li, g) holds Q[16k+li][32kk+8g..+7]) ----
+  auto load_q = [&](bf16x8(&dst)[NK], int b) {
+    const __amdgpu_buffer_rsrc_t r = block_rsrc(q, b, 2);
+    const int off = 2 * ((16 * k + li) * row_stride + h * D + 8 * g);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      dst[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64 * kk, 0, 0));
+  };
+
+  // ---- state waves: K and V move HBM -> registers -> LDS two blocks ahead.
+  // State thread u = t - 256: K chunk p has id = u + 256 p, row id / CH,
   // chunk id % CH (a wave reads whole rows: coalesced); V: row u / 4, chunk
-  // u % 4 of the 32-column value slice.
+  // u % 4 of the 32-column value slice. ----
   const int u = t - 256;
   const int vrow = u >> 2;
   const int vch = u & 3;
-  uint4 qreg[NQC], kreg[NQC], vreg;
-
-  auto load_block = [&](int64_t b0, int ell) {
-    const uint16_t* qb0 = q + b0 * row_stride + (int64_t)h * D;
-    const uint16_t* kb0 = kp + b0 * row_stride + (int64_t)h * D;
-    const uint16_t* vb0 = v + b0 * row_stride + (int64_t)h * D + c0;
-#pragma unroll
-    for (int p = 0; p < NQC; ++p) {
-      const int id = u + 256 * p;
-      const int row = id / CH;
-      const int off = row * row_stride + 8 * (id % CH);
-      if (row < ell) {
-        qreg[p] = *reinterpret_cast<const uint4*>(qb0 + off);
-        kreg[p] = *reinterpret_cast<const uint4*>(kb0 + off);
-      } else {
-        qreg[p] = make_uint4(0, 0, 0, 0);
-        kreg[p] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    vreg = vrow < ell ? *reinterpret_cast<const uint4*>(vb0 + vrow * row_stride + 8 * vch)
-                      : make_uint4(0, 0, 0, 0);
+  struct Stage {
+    uint4 k[NKC];
+    uint4 v;
   };
 
-  auto store_block = [&](int buf, int ell) {
+  auto load_kv = [&](Stage& r, int b) {
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kp, b, 2);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(v, b, 2);
 #pragma unroll
-    for (int p = 0; p < NQC; ++p) {
+    for (int p = 0; p < NKC; ++p) {
       const int id = u + 256 * p;
-      const int o = qk_off<D>(id / CH, id % CH);
-      *reinterpret_cast<uint4*>(&Qs[buf][o]) = qreg[p];
-      *reinterpret_cast<uint4*>(&Ks[buf][o]) = kreg[p];
+      r.k[p] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rk, 2 * ((id / CH) * row_stride + h * D + 8 * (id % CH)), 0, 0));
+    }
+    r.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rv, 2 * (vrow * row_stride + h * D + c0 + 8 * vch), 0, 0));
+  };
+
+  auto store_kv = [&](const Stage& r, int buf, int b) {
+    const int ell = block_len(b);
+#pragma unroll
+    for (int p = 0; p < NKC; ++p) {
+      const int id = u + 256 * p;
+      *reinterpret_cast<uint4*>(&Ks[buf][qk_off<D>(id / CH, id % CH)]) = r.k[p];
     }
     const int o = vrow * kVS + 8 * vch;
-    *reinterpret_cast<uint4*>(&Vs[buf][o]) = vreg;
+    *reinterpret_cast<uint4*>(&Vs[buf][o]) = r.v;
     // value row scaled by lambda^(ell-1-j), split hi/lo
     const float wv = vrow < ell ? exp2f((float)(ell - 1 - vrow) * l2) : 0.0f;
-    const uint32_t wd[4] = {vreg.x, vreg.y, vreg.z, vreg.w};
+    const uint32_t wd[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
     uint32_t hp[4], lp[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -307,20 +337,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     *reinterpret_cast<uint4*>(&Vl[buf][o]) = make_uint4(lp[0], lp[1], lp[2], lp[3]);
   };
 
-  auto block_len = [&](int b) -> int {
-    const int64_t rem = end - (start + (int64_t)b * kBeta);
-    return rem < kBeta ? (int)rem : kBeta;
-  };
-
   // ---- one block of a strip wave (strip index KS fixed at compile time) ----
-  auto strip_body = [&](auto KS_, int cur, int64_t b0, int ell) {
+  auto strip_body = [&](auto KS_, const bf16x8(&qb)[NK], int cur, int b) {
     constexpr int KS = decltype(KS_)::value;
-    const uint16_t* Qc = Qs[cur];
     const uint16_t* Kc = Ks[cur];
     const uint16_t* Vc = Vs[cur];
-    bf16x8 qb[NK];
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) qb[kk] = ld8(&Qc[qk_off<D>(16 * KS + li, 4 * kk + g)]);
 
     // scores S^T = K Q^T for tiles tj <= KS (independent chains interleaved)
     floatx4 sc[KS + 1];
@@ -353,6 +374,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       oe[tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 #pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+      for (int tc = 0; tc < 2; ++tc) {
+        const int so = (16 * tc + li) * SS + 32 * kk + 8 * g;
+        oe[tc] = mfma(ld8(&Sh[cur][so]), qb[kk], oe[tc]);
+        oe[tc] = mfma(ld8(&Sl[cur][so]), qb[kk], oe[tc]);
+      }
+    }
+#pragma unroll
     for (int kk2 = 0; kk2 < NJ; ++kk2) {
       const int j0 = 32 * kk2 + 4 * g + tr_r;
       const bf16x8 p_h = cat2(ph[2 * kk2], ph[2 * kk2 + 1]);
@@ -365,31 +395,25 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         oi[tc] = mfma(va, p_l, oi[tc]);
       }
     }
+    // rows past the end of the sequence fall outside the resource: dropped
+    constexpr int ES = kOutF32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t ro = block_rsrc(a.o, b, ES);
+    const int orow = (16 * KS + li) * row_stride + h * D + c0;
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
+    for (int tc = 0; tc < 2; ++tc) {
+      float out[4];
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc) {
-        const int so = (16 * tc + li) * SS + 32 * kk + 8 * g;
-        oe[tc] = mfma(ld8(&Sh[cur][so]), qb[kk], oe[tc]);
-        oe[tc] = mfma(ld8(&Sl[cur][so]), qb[kk], oe[tc]);
-      }
-    }
-    const int i = 16 * KS + li;
-    if (i < ell) {
-      const int64_t orow = (b0 + i) * (int64_t)row_stride + (int64_t)h * D + c0;
-#pragma unroll
-      for (int tc = 0; tc < 2; ++tc) {
-        float out[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) out[m] = fmaf(qdecay, oe[tc][m], oi[tc][m]);
-        const int64_t off = orow + 16 * tc + 4 * g;
-        if constexpr (kOutF32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(a.o) + off) =
-              make_float4(out[0], out[1], out[2], out[3]);
-        } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + off) =
-              make_uint2(cvt2(out[0], out[1]), cvt2(out[2], out[3]));
-        }
+      for (int m = 0; m < 4; ++m) out[m] = fmaf(qdecay, oe[tc][m], oi[tc][m]);
+      const int off = ES * (orow + 16 * tc + 4 * g);
+      if constexpr (kOutF32) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__builtin_bit_cast(unsigned, out[0]),
+                                                     __builtin_bit_cast(unsigned, out[1]),
+                                                     __builtin_bit_cast(unsigned, out[2]),
+                                                     __builtin_bit_cast(unsigned, out[3])},
+                                               ro, off, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{cvt2(out[0], out[1]), cvt2(out[2], out[3])},
+                                              ro, off, 0, 0);
       }
     }
   };
@@ -456,49 +480,68 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  if (!strip && nblocks > 0) {
-    load_block(start, block_len(0));
-    store_block(0, block_len(0));
-  }
-  lds_barrier();
-
-  for (int b = 0; b < nblocks; ++b) {
-    const int cur = b & 1;
-    const int64_t b0 = start + (int64_t)b * kBeta;
-    const int ell = block_len(b);
-    if (strip) {
+  // ---- pipeline ----
+  // Strip waves hold Q of block b in one register set and load block b+1
+  // into the other.  State waves keep two register stages: at block b, the
+  // stage that held block b (already in LDS) receives block b+2 from HBM,
+  // and the stage holding block b+1 is written to LDS after block b's
+  // arithmetic.  One barrier per block publishes the LDS writes.
+  // The two roles run separate loops with the same number of barriers, so
+  // the registers of one role are not kept live in the other.
+  if (strip) {
+    bf16x8 qa[NK], qb2[NK];
+    load_q(qa, 0);
+    lds_barrier();
+    auto sstep = [&](int b, bf16x8(&qc)[NK], bf16x8(&qn)[NK]) {
+      load_q(qn, b + 1);  // empty range past the last block
       switch (k) {
-        case 0: strip_body(IC<0>{}, cur, b0, ell); break;
-        case 1: strip_body(IC<1>{}, cur, b0, ell); break;
-        case 2: strip_body(IC<2>{}, cur, b0, ell); break;
-        default: strip_body(IC<3>{}, cur, b0, ell); break;
+        case 0: strip_body(IC<0>{}, qc, b & 1, b); break;
+        case 1: strip_body(IC<1>{}, qc, b & 1, b); break;
+        case 2: strip_body(IC<2>{}, qc, b & 1, b); break;
+        default: strip_body(IC<3>{}, qc, b & 1, b); break;
       }
-    } else {
-      const bool more = b + 1 < nblocks;
-      const int nell = more ? block_len(b + 1) : 0;
-      if (more) load_block(b0 + kBeta, nell);
+      lds_barrier();
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+      sstep(b, qa, qb2);
+      if (b + 1 < nblocks) sstep(b + 1, qb2, qa);
+    }
+  } else {
+    Stage r0, r1;
+    load_kv(r0, 0);
+    load_kv(r1, 1);
+    if (nblocks > 0) store_kv(r0, 0, 0);
+    lds_barrier();
+    auto tstep = [&](int b, Stage& rfree, Stage& rfull) {
+      const int cur = b & 1;
+      load_kv(rfree, b + 2);  // empty range past the last block
+      const int ell = block_len(b);
       switch (re - rb) {
         case 3: state_body(IC<3>{}, cur, ell); break;
         case 2: state_body(IC<2>{}, cur, ell); break;
         case 1: state_body(IC<1>{}, cur, ell); break;
         default: break;
       }
-      if (more) store_block(cur ^ 1, nell);
+      if (b + 1 < nblocks) store_kv(rfull, cur ^ 1, b + 1);
+      lds_barrier();
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+      tstep(b, r0, r1);
+      if (b + 1 < nblocks) tstep(b + 1, r1, r0);
     }
-    lds_barrier();
-  }
 
-  if (a.kv_final) {
+    if (a.kv_final) {
 #pragma unroll
-    for (int n = 0; n < MAXR; ++n) {
-      const int tr = rb + n;
-      if (tr < re) {
+      for (int n = 0; n < MAXR; ++n) {
+        const int tr = rb + n;
+        if (tr < re) {
 #pragma unroll
-        for (int tc = 0; tc < 2; ++tc)
+          for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            a.kv_final[state_off + (int64_t)(16 * tr + 4 * g + m) * D + c0 + 16 * tc + li] =
-                st[n][tc][m];
+            for (int m = 0; m < 4; ++m)
+              a.kv_final[state_off + (int64_t)(16 * tr + 4 * g + m) * D + c0 + 16 * tc + li] =
+                  st[n][tc][m];
+        }
       }
     }
   }

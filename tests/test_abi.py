@@ -99,6 +99,9 @@ BAD_PREFILL = [
     ("kv_final_overlaps_kv_init_partially", dict(kv_init=KVI, kv_final=KVI + 4),
      la.LA_ERR_INVALID_ARG),
     ("o_overlaps_kv_init", dict(kv_init=KVI, o=KVI + 16), la.LA_ERR_INVALID_ARG),
+    ("q_misaligned", dict(q=Q + 2), la.LA_ERR_INVALID_ARG),
+    ("o_misaligned", dict(o=O + 8), la.LA_ERR_INVALID_ARG),
+    ("kv_final_misaligned", dict(kv_final=KVF + 4), la.LA_ERR_INVALID_ARG),
 ]
 
 
@@ -139,6 +142,8 @@ BAD_DECODE = [
     ("o_overlaps_kv", dict(o=KVF + 8), la.LA_ERR_INVALID_ARG),
     ("kv_overlaps_q", dict(kv=Q - 16), la.LA_ERR_INVALID_ARG),
     ("o_overlaps_k", dict(o=K + 2), la.LA_ERR_INVALID_ARG),
+    ("kv_misaligned", dict(kv=KVF + 8), la.LA_ERR_INVALID_ARG),
+    ("v_misaligned", dict(v=V + 2), la.LA_ERR_INVALID_ARG),
 ]
 
 
