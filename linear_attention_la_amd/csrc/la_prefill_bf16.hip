@@ -24,8 +24,8 @@
 //    a valid operand layout when the value operand uses the same key order),
 //    adds diag(lambda^(i+1)) S^T Q^T and writes its rows of O;
 //  * state waves 4..7: own 16-row tiles of the 32-column state slice in fp32
-//    accumulators for the whole chain and advance them by K^T Vd; they also
-//    move K and V from HBM into LDS, two blocks ahead.
+//    accumulators for the whole chain and advance them by K^T Vd.
+// Strip waves stage K and state waves stage V (HBM -> LDS, two blocks ahead).
 // Wave k and wave k+4 share a SIMD; state rows are dealt so that the MFMA
 // work per SIMD is nearly even (strips near the diagonal are shorter).
 // LDS stages are double-buffered: block b+1 is loaded from HBM while block b
@@ -149,10 +149,10 @@ __device__ __forceinline__ int qk_off(int r, int c) {
 template <int D>
 struct RowSplit;
 template <>
-struct RowSplit<128> {  // 8 row tiles: 3, 3, 1, 1
-  static constexpr int kMax = 3;
-  __device__ static int begin(int k) { return k == 0 ? 0 : k == 1 ? 3 : k == 2 ? 6 : 7; }
-  __device__ static int end(int k) { return k == 0 ? 3 : k == 1 ? 6 : k == 2 ? 7 : 8; }
+struct RowSplit<128> {  // 8 row tiles: 2 per state wave
+  static constexpr int kMax = 2;
+  __device__ static int begin(int k) { return 2 * k; }
+  __device__ static int end(int k) { return 2 * k + 2; }
 };
 template <>
 struct RowSplit<64> {  // 4 row tiles: 2, 1, 1, 0
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int SS = D + 8;        // state^T row stride
   constexpr int NK = D / 32;       // k-steps over d
   constexpr int CH = D / 8;        // 16 B chunks per K row
-  constexpr int NKC = CH / 4;      // K chunks staged per state thread
+  constexpr int NKC = CH / 4;      // K chunks staged per strip thread
   constexpr int MAXR = RowSplit<D>::kMax;
   constexpr int KSZ = kBeta * D;
   constexpr int VSZ = kBeta * kVS;
@@ -287,39 +287,45 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       dst[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64 * kk, 0, 0));
   };
 
-  // ---- state waves: K and V move HBM -> registers -> LDS two blocks ahead.
-  // State thread u = t - 256: K chunk p has id = u + 256 p, row id / CH,
-  // chunk id % CH (a wave reads whole rows: coalesced); V: row u / 4, chunk
-  // u % 4 of the 32-column value slice. ----
+  // ---- staging: K and V move HBM -> registers -> LDS two blocks ahead.
+  // Strip thread t moves K chunks id = t + 256 p (row id / CH, chunk id % CH:
+  // a wave reads whole rows, coalesced).  State thread u = t - 256 moves the
+  // value slice: row u / 4, chunk u % 4, plus its lambda^(ell-1-j)-scaled
+  // hi/lo copies. ----
   const int u = t - 256;
   const int vrow = u >> 2;
   const int vch = u & 3;
-  struct Stage {
+  struct KStage {
     uint4 k[NKC];
+  };
+  struct VStage {
     uint4 v;
   };
 
-  auto load_kv = [&](Stage& r, int b) {
+  auto load_k = [&](KStage& r, int b) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(kp, b, 2);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(v, b, 2);
 #pragma unroll
     for (int p = 0; p < NKC; ++p) {
-      const int id = u + 256 * p;
+      const int id = t + 256 * p;
       r.k[p] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
                      rk, 2 * ((id / CH) * row_stride + h * D + 8 * (id % CH)), 0, 0));
     }
+  };
+  auto store_k = [&](const KStage& r, int buf) {
+#pragma unroll
+    for (int p = 0; p < NKC; ++p) {
+      const int id = t + 256 * p;
+      *reinterpret_cast<uint4*>(&Ks[buf][qk_off<D>(id / CH, id % CH)]) = r.k[p];
+    }
+  };
+  auto load_v = [&](VStage& r, int b) {
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(v, b, 2);
     r.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                         rv, 2 * (vrow * row_stride + h * D + c0 + 8 * vch), 0, 0));
   };
-
-  auto store_kv = [&](const Stage& r, int buf, int b) {
+  auto store_v = [&](const VStage& r, int buf, int b) {
     const int ell = block_len(b);
-#pragma unroll
-    for (int p = 0; p < NKC; ++p) {
-      const int id = u + 256 * p;
-      *reinterpret_cast<uint4*>(&Ks[buf][qk_off<D>(id / CH, id % CH)]) = r.k[p];
-    }
     const int o = vrow * kVS + 8 * vch;
     *reinterpret_cast<uint4*>(&Vs[buf][o]) = r.v;
     // value row scaled by lambda^(ell-1-j), split hi/lo
@@ -482,39 +488,45 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- pipeline ----
   // Strip waves hold Q of block b in one register set and load block b+1
-  // into the other.  State waves keep two register stages: at block b, the
-  // stage that held block b (already in LDS) receives block b+2 from HBM,
-  // and the stage holding block b+1 is written to LDS after block b's
-  // arithmetic.  One barrier per block publishes the LDS writes.
-  // The two roles run separate loops with the same number of barriers, so
-  // the registers of one role are not kept live in the other.
+  // into the other; both roles keep two register stages of their share of
+  // K / V: at block b, the stage that held block b (already in LDS) receives
+  // block b+2 from HBM, and the stage holding block b+1 is written to LDS
+  // after block b's arithmetic.  One barrier per block publishes the LDS
+  // writes.  The two roles run separate loops with the same number of
+  // barriers, so the registers of one role are not kept live in the other.
   if (strip) {
     bf16x8 qa[NK], qb2[NK];
+    KStage k0, k1;
     load_q(qa, 0);
+    load_k(k0, 0);
+    load_k(k1, 1);
+    store_k(k0, 0);
     lds_barrier();
-    auto sstep = [&](int b, bf16x8(&qc)[NK], bf16x8(&qn)[NK]) {
-      load_q(qn, b + 1);  // empty range past the last block
+    auto sstep = [&](int b, bf16x8(&qc)[NK], bf16x8(&qn)[NK], KStage& kfree, KStage& kfull) {
+      load_q(qn, b + 1);     // empty range past the last block
+      load_k(kfree, b + 2);  // likewise
       switch (k) {
         case 0: strip_body(IC<0>{}, qc, b & 1, b); break;
         case 1: strip_body(IC<1>{}, qc, b & 1, b); break;
         case 2: strip_body(IC<2>{}, qc, b & 1, b); break;
         default: strip_body(IC<3>{}, qc, b & 1, b); break;
       }
+      if (b + 1 < nblocks) store_k(kfull, (b & 1) ^ 1);
       lds_barrier();
     };
     for (int b = 0; b < nblocks; b += 2) {
-      sstep(b, qa, qb2);
-      if (b + 1 < nblocks) sstep(b + 1, qb2, qa);
+      sstep(b, qa, qb2, k0, k1);
+      if (b + 1 < nblocks) sstep(b + 1, qb2, qa, k1, k0);
     }
   } else {
-    Stage r0, r1;
-    load_kv(r0, 0);
-    load_kv(r1, 1);
-    if (nblocks > 0) store_kv(r0, 0, 0);
+    VStage r0, r1;
+    load_v(r0, 0);
+    load_v(r1, 1);
+    store_v(r0, 0, 0);
     lds_barrier();
-    auto tstep = [&](int b, Stage& rfree, Stage& rfull) {
+    auto tstep = [&](int b, VStage& rfree, VStage& rfull) {
       const int cur = b & 1;
-      load_kv(rfree, b + 2);  // empty range past the last block
+      load_v(rfree, b + 2);  // empty range past the last block
       const int ell = block_len(b);
       switch (re - rb) {
         case 3: state_body(IC<3>{}, cur, ell); break;
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         case 1: state_body(IC<1>{}, cur, ell); break;
         default: break;
       }
-      if (b + 1 < nblocks) store_kv(rfull, cur ^ 1, b + 1);
+      if (b + 1 < nblocks) store_v(rfull, cur ^ 1, b + 1);
       lds_barrier();
     };
     for (int b = 0; b < nblocks; b += 2) {
