@@ -26,8 +26,9 @@
 //  * state waves 4..7: own 16-row tiles of the 32-column state slice in fp32
 //    accumulators for the whole chain and advance them by K^T Vd.
 // Strip waves stage K and state waves stage V (HBM -> LDS, two blocks ahead).
-// Wave k and wave k+4 share a SIMD; state rows are dealt so that the MFMA
-// work per SIMD is nearly even (strips near the diagonal are shorter).
+// Wave k and wave k+4 share a SIMD; each state wave owns a pair of 16-row
+// state tiles (for d = 64 only state waves 0 and 1 have one, beside the two
+// shortest query strips).
 // LDS stages are double-buffered: block b+1 is loaded from HBM while block b
 // is computed, so each block needs one workgroup barrier.  Only the state
 // waves load and only the strip waves store, and the barrier waits for LDS
@@ -39,14 +40,16 @@
 // two MFMAs, so they enter the products with ~16 significant bits; inputs
 // are bf16 already and every sum is fp32.  The state is stored in fp32.
 //
-// LDS (bf16 bits):
-//   Ks      [2][64][d]    rows with 16 B chunks XOR-swizzled per row (see
-//                         swz): operand reads and transposed reads of K are
-//                         bank-conflict free
-//   Vs, Vh, Vl [2][64][48] the value slice, and its lambda^(ell-1-j)-scaled
-//                         rows as hi/lo (row stride 96 B: conflict-free
-//                         transposed reads)
-//   Sh, Sl  [2][32][d+8]  state^T hi/lo for the Q S product
+// LDS (bf16 bits).  The LDS of gfx950 serves 256 B per clock to reads (a
+// 16 B read serves 16 lanes per clock, a transposed 8 B read 32 lanes) and
+// 128 B per clock to writes (a 16 B write serves 8 consecutive lanes).  Each
+// array is laid out so that every access pattern issued below is free of
+// bank conflicts:
+//   Ks      [2][64][d]    16 B chunk c of row r at chunk c ^ kswz(r)
+//   Vs, Vh, Vl [2][64][32] the value slice, and its lambda^(ell-1-j)-scaled
+//                         rows as hi/lo; chunk c of row j at c ^ ((j/2) % 4)
+//   Sh, Sl  [2][32][d]    state^T hi/lo for the Q S product; chunk q of
+//                         row c at q ^ (c % (d/8))
 // MFMA operand layout (16x16x32 bf16): lane l supplies row (l % 16) of A and
 // column (l % 16) of B, 8 k-values per lane in lane group g = l / 16; the 4
 // results of lane l sit at rows 4g + m, column l % 16.  The order of the 8
@@ -65,7 +68,6 @@ namespace {
 constexpr int kBeta = 64;
 constexpr int kThreads = 512;
 constexpr int kDV = kBf16Cols;  // 32 value columns per workgroup
-constexpr int kVS = 48;         // V row stride (elements)
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -126,39 +128,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Swizzle of the 16 B chunks of a Q/K row.  The LDS serves 128 B per clock
-// (32 banks): a 16 B read is served 8 lanes at a time, an 8 B read 16 lanes
-// at a time.  Chunk c of row r is stored at chunk c ^ swz(r), which keeps
-//  * 8 consecutive rows of one chunk (MFMA operand reads, 16 B/lane) and
-//  * 4 consecutive rows of an aligned chunk pair (transposed reads of K,
-//    8 B/lane, 16 lanes)
-// on distinct banks.  Every row is a multiple of 128 B long.
+// Swizzle of the 16 B chunks of a K row: a permutation of the bits of the
+// row index, chosen so that three patterns are free of bank conflicts:
+//  * one chunk of 16 consecutive rows (MFMA operand reads, 16 B per lane),
+//  * four chunks of 8 consecutive rows (transposed reads, 8 B per lane, with
+//    the row pieces that srow() below assigns), and
+//  * whole rows (staging writes).
 template <int D>
-__device__ __forceinline__ int swz(int r) {
-  return 2 * (r & 3) + ((r >> 2) & 1);
+__device__ __forceinline__ int kswz(int r);
+template <>
+__device__ __forceinline__ int kswz<128>(int r) {
+  return (r & 1) | ((r & 6) << 1) | ((r & 8) >> 2);
 }
-// Element offset of 16 B chunk c of row r.
+template <>
+__device__ __forceinline__ int kswz<64>(int r) {
+  return ((r & 2) >> 1) | (r & 4) | ((r & 8) >> 2);
+}
+// Element offset of 16 B chunk c of K row r.
 template <int D>
 __device__ __forceinline__ int qk_off(int r, int c) {
-  return r * D + 8 * (c ^ swz<D>(r));
+  return r * D + 8 * (c ^ kswz<D>(r));
 }
 
-// State row tiles (16 rows x both 16-column tiles) owned by state wave k.
-// The strip wave on the same SIMD has a causal strip of k+1 score tiles, so
-// state waves beside long strips get fewer row tiles.
+// Element offset of (row j, column col) of a value-slice array (64 B rows).
+__device__ __forceinline__ int v_off(int j, int col) {
+  return j * kDV + 8 * ((col >> 3) ^ ((j >> 1) & 3)) + (col & 7);
+}
+
+// Element offset of state^T row c (a value column), key rows 8q .. 8q+7.
 template <int D>
-struct RowSplit;
-template <>
-struct RowSplit<128> {  // 8 row tiles: 2 per state wave
+__device__ __forceinline__ int s_off(int c, int q) {
+  return c * D + 8 * (q ^ (c & (D / 8 - 1)));
+}
+
+// First of the 4 consecutive key rows of state tile n held by lane group g
+// (accumulator rows 4g .. 4g+3).  Tiles 2p and 2p+1 together give group g
+// the 8 rows 32p + 8g .. 32p + 8g + 7, so that a lane writes its state^T
+// values as one 16 B chunk; tile 2p takes the lower half for even g and the
+// upper half for odd g, which spreads the transposed K reads of a tile over
+// both 8 B halves of every chunk.
+__device__ __forceinline__ int srow(int n, int g) {
+  return 32 * (n >> 1) + 8 * g + 4 * ((n & 1) ^ (g & 1));
+}
+
+// State row tiles [begin, end) owned by state wave k: the pair (2k, 2k+1).
+// d = 128: 8 tiles, 2 per state wave.  d = 64: 4 tiles on state waves 0 and
+// 1, which share their SIMDs with the two shortest query strips.
+template <int D>
+struct RowSplit {
+  static constexpr int kTiles = D / 16;
   static constexpr int kMax = 2;
-  __device__ static int begin(int k) { return 2 * k; }
-  __device__ static int end(int k) { return 2 * k + 2; }
-};
-template <>
-struct RowSplit<64> {  // 4 row tiles: 2, 1, 1, 0
-  static constexpr int kMax = 2;
-  __device__ static int begin(int k) { return k == 0 ? 0 : k == 1 ? 2 : k == 2 ? 3 : 4; }
-  __device__ static int end(int k) { return k == 0 ? 2 : k == 1 ? 3 : 4; }
+  __device__ static int begin(int k) { return 2 * k < kTiles ? 2 * k : kTiles; }
+  __device__ static int end(int k) { return 2 * k + 2 < kTiles ? 2 * k + 2 : kTiles; }
 };
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
@@ -175,20 +196,19 @@ using IC = std::integral_constant<int, N>;
 template <int D, bool kOutF32>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NDV = D / kDV;
-  constexpr int SS = D + 8;        // state^T row stride
   constexpr int NK = D / 32;       // k-steps over d
   constexpr int CH = D / 8;        // 16 B chunks per K row
   constexpr int NKC = CH / 4;      // K chunks staged per strip thread
   constexpr int MAXR = RowSplit<D>::kMax;
   constexpr int KSZ = kBeta * D;
-  constexpr int VSZ = kBeta * kVS;
+  constexpr int VSZ = kBeta * kDV;
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][VSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Vh[2][VSZ];
   __shared__ __attribute__((aligned(16))) uint16_t Vl[2][VSZ];
-  __shared__ __attribute__((aligned(16))) uint16_t Sh[2][kDV * SS];
-  __shared__ __attribute__((aligned(16))) uint16_t Sl[2][kDV * SS];
+  __shared__ __attribute__((aligned(16))) uint16_t Sh[2][kDV * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Sl[2][kDV * D];
 
   const int H = a.num_heads;
   const int item = xcd_remap(blockIdx.x, a.num_items, NDV);
@@ -238,31 +258,39 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   const float qdecay = exp2f((float)(16 * k + li + 1) * l2);  // lambda^(i+1)
 
   // ---- state row tiles (state waves), fp32 accumulator layout ----
-  // st[n][tc]: rows 16 (rb + n) + 4g + m, column 16 tc + li of the slice.
+  // st[n][tc]: key rows srow(rb + n, g) + m, column 16 tc + li of the slice.
   const int rb = RowSplit<D>::begin(k);
   const int re = strip ? rb : RowSplit<D>::end(k);
+  // Writes state tiles (rb, rb+1) to state^T as hi/lo chunks in buffer buf.
+  auto put_state = [&](const floatx4(&x)[MAXR][2], int buf) {
+    const bool odd = g & 1;
+#pragma unroll
+    for (int tc = 0; tc < 2; ++tc) {
+      uint2 h0, l0, h1, l1;
+      split4(x[0][tc], h0, l0);
+      split4(x[1][tc], h1, l1);
+      const uint4 hv = odd ? make_uint4(h1.x, h1.y, h0.x, h0.y) : make_uint4(h0.x, h0.y, h1.x, h1.y);
+      const uint4 lv = odd ? make_uint4(l1.x, l1.y, l0.x, l0.y) : make_uint4(l0.x, l0.y, l1.x, l1.y);
+      const int so = s_off<D>(16 * tc + li, 4 * (rb >> 1) + g);
+      *reinterpret_cast<uint4*>(&Sh[buf][so]) = hv;
+      *reinterpret_cast<uint4*>(&Sl[buf][so]) = lv;
+    }
+  };
   floatx4 st[MAXR][2];
 #pragma unroll
   for (int n = 0; n < MAXR; ++n) {
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc) {
       st[n][tc] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int tr = rb + n;
-      if (tr < re) {
-        if (a.kv_init) {
+      if (rb + n < re && a.kv_init) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m)
-            st[n][tc][m] =
-                a.kv_init[state_off + (int64_t)(16 * tr + 4 * g + m) * D + c0 + 16 * tc + li];
-        }
-        uint2 hi, lo;
-        split4(st[n][tc], hi, lo);
-        const int so = (16 * tc + li) * SS + 16 * tr + 4 * g;
-        *reinterpret_cast<uint2*>(&Sh[0][so]) = hi;
-        *reinterpret_cast<uint2*>(&Sl[0][so]) = lo;
+        for (int m = 0; m < 4; ++m)
+          st[n][tc][m] =
+              a.kv_init[state_off + (int64_t)(srow(rb + n, g) + m) * D + c0 + 16 * tc + li];
       }
     }
   }
+  if (re > rb) put_state(st, 0);
 
   // Valid rows of block b (0 past the end of the sequence).
   auto block_len = [&](int b) -> int {
@@ -326,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   };
   auto store_v = [&](const VStage& r, int buf, int b) {
     const int ell = block_len(b);
-    const int o = vrow * kVS + 8 * vch;
+    const int o = v_off(vrow, 8 * vch);
     *reinterpret_cast<uint4*>(&Vs[buf][o]) = r.v;
     // value row scaled by lambda^(ell-1-j), split hi/lo
     const float wv = vrow < ell ? exp2f((float)(ell - 1 - vrow) * l2) : 0.0f;
@@ -383,7 +411,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        const int so = (16 * tc + li) * SS + 32 * kk + 8 * g;
+        const int so = s_off<D>(16 * tc + li, 4 * kk + g);
         oe[tc] = mfma(ld8(&Sh[cur][so]), qb[kk], oe[tc]);
         oe[tc] = mfma(ld8(&Sl[cur][so]), qb[kk], oe[tc]);
       }
@@ -395,8 +423,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       const bf16x8 p_l = cat2(pl[2 * kk2], pl[2 * kk2 + 1]);
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        const bf16x8 va = cat(ld_tr(&Vc[j0 * kVS + 16 * tc + 4 * tr_a]),
-                              ld_tr(&Vc[(j0 + 16) * kVS + 16 * tc + 4 * tr_a]));
+        const bf16x8 va = cat(ld_tr(&Vc[v_off(j0, 16 * tc + 4 * tr_a)]),
+                              ld_tr(&Vc[v_off(j0 + 16, 16 * tc + 4 * tr_a)]));
         oi[tc] = mfma(va, p_h, oi[tc]);
         oi[tc] = mfma(va, p_l, oi[tc]);
       }
@@ -424,9 +452,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- one block of a state wave (NR row tiles fixed at compile time) ----
-  auto state_body = [&](auto NR_, int cur, int ell) {
-    constexpr int NR = decltype(NR_)::value;
+  // ---- one block of a state wave (its pair of row tiles) ----
+  auto state_body = [&](int cur, int ell) {
+    constexpr int NR = MAXR;
     const uint16_t* Kc = Ks[cur];
     const uint16_t* Hc = Vh[cur];
     const uint16_t* Lc = Vl[cur];
@@ -439,24 +467,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       for (int tc = 0; tc < 2; ++tc) {
         const int j0 = 32 * kk2 + 4 * g + tr_r;
         const int vo = 16 * tc + 4 * tr_a;
-        vh[kk2][tc] = cat(ld_tr(&Hc[j0 * kVS + vo]), ld_tr(&Hc[(j0 + 16) * kVS + vo]));
-        vl[kk2][tc] = cat(ld_tr(&Lc[j0 * kVS + vo]), ld_tr(&Lc[(j0 + 16) * kVS + vo]));
+        vh[kk2][tc] = cat(ld_tr(&Hc[v_off(j0, vo)]), ld_tr(&Hc[v_off(j0 + 16, vo)]));
+        vl[kk2][tc] = cat(ld_tr(&Lc[v_off(j0, vo)]), ld_tr(&Lc[v_off(j0 + 16, vo)]));
       }
     }
-    bf16x8 ka[NR > 0 ? NR : 1][2];
+    bf16x8 ka[NR][2];
 #pragma unroll
     for (int n = 0; n < NR; ++n) {
       const int tr = rb + n;
 #pragma unroll
       for (int kk2 = 0; kk2 < 2; ++kk2) {
         const int j0 = 32 * kk2 + 4 * g + tr_r;
-        const int kc = 2 * tr + (tr_a >> 1);
-        const int kh = 4 * (tr_a & 1);
-        ka[n][kk2] = cat(ld_tr(&Kc[qk_off<D>(j0, kc) + kh]),
-                         ld_tr(&Kc[qk_off<D>(j0 + 16, kc) + kh]));
+        const int e = srow(tr, tr_a);  // A rows 4 tr_a .. 4 tr_a + 3 of tile tr
+        ka[n][kk2] = cat(ld_tr(&Kc[qk_off<D>(j0, e >> 3) + (e & 7)]),
+                         ld_tr(&Kc[qk_off<D>(j0 + 16, e >> 3) + (e & 7)]));
       }
     }
-    floatx4 acc[NR > 0 ? NR : 1][2];
+    floatx4 acc[NR][2];
 #pragma unroll
     for (int n = 0; n < NR; ++n)
 #pragma unroll
@@ -473,17 +500,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
         for (int tc = 0; tc < 2; ++tc) acc[n][tc] = mfma(ka[n][kk2], vl[kk2][tc], acc[n][tc]);
     }
 #pragma unroll
-    for (int n = 0; n < NR; ++n) {
+    for (int n = 0; n < NR; ++n)
 #pragma unroll
-      for (int tc = 0; tc < 2; ++tc) {
-        st[n][tc] = acc[n][tc];
-        uint2 hi, lo;
-        split4(acc[n][tc], hi, lo);
-        const int so = (16 * tc + li) * SS + 16 * (rb + n) + 4 * g;
-        *reinterpret_cast<uint2*>(&Sh[cur ^ 1][so]) = hi;
-        *reinterpret_cast<uint2*>(&Sl[cur ^ 1][so]) = lo;
-      }
-    }
+      for (int tc = 0; tc < 2; ++tc) st[n][tc] = acc[n][tc];
+    put_state(st, cur ^ 1);
   };
 
   // ---- pipeline ----
@@ -528,12 +548,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       const int cur = b & 1;
       load_v(rfree, b + 2);  // empty range past the last block
       const int ell = block_len(b);
-      switch (re - rb) {
-        case 3: state_body(IC<3>{}, cur, ell); break;
-        case 2: state_body(IC<2>{}, cur, ell); break;
-        case 1: state_body(IC<1>{}, cur, ell); break;
-        default: break;
-      }
+      if (re > rb) state_body(cur, ell);
       if (b + 1 < nblocks) store_v(rfull, cur ^ 1, b + 1);
       lds_barrier();
     };
@@ -551,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
           for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-              a.kv_final[state_off + (int64_t)(16 * tr + 4 * g + m) * D + c0 + 16 * tc + li] =
+              a.kv_final[state_off + (int64_t)(srow(tr, g) + m) * D + c0 + 16 * tc + li] =
                   st[n][tc][m];
         }
       }
