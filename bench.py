@@ -230,6 +230,52 @@ def bench_sweep(dev, reps=5):
     return res
 
 
+SEG_H, SEG_N, SEG_LEN = 8, 1 << 20, 1 << 16
+
+
+def bench_segmented(dev, reps=3):
+    """Low-parallelism case: B=1, H=8, N=1,048,576, d=128 (one GPU's share
+    of 64 heads split over 8 GPUs by head).  la_prefill has only 8 x 4 = 32
+    chains; la_prefill_segmented cuts the sequence into 16 segments of 65,536
+    tokens (512 chains) and reads K and V a second time for the segment
+    states."""
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, workload
+
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB cache flush
+    s = torch.cuda.current_stream()
+    decay = np.asarray(workload("n1m")["decay"][:SEG_H], np.float32)
+    q, k, v = device_qkv(SEG_N, SEG_H, D, 1006, dev)
+    cu = np.array([0, SEG_N], np.int32)
+    cu_dev = torch.from_numpy(cu).to(dev)
+    o = torch.empty_like(q)
+    kvf = torch.empty((1, SEG_H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(la.prefill_segmented_workspace_size(cu, SEG_H, D, SEG_LEN),
+                     dtype=torch.uint8, device=dev)
+    plain = lambda i: la.prefill(q, k, v, cu_dev, decay, out=o, kv_final=kvf,  # noqa: E731
+                                 cu_seqlens_host=cu)
+    seg = lambda i: la.prefill_segmented(q, k, v, cu_dev, decay, SEG_LEN, out=o,  # noqa: E731
+                                         kv_final=kvf, cu_seqlens_host=cu, workspace=ws)
+    plain(0)
+    seg(0)
+    tp = timed_launches(plain, reps, s, flush=lambda: scratch.zero_())
+    ts = timed_launches(seg, reps, s, flush=lambda: scratch.zero_())
+    by = prefill_bytes(SEG_N, 1, heads=SEG_H)
+    res = {"workload": f"B=1 H={SEG_H} N={SEG_N} d={D} bf16, one sequence",
+           "segment_len": SEG_LEN, "segments": SEG_N // SEG_LEN,
+           "plain_us": round(tp * 1e6, 1), "segmented_us": round(ts * 1e6, 1),
+           "speedup": round(tp / ts, 2),
+           "plain_frac_of_8TBs": round(by / tp / 1e9 / HBM_PEAK_GBS, 4),
+           "segmented_frac_of_8TBs": round(by / ts / 1e9 / HBM_PEAK_GBS, 4),
+           "segmented_tokens_per_s": round(SEG_N / ts, 0),
+           "extra_kv_bytes_segmented": SEG_N * SEG_H * D * 2 * 2}
+    del q, k, v, o, kvf, ws, scratch
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +287,8 @@ def main():
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time la_decode on the 256 x 64-head serving batch")
+    ap.add_argument("--segmented-only", action="store_true",
+                    help="only time la_prefill vs la_prefill_segmented at B=1, H=8, N=1M")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -253,6 +301,9 @@ def main():
     from la_inputs import device_qkv, workload
 
     dev = torch.device("cuda:0")
+    if args.segmented_only:
+        print(json.dumps({"segmented": bench_segmented(dev)}), flush=True)
+        return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -323,6 +374,7 @@ def main():
         del dec_state
         torch.cuda.empty_cache()
         line["sweep"] = bench_sweep(dev)
+        line["segmented"] = bench_segmented(dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     else:

@@ -52,6 +52,7 @@
 #ifndef LA_H_
 #define LA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -112,6 +113,52 @@ la_status la_prefill(const void* q, const void* k, const void* v,
                      int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
                      const float* decay, const float* kv_init, void* o, float* kv_final,
                      void* stream);
+
+/*
+ * la_prefill_segmented -- la_prefill with every sequence cut into segments of
+ * segment_len tokens that run as parallel chains; same results (up to the
+ * order of fp32 sums) and the same arguments, plus:
+ *
+ *   segment_len      tokens per segment, a positive multiple of 64; the last
+ *                    segment of a sequence may be shorter.  A sequence of L
+ *                    tokens gives max(1, ceil(L / segment_len)) segments.
+ *   workspace        device scratch of at least the size that
+ *                    la_prefill_segmented_workspace_size reports for the same
+ *                    num_seqs, cu_seqlens_host, num_heads, head_dim and
+ *                    segment_len; 16-byte aligned; overlaps no other buffer;
+ *                    contents on entry are ignored and on return undefined.
+ *   workspace_bytes  its size.
+ *
+ * It raises the number of workgroups when few (sequence, head) pairs exist.
+ * The segment states are found without any exchange beyond the device: the
+ * local decayed state of each segment (a state-only pass over K and V) is
+ * chained in order, S_(i+1) = lambda^(len_i) S_i + Shat_i, which is the
+ * local-prefix-sum step of the LASP+ sequence split (mizuki blog
+ * "MiniMax-01：4M 上下文破局", 五) done on one device; then each segment runs
+ * the prefill from its start state.  K and V are read twice.  in_dtype must
+ * be LA_BF16 (LA_FP32 is LA_ERR_UNSUPPORTED).  Errors as la_prefill, plus
+ * LA_ERR_INVALID_ARG for a bad segment_len or a NULL, misaligned, short or
+ * overlapping workspace.  Four kernels are enqueued on `stream`; nothing
+ * synchronises.
+ */
+la_status la_prefill_segmented(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                               int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                               const float* decay, const float* kv_init, void* o,
+                               float* kv_final, int32_t segment_len, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * la_prefill_segmented_workspace_size -- bytes of workspace that
+ * la_prefill_segmented needs for these arguments (host only, no device
+ * call).  *bytes is 0 on error.  Errors: LA_ERR_INVALID_ARG (NULL bytes or
+ * cu_seqlens_host, bad cu_seqlens, num_seqs < 0, bad segment_len),
+ * LA_ERR_UNSUPPORTED (heads or head_dim as la_prefill, too many segments).
+ */
+la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                              int32_t num_heads, int32_t head_dim,
+                                              int32_t segment_len, size_t* bytes);
 
 /*
  * la_decode -- one decode token per sequence, updating fp32 states in place.

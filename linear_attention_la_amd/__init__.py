@@ -6,6 +6,7 @@ the computation runs in the HIP kernels.  There is no CPU fallback: if the
 library is missing, every call raises.
 
     o, kv = prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None)
+    o, kv = prefill_segmented(q, k, v, cu_seqlens, decay, segment_len)
     o = decode(q, k, v, kv, decay)          # kv updated in place
 """
 
@@ -21,9 +22,13 @@ from ._binding import (  # noqa: F401
     lib,
     lib_path,
     la_prefill,
+    la_prefill_segmented,
+    la_prefill_segmented_workspace_size,
     la_decode,
     la_status_str,
     la_last_error,
     prefill,
+    prefill_segmented,
+    prefill_segmented_workspace_size,
     decode,
 )

@@ -53,6 +53,12 @@ def lib():
     L.la_prefill.restype = ctypes.c_int
     L.la_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int, ctypes.c_int,
                              vp, vp, vp, vp, vp]
+    L.la_prefill_segmented.restype = ctypes.c_int
+    L.la_prefill_segmented.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
+                                       ctypes.c_int, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
+    L.la_prefill_segmented_workspace_size.restype = ctypes.c_int
+    L.la_prefill_segmented_workspace_size.argtypes = [i32, vp, i32, i32, i32,
+                                                      ctypes.POINTER(ctypes.c_size_t)]
     L.la_decode.restype = ctypes.c_int
     L.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
     L.la_status_str.restype = ctypes.c_char_p
@@ -70,6 +76,24 @@ def la_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
     return lib().la_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
                             num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o,
                             kv_final, stream)
+
+
+def la_prefill_segmented(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                         num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
+                         segment_len, workspace, workspace_bytes, stream):
+    return lib().la_prefill_segmented(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                      total_tokens, num_heads, head_dim, in_dtype, out_dtype,
+                                      decay, kv_init, o, kv_final, segment_len, workspace,
+                                      workspace_bytes, stream)
+
+
+def la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
+                                        segment_len):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = lib().la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
+                                                   segment_len, ctypes.byref(n))
+    return st, n.value
 
 
 def la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream):
@@ -122,18 +146,12 @@ def _host_decay(decay, num_heads):
     return d
 
 
-def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=None,
-            final_state=True, out=None, kv_final=None, cu_seqlens_host=None):
-    """Packed varlen prefill.  q, k, v: device [T, H, d] (bf16 or fp32, same
-    dtype, contiguous).  cu_seqlens: [S+1] int (host or device).  decay: host
-    [H] floats in (0, 1].  kv_init: device fp32 [S, H, d, d] or None.
+class _Prefill:
+    """Marshalled arguments of a prefill call."""
 
-    Returns (o [T, H, d], kv_final [S, H, d, d] or None).  ``out`` and
-    ``kv_final`` may supply preallocated outputs; ``kv_final`` may be
-    ``kv_init`` itself (in-place continuation).  When cu_seqlens is a device
-    tensor, passing its host copy as ``cu_seqlens_host`` (a CPU int32 tensor or
-    array with the same contents) avoids a device-to-host copy, which would
-    synchronise the stream on every call."""
+
+def _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state, out,
+                     kv_final, cu_seqlens_host):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
@@ -179,13 +197,69 @@ def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=Non
         kv_final = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
     if not final_state:
         kv_final = None
-    st = la_prefill(q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_dev.data_ptr(),
-                    cu_host.data_ptr(), S, T, H, d, in_code, out_code,
-                    dec.ctypes.data, None if kv_init is None else kv_init.data_ptr(),
-                    out.data_ptr(), None if kv_final is None else kv_final.data_ptr(),
-                    _stream_handle(stream, dev))
+    m = _Prefill()
+    m.T, m.H, m.d, m.S, m.dev = T, H, d, S, dev
+    m.in_code, m.out_code = in_code, out_code
+    m.cu_dev, m.cu_host, m.dec = cu_dev, cu_host, dec
+    m.out, m.kv_final = out, kv_final
+    m.args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), cu_dev.data_ptr(), cu_host.data_ptr(), S,
+              T, H, d, in_code, out_code, dec.ctypes.data,
+              None if kv_init is None else kv_init.data_ptr(), out.data_ptr(),
+              None if kv_final is None else kv_final.data_ptr())
+    m.stream = _stream_handle(stream, dev)
+    return m
+
+
+def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=None,
+            final_state=True, out=None, kv_final=None, cu_seqlens_host=None):
+    """Packed varlen prefill.  q, k, v: device [T, H, d] (bf16 or fp32, same
+    dtype, contiguous).  cu_seqlens: [S+1] int (host or device).  decay: host
+    [H] floats in (0, 1].  kv_init: device fp32 [S, H, d, d] or None.
+
+    Returns (o [T, H, d], kv_final [S, H, d, d] or None).  ``out`` and
+    ``kv_final`` may supply preallocated outputs; ``kv_final`` may be
+    ``kv_init`` itself (in-place continuation).  When cu_seqlens is a device
+    tensor, passing its host copy as ``cu_seqlens_host`` (a CPU int32 tensor or
+    array with the same contents) avoids a device-to-host copy, which would
+    synchronise the stream on every call."""
+    m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
+                         out, kv_final, cu_seqlens_host)
+    _check(la_prefill(*m.args, m.stream))
+    return m.out, m.kv_final
+
+
+def prefill_segmented_workspace_size(cu_seqlens_host, num_heads, head_dim, segment_len):
+    """Bytes of workspace that prefill_segmented needs (host computation)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32).reshape(-1))
+    st, n = la_prefill_segmented_workspace_size(cu.shape[0] - 1, cu.ctypes.data, num_heads,
+                                                head_dim, segment_len)
     _check(st)
-    return out, kv_final
+    return n
+
+
+def prefill_segmented(q, k, v, cu_seqlens, decay, segment_len, kv_init=None, out_dtype=None,
+                      stream=None, final_state=True, out=None, kv_final=None,
+                      cu_seqlens_host=None, workspace=None):
+    """prefill() with every sequence cut into segments of ``segment_len``
+    tokens (a multiple of 64) processed as parallel chains.  ``workspace``: a
+    device tensor of at least prefill_segmented_workspace_size() bytes, or
+    None to allocate one.  Same returns as prefill()."""
+    torch = _torch()
+    m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
+                         out, kv_final, cu_seqlens_host)
+    st, need = la_prefill_segmented_workspace_size(m.S, m.cu_host.data_ptr(), m.H, m.d,
+                                                   segment_len)
+    _check(st)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
+        if stream is not None:
+            workspace.record_stream(stream)
+    elif not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
+              and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(la_prefill_segmented(*m.args, segment_len, workspace.data_ptr(), nbytes, m.stream))
+    return m.out, m.kv_final
 
 
 def decode(q, k, v, kv, decay, stream=None, out=None):

@@ -68,6 +68,120 @@ la_status check_heads_dim(int32_t num_heads, int32_t head_dim) {
   return LA_OK;
 }
 
+la_status check_cu(const int32_t* cu, int32_t num_seqs) {
+  if (cu[0] != 0) return fail(LA_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    if (cu[s + 1] < cu[s])
+      return fail(LA_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s], cu[s + 1]);
+  }
+  return LA_OK;
+}
+
+// Validation shared by la_prefill and la_prefill_segmented (everything
+// except the workspace).  Returns LA_OK for num_seqs == 0 after checking the
+// scalar arguments.
+la_status check_prefill(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                        int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                        int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                        const float* decay, const float* kv_init, const void* o,
+                        const float* kv_final, int32_t items_seqs) {
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  if (total_tokens < 0)
+    return fail(LA_ERR_INVALID_ARG, "total_tokens = %lld < 0", (long long)total_tokens);
+  if (total_tokens >= (int64_t)1 << 31)
+    return fail(LA_ERR_INVALID_ARG, "total_tokens = %lld does not fit int32 cu_seqlens",
+                (long long)total_tokens);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(LA_ERR_INVALID_ARG, "in_dtype = %d", (int)in_dtype);
+  if (!valid_dtype(out_dtype)) return fail(LA_ERR_INVALID_ARG, "out_dtype = %d", (int)out_dtype);
+  if (in_dtype == LA_FP32 && out_dtype == LA_BF16)
+    return fail(LA_ERR_UNSUPPORTED, "fp32 input with bf16 output is not supported");
+  if ((st = check_decay(decay, num_heads)) != LA_OK) return st;
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  if ((int64_t)cu_seqlens_host[num_seqs] != total_tokens)
+    return fail(LA_ERR_INVALID_ARG, "cu_seqlens[%d] = %d != total_tokens = %lld", num_seqs,
+                cu_seqlens_host[num_seqs], (long long)total_tokens);
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens_dev) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
+  if (total_tokens > 0 && (!q || !k || !v || !o))
+    return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL when total_tokens > 0");
+
+  const void* ptrs[] = {q, k, v, o, kv_init, kv_final};
+  const char* names[] = {"q", "k", "v", "o", "kv_init", "kv_final"};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+
+  const int cols = in_dtype == LA_BF16 ? la::kBf16Cols : la::kF32Cols;
+  const int64_t items = (int64_t)items_seqs * num_heads * (head_dim / cols);
+  if (items >= ((int64_t)1 << 31))
+    return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
+
+  // Aliasing: o and kv_final are written; they may overlap no input, except
+  // that kv_final may be exactly kv_init.
+  const size_t tok_bytes = (size_t)total_tokens * num_heads * head_dim;
+  const size_t state_bytes = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  const Range rq = range("q", q, tok_bytes * dtype_size(in_dtype));
+  const Range rk = range("k", k, tok_bytes * dtype_size(in_dtype));
+  const Range rv = range("v", v, tok_bytes * dtype_size(in_dtype));
+  const Range ro = range("o", o, tok_bytes * dtype_size(out_dtype));
+  const Range ri = range("kv_init", kv_init, kv_init ? state_bytes : 0);
+  const Range rf = range("kv_final", kv_final, kv_final ? state_bytes : 0);
+  const Range* ins[] = {&rq, &rk, &rv, &ri};
+  for (const Range* in : ins) {
+    if (overlap(ro, *in)) return fail(LA_ERR_INVALID_ARG, "o overlaps %s", in->name);
+    if (in == &ri && kv_init == kv_final) continue;
+    if (overlap(rf, *in)) return fail(LA_ERR_INVALID_ARG, "kv_final overlaps %s", in->name);
+  }
+  if (overlap(ro, rf)) return fail(LA_ERR_INVALID_ARG, "o overlaps kv_final");
+  return LA_OK;
+}
+
+la_status check_segment_len(int32_t segment_len) {
+  if (segment_len <= 0 || segment_len % 64 != 0)
+    return fail(LA_ERR_INVALID_ARG, "segment_len = %d is not a positive multiple of 64",
+                segment_len);
+  return LA_OK;
+}
+
+// Byte offsets of the segmented-prefill workspace sections (each 256 B
+// aligned): cu_seg [n+1], init_slot [n], final_slot [n], seq_first [S+1]
+// (int32), then fp32 states [(n + S), H, d, d], n = number of segments.
+struct SegmentLayout {
+  int32_t num_segments;
+  size_t cu_seg, init_slot, final_slot, seq_first, states, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
+                         int32_t head_dim, int32_t segment_len, SegmentLayout* lay) {
+  int64_t n = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t len = (int64_t)cu[s + 1] - cu[s];
+    n += len <= 0 ? 1 : (len + segment_len - 1) / segment_len;
+  }
+  if (n + num_seqs >= ((int64_t)1 << 31))
+    return fail(LA_ERR_UNSUPPORTED, "%lld segments exceed the int32 range", (long long)n);
+  lay->num_segments = (int32_t)n;
+  size_t off = 0;
+  lay->cu_seg = off;
+  off = align256(off + (size_t)(n + 1) * 4);
+  lay->init_slot = off;
+  off = align256(off + (size_t)n * 4);
+  lay->final_slot = off;
+  off = align256(off + (size_t)n * 4);
+  lay->seq_first = off;
+  off = align256(off + (size_t)(num_seqs + 1) * 4);
+  lay->states = off;
+  off += (size_t)(n + num_seqs) * num_heads * head_dim * head_dim * 4;
+  lay->total = off;
+  return LA_OK;
+}
+
 la_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -95,63 +209,10 @@ la_status la_prefill(const void* q, const void* k, const void* v,
                      int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
                      const float* decay, const float* kv_init, void* o, float* kv_final,
                      void* stream) {
-  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
-  if (total_tokens < 0)
-    return fail(LA_ERR_INVALID_ARG, "total_tokens = %lld < 0", (long long)total_tokens);
-  if (total_tokens >= (int64_t)1 << 31)
-    return fail(LA_ERR_INVALID_ARG, "total_tokens = %lld does not fit int32 cu_seqlens",
-                (long long)total_tokens);
-  la_status st = check_heads_dim(num_heads, head_dim);
-  if (st != LA_OK) return st;
-  if (!valid_dtype(in_dtype)) return fail(LA_ERR_INVALID_ARG, "in_dtype = %d", (int)in_dtype);
-  if (!valid_dtype(out_dtype)) return fail(LA_ERR_INVALID_ARG, "out_dtype = %d", (int)out_dtype);
-  if (in_dtype == LA_FP32 && out_dtype == LA_BF16)
-    return fail(LA_ERR_UNSUPPORTED, "fp32 input with bf16 output is not supported");
-  if ((st = check_decay(decay, num_heads)) != LA_OK) return st;
-  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
-  if (cu_seqlens_host[0] != 0)
-    return fail(LA_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu_seqlens_host[0]);
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    if (cu_seqlens_host[s + 1] < cu_seqlens_host[s])
-      return fail(LA_ERR_INVALID_ARG, "cu_seqlens decreases at %d (%d -> %d)", s,
-                  cu_seqlens_host[s], cu_seqlens_host[s + 1]);
-  }
-  if ((int64_t)cu_seqlens_host[num_seqs] != total_tokens)
-    return fail(LA_ERR_INVALID_ARG, "cu_seqlens[%d] = %d != total_tokens = %lld", num_seqs,
-                cu_seqlens_host[num_seqs], (long long)total_tokens);
-  if (num_seqs == 0) return ok();
-  if (!cu_seqlens_dev) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
-  if (total_tokens > 0 && (!q || !k || !v || !o))
-    return fail(LA_ERR_INVALID_ARG, "q, k, v and o must be non-NULL when total_tokens > 0");
-
-  const void* ptrs[] = {q, k, v, o, kv_init, kv_final};
-  const char* names[] = {"q", "k", "v", "o", "kv_init", "kv_final"};
-  for (int i = 0; i < 6; ++i)
-    if (!aligned16(ptrs[i]))
-      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
-
-  const int cols = in_dtype == LA_BF16 ? la::kBf16Cols : la::kF32Cols;
-  const int64_t items = (int64_t)num_seqs * num_heads * (head_dim / cols);
-  if (items >= ((int64_t)1 << 31))
-    return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
-
-  // Aliasing: o and kv_final are written; they may overlap no input, except
-  // that kv_final may be exactly kv_init.
-  const size_t tok_bytes = (size_t)total_tokens * num_heads * head_dim;
-  const size_t state_bytes = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
-  const Range rq = range("q", q, tok_bytes * dtype_size(in_dtype));
-  const Range rk = range("k", k, tok_bytes * dtype_size(in_dtype));
-  const Range rv = range("v", v, tok_bytes * dtype_size(in_dtype));
-  const Range ro = range("o", o, tok_bytes * dtype_size(out_dtype));
-  const Range ri = range("kv_init", kv_init, kv_init ? state_bytes : 0);
-  const Range rf = range("kv_final", kv_final, kv_final ? state_bytes : 0);
-  const Range* ins[] = {&rq, &rk, &rv, &ri};
-  for (const Range* in : ins) {
-    if (overlap(ro, *in)) return fail(LA_ERR_INVALID_ARG, "o overlaps %s", in->name);
-    if (in == &ri && kv_init == kv_final) continue;
-    if (overlap(rf, *in)) return fail(LA_ERR_INVALID_ARG, "kv_final overlaps %s", in->name);
-  }
-  if (overlap(ro, rf)) return fail(LA_ERR_INVALID_ARG, "o overlaps kv_final");
+  la_status st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                               num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o,
+                               kv_final, num_seqs);
+  if (st != LA_OK || num_seqs == 0) return st;
 
   la::PrefillArgs a;
   memset(&a, 0, sizeof(a));
@@ -164,13 +225,119 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   a.kv_final = kv_final;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
-  a.num_items = (int32_t)items;
+  const int cols = in_dtype == LA_BF16 ? la::kBf16Cols : la::kF32Cols;
+  a.num_items = (int32_t)((int64_t)num_seqs * num_heads * (head_dim / cols));
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = in_dtype == LA_BF16 ? la::launch_prefill_bf16(a, head_dim, out_dtype, s)
+  hipError_t e = in_dtype == LA_BF16 ? la::launch_prefill_bf16(a, head_dim, out_dtype, false, s)
                                      : la::launch_prefill_f32(a, head_dim, out_dtype, s);
   return hip_status(e, "la_prefill launch");
+}
+
+la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                              int32_t num_heads, int32_t head_dim,
+                                              int32_t segment_len, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if ((st = check_segment_len(segment_len)) != LA_OK) return st;
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  SegmentLayout lay;
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
+    return st;
+  *bytes = lay.total;
+  return ok();
+}
+
+la_status la_prefill_segmented(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                               int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                               const float* decay, const float* kv_init, void* o,
+                               float* kv_final, int32_t segment_len, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  la_status st = check_segment_len(segment_len);
+  if (st != LA_OK) return st;
+  if (in_dtype != LA_BF16 && valid_dtype(in_dtype))
+    return fail(LA_ERR_UNSUPPORTED, "the segmented prefill takes bf16 inputs only");
+  if ((st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                          num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
+                          num_seqs)) != LA_OK)
+    return st;
+  if (num_seqs == 0) return ok();
+  SegmentLayout lay;
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
+    return st;
+  if (!workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(LA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes,
+                lay.total);
+  // The workspace may overlap no argument buffer.
+  {
+    const size_t tok = (size_t)total_tokens * num_heads * head_dim;
+    const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+    const Range rw = range("workspace", workspace, lay.total);
+    const Range others[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
+                            range("o", o, tok * dtype_size(out_dtype)),
+                            range("kv_init", kv_init, kv_init ? sb : 0),
+                            range("kv_final", kv_final, kv_final ? sb : 0)};
+    for (const Range& r : others)
+      if (overlap(rw, r)) return fail(LA_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+  }
+  const int64_t items = (int64_t)lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
+  if (items >= ((int64_t)1 << 31) ||
+      (int64_t)num_seqs * num_heads * (head_dim * head_dim / 1024) >= ((int64_t)1 << 31))
+    return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
+
+  char* ws = static_cast<char*>(workspace);
+  int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + lay.cu_seg);
+  int32_t* init_slot = reinterpret_cast<int32_t*>(ws + lay.init_slot);
+  int32_t* final_slot = reinterpret_cast<int32_t*>(ws + lay.final_slot);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + lay.seq_first);
+  float* states = reinterpret_cast<float*>(ws + lay.states);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float l2[LA_MAX_HEADS];
+  for (int32_t h = 0; h < num_heads; ++h) l2[h] = (float)log2((double)decay[h]);
+
+  hipError_t e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, segment_len, cu_seg, init_slot,
+                                         final_slot, seq_first, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_segmented plan launch");
+
+  // pass 1: local decayed state of every segment, from a zero state
+  la::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seg;
+  a.kv_final = states;
+  a.final_slot = final_slot;
+  a.num_seqs = lay.num_segments;
+  a.num_heads = num_heads;
+  a.num_items = (int32_t)items;
+  for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
+  e = la::launch_prefill_bf16(a, head_dim, LA_BF16, true, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_segmented state pass launch");
+
+  // pass 2: states at every segment start (and the final states)
+  e = la::launch_segment_prefix(cu_seg, seq_first, num_seqs, num_heads, head_dim, l2, kv_init,
+                                states, kv_final, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_segmented prefix launch");
+
+  // pass 3: outputs of every segment from its start state
+  a.kv_init = states;
+  a.init_slot = init_slot;
+  a.kv_final = nullptr;
+  a.final_slot = nullptr;
+  a.o = o;
+  e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, s);
+  return hip_status(e, "la_prefill_segmented output pass launch");
 }
 
 la_status la_decode(const void* q, const void* k, const void* v, float* kv,

@@ -17,9 +17,14 @@ struct PrefillArgs {
   const void* k;
   const void* v;
   const int32_t* cu_seqlens;  // device [S+1]
-  const float* kv_init;       // device [S,H,d,d] or nullptr
-  void* o;                    // device [T,H,d]
-  float* kv_final;            // device [S,H,d,d] or nullptr
+  const float* kv_init;       // device [*,H,d,d] or nullptr
+  void* o;                    // device [T,H,d] (unused by a state-only pass)
+  float* kv_final;            // device [*,H,d,d] or nullptr
+  // Optional device [S] maps from sequence to state slot of kv_init /
+  // kv_final (nullptr: slot s for sequence s).  Only the bf16 kernel reads
+  // them; the segmented prefill uses them to address its state workspace.
+  const int32_t* init_slot;
+  const int32_t* final_slot;
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_items;          // S * H * (d / value-columns per workgroup)
@@ -39,8 +44,27 @@ struct DecodeArgs {
 
 // Each returns hipSuccess or the launch error.  The caller has validated
 // every argument.
+// state_only: compute and write only the final states (no O): K and V are
+// read, Q is not.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, la_dtype out_dtype,
-                               hipStream_t stream);
+                               bool state_only, hipStream_t stream);
+
+// Segmented prefill helpers (la_segment.hip).  Plan: from cu_seqlens [S+1]
+// and segment_len, write cu_seg [n_seg+1], init_slot/final_slot [n_seg] and
+// seq_first [S+1] (first segment of each sequence) for a state workspace
+// holding n_seg + S slots: sequence s owns slots seq_first[s] + s ..
+// seq_first[s] + s + n_s.
+hipError_t launch_segment_plan(const int32_t* cu_seqlens, int32_t num_seqs, int32_t segment_len,
+                               int32_t* cu_seg, int32_t* init_slot, int32_t* final_slot,
+                               int32_t* seq_first, hipStream_t stream);
+// Prefix over segments: slot 0 of each sequence <- kv_init (or 0); slot i+1
+// <- lambda^len_i * slot i + slot i+1 (which holds segment i's local
+// state); the last slot is also written to kv_final (if not null).
+// log2_decay: host [H] (passed by value to the kernel).
+hipError_t launch_segment_prefix(const int32_t* cu_seg, const int32_t* seq_first, int32_t num_seqs,
+                                 int32_t num_heads, int32_t head_dim, const float* log2_decay,
+                                 const float* kv_init, float* states, float* kv_final,
+                                 hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, la_dtype out_dtype,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, la_dtype in_dtype,

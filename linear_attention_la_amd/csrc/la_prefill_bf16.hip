@@ -193,7 +193,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int D, bool kOutF32>
+template <int D, bool kOutF32, bool kStateOnly>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NDV = D / kDV;
   constexpr int NK = D / 32;       // k-steps over d
@@ -233,7 +233,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   const uint16_t* __restrict__ q = static_cast<const uint16_t*>(a.q);
   const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ v = static_cast<const uint16_t*>(a.v);
-  const int64_t state_off = ((int64_t)s * H + h) * D * D;
+  // state slots of this sequence in kv_init / kv_final
+  const int64_t init_off = ((int64_t)(a.init_slot ? a.init_slot[s] : s) * H + h) * D * D;
+  const int64_t final_off = ((int64_t)(a.final_slot ? a.final_slot[s] : s) * H + h) * D * D;
   const int row_stride = H * D;  // elements between tokens (< 2^15)
   const float l2 = a.log2_decay[h];
   const float lam_beta = exp2f((float)kBeta * l2);
@@ -286,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
           st[n][tc][m] =
-              a.kv_init[state_off + (int64_t)(srow(rb + n, g) + m) * D + c0 + 16 * tc + li];
+              a.kv_init[init_off + (int64_t)(srow(rb + n, g) + m) * D + c0 + 16 * tc + li];
       }
     }
   }
@@ -514,7 +516,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   // after block b's arithmetic.  One barrier per block publishes the LDS
   // writes.  The two roles run separate loops with the same number of
   // barriers, so the registers of one role are not kept live in the other.
-  if (strip) {
+  if (strip && kStateOnly) {
+    // state-only pass: the strip waves only stage K
+    KStage k0, k1;
+    load_k(k0, 0);
+    load_k(k1, 1);
+    store_k(k0, 0);
+    lds_barrier();
+    auto kstep = [&](int b, KStage& kfree, KStage& kfull) {
+      load_k(kfree, b + 2);  // empty range past the last block
+      if (b + 1 < nblocks) store_k(kfull, (b & 1) ^ 1);
+      lds_barrier();
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+      kstep(b, k0, k1);
+      if (b + 1 < nblocks) kstep(b + 1, k1, k0);
+    }
+  } else if (strip) {
     bf16x8 qa[NK], qb2[NK];
     KStage k0, k1;
     load_q(qa, 0);
@@ -566,7 +584,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
           for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-              a.kv_final[state_off + (int64_t)(srow(tr, g) + m) * D + c0 + 16 * tc + li] =
+              a.kv_final[final_off + (int64_t)(srow(tr, g) + m) * D + c0 + 16 * tc + li] =
                   st[n][tc][m];
         }
       }
@@ -575,21 +593,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, la_dtype out_dtype, hipStream_t stream) {
+hipError_t launch_d(const PrefillArgs& a, la_dtype out_dtype, bool state_only, hipStream_t stream) {
   const dim3 grid(a.num_items), block(kThreads);
-  if (out_dtype == LA_FP32)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), grid, block, 0, stream, a);
+  if (state_only)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, stream, a);
+  else if (out_dtype == LA_FP32)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, la_dtype out_dtype,
-                               hipStream_t stream) {
-  if (head_dim == 64) return launch_d<64>(a, out_dtype, stream);
-  return launch_d<128>(a, out_dtype, stream);
+                               bool state_only, hipStream_t stream) {
+  if (head_dim == 64) return launch_d<64>(a, out_dtype, state_only, stream);
+  return launch_d<128>(a, out_dtype, state_only, stream);
 }
 
 }  // namespace la

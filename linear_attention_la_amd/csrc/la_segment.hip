@@ -1,0 +1,135 @@
+// Segmented prefill: planning and the prefix over segment states.
+//
+// A long sequence is cut into segments that are processed as independent
+// chains, which multiplies the number of workgroups when few (sequence,
+// head) pairs exist.  Segment i of a sequence needs the state reached at its
+// start; it is obtained from the local decayed state of every earlier
+// segment, Shat_i = sum_{j in i} lambda^(len_i - 1 - j) k_j^T v_j (computed
+// by a state-only pass of the prefill kernel), chained in order:
+//   S_0 = S_init,   S_(i+1) = lambda^(len_i) S_i + Shat_i.
+// This is the one-exchange sequence split of LASP+ (mizuki blog "MiniMax-01：
+// 4M 上下文破局", 五: local prefix sums, then an all-gather) carried out on
+// one device; it is exact: expanding the chain gives the same sum of decayed
+// k_j^T v_j terms as the token recurrence.
+
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ int segments_of(int32_t len, int32_t segment_len) {
+  return len <= 0 ? 1 : (int)((len + (int64_t)segment_len - 1) / segment_len);
+}
+
+// One workgroup.  Thread t owns a contiguous range of sequences; a prefix
+// sum of the per-thread segment counts gives each thread its first segment.
+__global__ __launch_bounds__(kPlanThreads) void segment_plan_kernel(
+    const int32_t* __restrict__ cu, int32_t num_seqs, int32_t segment_len, int32_t* cu_seg,
+    int32_t* init_slot, int32_t* final_slot, int32_t* seq_first) {
+  __shared__ int32_t part[kPlanThreads];
+  const int t = threadIdx.x;
+  const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
+  const int s0 = min(num_seqs, t * per);
+  const int s1 = min(num_seqs, s0 + per);
+  int32_t count = 0;
+  for (int s = s0; s < s1; ++s) count += segments_of(cu[s + 1] - cu[s], segment_len);
+  part[t] = count;
+  __syncthreads();
+  if (t == 0) {
+    int32_t run = 0;
+    for (int i = 0; i < kPlanThreads; ++i) {
+      const int32_t c = part[i];
+      part[i] = run;  // exclusive prefix
+      run += c;
+    }
+    seq_first[num_seqs] = run;
+    cu_seg[run] = cu[num_seqs];
+  }
+  __syncthreads();
+  int32_t g = part[t];
+  for (int s = s0; s < s1; ++s) {
+    seq_first[s] = g;
+    const int32_t start = cu[s];
+    const int32_t len = cu[s + 1] - start;
+    const int n = segments_of(len, segment_len);
+    for (int i = 0; i < n; ++i, ++g) {
+      const int64_t off = (int64_t)i * segment_len;
+      cu_seg[g] = start + (int32_t)(off < len ? off : len);
+      init_slot[g] = g + s;       // slot of the state at the segment start
+      final_slot[g] = g + s + 1;  // slot receiving its local state
+    }
+  }
+}
+
+struct PrefixArgs {
+  const int32_t* cu_seg;
+  const int32_t* seq_first;
+  const float* kv_init;
+  float* states;
+  float* kv_final;
+  int32_t num_heads;
+  int32_t chunks;  // float4 chunks of 256 threads per d x d state
+  float log2_decay[LA_MAX_HEADS];
+};
+
+// Workgroup (s, h, chunk): each thread carries 4 consecutive state elements
+// through the segments of sequence s.
+__global__ __launch_bounds__(256) void segment_prefix_kernel(PrefixArgs a, int64_t dd) {
+  const int chunk = blockIdx.x % a.chunks;
+  const int sh = blockIdx.x / a.chunks;
+  const int h = sh % a.num_heads;
+  const int s = sh / a.num_heads;
+  const int64_t e = ((int64_t)chunk * 256 + threadIdx.x) * 4;
+  const int64_t head_off = (int64_t)h * dd + e;
+  const int64_t slot_stride = (int64_t)a.num_heads * dd;
+  float4 x = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (a.kv_init) x = *reinterpret_cast<const float4*>(a.kv_init + (int64_t)s * slot_stride + head_off);
+  const int32_t first = a.seq_first[s];
+  const int32_t n = a.seq_first[s + 1] - first;
+  float* slot = a.states + (int64_t)(first + s) * slot_stride + head_off;
+  *reinterpret_cast<float4*>(slot) = x;
+  const float l2 = a.log2_decay[h];
+  for (int i = 0; i < n; ++i) {
+    const int32_t len = a.cu_seg[first + i + 1] - a.cu_seg[first + i];
+    const float f = exp2f((float)len * l2);  // lambda^len
+    float* next = slot + (int64_t)(i + 1) * slot_stride;
+    const float4 loc = *reinterpret_cast<const float4*>(next);
+    x = make_float4(fmaf(f, x.x, loc.x), fmaf(f, x.y, loc.y), fmaf(f, x.z, loc.z),
+                    fmaf(f, x.w, loc.w));
+    *reinterpret_cast<float4*>(next) = x;
+  }
+  if (a.kv_final) *reinterpret_cast<float4*>(a.kv_final + (int64_t)s * slot_stride + head_off) = x;
+}
+
+}  // namespace
+
+hipError_t launch_segment_plan(const int32_t* cu_seqlens, int32_t num_seqs, int32_t segment_len,
+                               int32_t* cu_seg, int32_t* init_slot, int32_t* final_slot,
+                               int32_t* seq_first, hipStream_t stream) {
+  hipLaunchKernelGGL(segment_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_seqlens,
+                     num_seqs, segment_len, cu_seg, init_slot, final_slot, seq_first);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_prefix(const int32_t* cu_seg, const int32_t* seq_first, int32_t num_seqs,
+                                 int32_t num_heads, int32_t head_dim, const float* log2_decay,
+                                 const float* kv_init, float* states, float* kv_final,
+                                 hipStream_t stream) {
+  PrefixArgs a;
+  a.cu_seg = cu_seg;
+  a.seq_first = seq_first;
+  a.kv_init = kv_init;
+  a.states = states;
+  a.kv_final = kv_final;
+  a.num_heads = num_heads;
+  const int64_t dd = (int64_t)head_dim * head_dim;
+  a.chunks = (int32_t)(dd / 1024);  // d = 64: 4, d = 128: 16
+  for (int h = 0; h < num_heads; ++h) a.log2_decay[h] = log2_decay[h];
+  const int64_t blocks = (int64_t)num_seqs * num_heads * a.chunks;
+  hipLaunchKernelGGL(segment_prefix_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, dd);
+  return hipGetLastError();
+}
+
+}  // namespace la

@@ -27,7 +27,8 @@ def _declared_functions():
 
 def test_header_declares_entry_points():
     names = _declared_functions()
-    for n in ("la_prefill", "la_decode", "la_status_str", "la_last_error"):
+    for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
+              "la_decode", "la_status_str", "la_last_error"):
         assert n in names
 
 
@@ -168,3 +169,74 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="not found"):
         _binding.lib()
     monkeypatch.setattr(_binding, "_lib", None)
+
+
+# ---- segmented prefill (host-side checks only) ----
+
+def _ws_size(cu, H=4, d=128, seg=64):
+    cu = np.asarray(cu, np.int32)
+    return la.la_prefill_segmented_workspace_size(cu.shape[0] - 1, cu.ctypes.data, H, d, seg)
+
+
+def test_segmented_workspace_size_layout():
+    """8 segments (lengths 100, 0, 300 at 64 tokens each: 2 + 1 + 5), 4
+    sections of int32 padded to 256 B, then (8 + 3) fp32 states of 4 x 128^2."""
+    st, n = _ws_size([0, 100, 100, 400])
+    assert st == la.LA_OK
+    assert n == 4 * 256 + 11 * 4 * 128 * 128 * 4
+    st, n = _ws_size([0, 64], seg=64)       # exactly one segment
+    assert st == la.LA_OK and n == 4 * 256 + 2 * 4 * 128 * 128 * 4
+    st, n = _ws_size([0], seg=64)           # no sequences: the empty slot sections take no space
+    assert st == la.LA_OK and n == 2 * 256
+
+
+@pytest.mark.parametrize("seg", [0, -64, 100, 63])
+def test_segmented_workspace_size_rejects_segment_len(seg):
+    st, n = _ws_size([0, 100], seg=seg)
+    assert st == la.LA_ERR_INVALID_ARG and n == 0
+    assert la.la_last_error()
+
+
+def test_segmented_workspace_size_rejects_bad_cu():
+    assert _ws_size([1, 100])[0] == la.LA_ERR_INVALID_ARG
+    assert _ws_size([0, 100, 50])[0] == la.LA_ERR_INVALID_ARG
+    assert _ws_size([0, 100], d=96)[0] == la.LA_ERR_UNSUPPORTED
+
+
+WS = 0x90000000
+
+
+def _seg(**kw):
+    args = dict(q=Q, k=K, v=V, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2, T=T,
+                H=H, d=D, in_dt=la.LA_BF16, out_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), kv_init=None, o=O, kv_final=KVF, seg=64,
+                ws=WS, ws_bytes=1 << 30)
+    args.update(kw)
+    cu = args["cu_host"]
+    st = la.la_prefill_segmented(args["q"], args["k"], args["v"], args["cu_dev"],
+                                 None if cu is None else cu.ctypes.data, args["S"], args["T"],
+                                 args["H"], args["d"], args["in_dt"], args["out_dt"],
+                                 args["decay"].ctypes.data, args["kv_init"], args["o"],
+                                 args["kv_final"], args["seg"], args["ws"], args["ws_bytes"], None)
+    return st, la.la_last_error()
+
+
+BAD_SEGMENTED = [
+    ("segment_len_zero", dict(seg=0), la.LA_ERR_INVALID_ARG),
+    ("segment_len_not_multiple", dict(seg=96), la.LA_ERR_INVALID_ARG),
+    ("fp32_input", dict(in_dt=la.LA_FP32, out_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
+    ("workspace_null", dict(ws=None), la.LA_ERR_INVALID_ARG),
+    ("workspace_misaligned", dict(ws=WS + 8), la.LA_ERR_INVALID_ARG),
+    ("workspace_too_small", dict(ws_bytes=4096), la.LA_ERR_INVALID_ARG),
+    ("workspace_overlaps_q", dict(ws=Q + 256), la.LA_ERR_INVALID_ARG),
+    ("workspace_overlaps_kv_final", dict(ws=KVF - 4096), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_k", dict(o=K + 64), la.LA_ERR_INVALID_ARG),
+    ("cu_last_mismatch", dict(cu_host=np.array([0, 40, 99], np.int32)), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_SEGMENTED, ids=[b[0] for b in BAD_SEGMENTED])
+def test_segmented_rejects(name, kw, code):
+    st, msg = _seg(**kw)
+    assert st == code, (st, msg)
+    assert msg

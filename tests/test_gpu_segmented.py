@@ -1,0 +1,113 @@
+"""GPU parity of la_prefill_segmented (sequences cut into parallel segments)
+against the fp64 oracle, and its agreement with la_prefill (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import cu_seqlens, device_qkv, host_qkv, random_states, workload
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _run(dev, lengths, H, d, decay, seed, segment_len, kv_init=False, out_f32=False,
+         in_place=False):
+    import torch
+    import linear_attention_la_amd as la
+
+    say(f"case segmented lengths={list(lengths)[:8]} H={H} d={d} segment_len={segment_len} "
+        f"kv_init={kv_init} out_f32={out_f32} in_place={in_place}")
+    T = int(sum(lengths))
+    q, k, v = host_qkv(T, H, d, seed, "bf16")
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(len(lengths), H, d, seed + 7, scale=0.1) if kv_init else None
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    kv0d = to_dev(kv0, torch.float32, dev) if kv_init else None
+    o, kv = la.prefill_segmented(qd, kd, vd, cu, decay, segment_len, kv_init=kv0d,
+                                 out_dtype=torch.float32 if out_f32 else None,
+                                 kv_final=kv0d if in_place else None)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0)
+    return to_np(o), to_np(kv), o_ref, kv_ref
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("segment_len", [64, 128, 192])
+def test_ragged_segments(dev, d, segment_len):
+    """Lengths below, at and across segment boundaries (empty, 1, 63..65,
+    several segments plus a tail), decays from none to strong."""
+    lengths = [1, 63, 64, 65, 129, 0, 300, 17, 450]
+    decay = np.array([1.0, 0.99, 0.9, 0.5], np.float32)
+    o, kv, o_ref, kv_ref = _run(dev, lengths, 4, d, decay, 31 + d + segment_len, segment_len)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="segmented o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="segmented kv")
+    say("segmented ragged", s1, s2)
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_kv_init_and_fp32_out(dev, in_place):
+    """Initial states carried into the first segment; fp32 output; the final
+    state written over kv_init (in-place continuation)."""
+    lengths = [200, 0, 513]
+    decay = np.array([0.999, 0.97, 0.8], np.float32)
+    o, kv, o_ref, kv_ref = _run(dev, lengths, 3, 128, decay, 77, 128, kv_init=True, out_f32=True,
+                                in_place=in_place)
+    parity.check(o, o_ref, 1, 1e-2, what="segmented kv_init o")
+    parity.check(kv, kv_ref, 1, 1e-2, what="segmented kv_init kv")
+
+
+def test_long_sequence_two_heads(dev):
+    """One 65,536-token sequence, 2 heads, 16 segments of 4096: every output
+    and the final state against the oracle."""
+    w = workload("sweep65536")
+    decay = np.asarray(w["decay"][:2], np.float32)
+    o, kv, o_ref, kv_ref = _run(dev, [65536], 2, 128, decay, 91, 4096)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="segmented 64K o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="segmented 64K kv")
+    say("segmented 64K", s1, s2)
+
+
+def test_matches_unsegmented_n8k(dev):
+    """B=1, H=64, N=8192 with 4 segments agrees with la_prefill to the
+    oracle tolerance on every head (same inputs, different fp32 sum order)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload("n8k")
+    say("case segmented vs la_prefill n8k")
+    q, k, v = device_qkv(8192, 64, 128, w["seed"], dev)
+    cu = torch.tensor([0, 8192], dtype=torch.int32, device=dev)
+    o1, kv1 = la.prefill(q, k, v, cu, w["decay"], cu_seqlens_host=[0, 8192])
+    o2, kv2 = la.prefill_segmented(q, k, v, cu, w["decay"], 2048, cu_seqlens_host=[0, 8192])
+    torch.cuda.synchronize()
+    s1 = parity.check(to_np(o2), to_np(o1), 1, 1e-2, out_bf16=True, what="seg vs plain o")
+    s2 = parity.check(to_np(kv2), to_np(kv1), 1, 1e-2, what="seg vs plain kv")
+    say("segmented vs plain", s1, s2)
+
+
+def test_caller_workspace_reused(dev):
+    """A caller-provided workspace serves two calls of different sizes."""
+    import torch
+    import linear_attention_la_amd as la
+
+    decay = np.array([0.95, 0.6], np.float32)
+    big = la.prefill_segmented_workspace_size(cu_seqlens([700, 300]), 2, 128, 128)
+    ws = torch.empty(big, dtype=torch.uint8, device=dev)
+    for lengths, seed in (([700, 300], 5), ([130], 6)):
+        say(f"case workspace reuse lengths={lengths}")
+        T = sum(lengths)
+        q, k, v = host_qkv(T, 2, 128, seed, "bf16")
+        cu = cu_seqlens(lengths)
+        qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+        o, kv = la.prefill_segmented(qd, kd, vd, cu, decay, 128, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay)
+        parity.check(to_np(o), o_ref, 1, 1e-2, out_bf16=True, what="workspace reuse o")
+        parity.check(to_np(kv), kv_ref, 1, 1e-2, what="workspace reuse kv")
