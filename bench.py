@@ -159,6 +159,36 @@ def bench_decode(dev, reps=20):
             "bytes_per_launch": decode_bytes(B)}, (q, k, v, kv, out, w)
 
 
+def bench_decode_pool(dev, reps=20, pool_size=1024):
+    """la_decode_pool: the 256-sequence serving batch at random distinct
+    slots of a pool of 1024 states (H=64, d=128); same bytes as la_decode."""
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states, workload
+
+    w = workload("mixed_decode")
+    B = w["batch"]
+    pool = device_states(pool_size, H, D, w["seed"] + 2, dev, scale=0.5)
+    slots_h = np.random.default_rng(w["seed"]).choice(pool_size, size=B, replace=False)
+    slots_h = slots_h.astype(np.int32)
+    slots = torch.from_numpy(slots_h).to(dev)
+    q, k, v = (x.view(B, H, D) for x in device_qkv(B, H, D, w["seed"] + 1, dev))
+    out = torch.empty_like(q)
+    s = torch.cuda.current_stream()
+    run = lambda i: la.decode_pool(q, k, v, pool, slots, w["decay"], out=out,  # noqa: E731
+                                   slots_host=slots_h)
+    for _ in range(3):
+        run(0)
+    t = timed_launches(run, reps, s)
+    gbs = decode_bytes(B) / t / 1e9
+    del pool
+    torch.cuda.empty_cache()
+    return {"batch": B, "pool_size": pool_size, "heads": H, "head_dim": D,
+            "us": round(t * 1e6, 2), "GB_per_s": round(gbs, 1),
+            "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def bench_mixed(dev, dec_state, reps=10):
     import torch
 
@@ -287,6 +317,8 @@ def main():
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time la_decode on the 256 x 64-head serving batch")
+    ap.add_argument("--pool-only", action="store_true",
+                    help="only time la_decode_pool (256 sequences on a pool of 1024)")
     ap.add_argument("--segmented-only", action="store_true",
                     help="only time la_prefill vs la_prefill_segmented at B=1, H=8, N=1M")
     args = ap.parse_args()
@@ -301,6 +333,9 @@ def main():
     from la_inputs import device_qkv, workload
 
     dev = torch.device("cuda:0")
+    if args.pool_only:
+        print(json.dumps({"decode_pool": bench_decode_pool(dev)}), flush=True)
+        return
     if args.segmented_only:
         print(json.dumps({"segmented": bench_segmented(dev)}), flush=True)
         return
@@ -370,6 +405,7 @@ def main():
     if not args.no_extra:
         dec, dec_state = bench_decode(dev)
         line["decode"] = dec
+        line["decode_pool"] = bench_decode_pool(dev)
         line["mixed"] = bench_mixed(dev, dec_state)
         del dec_state
         torch.cuda.empty_cache()

@@ -184,6 +184,29 @@ la_status la_decode(const void* q, const void* k, const void* v, float* kv,
                     const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
                     la_dtype in_dtype, void* o, void* stream);
 
+/*
+ * la_decode_pool -- la_decode on a state pool: sequence b reads and updates
+ * state kv_pool[slots[b]], so a server can keep the states of all live
+ * sequences in one pool and decode any subset of them in one launch (the
+ * serving engine's length-1 path, jvyan.cn 二、计算优化; CSDN §3.2).
+ *
+ *   kv_pool     device fp32 [pool_size, H, d, d], read and written in place;
+ *               entries no slot names are not touched.
+ *   pool_size   number of states in the pool (>= 0).
+ *   slots_dev   device int32 [batch]: pool index of sequence b.
+ *   slots_host  host int32 [batch], same contents; validated before any
+ *               launch: every slot in [0, pool_size) and no slot twice.
+ *   q, k, v, o, decay, batch, num_heads, head_dim, in_dtype, stream: as in
+ *               la_decode; o must not overlap the pool.
+ *
+ * Errors as la_decode, plus LA_ERR_INVALID_ARG for a NULL slot array, a slot
+ * out of range or a repeated slot.
+ */
+la_status la_decode_pool(const void* q, const void* k, const void* v, float* kv_pool,
+                         int32_t pool_size, const int32_t* slots_dev, const int32_t* slots_host,
+                         const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                         la_dtype in_dtype, void* o, void* stream);
+
 /* Static, never-NULL name of a status code. */
 const char* la_status_str(la_status s);
 

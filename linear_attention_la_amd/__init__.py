@@ -8,6 +8,7 @@ library is missing, every call raises.
     o, kv = prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None)
     o, kv = prefill_segmented(q, k, v, cu_seqlens, decay, segment_len)
     o = decode(q, k, v, kv, decay)          # kv updated in place
+    o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
 """
 
 from ._binding import (  # noqa: F401
@@ -25,10 +26,12 @@ from ._binding import (  # noqa: F401
     la_prefill_segmented,
     la_prefill_segmented_workspace_size,
     la_decode,
+    la_decode_pool,
     la_status_str,
     la_last_error,
     prefill,
     prefill_segmented,
     prefill_segmented_workspace_size,
     decode,
+    decode_pool,
 )

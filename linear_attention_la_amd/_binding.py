@@ -61,6 +61,9 @@ def lib():
                                                       ctypes.POINTER(ctypes.c_size_t)]
     L.la_decode.restype = ctypes.c_int
     L.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
+    L.la_decode_pool.restype = ctypes.c_int
+    L.la_decode_pool.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, ctypes.c_int,
+                                 vp, vp]
     L.la_status_str.restype = ctypes.c_char_p
     L.la_status_str.argtypes = [ctypes.c_int]
     L.la_last_error.restype = ctypes.c_char_p
@@ -98,6 +101,12 @@ def la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, he
 
 def la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream):
     return lib().la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream)
+
+
+def la_decode_pool(q, k, v, kv_pool, pool_size, slots_dev, slots_host, decay, batch, num_heads,
+                   head_dim, in_dtype, o, stream):
+    return lib().la_decode_pool(q, k, v, kv_pool, pool_size, slots_dev, slots_host, decay, batch,
+                                num_heads, head_dim, in_dtype, o, stream)
 
 
 def la_status_str(s):
@@ -280,5 +289,51 @@ def decode(q, k, v, kv, decay, stream=None, out=None):
         out = torch.empty_like(q)
     st = la_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(), dec.ctypes.data,
                    B, H, d, _dtype_code(q), out.data_ptr(), _stream_handle(stream, q.device))
+    _check(st)
+    return out
+
+
+def decode_pool(q, k, v, kv_pool, slots, decay, stream=None, out=None, slots_host=None):
+    """One decode token per sequence on a state pool.  q, k, v: device
+    [B, H, d]; kv_pool: device fp32 [P, H, d, d] updated in place at the
+    slots; slots: [B] int (host or device), distinct, in [0, P).  Passing the
+    host copy as ``slots_host`` with a device int32 ``slots`` avoids a
+    device-to-host copy.  Returns o [B, H, d]."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3 \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, d] device tensor")
+    B, H, d = q.shape
+    if (not kv_pool.is_cuda or kv_pool.dtype != torch.float32 or not kv_pool.is_contiguous()
+            or kv_pool.dim() != 4 or tuple(kv_pool.shape[1:]) != (H, d, d)):
+        raise ValueError("kv_pool must be a contiguous fp32 device tensor [P, H, d, d]")
+    P = kv_pool.shape[0]
+    dev = q.device
+    if slots_host is not None:
+        sl_host = np.ascontiguousarray(
+            slots_host.cpu().numpy() if isinstance(slots_host, torch.Tensor) else slots_host,
+            dtype=np.int32)
+        if not (isinstance(slots, torch.Tensor) and slots.is_cuda and slots.dtype == torch.int32
+                and slots.is_contiguous()):
+            raise ValueError("slots_host needs slots as a contiguous int32 device tensor")
+        sl_dev = slots
+    elif isinstance(slots, torch.Tensor):
+        sl_host = slots.detach().to("cpu", torch.int32).contiguous().numpy()
+        sl_dev = slots if (slots.is_cuda and slots.dtype == torch.int32
+                           and slots.is_contiguous()) else torch.from_numpy(sl_host).to(dev)
+    else:
+        sl_host = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+        sl_dev = torch.from_numpy(sl_host).to(dev)
+    if stream is not None and sl_dev is not slots:
+        sl_dev.record_stream(stream)
+    if sl_host.shape != (B,):
+        raise ValueError(f"slots has shape {sl_host.shape}, expected ({B},)")
+    dec = _host_decay(decay, H)
+    if out is None:
+        out = torch.empty_like(q)
+    st = la_decode_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_pool.data_ptr(), P,
+                        sl_dev.data_ptr(), sl_host.ctypes.data, dec.ctypes.data, B, H, d,
+                        _dtype_code(q), out.data_ptr(), _stream_handle(stream, dev))
     _check(st)
     return out

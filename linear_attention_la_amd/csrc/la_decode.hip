@@ -10,6 +10,10 @@
 // 64 KiB fp32 state (d = 128) is read once and written once: the kernel is a
 // pure HBM stream (0.5 flop per byte).
 //
+// A state pool is supported: with a slot map, sequence b reads and writes
+// state slots[b] of the pool instead of state b (serving keeps the states of
+// all live sequences in one pool and decodes any subset of them).
+//
 // Layout: one workgroup per (b, h).  Thread t owns the column quad
 // 4*(t % (d/4)) and rows r = t / (d/4) + RP*n; each row of the state is read
 // with float4 loads by d/4 consecutive lanes (coalesced 512 B rows for
@@ -53,6 +57,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
   const int bh = blockIdx.x;
   const int h = bh % a.num_heads;
+  const int b = bh / a.num_heads;
+  const int64_t slot = a.slots ? a.slots[b] : b;  // validated on the host
   const int t = threadIdx.x;
   const int cq = t % CQ;
   const int rp = t / CQ;
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const InT* __restrict__ q = static_cast<const InT*>(a.q);
   const InT* __restrict__ k = static_cast<const InT*>(a.k);
   const InT* __restrict__ v = static_cast<const InT*>(a.v);
-  floatx4* __restrict__ S = reinterpret_cast<floatx4*>(a.kv + (int64_t)bh * D * D);
+  floatx4* __restrict__ S = reinterpret_cast<floatx4*>(a.kv + (slot * a.num_heads + h) * D * D);
 
   // Issue the whole state stream first (NR independent 16 B loads/thread).
   floatx4 sv[NR];

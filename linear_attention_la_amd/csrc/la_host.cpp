@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <vector>
+
 #include "la.h"
 #include "la_internal.h"
 
@@ -182,9 +184,63 @@ la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
   return LA_OK;
 }
 
+// Decode with num_states states in kv; sequence b uses state slots[b] (or b
+// when slots is NULL).  The slot array has been validated by the caller.
+la_status decode_common(const void* q, const void* k, const void* v, float* kv,
+                        int32_t num_states, const int32_t* slots_dev, const int32_t* slots_host,
+                        const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                        la_dtype in_dtype, void* o, void* stream);
+
 la_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+la_status decode_common(const void* q, const void* k, const void* v, float* kv,
+                        int32_t num_states, const int32_t* slots_dev, const int32_t* slots_host,
+                        const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                        la_dtype in_dtype, void* o, void* stream) {
+  (void)slots_host;
+  if (batch < 0) return fail(LA_ERR_INVALID_ARG, "batch = %d < 0", batch);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(LA_ERR_INVALID_ARG, "in_dtype = %d", (int)in_dtype);
+  if ((st = check_decay(decay, num_heads)) != LA_OK) return st;
+  if (batch == 0) return ok();
+  if (!q || !k || !v || !kv || !o)
+    return fail(LA_ERR_INVALID_ARG, "q, k, v, kv and o must be non-NULL");
+  const void* ptrs[] = {q, k, v, kv, o};
+  const char* names[] = {"q", "k", "v", "kv", "o"};
+  for (int i = 0; i < 5; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  if ((int64_t)batch * num_heads >= ((int64_t)1 << 31))
+    return fail(LA_ERR_UNSUPPORTED, "batch * num_heads exceeds the grid limit");
+
+  const size_t vec_bytes = (size_t)batch * num_heads * head_dim * dtype_size(in_dtype);
+  const Range rq = range("q", q, vec_bytes), rk = range("k", k, vec_bytes),
+              rv = range("v", v, vec_bytes), ro = range("o", o, vec_bytes);
+  const Range rs = range("kv", kv, (size_t)num_states * num_heads * head_dim * head_dim * 4);
+  const Range* others[] = {&rq, &rk, &rv, &rs};
+  for (const Range* x : others)
+    if (overlap(ro, *x)) return fail(LA_ERR_INVALID_ARG, "o overlaps %s", x->name);
+  const Range* vecs[] = {&rq, &rk, &rv};
+  for (const Range* x : vecs)
+    if (overlap(rs, *x)) return fail(LA_ERR_INVALID_ARG, "kv overlaps %s", x->name);
+
+  la::DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.kv = kv;
+  a.slots = slots_dev;
+  a.o = o;
+  a.batch = batch;
+  a.num_heads = num_heads;
+  for (int32_t h = 0; h < num_heads; ++h) a.decay[h] = decay[h];
+  hipError_t e = la::launch_decode(a, head_dim, in_dtype, static_cast<hipStream_t>(stream));
+  return hip_status(e, "la_decode launch");
 }
 
 }  // namespace
@@ -343,45 +399,31 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
 la_status la_decode(const void* q, const void* k, const void* v, float* kv,
                     const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
                     la_dtype in_dtype, void* o, void* stream) {
+  return decode_common(q, k, v, kv, batch, nullptr, nullptr, decay, batch, num_heads, head_dim,
+                       in_dtype, o, stream);
+}
+
+la_status la_decode_pool(const void* q, const void* k, const void* v, float* kv_pool,
+                         int32_t pool_size, const int32_t* slots_dev, const int32_t* slots_host,
+                         const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                         la_dtype in_dtype, void* o, void* stream) {
   if (batch < 0) return fail(LA_ERR_INVALID_ARG, "batch = %d < 0", batch);
-  la_status st = check_heads_dim(num_heads, head_dim);
-  if (st != LA_OK) return st;
-  if (!valid_dtype(in_dtype)) return fail(LA_ERR_INVALID_ARG, "in_dtype = %d", (int)in_dtype);
-  if ((st = check_decay(decay, num_heads)) != LA_OK) return st;
-  if (batch == 0) return ok();
-  if (!q || !k || !v || !kv || !o)
-    return fail(LA_ERR_INVALID_ARG, "q, k, v, kv and o must be non-NULL");
-  const void* ptrs[] = {q, k, v, kv, o};
-  const char* names[] = {"q", "k", "v", "kv", "o"};
-  for (int i = 0; i < 5; ++i)
-    if (!aligned16(ptrs[i]))
-      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
-  if ((int64_t)batch * num_heads >= ((int64_t)1 << 31))
-    return fail(LA_ERR_UNSUPPORTED, "batch * num_heads exceeds the grid limit");
-
-  const size_t vec_bytes = (size_t)batch * num_heads * head_dim * dtype_size(in_dtype);
-  const Range rq = range("q", q, vec_bytes), rk = range("k", k, vec_bytes),
-              rv = range("v", v, vec_bytes), ro = range("o", o, vec_bytes);
-  const Range rs = range("kv", kv, (size_t)batch * num_heads * head_dim * head_dim * 4);
-  const Range* others[] = {&rq, &rk, &rv, &rs};
-  for (const Range* x : others)
-    if (overlap(ro, *x)) return fail(LA_ERR_INVALID_ARG, "o overlaps %s", x->name);
-  const Range* vecs[] = {&rq, &rk, &rv};
-  for (const Range* x : vecs)
-    if (overlap(rs, *x)) return fail(LA_ERR_INVALID_ARG, "kv overlaps %s", x->name);
-
-  la::DecodeArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.kv = kv;
-  a.o = o;
-  a.batch = batch;
-  a.num_heads = num_heads;
-  for (int32_t h = 0; h < num_heads; ++h) a.decay[h] = decay[h];
-  hipError_t e = la::launch_decode(a, head_dim, in_dtype, static_cast<hipStream_t>(stream));
-  return hip_status(e, "la_decode launch");
+  if (pool_size < 0) return fail(LA_ERR_INVALID_ARG, "pool_size = %d < 0", pool_size);
+  if (batch > 0) {
+    if (!slots_dev || !slots_host)
+      return fail(LA_ERR_INVALID_ARG, "slots_dev and slots_host must be non-NULL");
+    // every slot in range and used once (two sequences on one state would race)
+    std::vector<uint8_t> used((size_t)pool_size, 0);
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t x = slots_host[b];
+      if (x < 0 || x >= pool_size)
+        return fail(LA_ERR_INVALID_ARG, "slots[%d] = %d is outside [0, %d)", b, x, pool_size);
+      if (used[(size_t)x]) return fail(LA_ERR_INVALID_ARG, "slot %d is used twice", x);
+      used[(size_t)x] = 1;
+    }
+  }
+  return decode_common(q, k, v, kv_pool, pool_size, slots_dev, slots_host, decay, batch,
+                       num_heads, head_dim, in_dtype, o, stream);
 }
 
 }  // extern "C"

@@ -36,6 +36,8 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   float* kv;
+  // Optional device [B]: sequence b uses state kv[slots[b]] (nullptr: kv[b]).
+  const int32_t* slots;
   void* o;
   int32_t batch;
   int32_t num_heads;

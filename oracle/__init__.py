@@ -38,4 +38,5 @@ from .lightning import (  # noqa: F401
     decode_step,
     prefill_varlen,
     decode_batch,
+    decode_pool,
 )

@@ -254,3 +254,29 @@ def decode_batch(q, k, v, kv, decay, heads=None):
         for h in heads:
             o[b, h], kv_new[b, h] = decode_step(q[b, h], k[b, h], v[b, h], kv[b, h], decay[h])
     return o, kv_new
+
+
+def decode_pool(q, k, v, pool, slots, decay, heads=None):
+    """Decode step on a pool of states: sequence b reads and updates state
+    ``pool[slots[b]]`` (the serving engine keeps every live sequence's state
+    in one pool and decodes a subset of them, [JVY] 二、计算优化).
+
+    q, k, v [B, H, d]; pool [P, H, d_k, d_v]; slots [B] distinct indices into
+    the pool.  Each step is ``decode_step``.  Returns (o [B, H, d_v],
+    pool_new [P, H, d_k, d_v]); entries that no slot names are copied
+    unchanged and the input pool is not modified.
+    """
+    slots = [int(x) for x in np.asarray(slots).reshape(-1).tolist()]
+    if len(set(slots)) != len(slots):
+        raise ValueError("a slot is used twice")
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    decay = _f64(decay)
+    heads = range(H) if heads is None else heads
+    pool_new = _f64(pool).copy()
+    o = np.zeros((B, H, dv))
+    for b, sl in enumerate(slots):
+        for h in heads:
+            o[b, h], pool_new[sl, h] = decode_step(q[b, h], k[b, h], v[b, h], pool[sl, h],
+                                                   decay[h])
+    return o, pool_new

@@ -246,5 +246,20 @@ def pin_packing(orc):
             _close(od[b, h], qd[b, h] @ S, 1e-13, "decode_batch per-head o")
 
 
+def pin_decode_pool(orc):
+    """Pool decode, worked by hand with d = 1 and lambda = 1/2 (exact in
+    binary): pool [2, 3, 5], slots [2, 0], q [1, 2], k [3, 1], v [1/2, 4].
+    Sequence 0 on slot 2: S = 5/2 + 3/2 = 4, o = 4.  Sequence 1 on slot 0:
+    S = 1 + 4 = 5, o = 10.  Slot 1 is untouched: pool becomes [5, 3, 4]."""
+    pool = np.array([2.0, 3.0, 5.0]).reshape(3, 1, 1, 1)
+    q = np.array([1.0, 2.0]).reshape(2, 1, 1)
+    k = np.array([3.0, 1.0]).reshape(2, 1, 1)
+    v = np.array([0.5, 4.0]).reshape(2, 1, 1)
+    o, pool_new = orc.decode_pool(q, k, v, pool, [2, 0], np.array([0.5]))
+    _close(o.reshape(-1), np.array([4.0, 10.0]), 0.0, "pool decode o")
+    _close(pool_new.reshape(-1), np.array([5.0, 3.0, 4.0]), 0.0, "pool decode states")
+    _close(pool.reshape(-1), np.array([2.0, 3.0, 5.0]), 0.0, "input pool unchanged")
+
+
 ALL_PINS = [pin_golden, pin_exact_rational, pin_lfilter, pin_nodecay_library, pin_geometric,
-            pin_three_way, pin_continuation, pin_decode_consistency, pin_packing]
+            pin_three_way, pin_continuation, pin_decode_consistency, pin_packing, pin_decode_pool]

@@ -28,7 +28,7 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
-              "la_decode", "la_status_str", "la_last_error"):
+              "la_decode", "la_decode_pool", "la_status_str", "la_last_error"):
         assert n in names
 
 
@@ -240,3 +240,47 @@ def test_segmented_rejects(name, kw, code):
     st, msg = _seg(**kw)
     assert st == code, (st, msg)
     assert msg
+
+
+# ---- decode on a state pool (host-side checks only) ----
+
+POOL = 0xA0000000
+
+
+def _pool(**kw):
+    args = dict(q=Q, k=K, v=V, pool=POOL, P=10, slots=np.array([3, 0, 7], np.int32),
+                slots_dev=CUD, decay=np.full(H, 0.9, np.float32), B=3, H=H, d=D,
+                dt=la.LA_BF16, o=O)
+    args.update(kw)
+    sl = args["slots"]
+    st = la.la_decode_pool(args["q"], args["k"], args["v"], args["pool"], args["P"],
+                           args["slots_dev"], None if sl is None else sl.ctypes.data,
+                           args["decay"].ctypes.data, args["B"], args["H"], args["d"], args["dt"],
+                           args["o"], None)
+    return st, la.la_last_error()
+
+
+BAD_POOL = [
+    ("slot_out_of_range", dict(slots=np.array([3, 0, 10], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("slot_negative", dict(slots=np.array([3, -1, 7], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("slot_repeated", dict(slots=np.array([3, 0, 3], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("slots_host_null", dict(slots=None), la.LA_ERR_INVALID_ARG),
+    ("slots_dev_null", dict(slots_dev=None), la.LA_ERR_INVALID_ARG),
+    ("pool_size_negative", dict(P=-1), la.LA_ERR_INVALID_ARG),
+    ("pool_empty", dict(P=0), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_pool", dict(o=POOL + 10 * 4 * 128 * 128 * 4 - 64), la.LA_ERR_INVALID_ARG),
+    ("pool_overlaps_q", dict(pool=Q - 64), la.LA_ERR_INVALID_ARG),
+    ("head_dim_32", dict(d=32), la.LA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_POOL, ids=[b[0] for b in BAD_POOL])
+def test_decode_pool_rejects(name, kw, code):
+    st, msg = _pool(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_decode_pool_zero_batch_is_noop():
+    st, msg = _pool(B=0, slots=None, slots_dev=None, q=None, k=None, v=None, o=None)
+    assert st == la.LA_OK, msg

@@ -44,6 +44,8 @@ MUTATIONS = {
     "varlen_swapped_kv": ("qs, ks, vs = q[a:b, h, :], k[a:b, h, :], v[a:b, h, :]",
                           "qs, ks, vs = q[a:b, h, :], v[a:b, h, :], k[a:b, h, :]"),
     "varlen_ignores_init": ("s0 = None if kv_init is None else _f64(kv_init[s, h])", "s0 = None"),
+    "pool_writes_batch_index": ("o[b, h], pool_new[sl, h] = decode_step(", "o[b, h], pool_new[b, h] = decode_step("),
+    "pool_reads_batch_index": ("v[b, h], pool[sl, h],", "v[b, h], pool[b, h],"),
 }
 
 
