@@ -39,4 +39,7 @@ from .lightning import (  # noqa: F401
     prefill_varlen,
     decode_batch,
     decode_pool,
+    backward_quadratic,
+    backward_recurrent,
+    backward_varlen,
 )

@@ -280,3 +280,105 @@ def decode_pool(q, k, v, pool, slots, decay, heads=None):
             o[b, h], pool_new[sl, h] = decode_step(q[b, h], k[b, h], v[b, h], pool[sl, h],
                                                    decay[h])
     return o, pool_new
+
+
+# ---------------------------------------------------------------------------
+# Backward.  The pages give the forward only; the gradients below follow from
+# its definition (the quadratic form above) by the chain rule.  With
+# A[t, j] = lam^(t-j) (do_t . v_j) and B[t, j] = lam^(t-j) (q_t . k_j) for
+# t >= j (else 0), and the loss seen through dO = dL/dO and dS_L = dL/dS_L:
+#   dQ  = A K + diag(lam^(t+1)) dO S0^T
+#   dK  = A^T Q + diag(lam^(L-1-j)) V dS_L^T
+#   dV  = B^T dO + diag(lam^(L-1-j)) K dS_L
+#   dS0 = Q^T diag(lam^(t+1)) dO + lam^L dS_L
+# dK and dV gather over t >= j: a chain running backwards in time.
+# ---------------------------------------------------------------------------
+
+def backward_quadratic(q, k, v, do, lam, s0=None, ds_final=None):
+    """Gradients of ``quadratic`` for the upstream gradients do [L, d_v] of
+    the output and ds_final [d_k, d_v] of the final state (None = 0).
+
+    Returns (dq [L, d_k], dk [L, d_k], dv [L, d_v], ds0 [d_k, d_v]); ds0 is
+    the gradient with respect to the initial state (defined when s0 is None,
+    i.e. a zero initial state).  Uses L x L matrices, so keep L modest.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    L = q.shape[0]
+    lam = float(lam)
+    m = decay_mask(lam, L)
+    a = (do @ v.T) * m
+    b = (q @ k.T) * m
+    t = np.arange(L, dtype=np.float64)
+    dq = a @ k
+    dk = a.T @ q
+    dv = b.T @ do
+    ds0 = (q * (lam ** (t + 1))[:, None]).T @ do
+    if s0 is not None:
+        dq = dq + (lam ** (t + 1))[:, None] * (do @ _f64(s0).T)
+    if ds_final is not None:
+        g = _f64(ds_final)
+        w = lam ** (L - 1 - t)
+        dk = dk + w[:, None] * (v @ g.T)
+        dv = dv + w[:, None] * (k @ g)
+        ds0 = ds0 + lam ** L * g
+    return dq, dk, dv, ds0
+
+
+def backward_recurrent(q, k, v, do, lam, s0=None, ds_final=None):
+    """The same gradients as two token chains.
+
+    Forward in time, the forward state S_t (as in ``recurrent``) gives
+    dq_t = S_t do_t.  Backward in time, R_j = lam R_(j+1) + q_j^T do_j with
+    R_(L-1) = q_(L-1)^T do_(L-1) + dS_L gives dk_j = R_j v_j and
+    dv_j = R_j^T k_j, and dS0 = lam R_0 (dS_L when L = 0).
+    Returns (dq, dk, dv, ds0) as ``backward_quadratic``.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    L = q.shape[0]
+    dk_, dv_ = k.shape[1], v.shape[1]
+    lam = float(lam)
+    S = np.zeros((dk_, dv_)) if s0 is None else _f64(s0).copy()
+    dq = np.zeros((L, dk_))
+    for t in range(L):
+        S = lam * S + np.outer(k[t], v[t])
+        dq[t] = S @ do[t]
+    R = np.zeros((dk_, dv_)) if ds_final is None else _f64(ds_final).copy()
+    dk = np.zeros((L, dk_))
+    dv = np.zeros((L, dv_))
+    for j in range(L - 1, -1, -1):
+        if j < L - 1:
+            R = lam * R
+        R = R + np.outer(q[j], do[j])
+        dk[j] = R @ v[j]
+        dv[j] = R.T @ k[j]
+    ds0 = lam * R if L > 0 else R
+    return dq, dk, dv, ds0
+
+
+def backward_varlen(q, k, v, do, cu_seqlens, decay, kv_init=None, dkv_final=None,
+                    form="recurrent", heads=None):
+    """Gradients of ``prefill_varlen`` over packed sequences.
+
+    q, k, v, do [T, H, d]; kv_init, dkv_final [S, H, d, d] or None.  Returns
+    (dq, dk, dv [T, H, d], dkv_init [S, H, d, d]).  ``heads`` restricts the
+    work to a subset of heads (other heads stay zero).
+    """
+    fn = {"recurrent": backward_recurrent, "quadratic": backward_quadratic}[form]
+    T, H, dk_ = q.shape
+    dv_ = v.shape[2]
+    cu = [int(x) for x in np.asarray(cu_seqlens).tolist()]
+    S = len(cu) - 1
+    decay = _f64(decay)
+    heads = range(H) if heads is None else heads
+    dq = np.zeros((T, H, dk_))
+    dk = np.zeros((T, H, dk_))
+    dv = np.zeros((T, H, dv_))
+    dkv0 = np.zeros((S, H, dk_, dv_))
+    for s in range(S):
+        a, b = cu[s], cu[s + 1]
+        for h in heads:
+            s0 = None if kv_init is None else _f64(kv_init[s, h])
+            g = None if dkv_final is None else _f64(dkv_final[s, h])
+            r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[h], s0, g)
+            dq[a:b, h], dk[a:b, h], dv[a:b, h], dkv0[s, h] = r
+    return dq, dk, dv, dkv0

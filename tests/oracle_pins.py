@@ -261,5 +261,67 @@ def pin_decode_pool(orc):
     _close(pool.reshape(-1), np.array([2.0, 3.0, 5.0]), 0.0, "input pool unchanged")
 
 
+def pin_backward_autograd(orc):
+    """Backward against automatic differentiation: torch (float64, CPU)
+    differentiates a token-by-token forward, S_t = lam S_(t-1) + k_t^T v_t,
+    o_t = q_t S_t, through the loss sum(O * dO) + sum(S_L * dS_L); both
+    oracle backward forms must give the same gradients, also for the initial
+    state and with neither initial state nor final-state gradient."""
+    import torch
+
+    rng = _rng(31)
+    L, dk, dv = 11, 3, 4
+    for lam, with_s0, with_g in ((0.8, True, True), (1.0, True, False), (0.5, False, True),
+                                 (0.9, False, False)):
+        q, k = rng.standard_normal((L, dk)), rng.standard_normal((L, dk))
+        v, do = rng.standard_normal((L, dv)), rng.standard_normal((L, dv))
+        s0 = rng.standard_normal((dk, dv))
+        g = rng.standard_normal((dk, dv))
+        if not with_s0:
+            s0 = np.zeros((dk, dv))  # ds0 is then the gradient at a zero initial state
+        tq, tk, tv, ts0 = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                           for x in (q, k, v, s0))
+        S = ts0
+        outs = []
+        for t in range(L):
+            S = lam * S + torch.outer(tk[t], tv[t])
+            outs.append(tq[t] @ S)
+        loss = (torch.stack(outs) * torch.tensor(do)).sum()
+        if with_g:
+            loss = loss + (S * torch.tensor(g)).sum()
+        loss.backward()
+        ref = [x.grad.numpy() for x in (tq, tk, tv, ts0)]
+        for fn in (orc.backward_quadratic, orc.backward_recurrent):
+            got = fn(q, k, v, do, lam, s0 if with_s0 else None, g if with_g else None)
+            for name, a, b in zip(("dq", "dk", "dv", "ds0"), got, ref):
+                _close(a, b, 1e-12, f"{fn.__name__} {name} lam={lam}")
+
+
+def pin_backward_finite_difference(orc):
+    """Central differences of a scalar loss through the oracle's forward
+    (quadratic form) on a tiny problem match the backward within the
+    difference error."""
+    rng = _rng(37)
+    L, d, lam, h = 5, 2, 0.7, 1e-6
+    q, k, v, do = (rng.standard_normal((L, d)) for _ in range(4))
+    s0, g = rng.standard_normal((d, d)), rng.standard_normal((d, d))
+
+    def loss(q_, k_, v_, s0_):
+        o, sl = orc.quadratic(q_, k_, v_, lam, s0_)
+        return float((o * do).sum() + (sl * g).sum())
+
+    grads = orc.backward_quadratic(q, k, v, do, lam, s0, g)
+    for which, arr in enumerate((q, k, v, s0)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            args = [q.copy(), k.copy(), v.copy(), s0.copy()]
+            args[which][idx] += h
+            up = loss(*args)
+            args[which][idx] -= 2 * h
+            num[idx] = (up - loss(*args)) / (2 * h)
+        _close(grads[which], num, 1e-6, f"finite difference input {which}")
+
+
 ALL_PINS = [pin_golden, pin_exact_rational, pin_lfilter, pin_nodecay_library, pin_geometric,
-            pin_three_way, pin_continuation, pin_decode_consistency, pin_packing, pin_decode_pool]
+            pin_three_way, pin_continuation, pin_decode_consistency, pin_packing, pin_decode_pool,
+            pin_backward_autograd, pin_backward_finite_difference]

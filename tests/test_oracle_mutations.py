@@ -27,8 +27,8 @@ MUTATIONS = {
     "recurrent_read_before_update": (
         "S = lam * S + np.outer(k[t], v[t])\n        o[t] = q[t] @ S",
         "o[t] = q[t] @ S\n        S = lam * S + np.outer(k[t], v[t])"),
-    "recurrent_transposed_outer": ("S = lam * S + np.outer(k[t], v[t])",
-                                   "S = lam * S + np.outer(v[t], k[t])"),
+    "recurrent_transposed_outer": ("S = lam * S + np.outer(k[t], v[t])\n        o[t] = q[t] @ S",
+                                   "S = lam * S + np.outer(v[t], k[t])\n        o[t] = q[t] @ S"),
     "blockwise_inter_exponent": ("inter = (lam ** (loc + 1))", "inter = (lam ** loc)"),
     "blockwise_drops_inter": ("o[b0:b0 + ell] = intra + inter", "o[b0:b0 + ell] = intra"),
     "blockwise_state_decay": ("S = lam ** ell * S +", "S = lam ** (ell - 1) * S +"),
@@ -43,9 +43,20 @@ MUTATIONS = {
                                 "os_, st = blockwise(qs, ks, vs, decay[0], beta, s0)"),
     "varlen_swapped_kv": ("qs, ks, vs = q[a:b, h, :], k[a:b, h, :], v[a:b, h, :]",
                           "qs, ks, vs = q[a:b, h, :], v[a:b, h, :], k[a:b, h, :]"),
-    "varlen_ignores_init": ("s0 = None if kv_init is None else _f64(kv_init[s, h])", "s0 = None"),
+    "varlen_ignores_init": ("s0 = None if kv_init is None else _f64(kv_init[s, h])\n            qs, ks",
+                            "s0 = None\n            qs, ks"),
     "pool_writes_batch_index": ("o[b, h], pool_new[sl, h] = decode_step(", "o[b, h], pool_new[b, h] = decode_step("),
     "pool_reads_batch_index": ("v[b, h], pool[sl, h],", "v[b, h], pool[b, h],"),
+    "bwd_quad_dk_untransposed": ("    dk = a.T @ q\n", "    dk = a @ q\n"),
+    "bwd_quad_dv_wrong_scores": ("    dv = b.T @ do\n", "    dv = a.T @ do\n"),
+    "bwd_quad_ds0_exponent": ("    ds0 = (q * (lam ** (t + 1))[:, None]).T @ do",
+                              "    ds0 = (q * (lam ** t)[:, None]).T @ do"),
+    "bwd_quad_drops_final_grad_dk": ("        dk = dk + w[:, None] * (v @ g.T)\n", ""),
+    "bwd_quad_s0_untransposed": ("(do @ _f64(s0).T)", "(do @ _f64(s0))"),
+    "bwd_rec_reads_before_update": ("        S = lam * S + np.outer(k[t], v[t])\n        dq[t] = S @ do[t]",
+                                    "        dq[t] = S @ do[t]\n        S = lam * S + np.outer(k[t], v[t])"),
+    "bwd_rec_no_reverse_decay": ("        if j < L - 1:\n            R = lam * R\n", ""),
+    "bwd_rec_dv_untransposed": ("        dv[j] = R.T @ k[j]", "        dv[j] = R @ k[j]"),
 }
 
 
