@@ -161,6 +161,57 @@ la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* c
                                               int32_t segment_len, size_t* bytes);
 
 /*
+ * la_prefill_backward -- gradients of la_prefill with respect to q, k, v and
+ * the initial state, for upstream gradients d_o of the output and dkv_final
+ * of the final state.
+ *
+ * The pages give only the forward; differentiating the causal decayed form
+ * (see the top of this header) gives, per sequence and head, with
+ * M[t][j] = lambda^(t-j) for t >= j and 0 otherwise:
+ *     dQ  = [(dO V^T) .* M] K   + diag(lambda^(t+1)) dO S_init^T
+ *     dK  = [(dO V^T) .* M]^T Q + diag(lambda^(L-1-j)) V dS_L^T
+ *     dV  = [(Q K^T) .* M]^T dO + diag(lambda^(L-1-j)) K dS_L
+ *     dS_init = Q^T diag(lambda^(t+1)) dO + lambda^L dS_L
+ * dQ is the blockwise forward chain with dO, V, K in the roles of Q, K, V;
+ * dK and dV are the same chain run backwards in time (a reverse-direction
+ * state), in the intra-block / inter-block split of the forward (emonzhong.com
+ * 方法要点; mizuki blog 关键概念清单).
+ *
+ *   q, k, v, d_o     device [T, H, d], bf16 (in_dtype must be LA_BF16).
+ *   cu_seqlens_dev/host, num_seqs, total_tokens, num_heads, head_dim, decay:
+ *                    as in la_prefill (the forward's arguments).
+ *   grad_dtype       dtype of dq, dk, dv: LA_BF16 (RNE) or LA_FP32.
+ *   kv_init          device fp32 [S, H, d, d] initial states of the forward,
+ *                    or NULL (zero).
+ *   dkv_final        device fp32 [S, H, d, d] gradient of the final states,
+ *                    or NULL (zero).  Needs every decay >= 2^-64
+ *                    (else LA_ERR_UNSUPPORTED).
+ *   dq, dk, dv       device [T, H, d] of grad_dtype (written).
+ *   dkv_init         device fp32 [S, H, d, d] gradient of the initial states
+ *                    (written), or NULL to skip.
+ *   workspace        device scratch of la_prefill_backward_workspace_size
+ *                    bytes, needed when kv_init or dkv_final is given (may be
+ *                    NULL otherwise); 16-byte aligned.
+ *
+ * The outputs and the workspace may overlap nothing else.  Errors as
+ * la_prefill.  Up to seven kernels are enqueued on `stream`; nothing
+ * synchronises.
+ */
+la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
+                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                              int32_t head_dim, la_dtype in_dtype, la_dtype grad_dtype,
+                              const float* decay, const float* kv_init, const float* dkv_final,
+                              void* dq, void* dk, void* dv, float* dkv_init, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace for la_prefill_backward: num_seqs x num_heads x d x d
+ * fp32 (host only).  Errors: LA_ERR_INVALID_ARG (NULL bytes, num_seqs < 0),
+ * LA_ERR_UNSUPPORTED (heads or head_dim as la_prefill). */
+la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                             int32_t head_dim, size_t* bytes);
+
+/*
  * la_decode -- one decode token per sequence, updating fp32 states in place.
  *
  * The length-1 step that serving runs in its own kernel, apart from the

@@ -7,6 +7,7 @@ library is missing, every call raises.
 
     o, kv = prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None)
     o, kv = prefill_segmented(q, k, v, cu_seqlens, decay, segment_len)
+    dq, dk, dv, dkv0 = prefill_backward(q, k, v, do, cu_seqlens, decay, kv_init, dkv_final)
     o = decode(q, k, v, kv, decay)          # kv updated in place
     o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
 """
@@ -25,6 +26,8 @@ from ._binding import (  # noqa: F401
     la_prefill,
     la_prefill_segmented,
     la_prefill_segmented_workspace_size,
+    la_prefill_backward,
+    la_prefill_backward_workspace_size,
     la_decode,
     la_decode_pool,
     la_status_str,
@@ -32,6 +35,7 @@ from ._binding import (  # noqa: F401
     prefill,
     prefill_segmented,
     prefill_segmented_workspace_size,
+    prefill_backward,
     decode,
     decode_pool,
 )

@@ -59,6 +59,13 @@ def lib():
     L.la_prefill_segmented_workspace_size.restype = ctypes.c_int
     L.la_prefill_segmented_workspace_size.argtypes = [i32, vp, i32, i32, i32,
                                                       ctypes.POINTER(ctypes.c_size_t)]
+    L.la_prefill_backward.restype = ctypes.c_int
+    L.la_prefill_backward.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
+                                      ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+    L.la_prefill_backward_workspace_size.restype = ctypes.c_int
+    L.la_prefill_backward_workspace_size.argtypes = [i32, i32, i32,
+                                                     ctypes.POINTER(ctypes.c_size_t)]
     L.la_decode.restype = ctypes.c_int
     L.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
     L.la_decode_pool.restype = ctypes.c_int
@@ -101,6 +108,22 @@ def la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, he
 
 def la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream):
     return lib().la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream)
+
+
+def la_prefill_backward(q, k, v, d_o, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                        num_heads, head_dim, in_dtype, grad_dtype, decay, kv_init, dkv_final, dq,
+                        dk, dv, dkv_init, workspace, workspace_bytes, stream):
+    return lib().la_prefill_backward(q, k, v, d_o, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                     total_tokens, num_heads, head_dim, in_dtype, grad_dtype,
+                                     decay, kv_init, dkv_final, dq, dk, dv, dkv_init, workspace,
+                                     workspace_bytes, stream)
+
+
+def la_prefill_backward_workspace_size(num_seqs, num_heads, head_dim):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = lib().la_prefill_backward_workspace_size(num_seqs, num_heads, head_dim, ctypes.byref(n))
+    return st, n.value
 
 
 def la_decode_pool(q, k, v, kv_pool, pool_size, slots_dev, slots_host, decay, batch, num_heads,
@@ -337,3 +360,44 @@ def decode_pool(q, k, v, kv_pool, slots, decay, stream=None, out=None, slots_hos
                         _dtype_code(q), out.data_ptr(), _stream_handle(stream, dev))
     _check(st)
     return out
+
+
+def prefill_backward(q, k, v, d_o, cu_seqlens, decay, kv_init=None, dkv_final=None,
+                     grad_dtype=None, stream=None, init_grad=True, cu_seqlens_host=None,
+                     workspace=None, dq=None, dk=None, dv=None, dkv_init=None):
+    """Gradients of prefill().  q, k, v, d_o: device bf16 [T, H, d];
+    kv_init / dkv_final: device fp32 [S, H, d, d] or None.  Returns
+    (dq, dk, dv, dkv_init or None); grad_dtype defaults to the input dtype."""
+    torch = _torch()
+    m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, grad_dtype, stream, False, dq,
+                         None, cu_seqlens_host)
+    if not (isinstance(d_o, torch.Tensor) and d_o.is_cuda and d_o.shape == q.shape
+            and d_o.dtype == q.dtype and d_o.is_contiguous()):
+        raise ValueError("d_o must be a contiguous device tensor like q")
+    if dkv_final is not None and (not dkv_final.is_cuda or dkv_final.dtype != torch.float32
+                                  or not dkv_final.is_contiguous()
+                                  or tuple(dkv_final.shape) != (m.S, m.H, m.d, m.d)):
+        raise ValueError("dkv_final must be a contiguous fp32 device tensor [S, H, d, d]")
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    dk = torch.empty(q.shape, dtype=gdt, device=m.dev) if dk is None else dk
+    dv = torch.empty(q.shape, dtype=gdt, device=m.dev) if dv is None else dv
+    if init_grad and dkv_init is None:
+        dkv_init = torch.empty((m.S, m.H, m.d, m.d), dtype=torch.float32, device=m.dev)
+    if not init_grad:
+        dkv_init = None
+    st, need = la_prefill_backward_workspace_size(m.S, m.H, m.d)
+    _check(st)
+    if workspace is None and (kv_init is not None or dkv_final is not None):
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
+        if stream is not None:
+            workspace.record_stream(stream)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    (qp, kp, vp_, cud, cuh, S, T, H, d, in_code, out_code, decp, kvip, dqp, _) = m.args
+    _check(la_prefill_backward(qp, kp, vp_, d_o.data_ptr(), cud, cuh, S, T, H, d, in_code,
+                               out_code, decp, kvip,
+                               None if dkv_final is None else dkv_final.data_ptr(), dqp,
+                               dk.data_ptr(), dv.data_ptr(),
+                               None if dkv_init is None else dkv_init.data_ptr(),
+                               None if workspace is None else workspace.data_ptr(), nbytes,
+                               m.stream))
+    return m.out, dk, dv, dkv_init

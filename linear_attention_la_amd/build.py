@@ -28,7 +28,7 @@ FLAGS = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 SOURCES = ["la_host.cpp", "la_prefill_bf16.hip", "la_prefill_f32.hip", "la_decode.hip",
-           "la_segment.hip"]
+           "la_segment.hip", "la_state.hip"]
 
 
 def _compile(src):

@@ -286,7 +286,7 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = in_dtype == LA_BF16 ? la::launch_prefill_bf16(a, head_dim, out_dtype, false, s)
+  hipError_t e = in_dtype == LA_BF16 ? la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s)
                                      : la::launch_prefill_f32(a, head_dim, out_dtype, s);
   return hip_status(e, "la_prefill launch");
 }
@@ -378,7 +378,7 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   a.num_heads = num_heads;
   a.num_items = (int32_t)items;
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
-  e = la::launch_prefill_bf16(a, head_dim, LA_BF16, true, s);
+  e = la::launch_prefill_bf16(a, head_dim, LA_BF16, true, false, s);
   if (e != hipSuccess) return hip_status(e, "la_prefill_segmented state pass launch");
 
   // pass 2: states at every segment start (and the final states)
@@ -392,8 +392,149 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   a.kv_final = nullptr;
   a.final_slot = nullptr;
   a.o = o;
-  e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, s);
+  e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
   return hip_status(e, "la_prefill_segmented output pass launch");
+}
+
+la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                             int32_t head_dim, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  *bytes = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  return ok();
+}
+
+la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
+                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                              int32_t head_dim, la_dtype in_dtype, la_dtype grad_dtype,
+                              const float* decay, const float* kv_init, const float* dkv_final,
+                              void* dq, void* dk, void* dv, float* dkv_init, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  if (total_tokens < 0 || total_tokens >= (int64_t)1 << 31)
+    return fail(LA_ERR_INVALID_ARG, "total_tokens = %lld out of range", (long long)total_tokens);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if (!valid_dtype(in_dtype)) return fail(LA_ERR_INVALID_ARG, "in_dtype = %d", (int)in_dtype);
+  if (!valid_dtype(grad_dtype))
+    return fail(LA_ERR_INVALID_ARG, "grad_dtype = %d", (int)grad_dtype);
+  if (in_dtype != LA_BF16)
+    return fail(LA_ERR_UNSUPPORTED, "the backward takes bf16 inputs only");
+  if ((st = check_decay(decay, num_heads)) != LA_OK) return st;
+  if (dkv_final) {
+    for (int32_t h = 0; h < num_heads; ++h)
+      if (decay[h] < 0x1p-64f)
+        return fail(LA_ERR_UNSUPPORTED,
+                    "decay[%d] = %g < 2^-64 with a final-state gradient is not supported", h,
+                    (double)decay[h]);
+  }
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  if ((int64_t)cu_seqlens_host[num_seqs] != total_tokens)
+    return fail(LA_ERR_INVALID_ARG, "cu_seqlens[%d] = %d != total_tokens = %lld", num_seqs,
+                cu_seqlens_host[num_seqs], (long long)total_tokens);
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens_dev) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
+  if (total_tokens > 0 && (!q || !k || !v || !d_o || !dq || !dk || !dv))
+    return fail(LA_ERR_INVALID_ARG,
+                "q, k, v, d_o, dq, dk and dv must be non-NULL when total_tokens > 0");
+  const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  const bool need_ws = kv_init || dkv_final;
+  if (need_ws && !workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
+  if (need_ws && workspace_bytes < sb)
+    return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes, sb);
+  const void* ptrs[] = {q, k, v, d_o, dq, dk, dv, kv_init, dkv_final, dkv_init, workspace};
+  const char* names[] = {"q", "k", "v", "d_o", "dq", "dk", "dv", "kv_init", "dkv_final",
+                         "dkv_init", "workspace"};
+  for (int i = 0; i < 11; ++i)
+    if (!aligned16(ptrs[i]))
+      return fail(LA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+  const int64_t items = (int64_t)num_seqs * num_heads * (head_dim / la::kBf16Cols);
+  if (items >= ((int64_t)1 << 31) || (int64_t)num_seqs * num_heads * 16 >= ((int64_t)1 << 31))
+    return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
+  // Outputs and the workspace overlap nothing else.
+  {
+    const size_t tok = (size_t)total_tokens * num_heads * head_dim;
+    const Range ins[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
+                         range("d_o", d_o, tok * 2), range("kv_init", kv_init, kv_init ? sb : 0),
+                         range("dkv_final", dkv_final, dkv_final ? sb : 0)};
+    const Range outs[] = {range("dq", dq, tok * dtype_size(grad_dtype)),
+                          range("dk", dk, tok * dtype_size(grad_dtype)),
+                          range("dv", dv, tok * dtype_size(grad_dtype)),
+                          range("dkv_init", dkv_init, dkv_init ? sb : 0),
+                          range("workspace", workspace, need_ws ? sb : 0)};
+    for (int i = 0; i < 5; ++i) {
+      for (const Range& r : ins)
+        if (overlap(outs[i], r)) return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, r.name);
+      for (int j = i + 1; j < 5; ++j)
+        if (overlap(outs[i], outs[j]))
+          return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
+    }
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  float one[LA_MAX_HEADS], inv[LA_MAX_HEADS], lam[LA_MAX_HEADS];
+  la::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.cu_seqlens = cu_seqlens_dev;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_items = (int32_t)items;
+  for (int32_t h = 0; h < num_heads; ++h) {
+    a.log2_decay[h] = (float)log2((double)decay[h]);
+    one[h] = 1.0f;
+    inv[h] = (float)(1.0 / (double)decay[h]);
+    lam[h] = decay[h];
+  }
+  hipError_t e;
+  // dQ: the forward chain with dO as queries, V as keys, K as values, S0^T
+  if (kv_init) {
+    e = la::launch_state_transform(kv_init, ws, num_seqs, num_heads, head_dim, true, one, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward state launch");
+  }
+  a.q = d_o;
+  a.k = v;
+  a.v = k;
+  a.kv_init = kv_init ? ws : nullptr;
+  a.o = dq;
+  e = la::launch_prefill_bf16(a, head_dim, grad_dtype, false, false, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_backward dq launch");
+  // dK: backwards in time, V as queries, dO as keys, Q as values, dS_L^T / lambda
+  if (dkv_final) {
+    e = la::launch_state_transform(dkv_final, ws, num_seqs, num_heads, head_dim, true, inv, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward state launch");
+  }
+  a.q = v;
+  a.k = d_o;
+  a.v = q;
+  a.kv_init = dkv_final ? ws : nullptr;
+  a.o = dk;
+  e = la::launch_prefill_bf16(a, head_dim, grad_dtype, false, true, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_backward dk launch");
+  // dV: backwards in time, K as queries, Q as keys, dO as values, dS_L / lambda;
+  // its final state is dS0 / lambda
+  if (dkv_final) {
+    e = la::launch_state_transform(dkv_final, ws, num_seqs, num_heads, head_dim, false, inv, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward state launch");
+  }
+  a.q = k;
+  a.k = q;
+  a.v = d_o;
+  a.kv_init = dkv_final ? ws : nullptr;
+  a.o = dv;
+  a.kv_final = dkv_init;
+  e = la::launch_prefill_bf16(a, head_dim, grad_dtype, false, true, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_backward dv launch");
+  if (dkv_init) {
+    e = la::launch_state_transform(dkv_init, dkv_init, num_seqs, num_heads, head_dim, false, lam, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward state launch");
+  }
+  return ok();
 }
 
 la_status la_decode(const void* q, const void* k, const void* v, float* kv,

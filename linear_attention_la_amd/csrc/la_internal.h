@@ -47,9 +47,16 @@ struct DecodeArgs {
 // Each returns hipSuccess or the launch error.  The caller has validated
 // every argument.
 // state_only: compute and write only the final states (no O): K and V are
-// read, Q is not.
+// read, Q is not.  reverse: every sequence is processed backwards in time
+// (token i of the chain is row end-1-i of q, k, v and o).
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, la_dtype out_dtype,
-                               bool state_only, hipStream_t stream);
+                               bool state_only, bool reverse, hipStream_t stream);
+
+// out[s,h] = scale[h] * (transpose ? in[s,h]^T : in[s,h]) for num_states x H
+// fp32 d x d states (la_state.hip); out may be in only without transpose.
+hipError_t launch_state_transform(const float* in, float* out, int32_t num_states,
+                                  int32_t num_heads, int32_t head_dim, bool transpose,
+                                  const float* scale, hipStream_t stream);
 
 // Segmented prefill helpers (la_segment.hip).  Plan: from cu_seqlens [S+1]
 // and segment_len, write cu_seg [n_seg+1], init_slot/final_slot [n_seg] and

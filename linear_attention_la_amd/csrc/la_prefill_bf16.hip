@@ -193,7 +193,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
-template <int D, bool kOutF32, bool kStateOnly>
+template <int D, bool kOutF32, bool kStateOnly, bool kReverse>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NDV = D / kDV;
   constexpr int NK = D / 32;       // k-steps over d
@@ -301,17 +301,24 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   };
   // Buffer resource over the valid rows (all heads) of block b of a [T, H, d]
   // tensor with elements of `esize` bytes.
+  // With kReverse the chain runs backwards in time: logical token i of the
+  // sequence is physical row end - 1 - i, so block b holds the physical rows
+  // [end - 64b - ell, end - 64b) in decreasing order.  Rows are addressed
+  // inside a block resource by prow(); logical rows past the end of the
+  // sequence map outside the resource either way.
   auto block_rsrc = [&](const void* base, int b, int esize) {
-    const char* p = static_cast<const char*>(base) +
-                    (start + (int64_t)b * kBeta) * row_stride * (int64_t)esize;
-    return buf_rsrc(p, block_len(b) * row_stride * esize);
+    const int ell = block_len(b);
+    const int64_t row0 = kReverse ? end - (int64_t)b * kBeta - ell : start + (int64_t)b * kBeta;
+    const char* p = static_cast<const char*>(base) + row0 * row_stride * (int64_t)esize;
+    return buf_rsrc(p, ell * row_stride * esize);
   };
+  auto prow = [&](int r, int ell) { return kReverse ? ell - 1 - r : r; };
 
   // ---- strip waves: their 16 query rows go straight from HBM into the
   // MFMA operand registers (lane (li, g) holds Q[16k+li][32kk+8g..+7]) ----
   auto load_q = [&](bf16x8(&dst)[NK], int b) {
     const __amdgpu_buffer_rsrc_t r = block_rsrc(q, b, 2);
-    const int off = 2 * ((16 * k + li) * row_stride + h * D + 8 * g);
+    const int off = 2 * (prow(16 * k + li, block_len(b)) * row_stride + h * D + 8 * g);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk)
       dst[kk] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off + 64 * kk, 0, 0));
@@ -334,12 +341,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 
   auto load_k = [&](KStage& r, int b) {
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(kp, b, 2);
+    const int ell = block_len(b);
 #pragma unroll
     for (int p = 0; p < NKC; ++p) {
       const int id = t + 256 * p;
       r.k[p] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rk, 2 * ((id / CH) * row_stride + h * D + 8 * (id % CH)), 0, 0));
+                     rk, 2 * (prow(id / CH, ell) * row_stride + h * D + 8 * (id % CH)), 0, 0));
     }
   };
   auto store_k = [&](const KStage& r, int buf) {
@@ -352,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   auto load_v = [&](VStage& r, int b) {
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(v, b, 2);
     r.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                        rv, 2 * (vrow * row_stride + h * D + c0 + 8 * vch), 0, 0));
+                                        rv, 2 * (prow(vrow, block_len(b)) * row_stride + h * D + c0 + 8 * vch), 0, 0));
   };
   auto store_v = [&](const VStage& r, int buf, int b) {
     const int ell = block_len(b);
@@ -434,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // rows past the end of the sequence fall outside the resource: dropped
     constexpr int ES = kOutF32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t ro = block_rsrc(a.o, b, ES);
-    const int orow = (16 * KS + li) * row_stride + h * D + c0;
+    const int orow = prow(16 * KS + li, block_len(b)) * row_stride + h * D + c0;
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc) {
       float out[4];
@@ -593,23 +601,28 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(const PrefillArgs& a, la_dtype out_dtype, bool state_only, hipStream_t stream) {
+hipError_t launch_d(const PrefillArgs& a, la_dtype out_dtype, bool state_only, bool reverse,
+                    hipStream_t stream) {
   const dim3 grid(a.num_items), block(kThreads);
   if (state_only)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false>), grid, block, 0, stream, a);
+  else if (reverse && out_dtype == LA_FP32)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true>), grid, block, 0, stream, a);
+  else if (reverse)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, true>), grid, block, 0, stream, a);
   else if (out_dtype == LA_FP32)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, la_dtype out_dtype,
-                               bool state_only, hipStream_t stream) {
-  if (head_dim == 64) return launch_d<64>(a, out_dtype, state_only, stream);
-  return launch_d<128>(a, out_dtype, state_only, stream);
+                               bool state_only, bool reverse, hipStream_t stream) {
+  if (head_dim == 64) return launch_d<64>(a, out_dtype, state_only, reverse, stream);
+  return launch_d<128>(a, out_dtype, state_only, reverse, stream);
 }
 
 }  // namespace la

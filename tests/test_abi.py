@@ -28,6 +28,7 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
+              "la_prefill_backward", "la_prefill_backward_workspace_size",
               "la_decode", "la_decode_pool", "la_status_str", "la_last_error"):
         assert n in names
 
@@ -283,4 +284,65 @@ def test_decode_pool_rejects(name, kw, code):
 
 def test_decode_pool_zero_batch_is_noop():
     st, msg = _pool(B=0, slots=None, slots_dev=None, q=None, k=None, v=None, o=None)
+    assert st == la.LA_OK, msg
+
+
+# ---- backward (host-side checks only) ----
+
+DO_, DQ, DK, DV, DKV0, BWS = (0xB0000000 + 0x10000000 * i for i in range(6))
+
+
+def _bwd(**kw):
+    args = dict(q=Q, k=K, v=V, do=DO_, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2,
+                T=T, H=H, d=D, in_dt=la.LA_BF16, g_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), kv_init=KVI, dkv_final=KVF, dq=DQ, dk=DK,
+                dv=DV, dkv_init=DKV0, ws=BWS, ws_bytes=1 << 30)
+    args.update(kw)
+    cu = args["cu_host"]
+    st = la.la_prefill_backward(args["q"], args["k"], args["v"], args["do"], args["cu_dev"],
+                                None if cu is None else cu.ctypes.data, args["S"], args["T"],
+                                args["H"], args["d"], args["in_dt"], args["g_dt"],
+                                args["decay"].ctypes.data, args["kv_init"], args["dkv_final"],
+                                args["dq"], args["dk"], args["dv"], args["dkv_init"], args["ws"],
+                                args["ws_bytes"], None)
+    return st, la.la_last_error()
+
+
+def test_backward_workspace_size():
+    st, n = la.la_prefill_backward_workspace_size(2, 4, 128)
+    assert st == la.LA_OK and n == 2 * 4 * 128 * 128 * 4
+    assert la.la_prefill_backward_workspace_size(-1, 4, 128)[0] == la.LA_ERR_INVALID_ARG
+    assert la.la_prefill_backward_workspace_size(1, 4, 96)[0] == la.LA_ERR_UNSUPPORTED
+
+
+BAD_BACKWARD = [
+    ("fp32_inputs", dict(in_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
+    ("bad_grad_dtype", dict(g_dt=5), la.LA_ERR_INVALID_ARG),
+    ("tiny_decay_with_final_grad", dict(decay=np.array([0.9, 1e-30, 0.9, 0.9], np.float32)),
+     la.LA_ERR_UNSUPPORTED),
+    ("d_o_null", dict(do=None), la.LA_ERR_INVALID_ARG),
+    ("dk_null", dict(dk=None), la.LA_ERR_INVALID_ARG),
+    ("workspace_null", dict(ws=None), la.LA_ERR_INVALID_ARG),
+    ("workspace_short", dict(ws_bytes=1024), la.LA_ERR_INVALID_ARG),
+    ("dq_overlaps_d_o", dict(dq=DO_ + 64), la.LA_ERR_INVALID_ARG),
+    ("dk_overlaps_dv", dict(dk=DV - 64), la.LA_ERR_INVALID_ARG),
+    ("dkv_init_overlaps_workspace", dict(dkv_init=BWS + 64), la.LA_ERR_INVALID_ARG),
+    ("dkv_init_overlaps_dkv_final", dict(dkv_init=KVF), la.LA_ERR_INVALID_ARG),
+    ("dv_misaligned", dict(dv=DV + 4), la.LA_ERR_INVALID_ARG),
+    ("cu_decreasing", dict(cu_host=np.array([0, 60, 50], np.int32), T=50), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_BACKWARD, ids=[b[0] for b in BAD_BACKWARD])
+def test_backward_rejects(name, kw, code):
+    st, msg = _bwd(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_backward_no_states_needs_no_workspace():
+    """Without kv_init and dkv_final the workspace may be NULL (host check
+    passes; nothing is launched because there are no sequences)."""
+    st, msg = _bwd(S=0, T=0, cu_host=np.array([0], np.int32), kv_init=None, dkv_final=None,
+                   ws=None, ws_bytes=0)
     assert st == la.LA_OK, msg

@@ -1,0 +1,79 @@
+"""GPU parity of la_prefill_backward (dQ, dK, dV, dS_init) against the fp64
+oracle backward (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import cu_seqlens, host_qkv, random_states, workload
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _run(dev, lengths, H, d, decay, seed, kv_init, dkv_final, f32_grads=False, heads=None):
+    import torch
+    import linear_attention_la_amd as la
+
+    say(f"case backward lengths={list(lengths)[:8]} H={H} d={d} kv_init={kv_init} "
+        f"dkv_final={dkv_final} f32_grads={f32_grads}")
+    T = int(sum(lengths))
+    S = len(lengths)
+    q, k, v = host_qkv(T, H, d, seed, "bf16")
+    do = host_qkv(T, H, d, seed + 1, "bf16")[0]
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(S, H, d, seed + 7, scale=0.1) if kv_init else None
+    g = random_states(S, H, d, seed + 9, scale=0.1) if dkv_final else None
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v, do))
+    out = la.prefill_backward(qd, kd, vd, dod, cu, decay,
+                              kv_init=to_dev(kv0, torch.float32, dev) if kv_init else None,
+                              dkv_final=to_dev(g, torch.float32, dev) if dkv_final else None,
+                              grad_dtype=torch.float32 if f32_grads else None)
+    torch.cuda.synchronize()
+    ref = oracle.backward_varlen(q, k, v, do, cu, decay, kv_init=kv0, dkv_final=g, heads=heads)
+    return [to_np(x) for x in out], ref
+
+
+def _check(gpu, ref, f32_grads, heads=None, what=""):
+    sel = (lambda x: x) if heads is None else (lambda x: x[:, list(heads)])
+    stats = []
+    for name, a, b in zip(("dq", "dk", "dv"), gpu[:3], ref[:3]):
+        stats.append(parity.check(sel(a), sel(b), 1, 1e-2, out_bf16=not f32_grads,
+                                  what=f"{what} {name}"))
+    stats.append(parity.check(sel(gpu[3]), sel(ref[3]), 1, 1e-2, what=f"{what} dkv_init"))
+    return stats
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("kv_init,dkv_final", [(False, False), (True, True), (False, True)])
+def test_backward_ragged(dev, d, kv_init, dkv_final):
+    """Ragged lengths around the 64-token block (empty, 1, 63..65, several
+    blocks plus a tail), decays from none to strong, with and without an
+    initial state and a final-state gradient."""
+    lengths = [1, 63, 64, 65, 129, 0, 300, 17]
+    decay = np.array([1.0, 0.99, 0.9, 0.5], np.float32)
+    gpu, ref = _run(dev, lengths, 4, d, decay, 51 + d, kv_init, dkv_final)
+    say("backward ragged", _check(gpu, ref, False, what="ragged"))
+
+
+def test_backward_fp32_grads(dev):
+    lengths = [200, 0, 513]
+    decay = np.array([0.999, 0.97, 0.8], np.float32)
+    gpu, ref = _run(dev, lengths, 3, 128, decay, 83, True, True, f32_grads=True)
+    say("backward fp32 grads", _check(gpu, ref, True, what="fp32 grads"))
+
+
+def test_backward_n8k_sampled_heads(dev):
+    """B=1, H=64, N=8192, d=128 with the seeded decays (initial state and
+    final-state gradient): three heads (no, mid and strongest decay
+    included) against the oracle's two-chain backward."""
+    w = workload("n8k")
+    heads = [0, int(np.argmin(w["decay"])), int(np.argmax(w["decay"]))]
+    gpu, ref = _run(dev, w["lengths"], 64, 128, w["decay"], 1002, True, True, heads=heads)
+    say("backward n8k", _check(gpu, ref, False, heads=heads, what="n8k"))
