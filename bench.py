@@ -439,7 +439,7 @@ def main():
                    "heads": H, "head_dim": D, "beta": BETA, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "prefill_bf16_kernel<128,false>",
+                     "traffic": traffic, "kernel": "prefill_bf16_kernel<128, false, false, false>",
                      "kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes": by},
         "mfma": {"tflops_algorithmic_beta64": round(tflops, 2),
                  "frac_of_2500": round(tflops / BF16_PEAK_TFLOPS, 4)},
