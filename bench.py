@@ -42,6 +42,7 @@ BF16_PEAK_TFLOPS = 2500.0
 H, D, BETA = 64, 128, 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n8k_hbm_traffic.txt")
 KERNEL_SOURCES = ["linear_attention_la_amd/csrc/la_prefill_bf16.hip",
+                  "linear_attention_la_amd/csrc/la_mfma.h",
                   "linear_attention_la_amd/csrc/la_device.h",
                   "linear_attention_la_amd/csrc/la_internal.h"]
 

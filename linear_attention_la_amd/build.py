@@ -27,8 +27,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-SOURCES = ["la_host.cpp", "la_prefill_bf16.hip", "la_prefill_f32.hip", "la_decode.hip",
-           "la_segment.hip", "la_state.hip"]
+SOURCES = ["la_host.cpp", "la_prefill_bf16.hip", "la_prefill_wide.hip", "la_prefill_f32.hip",
+           "la_decode.hip", "la_segment.hip", "la_state.hip"]
 
 
 def _compile(src):

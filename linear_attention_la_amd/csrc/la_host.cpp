@@ -4,6 +4,7 @@
 // no device memory.
 
 #include <math.h>
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -140,6 +141,28 @@ la_status check_prefill(const void* q, const void* k, const void* v,
   }
   if (overlap(ro, rf)) return fail(LA_ERR_INVALID_ARG, "o overlaps kv_final");
   return LA_OK;
+}
+
+// Compute units of the current device (0 if unknown), cached per device.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The wide bf16 kernel (one workgroup per chain, d = 128) reads every input
+// row once per chain instead of once per 32-column slice; it is chosen when
+// there are at least as many chains as compute units, so that it fills the
+// GPU.
+bool use_wide(int64_t chains, int32_t head_dim) {
+  const int cus = device_cus();
+  return head_dim == 128 && cus > 0 && chains >= cus;
 }
 
 la_status check_segment_len(int32_t segment_len) {
@@ -286,8 +309,15 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = in_dtype == LA_BF16 ? la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s)
-                                     : la::launch_prefill_f32(a, head_dim, out_dtype, s);
+  hipError_t e;
+  if (in_dtype != LA_BF16) {
+    e = la::launch_prefill_f32(a, head_dim, out_dtype, s);
+  } else if (use_wide((int64_t)num_seqs * num_heads, head_dim)) {
+    a.num_items = num_seqs * num_heads;
+    e = la::launch_prefill_wide(a, out_dtype, false, s);
+  } else {
+    e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
+  }
   return hip_status(e, "la_prefill launch");
 }
 
@@ -378,7 +408,10 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   a.num_heads = num_heads;
   a.num_items = (int32_t)items;
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
-  e = la::launch_prefill_bf16(a, head_dim, LA_BF16, true, false, s);
+  const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
+  if (wide) a.num_items = lay.num_segments * num_heads;
+  e = wide ? la::launch_prefill_wide(a, LA_BF16, true, s)
+           : la::launch_prefill_bf16(a, head_dim, LA_BF16, true, false, s);
   if (e != hipSuccess) return hip_status(e, "la_prefill_segmented state pass launch");
 
   // pass 2: states at every segment start (and the final states)
@@ -392,7 +425,8 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   a.kv_final = nullptr;
   a.final_slot = nullptr;
   a.o = o;
-  e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
+  e = wide ? la::launch_prefill_wide(a, out_dtype, false, s)
+           : la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
   return hip_status(e, "la_prefill_segmented output pass launch");
 }
 

@@ -1,0 +1,396 @@
+// bf16 prefill for gfx950, wide decomposition (d = 128): one workgroup per
+// (sequence, head) chain.
+//
+// Method (emonzhong.com "MiniMax-01: Scaling Foundation Models with Lightning
+// Attention" 方法要点; CSDN "【AI论文】MiniMax-01:利用闪电注意力机制扩展基础模型"
+// §2.1; mizuki blog "MiniMax-01：4M 上下文破局" 关键概念清单): blocks of
+// BETA = 64 tokens, ell valid rows, local indices i (query) and j (key):
+//   P      = (Q_b K_b^T) .* M,  M[i][j] = lambda^(i-j) for i >= j, else 0
+//   O_b    = P V_b + diag(lambda^(i+1)) Q_b S_b          (left + right product)
+//   S_b+1  = lambda^ell S_b + K_b^T diag(lambda^(ell-1-j)) V_b
+//
+// Decomposition.  The 32-column kernel (la_prefill_bf16.hip) splits the state
+// over four workgroups per chain, each of which reads all Q and K rows and
+// forms Q K^T again.  Here one workgroup of 8 waves owns the whole chain, so
+// every input row crosses into the CU once and Q K^T is formed once; it
+// fills the GPU when there are at least as many chains as CUs (many
+// sequences, or a long sequence cut into segments).  Wave w owns value
+// columns [16w, 16w+16) of the fp32 d x d state -- all 128 key rows, eight
+// 16 x 16 accumulator tiles -- for the whole chain.  Per block:
+//   phase 1  waves 0..5 each form one 16-query x 32-key unit of P (scores,
+//            mask, decay, hi/lo split) and write it to LDS; every wave forms
+//            S^T Q^T for its 16 columns with its state registers as the A
+//            operand (the accumulator layout of a pair of key tiles is the
+//            operand layout of one 32-key step);
+//   phase 2  every wave completes O^T = V^T P^T + diag(lambda^(i+1)) S^T Q^T
+//            for its columns and stores them, then advances its state by
+//            K^T (diag(lambda^(ell-1-j)) V) -- the decayed values are formed in
+//            registers from the V^T operand it already holds.
+// Two barriers per block: one publishes the staged Q, K, V rows, one the
+// scores.  Q, K and V of block b+1 are loaded during block b and written to
+// the other LDS buffer at its end.
+//
+// Precision as in the 32-column kernel: P, the state operand of Q S and the
+// decayed V rows enter the MFMAs as bf16 hi/lo pairs; every sum is fp32 and
+// the state stays fp32.
+//
+// LDS (bf16 bits), every access pattern below free of bank conflicts on
+// gfx950 (reads 256 B/clk, writes 128 B/clk):
+//   Qs, Ks [2][64][128]  16 B chunk c of row r at chunk c ^ kswz(r); in Qs
+//                        the two 8 B halves of odd chunks are swapped
+//   Vs     [2][64][128]  chunk c of row r at chunk c ^ (2r mod 16)
+//   Ph, Pl [64][64]      query row i; 16 B unit u = 4 kk2 + g holds keys
+//                        32 kk2 + 4g + (0..3) and 32 kk2 + 16 + 4g + (0..3),
+//                        stored at unit u ^ (i mod 8)
+
+#include "la_internal.h"
+#include "la_mfma.h"
+
+namespace la {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBeta = 64;
+constexpr int kThreads = 512;
+constexpr int kTok = kBeta * kD;  // elements of one staged block
+
+__device__ __forceinline__ int v_woff(int r, int col) {
+  return r * kD + 8 * ((col >> 3) ^ ((2 * r) & 15)) + (col & 7);
+}
+__device__ __forceinline__ int p_off(int i, int u) { return i * kBeta + 8 * (u ^ (i & 7)); }
+
+// Score units: (query tile, 32-key step) pairs on or below the diagonal.
+__device__ __forceinline__ int unit_qt(int u) { return u < 2 ? u : u < 4 ? 2 : 3; }
+__device__ __forceinline__ int unit_kk2(int u) { return (u == 3 || u == 5) ? 1 : 0; }
+
+// Element e of a bf16x8 as float.  The whole vector is reinterpreted before
+// indexing: a bit cast applied to one element of a vector value is lowered by
+// this compiler to a splat of element 0.
+__device__ __forceinline__ float bf16_at(const bf16x8& x, int e) {
+  const v8i16 xi = __builtin_bit_cast(v8i16, x);
+  return __builtin_bit_cast(float, (uint32_t)(uint16_t)xi[e] << 16);
+}
+
+// The packed bf16 pair (-1, 0) (low half -1), produced in a scalar register:
+// left as a constant, the compiler encodes it as the inline constant -1.0,
+// whose fp32 bit pattern v_dot2 reads as the pair (0, -1).
+__device__ __forceinline__ uint32_t neg_lo_pair() {
+  uint32_t c;
+  asm("s_mov_b32 %0, 0xbf80" : "=s"(c));
+  return c;
+}
+
+// hi/lo split of 4 floats, hi = bf16(x), lo = bf16(x - hi), for a temporary
+// x: each difference is one v_dot2 of the packed hi pair with (-1, 0) or
+// (0, -1) accumulated onto x (exact in fp32, since hi is x rounded to bf16).
+// The dot product accumulates in place, so for an x that stays live (the
+// state) the plain split4 is cheaper.  nlo must be neg_lo_pair().
+__device__ __forceinline__ void split4t(floatx4 x, uint2& hi, uint2& lo, uint32_t nlo) {
+  const bf16x2 n_lo = __builtin_bit_cast(bf16x2, nlo);
+  const bf16x2 n_hi = __builtin_bit_cast(bf16x2, 0xBF800000u);
+  hi.x = cvt2(x[0], x[1]);
+  hi.y = cvt2(x[2], x[3]);
+  const bf16x2 h0 = __builtin_bit_cast(bf16x2, hi.x), h1 = __builtin_bit_cast(bf16x2, hi.y);
+  lo.x = cvt2(__builtin_amdgcn_fdot2_f32_bf16(h0, n_lo, x[0], false),
+              __builtin_amdgcn_fdot2_f32_bf16(h0, n_hi, x[1], false));
+  lo.y = cvt2(__builtin_amdgcn_fdot2_f32_bf16(h1, n_lo, x[2], false),
+              __builtin_amdgcn_fdot2_f32_bf16(h1, n_hi, x[3], false));
+}
+
+template <bool kOutF32, bool kStateOnly>
+__global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kStateOnly ? 8 : 2 * kTok];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kTok];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * kTok];
+  __shared__ __attribute__((aligned(16))) uint16_t Ph[kStateOnly ? 8 : kBeta * kBeta];
+  __shared__ __attribute__((aligned(16))) uint16_t Pl[kStateOnly ? 8 : kBeta * kBeta];
+
+  const int H = a.num_heads;
+  const int s = blockIdx.x / H;
+  const int h = blockIdx.x - s * H;
+  const int t = threadIdx.x;
+  const int w = uniform(t >> 6);  // value-column tile of this wave
+  const int c0 = 16 * w;
+  const int l = t & 63;
+  const int li = l & 15;
+  const int g = l >> 4;
+  const int tr_r = li >> 2;
+  const int tr_a = li & 3;
+  const uint32_t nlo = neg_lo_pair();
+
+  const int64_t start = a.cu_seqlens[s];
+  const int64_t end = a.cu_seqlens[s + 1];
+  const int nblocks = (int)((end - start + kBeta - 1) / kBeta);
+  const int row_stride = H * kD;
+  const float l2 = a.log2_decay[h];
+  const float lam_beta = exp2f((float)kBeta * l2);
+  const int64_t init_off = ((int64_t)(a.init_slot ? a.init_slot[s] : s) * H + h) * kD * kD;
+  const int64_t final_off = ((int64_t)(a.final_slot ? a.final_slot[s] : s) * H + h) * kD * kD;
+
+  auto block_len = [&](int b) -> int {
+    const int64_t rem = end - (start + (int64_t)b * kBeta);
+    return rem <= 0 ? 0 : rem < kBeta ? (int)rem : kBeta;
+  };
+  // Buffer resource over the valid rows (all heads) of block b: loads past
+  // the end of the sequence return zero and stores there are dropped.
+  auto block_rsrc = [&](const void* base, int b, int esize) {
+    const char* p = static_cast<const char*>(base) +
+                    (start + (int64_t)b * kBeta) * row_stride * (int64_t)esize;
+    return buf_rsrc(p, block_len(b) * row_stride * esize);
+  };
+
+  // ---- state: tile n holds key rows srow(n, g) + m, column c0 + li ----
+  floatx4 st[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    st[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (a.kv_init) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        st[n][m] = a.kv_init[init_off + (int64_t)(srow(n, g) + m) * kD + c0 + li];
+    }
+  }
+
+  // ---- per-lane decay factors ----
+  // Score unit of this wave (waves 0..5): query tile qt, keys 32 kk2 .. +31
+  // as key tiles kt = 2 kk2 and 2 kk2 + 1.  Element (key 16 kt + 4g + m,
+  // query 16 qt + li) has i - j = 16 (qt - kt) + li - 4g - m.
+  const int su = w < 6 ? w : 0;
+  const int sqt = unit_qt(su);
+  const int skk2 = unit_kk2(su);
+  floatx4 fs[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int kt = 2 * skk2 + e;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int x = 16 * (sqt - kt) + li - 4 * g - m;
+      fs[e][m] = x >= 0 ? exp2f((float)x * l2) : 0.0f;
+    }
+  }
+  float qdec[4];  // lambda^(i+1) of query 16 qt + li
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) qdec[qt] = exp2f((float)(16 * qt + li + 1) * l2);
+  // lambda^(ell-1-j) for the 16 tokens of this lane's V^T operands (key step
+  // kk2, element e: token 32 kk2 + 16 (e / 4) + 4g + e % 4); 0 past ell.
+  auto vweights = [&](float (&wv)[2][8], int ell) {
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 32 * kk2 + 16 * (e >> 2) + 4 * g + (e & 3);
+        wv[kk2][e] = j < ell ? exp2f((float)(ell - 1 - j) * l2) : 0.0f;
+      }
+  };
+  float wfull[2][8];
+  vweights(wfull, kBeta);
+
+  // ---- staging: thread t moves 16 B chunks t and t + 512 of each block
+  // (row id / 16, chunk id % 16) of Q, K and V ----
+  struct Stage {
+    uint4 q[2], k[2], v[2];
+  };
+  auto load_stage = [&](Stage& r, int b) {
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc(a.q, b, 2);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k, b, 2);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v, b, 2);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int id = t + kThreads * p;
+      const int off = 2 * ((id >> 4) * row_stride + h * kD + 8 * (id & 15));
+      if (!kStateOnly)
+        r.q[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      r.k[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+      r.v[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+    }
+  };
+  auto store_stage = [&](const Stage& r, int buf) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int id = t + kThreads * p;
+      const int row = id >> 4, ch = id & 15;
+      if (!kStateOnly) {
+        // odd chunks of Q rows are stored with their two 8 B halves swapped
+        const uint4 x = r.q[p];
+        *reinterpret_cast<uint4*>(&Qs[buf * kTok + qk_off<kD>(row, ch)]) =
+            (ch & 1) ? make_uint4(x.z, x.w, x.x, x.y) : x;
+      }
+      *reinterpret_cast<uint4*>(&Ks[buf * kTok + qk_off<kD>(row, ch)]) = r.k[p];
+      *reinterpret_cast<uint4*>(&Vs[buf * kTok + v_woff(row, 8 * ch)]) = r.v[p];
+    }
+  };
+
+  // ---- phase 1: one unit of P (waves 0..5) and S^T Q^T (all waves) ----
+  floatx4 oe[4];
+  const int hsw = 4 * (g & 1);  // element offset of a lane group's first Q half
+  auto phase1 = [&](auto cur_) {
+    constexpr int cur = decltype(cur_)::value;
+    const uint16_t* Qc = Qs + cur * kTok;
+    const uint16_t* Kc = Ks + cur * kTok;
+    if (w < 6) {
+      floatx4 sc[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) sc[e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      const bool upper = 2 * skk2 + 1 > sqt;  // second key tile above the diagonal
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int qo = qk_off<kD>(16 * sqt + li, 4 * kk + g);
+        const bf16x8 qb = cat(*reinterpret_cast<const v4i16*>(&Qc[qo + hsw]),
+                              *reinterpret_cast<const v4i16*>(&Qc[qo + 4 - hsw]));
+        sc[0] = mfma(ld8(&Kc[qk_off<kD>(32 * skk2 + li, 4 * kk + g)]), qb, sc[0]);
+        if (!upper) sc[1] = mfma(ld8(&Kc[qk_off<kD>(32 * skk2 + 16 + li, 4 * kk + g)]), qb, sc[1]);
+      }
+      uint2 h0, l0, h1, l1;
+      split4t(sc[0] * fs[0], h0, l0, nlo);
+      split4t(sc[1] * fs[1], h1, l1, nlo);
+      const int po = p_off(16 * sqt + li, 4 * skk2 + g);
+      *reinterpret_cast<uint4*>(&Ph[po]) = make_uint4(h0.x, h0.y, h1.x, h1.y);
+      *reinterpret_cast<uint4*>(&Pl[po]) = make_uint4(l0.x, l0.y, l1.x, l1.y);
+    }
+    // S^T Q^T: the A operand of key step kk is the pair of state tiles
+    // (2kk, 2kk+1), whose lane group g holds keys 32kk + 8g + (0..7) -- in
+    // the order (4..7, 0..3) for odd g (see srow), which is the order in
+    // which Q chunk 4kk + g is stored.
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) oe[qt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint2 ah0, al0, ah1, al1;
+      split4(st[2 * kk], ah0, al0);
+      split4(st[2 * kk + 1], ah1, al1);
+      const bf16x8 ahi = cat2(ah0, ah1);
+      const bf16x8 alo = cat2(al0, al1);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        const bf16x8 qb = ld8(&Qc[qk_off<kD>(16 * qt + li, 4 * kk + g)]);
+        oe[qt] = mfma(ahi, qb, oe[qt]);
+        oe[qt] = mfma(alo, qb, oe[qt]);
+      }
+    }
+  };
+
+  // ---- phase 2: P V, output, state update ----
+  auto phase2 = [&](auto cur_, int b) {
+    constexpr int cur = decltype(cur_)::value;
+    const uint16_t* Kc = Ks + cur * kTok;
+    const uint16_t* Vc = Vs + cur * kTok;
+    const int ell = block_len(b);
+    // V^T operands of this wave's columns: lane (li, g) holds column c0 + li
+    // of tokens 32 kk2 + 4g + (0..3) and 32 kk2 + 16 + 4g + (0..3)
+    bf16x8 va[2];
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const int j0 = 32 * kk2 + 4 * g + tr_r;
+      va[kk2] = cat(ld_tr(&Vc[v_woff(j0, c0 + 4 * tr_a)]), ld_tr(&Vc[v_woff(j0 + 16, c0 + 4 * tr_a)]));
+    }
+    if (!kStateOnly) {
+      constexpr int ES = kOutF32 ? 4 : 2;
+      const __amdgpu_buffer_rsrc_t ro = block_rsrc(a.o, b, ES);
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) {
+        floatx4 acc = oe[qt] * qdec[qt];
+#pragma unroll
+        for (int kk2 = 0; kk2 <= qt / 2; ++kk2) {
+          const int po = p_off(16 * qt + li, 4 * kk2 + g);
+          acc = mfma(va[kk2], ld8(&Ph[po]), acc);
+          acc = mfma(va[kk2], ld8(&Pl[po]), acc);
+        }
+        // lane (li, g): query 16 qt + li, value columns c0 + 4g + (0..3)
+        const int off = ES * ((16 * qt + li) * row_stride + h * kD + c0 + 4 * g);
+        if constexpr (kOutF32) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3])},
+                                                ro, off, 0, 0);
+        }
+      }
+    }
+    // decayed values lambda^(ell-1-j) V as hi/lo operands; only the last
+    // block of a chain can be partial, so its weights replace the full ones
+    if (ell != kBeta) vweights(wfull, ell);
+    bf16x8 vdh[2], vdl[2];
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      floatx4 x0, x1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x0[e] = bf16_at(va[kk2], e) * wfull[kk2][e];
+        x1[e] = bf16_at(va[kk2], e + 4) * wfull[kk2][e + 4];
+      }
+      uint2 h0, l0, h1, l1;
+      split4t(x0, h0, l0, nlo);
+      split4t(x1, h1, l1, nlo);
+      vdh[kk2] = cat2(h0, h1);
+      vdl[kk2] = cat2(l0, l1);
+    }
+    const float fl = ell == kBeta ? lam_beta : exp2f((float)ell * l2);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st[n] = st[n] * fl;
+#pragma unroll
+    for (int kk2 = 0; kk2 < 2; ++kk2) {
+      const int j0 = 32 * kk2 + 4 * g + tr_r;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int e = srow(n, tr_a);  // A rows 4 tr_a .. 4 tr_a + 3 of key tile n
+        const bf16x8 ka = cat(ld_tr(&Kc[qk_off<kD>(j0, e >> 3) + (e & 7)]),
+                              ld_tr(&Kc[qk_off<kD>(j0 + 16, e >> 3) + (e & 7)]));
+        st[n] = mfma(ka, vdh[kk2], st[n]);
+        st[n] = mfma(ka, vdl[kk2], st[n]);
+      }
+    }
+  };
+
+  // ---- pipeline ----
+  {
+    Stage r;
+    load_stage(r, 0);
+    store_stage(r, 0);
+  }
+  lds_barrier();
+  // Block b uses LDS buffer b % 2; the loop is unrolled by two so that every
+  // LDS address is a per-lane base plus a constant.
+  auto step = [&](int b, auto cur_) {
+    constexpr int cur = decltype(cur_)::value;
+    Stage r;
+    load_stage(r, b + 1);  // empty range past the last block
+    // Compiler-only memory fence: the loads stay here, at the top of the
+    // block, instead of being sunk next to their use at its end (which would
+    // expose their latency).  It emits no instruction and waits for nothing.
+    asm volatile("" ::: "memory");
+    if (!kStateOnly) {
+      phase1(cur_);
+      lds_barrier();
+    }
+    phase2(cur_, b);
+    if (b + 1 < nblocks) store_stage(r, cur ^ 1);
+    lds_barrier();
+  };
+  for (int b = 0; b < nblocks; b += 2) {
+    step(b, IC<0>{});
+    if (b + 1 < nblocks) step(b + 1, IC<1>{});
+  }
+
+  if (a.kv_final) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        a.kv_final[final_off + (int64_t)(srow(n, g) + m) * kD + c0 + li] = st[n][m];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool state_only,
+                               hipStream_t stream) {
+  const dim3 grid(a.num_items), block(kThreads);
+  if (state_only)
+    hipLaunchKernelGGL((prefill_wide_kernel<false, true>), grid, block, 0, stream, a);
+  else if (out_dtype == LA_FP32)
+    hipLaunchKernelGGL((prefill_wide_kernel<true, false>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_wide_kernel<false, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace la

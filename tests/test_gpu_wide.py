@@ -1,0 +1,155 @@
+"""GPU parity of the wide bf16 prefill kernel (one workgroup per chain, d = 128)
+against the fp64 oracle (needs an MI355X).
+
+The library takes the wide kernel when a call has at least as many (sequence,
+head) chains -- or (segment, head) chains in the segmented prefill -- as the
+GPU has compute units; every case here is sized past that point (64 heads and
+enough sequences or segments), which the tests assert."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import cu_seqlens, host_int_qkv, host_qkv, random_states, rne_bf16, workload
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+H = 64
+D = 128
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _assert_wide(chains):
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert chains >= cus, f"{chains} chains < {cus} compute units: the wide kernel is not used"
+
+
+def _decay():
+    d = np.asarray(workload("n8k")["decay"], np.float32).copy()
+    d[0], d[1], d[2] = 1.0, 0.5, 0.9  # no decay, strong decay, medium
+    return d
+
+
+def _run(dev, lengths, seed, kv_init=False, out_f32=False, in_place=False, segment_len=None):
+    import torch
+    import linear_attention_la_amd as la
+
+    say(f"case wide lengths={list(lengths)[:8]} kv_init={kv_init} out_f32={out_f32} "
+        f"in_place={in_place} segment_len={segment_len}")
+    T = int(sum(lengths))
+    decay = _decay()
+    q, k, v = host_qkv(T, H, D, seed, "bf16")
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(len(lengths), H, D, seed + 7, scale=0.1) if kv_init else None
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    kv0d = to_dev(kv0, torch.float32, dev) if kv_init else None
+    out_dtype = torch.float32 if out_f32 else None
+    kv_final = kv0d if in_place else None
+    if segment_len is None:
+        _assert_wide(len(lengths) * H)
+        o, kv = la.prefill(qd, kd, vd, cu, decay, kv_init=kv0d, out_dtype=out_dtype,
+                           kv_final=kv_final)
+    else:
+        segs = sum(max(1, -(-n // segment_len)) for n in lengths)
+        _assert_wide(segs * H)
+        o, kv = la.prefill_segmented(qd, kd, vd, cu, decay, segment_len, kv_init=kv0d,
+                                     out_dtype=out_dtype, kv_final=kv_final)
+    torch.cuda.synchronize()
+    if in_place:
+        assert kv.data_ptr() == kv0d.data_ptr()
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0, beta=64)
+    return to_np(o), to_np(kv), o_ref, kv_ref
+
+
+@pytest.mark.parametrize("out_f32", [False, True])
+@pytest.mark.parametrize("kv_init", [False, True])
+def test_wide_ragged(dev, out_f32, kv_init):
+    """Eight sequences x 64 heads: lengths 1, 63, 64, 65 (block edges), empty,
+    several blocks with a tail; every head and sequence against the oracle."""
+    lengths = [1, 63, 64, 65, 0, 300, 129, 17]
+    o, kv, o_ref, kv_ref = _run(dev, lengths, 101 + 2 * out_f32 + kv_init, kv_init, out_f32)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=not out_f32, what="wide o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="wide kv")
+    say("wide ragged", s1, s2)
+
+
+def test_wide_in_place_continuation(dev):
+    """Final states written over kv_init (aliasing allowed)."""
+    o, kv, o_ref, kv_ref = _run(dev, [200, 0, 513, 64], 111, kv_init=True, in_place=True)
+    parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="wide in-place o")
+    parity.check(kv, kv_ref, 1, 1e-2, what="wide in-place kv")
+
+
+@pytest.mark.parametrize("kv_init", [False, True])
+def test_wide_segmented(dev, kv_init):
+    """One 1000-token sequence cut into 4 segments of 256 (the last one
+    ragged): both segmented passes run the wide kernel."""
+    o, kv, o_ref, kv_ref = _run(dev, [1000], 121 + kv_init, kv_init=kv_init, segment_len=256)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="wide segmented o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="wide segmented kv")
+    say("wide segmented", s1, s2)
+
+
+def test_wide_exact_integer_inputs_bitwise(dev):
+    """Entries in {-1, 0, 1} with decay 1 (sequences up to 256 tokens) or 0.5
+    (up to 12 tokens): every intermediate is exact, so the wide kernel equals
+    the exact result bit for bit (fp32 output, final state) and its
+    round-to-nearest-even bf16 value (bf16 output)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    for lengths, lam in (([256, 100, 37, 1], 1.0), ([12, 5, 1, 9], 0.5)):
+        say(f"exact wide case lengths={lengths} decay={lam}")
+        _assert_wide(len(lengths) * H)
+        decay = np.full(H, lam, np.float32)
+        T = sum(lengths)
+        q, k, v = host_int_qkv(T, H, D, 9)
+        cu = cu_seqlens(lengths)
+        qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+        o32, kv = la.prefill(qd, kd, vd, cu, decay, out_dtype=torch.float32)
+        o16, _ = la.prefill(qd, kd, vd, cu, decay)
+        torch.cuda.synchronize()
+        o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, beta=64)
+        assert np.array_equal(to_np(o32), o_ref)
+        assert np.array_equal(to_np(kv), kv_ref)
+        assert np.array_equal(to_np(o16), rne_bf16(o_ref.astype(np.float32)).astype(np.float64))
+
+
+def test_wide_zero_length_sequences(dev):
+    """Four empty sequences x 64 heads: no rows; final state = initial state."""
+    import torch
+    import linear_attention_la_amd as la
+
+    _assert_wide(4 * H)
+    kv0 = random_states(4, H, D, 13)
+    kv0d = to_dev(kv0, torch.float32, dev)
+    qd = torch.empty((0, H, D), dtype=torch.bfloat16, device=dev)
+    o, kv = la.prefill(qd, qd.clone(), qd.clone(), [0, 0, 0, 0, 0], _decay(), kv_init=kv0d)
+    torch.cuda.synchronize()
+    assert o.shape == (0, H, D)
+    assert np.array_equal(to_np(kv), kv0.astype(np.float64))
+
+
+def test_wide_determinism_bitwise(dev):
+    """Two runs of a wide launch agree bit for bit."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [700, 33, 64, 1500]
+    _assert_wide(len(lengths) * H)
+    q, k, v = host_qkv(sum(lengths), H, D, 17, "bf16")
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    cu = cu_seqlens(lengths)
+    o1, kv1 = la.prefill(qd, kd, vd, cu, _decay())
+    o2, kv2 = la.prefill(qd, kd, vd, cu, _decay())
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(kv1, kv2)
