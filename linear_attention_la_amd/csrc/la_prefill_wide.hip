@@ -260,12 +260,16 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
       split4(st[2 * kk + 1], ah1, al1);
       const bf16x8 ahi = cat2(ah0, ah1);
       const bf16x8 alo = cat2(al0, al1);
+      // the hi products of the four query tiles, then the lo products: no
+      // MFMA waits for the one just before it
+      bf16x8 qb[4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        const bf16x8 qb = ld8(&Qc[qk_off<kD>(16 * qt + li, 4 * kk + g)]);
-        oe[qt] = mfma(ahi, qb, oe[qt]);
-        oe[qt] = mfma(alo, qb, oe[qt]);
+        qb[qt] = ld8(&Qc[qk_off<kD>(16 * qt + li, 4 * kk + g)]);
+        oe[qt] = mfma(ahi, qb[qt], oe[qt]);
       }
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) oe[qt] = mfma(alo, qb[qt], oe[qt]);
     }
   };
 
@@ -286,22 +290,26 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
     if (!kStateOnly) {
       constexpr int ES = kOutF32 ? 4 : 2;
       const __amdgpu_buffer_rsrc_t ro = block_rsrc(a.o, b, ES);
+      floatx4 acc[4];
+#pragma unroll
+      for (int qt = 0; qt < 4; ++qt) acc[qt] = oe[qt] * qdec[qt];
+      // hi products of every (query tile, key step), then the lo products
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+        for (int kk2 = 0; kk2 < 2; ++kk2)
+#pragma unroll
+          for (int qt = 2 * kk2; qt < 4; ++qt)
+            acc[qt] = mfma(va[kk2], ld8(&(hl ? Pl : Ph)[p_off(16 * qt + li, 4 * kk2 + g)]), acc[qt]);
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
-        floatx4 acc = oe[qt] * qdec[qt];
-#pragma unroll
-        for (int kk2 = 0; kk2 <= qt / 2; ++kk2) {
-          const int po = p_off(16 * qt + li, 4 * kk2 + g);
-          acc = mfma(va[kk2], ld8(&Ph[po]), acc);
-          acc = mfma(va[kk2], ld8(&Pl[po]), acc);
-        }
         // lane (li, g): query 16 qt + li, value columns c0 + 4g + (0..3)
         const int off = ES * ((16 * qt + li) * row_stride + h * kD + c0 + 4 * g);
         if constexpr (kOutF32) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[qt]), ro, off, 0, 0);
         } else {
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{cvt2(acc[0], acc[1]), cvt2(acc[2], acc[3])},
-                                                ro, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              u32x2{cvt2(acc[qt][0], acc[qt][1]), cvt2(acc[qt][2], acc[qt][3])}, ro, off, 0, 0);
         }
       }
     }
@@ -329,13 +337,19 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
 #pragma unroll
     for (int kk2 = 0; kk2 < 2; ++kk2) {
       const int j0 = 32 * kk2 + 4 * g + tr_r;
+      // four key tiles at a time: their hi products, then their lo products
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const int e = srow(n, tr_a);  // A rows 4 tr_a .. 4 tr_a + 3 of key tile n
-        const bf16x8 ka = cat(ld_tr(&Kc[qk_off<kD>(j0, e >> 3) + (e & 7)]),
-                              ld_tr(&Kc[qk_off<kD>(j0 + 16, e >> 3) + (e & 7)]));
-        st[n] = mfma(ka, vdh[kk2], st[n]);
-        st[n] = mfma(ka, vdl[kk2], st[n]);
+      for (int n0 = 0; n0 < 8; n0 += 4) {
+        bf16x8 ka[4];
+#pragma unroll
+        for (int n = n0; n < n0 + 4; ++n) {
+          const int e = srow(n, tr_a);  // A rows 4 tr_a .. 4 tr_a + 3 of key tile n
+          ka[n - n0] = cat(ld_tr(&Kc[qk_off<kD>(j0, e >> 3) + (e & 7)]),
+                           ld_tr(&Kc[qk_off<kD>(j0 + 16, e >> 3) + (e & 7)]));
+          st[n] = mfma(ka[n - n0], vdh[kk2], st[n]);
+        }
+#pragma unroll
+        for (int n = n0; n < n0 + 4; ++n) st[n] = mfma(ka[n - n0], vdl[kk2], st[n]);
       }
     }
   };
