@@ -21,7 +21,9 @@ One JSON line is printed with the contract fields plus:
   decode        la_decode alone on 256 sequences x 64 heads: GB/s vs 8 TB/s.
   mixed         decode on one stream concurrent with a packed prefill of 8
                 sequences (lengths U[1K, 32K]) on another.
-  sweep         cold tokens/s at N = 1K ... 1M and for a packed varlen batch.
+  sweep         cold tokens/s at N = 1K ... 1M, for eight 8K sequences in one
+                call and for a packed varlen batch (the last two have enough
+                (sequence, head) chains for the one-workgroup-per-chain kernel).
 """
 
 import argparse
@@ -229,7 +231,11 @@ def bench_mixed(dev, dec_state, reps=10):
             "step_wall_us": round(wall * 1e6, 1)}
 
 
-def bench_sweep(dev, reps=5):
+SWEEP = ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodecay", "n1m",
+         "batch8_n8k", "varlen64")
+
+
+def bench_sweep(dev, reps=5, names=SWEEP):
     import torch
 
     import linear_attention_la_amd as la
@@ -238,8 +244,7 @@ def bench_sweep(dev, reps=5):
     scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB cache flush
     res = {}
     s = torch.cuda.current_stream()
-    for name in ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodecay",
-                 "n1m", "varlen64"):
+    for name in names:
         w = workload(name)
         cu = cu_seqlens(w["lengths"])
         T = int(cu[-1])
@@ -359,6 +364,8 @@ def main():
                     help="only time la_decode_pool (256 sequences on a pool of 1024)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time la_prefill_backward on the n8k workload")
+    ap.add_argument("--sweep-only", choices=SWEEP,
+                    help="only time one workload of the length / batch sweep")
     ap.add_argument("--segmented-only", action="store_true",
                     help="only time la_prefill vs la_prefill_segmented at B=1, H=8, N=1M")
     args = ap.parse_args()
@@ -381,6 +388,9 @@ def main():
         return
     if args.segmented_only:
         print(json.dumps({"segmented": bench_segmented(dev)}), flush=True)
+        return
+    if args.sweep_only:
+        print(json.dumps({"sweep": bench_sweep(dev, names=(args.sweep_only,))}), flush=True)
         return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)

@@ -15,6 +15,7 @@ batches, CSDN §3.2; separate decode and prefill on two streams, jvyan.cn
 * ``n8k``       1 x 8192 tokens, 64 heads, d=128, bf16.
 * ``sweep``     1 x {1K, 4K, 16K, 64K} tokens, plus a no-decay 64K run.
 * ``n1m``       1 x 1,048,576 tokens.
+* ``batch8_n8k`` 8 x 8192 tokens (the n8k shape, batched).
 * ``varlen64``  64 sequences, lengths log-uniform in [512, 131072].
 * ``mixed``     256 decode tokens (1 per sequence) beside a prefill of 8
                 sequences with lengths uniform in [1K, 32K].
@@ -30,7 +31,7 @@ import numpy as np
 
 DECAY_SEED = 2025
 SEEDS = {"tiny": 1001, "n8k": 1002, "sweep": 1003, "n1m": 1004, "varlen64": 1004,
-         "mixed": 1005}
+         "mixed": 1005, "batch8_n8k": 1006}
 
 
 def rne_bf16(x):
@@ -146,6 +147,10 @@ def workload(name):
         dec = np.ones(64, np.float32) if nodecay else decay_from_seed(64)
         return dict(name=name, lengths=[n], H=64, d=128, dtype="bf16", decay=dec,
                     seed=SEEDS["sweep"])
+    if name == "batch8_n8k":
+        # the n8k sequence shape, eight sequences in one call (512 chains)
+        return dict(name=name, lengths=[8192] * 8, H=64, d=128, dtype="bf16",
+                    decay=decay_from_seed(64), seed=SEEDS[name])
     if name == "n1m":
         return dict(name=name, lengths=[1 << 20], H=64, d=128, dtype="bf16",
                     decay=decay_from_seed(64), seed=SEEDS[name])
