@@ -334,54 +334,82 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
     const float fl = ell == kBeta ? lam_beta : exp2f((float)ell * l2);
 #pragma unroll
     for (int n = 0; n < 8; ++n) st[n] = st[n] * fl;
+    // Four groups (key step kk2, key tiles n0 .. n0+3): the K^T operands of
+    // group grp+1 are read before the MFMAs of group grp issue, so the LDS
+    // latency is covered; within a group the hi products of its four tiles
+    // go first, then the lo products.
+    auto kload = [&](bf16x8(&dst)[4], int grp) {
+      const int j0 = 32 * (grp >> 1) + 4 * g + tr_r;
 #pragma unroll
-    for (int kk2 = 0; kk2 < 2; ++kk2) {
-      const int j0 = 32 * kk2 + 4 * g + tr_r;
-      // four key tiles at a time: their hi products, then their lo products
-#pragma unroll
-      for (int n0 = 0; n0 < 8; n0 += 4) {
-        bf16x8 ka[4];
-#pragma unroll
-        for (int n = n0; n < n0 + 4; ++n) {
-          const int e = srow(n, tr_a);  // A rows 4 tr_a .. 4 tr_a + 3 of key tile n
-          ka[n - n0] = cat(ld_tr(&Kc[qk_off<kD>(j0, e >> 3) + (e & 7)]),
-                           ld_tr(&Kc[qk_off<kD>(j0 + 16, e >> 3) + (e & 7)]));
-          st[n] = mfma(ka[n - n0], vdh[kk2], st[n]);
-        }
-#pragma unroll
-        for (int n = n0; n < n0 + 4; ++n) st[n] = mfma(ka[n - n0], vdl[kk2], st[n]);
+      for (int i = 0; i < 4; ++i) {
+        const int e = srow(4 * (grp & 1) + i, tr_a);  // A rows 4 tr_a .. +3 of the key tile
+        dst[i] = cat(ld_tr(&Kc[qk_off<kD>(j0, e >> 3) + (e & 7)]),
+                     ld_tr(&Kc[qk_off<kD>(j0 + 16, e >> 3) + (e & 7)]));
       }
+    };
+    bf16x8 ka[2][4];
+    kload(ka[0], 0);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      if (grp < 3) kload(ka[(grp + 1) & 1], grp + 1);
+      const int kk2 = grp >> 1, n0 = 4 * (grp & 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[n0 + i] = mfma(ka[grp & 1][i], vdh[kk2], st[n0 + i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[n0 + i] = mfma(ka[grp & 1][i], vdl[kk2], st[n0 + i]);
     }
   };
 
   // ---- pipeline ----
-  {
-    Stage r;
-    load_stage(r, 0);
-    store_stage(r, 0);
-  }
-  lds_barrier();
-  // Block b uses LDS buffer b % 2; the loop is unrolled by two so that every
-  // LDS address is a per-lane base plus a constant.
-  auto step = [&](int b, auto cur_) {
-    constexpr int cur = decltype(cur_)::value;
-    Stage r;
-    load_stage(r, b + 1);  // empty range past the last block
-    // Compiler-only memory fence: the loads stay here, at the top of the
-    // block, instead of being sunk next to their use at its end (which would
-    // expose their latency).  It emits no instruction and waits for nothing.
-    asm volatile("" ::: "memory");
-    if (!kStateOnly) {
+  // Block b uses LDS buffer b % 2; the loops are unrolled by two so that
+  // every LDS address is a per-lane base plus a constant.  An empty
+  // asm volatile("" ::: "memory") after each block's loads is a compiler-only
+  // fence: it keeps the loads at the top of the block, instead of being sunk
+  // next to their use (which would expose their latency); it emits no
+  // instruction and waits for nothing.
+  if constexpr (kStateOnly) {
+    // Little arithmetic per block: the loads run two blocks ahead, through
+    // two register stages (the stage that held block b, already in LDS,
+    // receives block b+2; the one holding block b+1 goes to LDS at the end).
+    Stage s0, s1;
+    load_stage(s0, 0);
+    load_stage(s1, 1);
+    store_stage(s0, 0);
+    lds_barrier();
+    auto step = [&](int b, auto cur_, Stage& sfree, Stage& snext) {
+      constexpr int cur = decltype(cur_)::value;
+      load_stage(sfree, b + 2);  // empty range past the last block
+      asm volatile("" ::: "memory");
+      phase2(cur_, b);
+      if (b + 1 < nblocks) store_stage(snext, cur ^ 1);
+      lds_barrier();
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+      step(b, IC<0>{}, s0, s1);
+      if (b + 1 < nblocks) step(b + 1, IC<1>{}, s1, s0);
+    }
+  } else {
+    {
+      Stage r;
+      load_stage(r, 0);
+      store_stage(r, 0);
+    }
+    lds_barrier();
+    auto step = [&](int b, auto cur_) {
+      constexpr int cur = decltype(cur_)::value;
+      Stage r;
+      load_stage(r, b + 1);  // empty range past the last block
+      asm volatile("" ::: "memory");
       phase1(cur_);
       lds_barrier();
+      phase2(cur_, b);
+      if (b + 1 < nblocks) store_stage(r, cur ^ 1);
+      lds_barrier();
+    };
+    for (int b = 0; b < nblocks; b += 2) {
+      step(b, IC<0>{});
+      if (b + 1 < nblocks) step(b + 1, IC<1>{});
     }
-    phase2(cur_, b);
-    if (b + 1 < nblocks) store_stage(r, cur ^ 1);
-    lds_barrier();
-  };
-  for (int b = 0; b < nblocks; b += 2) {
-    step(b, IC<0>{});
-    if (b + 1 < nblocks) step(b + 1, IC<1>{});
   }
 
   if (a.kv_final) {
