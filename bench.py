@@ -266,27 +266,29 @@ def bench_sweep(dev, reps=5, names=SWEEP):
     return res
 
 
-def bench_backward(dev, reps=10):
+def bench_backward(dev, reps=10, name="n8k"):
     """la_prefill_backward on the n8k workload (B=1, H=64, N=8192, d=128,
-    bf16), with an initial state and a final-state gradient.  Algorithmic
-    bytes: q, k, v, dO read and dq, dk, dv written (14 d B per token and
-    head) plus kv_init and dkv_final read and dkv_init written."""
+    bf16; the 32-column kernel) or on batch8_n8k (eight such sequences: the
+    one-workgroup-per-chain kernel), with initial states and final-state
+    gradients.  Algorithmic bytes: q, k, v, dO read and dq, dk, dv written
+    (14 d B per token and head) plus kv_init and dkv_final read and dkv_init
+    written."""
     import torch
 
     import linear_attention_la_amd as la
-    from la_inputs import device_qkv, device_states, workload
+    from la_inputs import cu_seqlens, device_qkv, device_states, workload
 
-    w = workload("n8k")
-    N = w["lengths"][0]
+    w = workload(name)
+    cu = cu_seqlens(w["lengths"])
+    S, N = len(w["lengths"]), int(cu[-1])
     q, k, v = device_qkv(N, H, D, w["seed"], dev)
     do = device_qkv(N, H, D, w["seed"] + 11, dev)[0]
-    kv0 = device_states(1, H, D, w["seed"] + 12, dev, scale=0.1)
-    g = device_states(1, H, D, w["seed"] + 13, dev, scale=0.1)
-    cu = np.array([0, N], np.int32)
+    kv0 = device_states(S, H, D, w["seed"] + 12, dev, scale=0.1)
+    g = device_states(S, H, D, w["seed"] + 13, dev, scale=0.1)
     cu_dev = torch.from_numpy(cu).to(dev)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     dkv0 = torch.empty_like(kv0)
-    ws = torch.empty(la.la_prefill_backward_workspace_size(1, H, D)[1], dtype=torch.uint8,
+    ws = torch.empty(la.la_prefill_backward_workspace_size(S, H, D)[1], dtype=torch.uint8,
                      device=dev)
     run = lambda i: la.prefill_backward(q, k, v, do, cu_dev, w["decay"], kv_init=kv0,  # noqa
                                         dkv_final=g, cu_seqlens_host=cu, workspace=ws, dq=dq,
@@ -294,10 +296,11 @@ def bench_backward(dev, reps=10):
     for _ in range(3):
         run(0)
     t = timed_launches(run, reps, torch.cuda.current_stream())
-    by = N * H * 14 * D + 3 * H * D * D * 4
+    by = N * H * 14 * D + 3 * S * H * D * D * 4
     del q, k, v, do, dq, dk, dv, ws
     torch.cuda.empty_cache()
-    return {"workload": f"la_prefill_backward B=1 H={H} N={N} d={D} bf16 (kv_init, dkv_final)",
+    return {"workload": f"la_prefill_backward B={S} H={H} N={N // S} d={D} bf16 "
+                        "(kv_init, dkv_final)",
             "us": round(t * 1e6, 1), "tokens_per_s": round(N / t, 0),
             "GB_per_s": round(by / t / 1e9, 1), "frac_of_8TBs": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": by}
@@ -363,7 +366,7 @@ def main():
     ap.add_argument("--pool-only", action="store_true",
                     help="only time la_decode_pool (256 sequences on a pool of 1024)")
     ap.add_argument("--backward-only", action="store_true",
-                    help="only time la_prefill_backward on the n8k workload")
+                    help="only time la_prefill_backward on n8k and batch8_n8k")
     ap.add_argument("--sweep-only", choices=SWEEP,
                     help="only time one workload of the length / batch sweep")
     ap.add_argument("--segmented-only", action="store_true",
@@ -384,7 +387,8 @@ def main():
         print(json.dumps({"decode_pool": bench_decode_pool(dev)}), flush=True)
         return
     if args.backward_only:
-        print(json.dumps({"backward": bench_backward(dev)}), flush=True)
+        print(json.dumps({"backward": bench_backward(dev),
+                          "backward_batch8": bench_backward(dev, name="batch8_n8k")}), flush=True)
         return
     if args.segmented_only:
         print(json.dumps({"segmented": bench_segmented(dev)}), flush=True)
@@ -465,6 +469,7 @@ def main():
         line["sweep"] = bench_sweep(dev)
         line["segmented"] = bench_segmented(dev)
         line["backward"] = bench_backward(dev)
+        line["backward_batch8"] = bench_backward(dev, name="batch8_n8k")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     else:

@@ -314,7 +314,7 @@ la_status la_prefill(const void* q, const void* k, const void* v,
     e = la::launch_prefill_f32(a, head_dim, out_dtype, s);
   } else if (use_wide((int64_t)num_seqs * num_heads, head_dim)) {
     a.num_items = num_seqs * num_heads;
-    e = la::launch_prefill_wide(a, out_dtype, false, s);
+    e = la::launch_prefill_wide(a, out_dtype, false, false, s);
   } else {
     e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
   }
@@ -410,7 +410,7 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
   const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
   if (wide) a.num_items = lay.num_segments * num_heads;
-  e = wide ? la::launch_prefill_wide(a, LA_BF16, true, s)
+  e = wide ? la::launch_prefill_wide(a, LA_BF16, true, false, s)
            : la::launch_prefill_bf16(a, head_dim, LA_BF16, true, false, s);
   if (e != hipSuccess) return hip_status(e, "la_prefill_segmented state pass launch");
 
@@ -425,7 +425,7 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   a.kv_final = nullptr;
   a.final_slot = nullptr;
   a.o = o;
-  e = wide ? la::launch_prefill_wide(a, out_dtype, false, s)
+  e = wide ? la::launch_prefill_wide(a, out_dtype, false, false, s)
            : la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
   return hip_status(e, "la_prefill_segmented output pass launch");
 }
@@ -525,6 +525,15 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     inv[h] = (float)(1.0 / (double)decay[h]);
     lam[h] = decay[h];
   }
+  // Each pass runs the wide kernel when there are enough chains to fill the
+  // GPU, else the 32-column kernel.
+  const bool wide = use_wide((int64_t)num_seqs * num_heads, head_dim);
+  auto pass = [&](bool reverse) {
+    if (!wide) return la::launch_prefill_bf16(a, head_dim, grad_dtype, false, reverse, s);
+    la::PrefillArgs w = a;
+    w.num_items = num_seqs * num_heads;
+    return la::launch_prefill_wide(w, grad_dtype, false, reverse, s);
+  };
   hipError_t e;
   // dQ: the forward chain with dO as queries, V as keys, K as values, S0^T
   if (kv_init) {
@@ -536,7 +545,7 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
   a.v = k;
   a.kv_init = kv_init ? ws : nullptr;
   a.o = dq;
-  e = la::launch_prefill_bf16(a, head_dim, grad_dtype, false, false, s);
+  e = pass(false);
   if (e != hipSuccess) return hip_status(e, "la_prefill_backward dq launch");
   // dK: backwards in time, V as queries, dO as keys, Q as values, dS_L^T / lambda
   if (dkv_final) {
@@ -548,7 +557,7 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
   a.v = q;
   a.kv_init = dkv_final ? ws : nullptr;
   a.o = dk;
-  e = la::launch_prefill_bf16(a, head_dim, grad_dtype, false, true, s);
+  e = pass(true);
   if (e != hipSuccess) return hip_status(e, "la_prefill_backward dk launch");
   // dV: backwards in time, K as queries, Q as keys, dO as values, dS_L / lambda;
   // its final state is dS0 / lambda
@@ -562,7 +571,7 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
   a.kv_init = dkv_final ? ws : nullptr;
   a.o = dv;
   a.kv_final = dkv_init;
-  e = la::launch_prefill_bf16(a, head_dim, grad_dtype, false, true, s);
+  e = pass(true);
   if (e != hipSuccess) return hip_status(e, "la_prefill_backward dv launch");
   if (dkv_init) {
     e = la::launch_state_transform(dkv_init, dkv_init, num_seqs, num_heads, head_dim, false, lam, s);

@@ -54,9 +54,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, la_dtype out_
 
 // Wide decomposition (la_prefill_wide.hip): one workgroup per (sequence,
 // head) chain for d = 128 with bf16 inputs; a.num_items = S * H.  Same
-// semantics as launch_prefill_bf16 (forward direction only).
+// semantics as launch_prefill_bf16 (state_only runs forward only).
 hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool state_only,
-                               hipStream_t stream);
+                               bool reverse, hipStream_t stream);
 
 // out[s,h] = scale[h] * (transpose ? in[s,h]^T : in[s,h]) for num_states x H
 // fp32 d x d states (la_state.hip); out may be in only without transpose.

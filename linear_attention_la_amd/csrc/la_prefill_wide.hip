@@ -97,7 +97,7 @@ __device__ __forceinline__ void split4t(floatx4 x, uint2& hi, uint2& lo, uint32_
               __builtin_amdgcn_fdot2_f32_bf16(h1, n_hi, x[3], false));
 }
 
-template <bool kOutF32, bool kStateOnly>
+template <bool kOutF32, bool kStateOnly, bool kReverse>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[kStateOnly ? 8 : 2 * kTok];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kTok];
@@ -133,11 +133,18 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   };
   // Buffer resource over the valid rows (all heads) of block b: loads past
   // the end of the sequence return zero and stores there are dropped.
+  // With kReverse the chain runs backwards in time: logical token i of the
+  // sequence is physical row end - 1 - i, so block b holds the physical rows
+  // [end - 64b - ell, end - 64b) in decreasing order.  Rows are addressed
+  // inside a block resource by prow(); logical rows past the end of the
+  // sequence map outside the resource either way.
   auto block_rsrc = [&](const void* base, int b, int esize) {
-    const char* p = static_cast<const char*>(base) +
-                    (start + (int64_t)b * kBeta) * row_stride * (int64_t)esize;
-    return buf_rsrc(p, block_len(b) * row_stride * esize);
+    const int ell = block_len(b);
+    const int64_t row0 = kReverse ? end - (int64_t)b * kBeta - ell : start + (int64_t)b * kBeta;
+    const char* p = static_cast<const char*>(base) + row0 * row_stride * (int64_t)esize;
+    return buf_rsrc(p, ell * row_stride * esize);
   };
+  auto prow = [&](int r, int ell) { return kReverse ? ell - 1 - r : r; };
 
   // ---- state: tile n holds key rows srow(n, g) + m, column c0 + li ----
   floatx4 st[8];
@@ -194,10 +201,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
     const __amdgpu_buffer_rsrc_t rq = block_rsrc(a.q, b, 2);
     const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k, b, 2);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v, b, 2);
+    const int ell = block_len(b);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       const int id = t + kThreads * p;
-      const int off = 2 * ((id >> 4) * row_stride + h * kD + 8 * (id & 15));
+      const int off = 2 * (prow(id >> 4, ell) * row_stride + h * kD + 8 * (id & 15));
       if (!kStateOnly)
         r.q[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
       r.k[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         // lane (li, g): query 16 qt + li, value columns c0 + 4g + (0..3)
-        const int off = ES * ((16 * qt + li) * row_stride + h * kD + c0 + 4 * g);
+        const int off = ES * (prow(16 * qt + li, ell) * row_stride + h * kD + c0 + 4 * g);
         if constexpr (kOutF32) {
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[qt]), ro, off, 0, 0);
         } else {
@@ -424,14 +432,19 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool state_only,
-                               hipStream_t stream) {
+                               bool reverse, hipStream_t stream) {
   const dim3 grid(a.num_items), block(kThreads);
+  const bool f32 = out_dtype == LA_FP32;
   if (state_only)
-    hipLaunchKernelGGL((prefill_wide_kernel<false, true>), grid, block, 0, stream, a);
-  else if (out_dtype == LA_FP32)
-    hipLaunchKernelGGL((prefill_wide_kernel<true, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_wide_kernel<false, true, false>), grid, block, 0, stream, a);
+  else if (reverse && f32)
+    hipLaunchKernelGGL((prefill_wide_kernel<true, false, true>), grid, block, 0, stream, a);
+  else if (reverse)
+    hipLaunchKernelGGL((prefill_wide_kernel<false, false, true>), grid, block, 0, stream, a);
+  else if (f32)
+    hipLaunchKernelGGL((prefill_wide_kernel<true, false, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((prefill_wide_kernel<false, false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((prefill_wide_kernel<false, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -77,3 +77,21 @@ def test_backward_n8k_sampled_heads(dev):
     heads = [0, int(np.argmin(w["decay"])), int(np.argmax(w["decay"]))]
     gpu, ref = _run(dev, w["lengths"], 64, 128, w["decay"], 1002, True, True, heads=heads)
     say("backward n8k", _check(gpu, ref, False, heads=heads, what="n8k"))
+
+
+@pytest.mark.parametrize("kv_init,dkv_final,f32_grads", [(False, False, False), (True, True, False),
+                                                         (True, True, True)])
+def test_backward_wide_path(dev, kv_init, dkv_final, f32_grads):
+    """Eight ragged sequences x 64 heads (512 chains: at least one per CU),
+    so all three passes run the one-workgroup-per-chain kernel, the dK and
+    dV passes in reverse time; every head against the oracle."""
+    import torch
+
+    lengths = [1, 63, 64, 65, 0, 300, 129, 17]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert len(lengths) * 64 >= cus
+    decay = np.asarray(workload("n8k")["decay"], np.float32).copy()
+    decay[0], decay[1] = 1.0, 0.5
+    gpu, ref = _run(dev, lengths, 64, 128, decay, 61 + kv_init + 2 * f32_grads, kv_init, dkv_final,
+                    f32_grads=f32_grads)
+    say("backward wide", _check(gpu, ref, f32_grads, what="wide"))
