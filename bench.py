@@ -21,7 +21,10 @@ One JSON line is printed with the contract fields plus:
   decode        la_decode alone on 256 sequences x 64 heads: GB/s vs 8 TB/s.
   mixed         decode on one stream concurrent with a packed prefill of 8
                 sequences (lengths U[1K, 32K]) on another.
-  sweep         cold tokens/s at N = 1K ... 1M, for eight 8K sequences in one
+  peaks         measured on the GPU: a 1 GiB read+write stream (HBM) and an 8192^3
+                bf16 matmul; roofline.frac_of_measured_stream relates the
+                prefill kernel to that stream.
+  sweep         cold tokens/s (median, min) at N = 1K ... 1M, for eight 8K sequences in one
                 call and for a packed varlen batch (the last two have enough
                 (sequence, head) chains for the one-workgroup-per-chain kernel).
 """
@@ -90,9 +93,9 @@ def measured_traffic():
         return None
 
 
-def timed_launches(fn, reps, stream, flush=None):
-    """Average duration (s) of `fn` over `reps` launches, by HIP events on
-    `stream`; `flush` runs between launches, outside the events."""
+def launch_times(fn, reps, stream, flush=None):
+    """Durations (s) of `reps` launches of `fn`, by HIP events on `stream`;
+    `flush` runs between launches, outside the events."""
     import torch
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
@@ -105,7 +108,44 @@ def timed_launches(fn, reps, stream, flush=None):
             fn(i)
             ends[i].record(stream)
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps / 1e3
+    return [s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends)]
+
+
+def timed_launches(fn, reps, stream, flush=None):
+    """Average duration (s) of `fn` over `reps` launches (see launch_times)."""
+    t = launch_times(fn, reps, stream, flush)
+    return sum(t) / len(t)
+
+
+def measured_peaks(dev):
+    """Peaks measured on this GPU: HBM GB/s of a 1 GiB fp32 stream that reads
+    and writes every element once (torch.mul with out=, the fastest of the
+    torch streaming kernels here; copy_ reaches less) and bf16 TFLOP/s of an
+    8192^3 torch matmul (hipBLASLt); both medians of 10 launches after
+    warm-up."""
+    import torch
+
+    s = torch.cuda.current_stream()
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    t = sorted(launch_times(lambda i: torch.mul(src, 1.0, out=dst), 10, s))[5]
+    stream_gbs = 2 * src.numel() * 4 / t / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b)
+    t = sorted(launch_times(lambda i: torch.matmul(a, b), 10, s))[5]
+    gemm_tflops = 2 * n ** 3 / t / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {"stream_GB_per_s": round(stream_gbs, 1), "stream_frac_of_8TBs": round(stream_gbs / HBM_PEAK_GBS, 4),
+            "bf16_gemm_TFLOP_per_s": round(gemm_tflops, 1),
+            "bf16_gemm_frac_of_2500": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+            "note": "1 GiB fp32 read+write stream (torch.mul out=); 8192^3 bf16 matmul (hipBLASLt)"}
 
 
 def cpu_baseline(budget_s=12.0):
@@ -235,7 +275,7 @@ SWEEP = ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodec
          "batch8_n8k", "varlen64")
 
 
-def bench_sweep(dev, reps=5, names=SWEEP):
+def bench_sweep(dev, reps=20, names=SWEEP):
     import torch
 
     import linear_attention_la_amd as la
@@ -255,9 +295,12 @@ def bench_sweep(dev, reps=5, names=SWEEP):
         run = lambda i: la.prefill(q, k, v, cu_dev, w["decay"], out=o, kv_final=kvf,  # noqa
                                    cu_seqlens_host=cu)
         run(0)
-        t = timed_launches(run, reps, s, flush=lambda: scratch.zero_())
+        n = reps if T <= 1 << 17 else 5  # >= 20 repeats, 5 for the 1M-token workloads
+        ts = sorted(launch_times(run, n, s, flush=lambda: scratch.zero_()))
+        t = ts[len(ts) // 2]
         by = prefill_bytes(T, len(w["lengths"]))
         res[name] = {"tokens": T, "seqs": len(w["lengths"]), "us": round(t * 1e6, 1),
+                     "us_min": round(ts[0] * 1e6, 1),
                      "tokens_per_s": round(T / t, 0), "GB_per_s": round(by / t / 1e9, 1),
                      "frac_of_8TBs": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
                      "tflops_beta64": round(prefill_flops(T) / t / 1e12, 1)}
@@ -467,6 +510,9 @@ def main():
         del dec_state
         torch.cuda.empty_cache()
         line["sweep"] = bench_sweep(dev)
+        peaks = measured_peaks(dev)
+        line["peaks"] = peaks
+        line["roofline"]["frac_of_measured_stream"] = round(achieved / peaks["stream_GB_per_s"], 4)
         line["segmented"] = bench_segmented(dev)
         line["backward"] = bench_backward(dev)
         line["backward_batch8"] = bench_backward(dev, name="batch8_n8k")
