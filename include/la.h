@@ -106,6 +106,14 @@ typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  *
  * Zero-length sequences produce no rows; their final state is kv_init's (or
  * zero).
+ *
+ * Kernels: bf16 inputs with d = 128 and at least as many (sequence, head)
+ * pairs as the current device has compute units run one workgroup per pair
+ * (each input row is read once); otherwise each pair is split by value
+ * columns over d / 32 workgroups.  Both give results within the same
+ * tolerance, not bitwise equal to each other; a given call is deterministic.
+ * A one-workgroup-per-pair launch occupies whole compute units, so work on
+ * another stream gets fewer of them while it runs.
  */
 la_status la_prefill(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -139,7 +147,8 @@ la_status la_prefill(const void* q, const void* k, const void* v,
  * be LA_BF16 (LA_FP32 is LA_ERR_UNSUPPORTED).  Errors as la_prefill, plus
  * LA_ERR_INVALID_ARG for a bad segment_len or a NULL, misaligned, short or
  * overlapping workspace.  Four kernels are enqueued on `stream`; nothing
- * synchronises.
+ * synchronises.  The two passes over the segments choose their kernel as
+ * la_prefill does, counting (segment, head) pairs.
  */
 la_status la_prefill_segmented(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -195,7 +204,7 @@ la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* c
  *
  * The outputs and the workspace may overlap nothing else.  Errors as
  * la_prefill.  Up to seven kernels are enqueued on `stream`; nothing
- * synchronises.
+ * synchronises.  The three chains choose their kernel as la_prefill does.
  */
 la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
