@@ -153,3 +153,62 @@ def test_wide_determinism_bitwise(dev):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert torch.equal(kv1, kv2)
+
+
+def test_wide_batch8_n8k_benchmark_launch(dev):
+    """Eight 8192-token sequences x 64 heads (the bench's batch8_n8k launch):
+    three heads over all eight sequences against the oracle, and every
+    output and final state against the 32-column kernel run one sequence
+    at a time on the same inputs (64 chains per call)."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv
+
+    w = workload("batch8_n8k")
+    cu = cu_seqlens(w["lengths"])
+    T, S = int(cu[-1]), len(w["lengths"])
+    _assert_wide(S * H)
+    say(f"case wide batch8_n8k T={T}")
+    qd, kd, vd = device_qkv(T, H, D, w["seed"], dev)
+    o, kv = la.prefill(qd, kd, vd, cu, w["decay"])
+    parts = [la.prefill(qd[cu[i]:cu[i + 1]].contiguous(), kd[cu[i]:cu[i + 1]].contiguous(),
+                        vd[cu[i]:cu[i + 1]].contiguous(), [0, int(cu[i + 1] - cu[i])], w["decay"])
+             for i in range(S)]
+    o_slice = torch.cat([p_[0] for p_ in parts])
+    kv_slice = torch.cat([p_[1] for p_ in parts])
+    torch.cuda.synchronize()
+    s1 = _compare_on_device(o, o_slice, bf16=True, what="wide vs 32-column o")
+    s2 = _compare_on_device(kv, kv_slice, bf16=False, what="wide vs 32-column kv")
+    say("wide vs 32-column", s1, s2)
+    for h in (0, int(np.argmin(w["decay"])), int(np.argmax(w["decay"]))):
+        q1, k1, v1 = (to_np(x[:, h, :])[:, None, :] for x in (qd, kd, vd))
+        o_ref, kv_ref = oracle.prefill_varlen(q1, k1, v1, cu, np.array([w["decay"][h]]), beta=256)
+        s3 = parity.check(to_np(o[:, h, :])[:, None, :], o_ref, 1, 1e-2, out_bf16=True,
+                          what=f"o head {h}")
+        s4 = parity.check(to_np(kv[:, h])[:, None], kv_ref, 1, 1e-2, what=f"kv head {h}")
+        say("wide batch8 head", h, s3, s4)
+
+
+def _compare_on_device(a, b, bf16, what, rel_tol=1e-2, elem_tol=2e-2):
+    """Per-head relative L2 <= rel_tol and elementwise |a - b| <= elem_tol *
+    rms_h(b), on the GPU (head axis 1); for bf16 tensors an element past the
+    elementwise bound passes only if a and b are at most one bf16 ulp apart
+    (both are rounded results)."""
+    import torch
+
+    x = a.float().transpose(0, 1).reshape(a.shape[1], -1)
+    y = b.float().transpose(0, 1).reshape(b.shape[1], -1)
+    diff = x - y
+    ny = torch.linalg.vector_norm(y, dim=1)
+    rel = torch.linalg.vector_norm(diff, dim=1) / ny
+    rms = ny / (y.shape[1] ** 0.5)
+    assert bool(torch.all(rel <= rel_tol)), f"{what}: max relative L2 {rel.max().item():.3e}"
+    over = diff.abs() > elem_tol * rms[:, None]
+    n_over = int(over.sum().item())
+    if n_over:
+        assert bf16, f"{what}: {n_over} elements over {elem_tol} * rms"
+        mag = torch.maximum(x.abs(), y.abs())
+        ulp = torch.exp2(torch.floor(torch.log2(mag.clamp_min(1e-30))) - 7)
+        bad = over & (diff.abs() > ulp)
+        assert not bool(bad.any()), f"{what}: {int(bad.sum().item())} elements over the bound"
+    return {"max_rel_l2": float(rel.max().item()), "format_explained": n_over}
