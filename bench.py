@@ -349,15 +349,16 @@ def bench_backward(dev, reps=10, name="n8k"):
             "algorithmic_bytes": by}
 
 
-SEG_H, SEG_N, SEG_LEN = 8, 1 << 20, 1 << 16
+SEG_H, SEG_N, SEG_LEN = 8, 1 << 20, 1 << 15
 
 
 def bench_segmented(dev, reps=3):
     """Low-parallelism case: B=1, H=8, N=1,048,576, d=128 (one GPU's share
-    of 64 heads split over 8 GPUs by head).  la_prefill has only 8 x 4 = 32
-    chains; la_prefill_segmented cuts the sequence into 16 segments of 65,536
-    tokens (512 chains) and reads K and V a second time for the segment
-    states."""
+    of 64 heads split over 8 GPUs by head).  la_prefill has only 8 (sequence,
+    head) chains (32 workgroups); la_prefill_segmented cuts the sequence into
+    32 segments of 32,768 tokens, 256 (segment, head) chains -- enough for the
+    one-workgroup-per-chain kernel -- and reads K and V a second time for the
+    segment states."""
     import torch
 
     import linear_attention_la_amd as la

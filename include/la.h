@@ -130,6 +130,9 @@ la_status la_prefill(const void* q, const void* k, const void* v,
  *   segment_len      tokens per segment, a positive multiple of 64; the last
  *                    segment of a sequence may be shorter.  A sequence of L
  *                    tokens gives max(1, ceil(L / segment_len)) segments.
+ *                    With d = 128, a length that makes segments x heads at
+ *                    least the device's compute-unit count runs both passes
+ *                    one workgroup per (segment, head) (see la_prefill).
  *   workspace        device scratch of at least the size that
  *                    la_prefill_segmented_workspace_size reports for the same
  *                    num_seqs, cu_seqlens_host, num_heads, head_dim and
