@@ -73,10 +73,21 @@ __device__ __forceinline__ int v_off(int j, int col) {
 }
 
 // Element offset of state^T row c (a value column), key rows 8q .. 8q+7.
+// The chunk swizzle keeps both access patterns free of bank conflicts: the
+// writer's 8 consecutive lanes take c = 16 tc + 0..7 and the reader's 16
+// lanes take c = sv_col(tc, 0..15) (bits 0, 1, 3, 4 of c vary, bit 2 fixed).
 template <int D>
 __device__ __forceinline__ int s_off(int c, int q) {
-  return c * D + 8 * (q ^ (c & (D / 8 - 1)));
+  const int key = (c & 3) | ((((c >> 2) ^ (c >> 3)) & 1) << 2) | (((c >> 4) & 1) << 3);
+  // d = 64: two 128 B rows share a bank line, so row parity (bit 0) already
+  // separates them and the key drops it
+  return c * D + 8 * (q ^ (D == 128 ? key : key >> 1));
 }
+
+// Value column of row r of the strip waves' column tile tc: tile tc takes
+// columns 8 (r / 4) + 4 tc + r % 4, so the two tiles' results in one lane
+// are 8 consecutive columns (one 16 B store of bf16).
+__device__ __forceinline__ int sv_col(int tc, int r) { return 8 * (r >> 2) + 4 * tc + (r & 3); }
 
 // State row tiles [begin, end) owned by state wave k: the pair (2k, 2k+1).
 // d = 128: 8 tiles, 2 per state wave.  d = 64: 4 tiles on state waves 0 and
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        const int so = s_off<D>(16 * tc + li, 4 * kk + g);
+        const int so = s_off<D>(sv_col(tc, li), 4 * kk + g);
         oe[tc] = mfma(ld8(&Sh[cur][so]), qb[kk], oe[tc]);
         oe[tc] = mfma(ld8(&Sl[cur][so]), qb[kk], oe[tc]);
       }
@@ -329,8 +340,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       const bf16x8 p_l = cat2(pl[2 * kk2], pl[2 * kk2 + 1]);
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        const bf16x8 va = cat(ld_tr(&Vc[v_off(j0, 16 * tc + 4 * tr_a)]),
-                              ld_tr(&Vc[v_off(j0 + 16, 16 * tc + 4 * tr_a)]));
+        const bf16x8 va = cat(ld_tr(&Vc[v_off(j0, 8 * tr_a + 4 * tc)]),
+                              ld_tr(&Vc[v_off(j0 + 16, 8 * tr_a + 4 * tc)]));
         oi[tc] = mfma(va, p_h, oi[tc]);
         oi[tc] = mfma(va, p_l, oi[tc]);
       }
@@ -338,23 +349,25 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     // rows past the end of the sequence fall outside the resource: dropped
     constexpr int ES = kOutF32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t ro = block_rsrc(a.o, b, ES);
-    const int orow = prow(16 * KS + li, block_len(b)) * row_stride + h * D + c0;
+    // lane (li, g) holds columns 8g .. 8g+7 of query row 16 KS + li
+    const int off = ES * (prow(16 * KS + li, block_len(b)) * row_stride + h * D + c0 + 8 * g);
+    float out[8];
 #pragma unroll
-    for (int tc = 0; tc < 2; ++tc) {
-      float out[4];
+    for (int tc = 0; tc < 2; ++tc)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) out[m] = fmaf(qdecay, oe[tc][m], oi[tc][m]);
-      const int off = ES * (orow + 16 * tc + 4 * g);
-      if constexpr (kOutF32) {
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__builtin_bit_cast(unsigned, out[0]),
-                                                     __builtin_bit_cast(unsigned, out[1]),
-                                                     __builtin_bit_cast(unsigned, out[2]),
-                                                     __builtin_bit_cast(unsigned, out[3])},
-                                               ro, off, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{cvt2(out[0], out[1]), cvt2(out[2], out[3])},
-                                              ro, off, 0, 0);
-      }
+      for (int m = 0; m < 4; ++m) out[4 * tc + m] = fmaf(qdecay, oe[tc][m], oi[tc][m]);
+    if constexpr (kOutF32) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__builtin_bit_cast(unsigned, out[4 * h2]),
+                                                     __builtin_bit_cast(unsigned, out[4 * h2 + 1]),
+                                                     __builtin_bit_cast(unsigned, out[4 * h2 + 2]),
+                                                     __builtin_bit_cast(unsigned, out[4 * h2 + 3])},
+                                               ro, off + 16 * h2, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{cvt2(out[0], out[1]), cvt2(out[2], out[3]), cvt2(out[4], out[5]), cvt2(out[6], out[7])},
+          ro, off, 0, 0);
     }
   };
 
