@@ -4,6 +4,7 @@
 // no device memory.
 
 #include <math.h>
+#include <algorithm>
 #include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
@@ -165,6 +166,24 @@ bool use_wide(int64_t chains, int32_t head_dim) {
   return head_dim == 128 && cus > 0 && chains >= cus;
 }
 
+// Longest sequences first: a grid with more chains than compute units runs
+// in waves of workgroups, and a long chain that starts in a late wave
+// stretches the launch.  Ties keep the index order; batches of one
+// sequence or more than kMaxOrder sequences keep the identity order.
+void set_order(la::PrefillArgs& a, const int32_t* cu_host, int32_t num_seqs) {
+  a.ordered = 0;
+  if (num_seqs < 2 || num_seqs > la::kMaxOrder) return;
+  std::vector<int> idx(num_seqs);
+  for (int i = 0; i < num_seqs; ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) {
+    return cu_host[x + 1] - cu_host[x] > cu_host[y + 1] - cu_host[y];
+  });
+  for (int i = 0; i < num_seqs; ++i) {
+    a.seq_order[i] = (uint16_t)idx[i];
+    if (idx[i] != i) a.ordered = 1;
+  }
+}
+
 la_status check_segment_len(int32_t segment_len) {
   if (segment_len <= 0 || segment_len % 64 != 0)
     return fail(LA_ERR_INVALID_ARG, "segment_len = %d is not a positive multiple of 64",
@@ -307,6 +326,7 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   const int cols = in_dtype == LA_BF16 ? la::kBf16Cols : la::kF32Cols;
   a.num_items = (int32_t)((int64_t)num_seqs * num_heads * (head_dim / cols));
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
+  set_order(a, cu_seqlens_host, num_seqs);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -525,6 +545,7 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     inv[h] = (float)(1.0 / (double)decay[h]);
     lam[h] = decay[h];
   }
+  set_order(a, cu_seqlens_host, num_seqs);
   // Each pass runs the wide kernel when there are enough chains to fill the
   // GPU, else the 32-column kernel.
   const bool wide = use_wide((int64_t)num_seqs * num_heads, head_dim);

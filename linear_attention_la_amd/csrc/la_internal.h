@@ -9,6 +9,10 @@
 
 namespace la {
 
+// Largest batch whose sequences the prefill dispatches in a chosen order
+// (the order travels in the kernel arguments, 2 bytes per sequence).
+constexpr int kMaxOrder = 512;
+
 // Arguments of one prefill launch.  log2_decay[h] = log2(lambda_h), computed
 // on the host in double precision and rounded to float; lambda = 1 gives
 // exactly 0, so every decay power of a no-decay head is exactly 1.
@@ -29,7 +33,17 @@ struct PrefillArgs {
   int32_t num_heads;
   int32_t num_items;          // S * H * (d / value-columns per workgroup)
   float log2_decay[LA_MAX_HEADS];
+  // Dispatch order of the sequences: with `ordered` set, the i-th sequence
+  // taken up by the grid is seq_order[i] (longest first, so the longest
+  // chains start in the first wave of workgroups); else sequence i.
+  int32_t ordered;
+  uint16_t seq_order[kMaxOrder];
 };
+
+// Sequence index of the idx-th sequence in dispatch order.
+__device__ __forceinline__ int seq_of(const PrefillArgs& a, int idx) {
+  return a.ordered ? (int)a.seq_order[idx] : idx;
+}
 
 struct DecodeArgs {
   const void* q;

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   const int cs = item % NDV;
   const int sh = item / NDV;
   const int h = sh % H;
-  const int s = sh / H;
+  const int s = seq_of(a, sh / H);
   const int c0 = cs * kDV;
   const int t = threadIdx.x;
   const int wid = uniform(t >> 6);

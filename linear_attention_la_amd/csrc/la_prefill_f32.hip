@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   const int cs = item % NDV;
   const int sh = item / NDV;
   const int h = sh % a.num_heads;
-  const int s = sh / a.num_heads;
+  const int s = seq_of(a, sh / a.num_heads);
   const int t = threadIdx.x;
   const int H = a.num_heads;
   const int c0 = cs * DV;

@@ -106,8 +106,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Pl[kStateOnly ? 8 : kBeta * kBeta];
 
   const int H = a.num_heads;
-  const int s = blockIdx.x / H;
-  const int h = blockIdx.x - s * H;
+  const int h = blockIdx.x % H;
+  const int s = seq_of(a, blockIdx.x / H);
   const int t = threadIdx.x;
   const int w = uniform(t >> 6);  // value-column tile of this wave
   const int c0 = 16 * w;

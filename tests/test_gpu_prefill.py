@@ -73,6 +73,27 @@ def test_bf16_ragged(dev, d, out_f32, kv_init):
     say("bf16 ragged", s1, s2)
 
 
+@pytest.mark.parametrize("nseq", [511, 512, 513, 700])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_many_sequences_dispatch_order(dev, nseq, dtype):
+    """Batches at and past the largest one dispatched longest-first (512
+    sequences; larger batches keep the index order): lengths 0..130 in a
+    shuffled order, so the longest-first order differs from the index
+    order, and every sequence and head against the oracle."""
+    rng = np.random.default_rng(600 + nseq)
+    lengths = rng.integers(0, 131, size=nseq)
+    lengths[:3] = (0, 1, 130)
+    rng.shuffle(lengths)
+    decay = np.array([1.0, 0.8], np.float32)
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    o, kv, o_ref, kv_ref = _run(dev, lengths.tolist(), 2, 64, dtype, decay, 31 + nseq,
+                                kv_init=True, out_f32=dtype == "fp32",
+                                beta=64 if dtype == "bf16" else 32)
+    s1 = parity.check(o, o_ref, 1, tol, out_bf16=dtype == "bf16", what=f"{nseq} seqs o")
+    s2 = parity.check(kv, kv_ref, 1, tol, what=f"{nseq} seqs kv")
+    say("many sequences", nseq, dtype, s1, s2)
+
+
 def test_bf16_n8k_all_heads(dev):
     """B=1, H=64, N=8192, d=128, bf16, seeded decay: every head checked."""
     w = workload("n8k")
