@@ -113,7 +113,10 @@ typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * columns over d / 32 workgroups.  Both give results within the same
  * tolerance, not bitwise equal to each other; a given call is deterministic.
  * A one-workgroup-per-pair launch occupies whole compute units, so work on
- * another stream gets fewer of them while it runs.
+ * another stream gets fewer of them while it runs.  Calls of 2 to 512
+ * sequences hand the sequences to the grid longest first (read from
+ * cu_seqlens_host), so that when the grid runs in several waves of
+ * workgroups the longest chains start in the first.
  */
 la_status la_prefill(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
