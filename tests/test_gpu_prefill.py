@@ -127,6 +127,22 @@ def test_exact_integer_inputs_bitwise(dev):
         assert np.array_equal(to_np(o16), rne_bf16(o_ref.astype(np.float32)).astype(np.float64))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_max_heads_extreme_decays(dev, d):
+    """LA_MAX_HEADS = 256 heads over three sequences (at d = 128 the 768
+    chains take the one-workgroup-per-chain kernel, at d = 64 the 32-column
+    kernel), with decays from 1 down to 1e-30, where lambda^2 already
+    underflows in fp32 and each row keeps only its diagonal term
+    (q_t . k_t) v_t."""
+    H = 256
+    decay = np.geomspace(1e-30, 1.0, H).astype(np.float32)
+    decay[:4] = (1.0, 1e-30, 0.5, 0.999999)
+    o, kv, o_ref, kv_ref = _run(dev, [130, 1, 64], H, d, "bf16", decay, 41 + d, kv_init=True)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="max heads o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="max heads kv")
+    say("max heads", d, s1, s2)
+
+
 def test_zero_length_sequences(dev):
     """All sequences empty: no rows, final state = initial state (or zero)."""
     import torch
