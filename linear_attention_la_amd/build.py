@@ -54,7 +54,10 @@ def build(verbose=False):
         if msgs.strip() and verbose:
             print(msgs, file=sys.stderr)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    # --no-undefined: a kernel whose host stub was not emitted (clang can drop
+    # it without a diagnostic) fails here instead of at load time.
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + \
+        [o for o, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
