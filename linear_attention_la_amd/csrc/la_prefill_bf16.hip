@@ -46,10 +46,12 @@
 // array is laid out so that every access pattern issued below is free of
 // bank conflicts:
 //   Ks      [2][64][d]    16 B chunk c of row r at chunk c ^ kswz(r)
-//   Vs, Vh, Vl [2][64][32] the value slice, and its lambda^(ell-1-j)-scaled
-//                         rows as hi/lo; chunk c of row j at c ^ ((j/2) % 4)
+//   Vs      [2][64][32]   the value slice; in rows j with bit 2 set the
+//                         8-byte halves of each 16-byte chunk are swapped
+//   Vh, Vl  [2][64][32]   its lambda^(ell-1-j)-scaled rows as hi/lo; chunk c
+//                         of row j at c ^ ((j/2) % 4)
 //   Sh, Sl  [2][32][d]    state^T hi/lo for the Q S product; chunk q of
-//                         row c at q ^ (c % (d/8))
+//                         row c at q ^ key(c) (s_off)
 // MFMA operand layout (16x16x32 bf16): lane l supplies row (l % 16) of A and
 // column (l % 16) of B, 8 k-values per lane in lane group g = l / 16; the 4
 // results of lane l sit at rows 4g + m, column l % 16.  The order of the 8
@@ -70,6 +72,15 @@ constexpr int kDV = kBf16Cols;  // 32 value columns per workgroup
 // Element offset of (row j, column col) of a value-slice array (64 B rows).
 __device__ __forceinline__ int v_off(int j, int col) {
   return j * kDV + 8 * ((col >> 3) ^ ((j >> 1) & 3)) + (col & 7);
+}
+
+// Layout of the plain value slice Vs, which only the strip waves read: in
+// rows with bit 2 set the two 8-byte halves of every 16-byte chunk trade
+// places, so that the transposed reads of the interleaved column tiles
+// (8 lanes of a row group take the 4 chunks of one half, lanes of row j and
+// j + 4 arrive together) fall on distinct banks.
+__device__ __forceinline__ int vs_off(int j, int col) {
+  return j * kDV + 8 * (col >> 3) + 4 * (((col >> 2) & 1) ^ ((j >> 2) & 1)) + (col & 3);
 }
 
 // Element offset of state^T row c (a value column), key rows 8q .. 8q+7.
@@ -272,7 +283,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
   auto store_v = [&](const VStage& r, int buf, int b) {
     const int ell = block_len(b);
     const int o = v_off(vrow, 8 * vch);
-    *reinterpret_cast<uint4*>(&Vs[buf][o]) = r.v;
+    *reinterpret_cast<uint4*>(&Vs[buf][vrow * kDV + 8 * vch]) =
+        vrow & 4 ? make_uint4(r.v.z, r.v.w, r.v.x, r.v.y) : r.v;  // vs_off layout
     // value row scaled by lambda^(ell-1-j), split hi/lo
     const float wv = vrow < ell ? exp2f((float)(ell - 1 - vrow) * l2) : 0.0f;
     const uint32_t wd[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
@@ -340,8 +352,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
       const bf16x8 p_l = cat2(pl[2 * kk2], pl[2 * kk2 + 1]);
 #pragma unroll
       for (int tc = 0; tc < 2; ++tc) {
-        const bf16x8 va = cat(ld_tr(&Vc[v_off(j0, 8 * tr_a + 4 * tc)]),
-                              ld_tr(&Vc[v_off(j0 + 16, 8 * tr_a + 4 * tc)]));
+        const bf16x8 va = cat(ld_tr(&Vc[vs_off(j0, 8 * tr_a + 4 * tc)]),
+                              ld_tr(&Vc[vs_off(j0 + 16, 8 * tr_a + 4 * tc)]));
         oi[tc] = mfma(va, p_h, oi[tc]);
         oi[tc] = mfma(va, p_l, oi[tc]);
       }
