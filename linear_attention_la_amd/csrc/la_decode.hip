@@ -55,14 +55,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __shared__ float qs[D], ks[D];
   __shared__ floatx4 red[RP][CQ];
 
-  const int bh = blockIdx.x;
-  const int h = bh % a.num_heads;
-  const int b = bh / a.num_heads;
+  const int h = blockIdx.x % a.num_heads;
+  const int b = (int)((int64_t)(blockIdx.x / a.num_heads) * a.b_step % a.batch);
   const int64_t slot = a.slots ? a.slots[b] : b;  // validated on the host
   const int t = threadIdx.x;
   const int cq = t % CQ;
   const int rp = t / CQ;
-  const int64_t vec_off = (int64_t)bh * D;
+  const int64_t vec_off = ((int64_t)b * a.num_heads + h) * D;
   const InT* __restrict__ q = static_cast<const InT*>(a.q);
   const InT* __restrict__ k = static_cast<const InT*>(a.k);
   const InT* __restrict__ v = static_cast<const InT*>(a.v);

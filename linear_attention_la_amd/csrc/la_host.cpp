@@ -184,6 +184,22 @@ void set_order(la::PrefillArgs& a, const int32_t* cu_host, int32_t num_seqs) {
   }
 }
 
+// Stride for the decode's walk through the batch: about 0.618 * batch, made
+// coprime to it so that i -> (i * step) % batch is a permutation.  Walking
+// the states in this scattered order, rather than in index order, avoids
+// the slow cases of streaming neighbouring states at once (median decode of
+// 256 x 64 states: 362-365 us scattered vs 389-392 us in order).
+int32_t batch_stride(int32_t batch) {
+  if (batch < 3) return 1;
+  int64_t step = (int64_t)((double)batch * 0.6180339887498949);
+  auto gcd = [](int64_t x, int64_t y) {
+    while (y) { const int64_t t = x % y; x = y; y = t; }
+    return x;
+  };
+  while (gcd(step, batch) != 1) ++step;
+  return (int32_t)step;
+}
+
 la_status check_segment_len(int32_t segment_len) {
   if (segment_len <= 0 || segment_len % 64 != 0)
     return fail(LA_ERR_INVALID_ARG, "segment_len = %d is not a positive multiple of 64",
@@ -280,6 +296,7 @@ la_status decode_common(const void* q, const void* k, const void* v, float* kv,
   a.o = o;
   a.batch = batch;
   a.num_heads = num_heads;
+  a.b_step = batch_stride(batch);
   for (int32_t h = 0; h < num_heads; ++h) a.decay[h] = decay[h];
   hipError_t e = la::launch_decode(a, head_dim, in_dtype, static_cast<hipStream_t>(stream));
   return hip_status(e, "la_decode launch");

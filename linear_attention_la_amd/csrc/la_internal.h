@@ -55,6 +55,10 @@ struct DecodeArgs {
   void* o;
   int32_t batch;
   int32_t num_heads;
+  // Workgroup i handles sequence (i / H * b_step) % batch (b_step coprime to
+  // batch; 1 = in order): a stride through the batch spreads the states that
+  // are streamed at the same time over memory.
+  int32_t b_step;
   float decay[LA_MAX_HEADS];
 };
 
