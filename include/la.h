@@ -126,6 +126,39 @@ la_status la_prefill(const void* q, const void* k, const void* v,
                      void* stream);
 
 /*
+ * la_prefill_pool -- la_prefill whose states live in a state pool: sequence
+ * s starts from kv_pool[slots[s]] and its final state is written back to the
+ * same slot.  A server keeps the states of all live sequences in one pool,
+ * prefills new chunks of any of them (continuing from the pooled state) and
+ * decodes them with la_decode_pool, with no copy between the two (the
+ * serving engine's length > 1 path beside its length-1 path, jvyan.cn
+ * 二、计算优化; CSDN §3.2).
+ *
+ *   kv_pool      device fp32 [pool_size, H, d, d], read and written in place;
+ *                entries no slot names are not touched.  A sequence that
+ *                starts from scratch needs its slot zeroed first.
+ *   pool_size    number of states in the pool (>= 0).
+ *   slots_dev    device int32 [S]: pool index of sequence s.
+ *   slots_host   host int32 [S], same contents; validated before any launch:
+ *                every slot in [0, pool_size) and no slot twice.
+ *   q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+ *   num_heads, head_dim, out_dtype, decay, o, stream: as in la_prefill;
+ *                in_dtype must be LA_BF16; o must not overlap the pool and
+ *                the pool must not overlap q, k or v.
+ *
+ * A zero-length sequence leaves its slot unchanged.  Errors as la_prefill,
+ * plus LA_ERR_INVALID_ARG for a NULL pool or slot array, a slot out of range
+ * or a repeated slot, and LA_ERR_UNSUPPORTED for fp32 inputs.
+ */
+la_status la_prefill_pool(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                          int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                          int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                          const float* decay, float* kv_pool, int32_t pool_size,
+                          const int32_t* slots_dev, const int32_t* slots_host, void* o,
+                          void* stream);
+
+/*
  * la_prefill_segmented -- la_prefill with every sequence cut into segments of
  * segment_len tokens that run as parallel chains; same results (up to the
  * order of fp32 sums) and the same arguments, plus:

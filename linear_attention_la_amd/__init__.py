@@ -10,6 +10,7 @@ library is missing, every call raises.
     dq, dk, dv, dkv0 = prefill_backward(q, k, v, do, cu_seqlens, decay, kv_init, dkv_final)
     o = decode(q, k, v, kv, decay)          # kv updated in place
     o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
+    o = prefill_pool(q, k, v, cu_seqlens, decay, pool, slots)   # continues from pool[slots]
 """
 
 from ._binding import (  # noqa: F401
@@ -30,6 +31,7 @@ from ._binding import (  # noqa: F401
     la_prefill_backward_workspace_size,
     la_decode,
     la_decode_pool,
+    la_prefill_pool,
     la_status_str,
     la_last_error,
     prefill,
@@ -38,4 +40,5 @@ from ._binding import (  # noqa: F401
     prefill_backward,
     decode,
     decode_pool,
+    prefill_pool,
 )

@@ -53,6 +53,9 @@ def lib():
     L.la_prefill.restype = ctypes.c_int
     L.la_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int, ctypes.c_int,
                              vp, vp, vp, vp, vp]
+    L.la_prefill_pool.restype = ctypes.c_int
+    L.la_prefill_pool.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
+                                  ctypes.c_int, vp, vp, i32, vp, vp, vp, vp]
     L.la_prefill_segmented.restype = ctypes.c_int
     L.la_prefill_segmented.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
                                        ctypes.c_int, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
@@ -104,6 +107,14 @@ def la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, he
     st = lib().la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
                                                    segment_len, ctypes.byref(n))
     return st, n.value
+
+
+def la_prefill_pool(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens, num_heads,
+                    head_dim, in_dtype, out_dtype, decay, kv_pool, pool_size, slots_dev,
+                    slots_host, o, stream):
+    return lib().la_prefill_pool(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                 total_tokens, num_heads, head_dim, in_dtype, out_dtype, decay,
+                                 kv_pool, pool_size, slots_dev, slots_host, o, stream)
 
 
 def la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream):
@@ -294,6 +305,55 @@ def prefill_segmented(q, k, v, cu_seqlens, decay, segment_len, kv_init=None, out
     return m.out, m.kv_final
 
 
+def _marshal_slots(slots, slots_host, n, dev, stream):
+    """Pool slots as (device int32 tensor, host int32 array) of shape [n]."""
+    torch = _torch()
+    if slots_host is not None:
+        sl_host = np.ascontiguousarray(
+            slots_host.cpu().numpy() if isinstance(slots_host, torch.Tensor) else slots_host,
+            dtype=np.int32)
+        if not (isinstance(slots, torch.Tensor) and slots.is_cuda and slots.dtype == torch.int32
+                and slots.is_contiguous()):
+            raise ValueError("slots_host needs slots as a contiguous int32 device tensor")
+        sl_dev = slots
+    elif isinstance(slots, torch.Tensor):
+        sl_host = slots.detach().to("cpu", torch.int32).contiguous().numpy()
+        sl_dev = slots if (slots.is_cuda and slots.dtype == torch.int32
+                           and slots.is_contiguous()) else torch.from_numpy(sl_host).to(dev)
+    else:
+        sl_host = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+        sl_dev = torch.from_numpy(sl_host).to(dev)
+    if stream is not None and sl_dev is not slots:
+        sl_dev.record_stream(stream)  # temporary read by a kernel on another stream
+    if sl_host.shape != (n,):
+        raise ValueError(f"slots has shape {sl_host.shape}, expected ({n},)")
+    return sl_dev, sl_host
+
+
+def prefill_pool(q, k, v, cu_seqlens, decay, kv_pool, slots, out_dtype=None, stream=None,
+                 out=None, cu_seqlens_host=None, slots_host=None):
+    """Packed varlen prefill on a state pool: sequence s continues from
+    kv_pool[slots[s]] and writes its final state back to that slot (in
+    place).  q, k, v: device bf16 [T, H, d]; kv_pool: device fp32
+    [P, H, d, d]; slots: [S] int (host or device), distinct, in [0, P).
+    Passing host copies (``cu_seqlens_host``, ``slots_host``) with device
+    int32 ``cu_seqlens`` and ``slots`` avoids device-to-host copies.
+    Returns o [T, H, d]."""
+    torch = _torch()
+    m = _marshal_prefill(q, k, v, cu_seqlens, decay, None, out_dtype, stream, False, out, None,
+                         cu_seqlens_host)
+    if (not isinstance(kv_pool, torch.Tensor) or not kv_pool.is_cuda
+            or kv_pool.dtype != torch.float32 or not kv_pool.is_contiguous()
+            or kv_pool.dim() != 4 or tuple(kv_pool.shape[1:]) != (m.H, m.d, m.d)):
+        raise ValueError("kv_pool must be a contiguous fp32 device tensor [P, H, d, d]")
+    sl_dev, sl_host = _marshal_slots(slots, slots_host, m.S, m.dev, stream)
+    _check(la_prefill_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.cu_dev.data_ptr(),
+                           m.cu_host.data_ptr(), m.S, m.T, m.H, m.d, m.in_code, m.out_code,
+                           m.dec.ctypes.data, kv_pool.data_ptr(), kv_pool.shape[0],
+                           sl_dev.data_ptr(), sl_host.ctypes.data, m.out.data_ptr(), m.stream))
+    return m.out
+
+
 def decode(q, k, v, kv, decay, stream=None, out=None):
     """One decode token per sequence.  q, k, v: device [B, H, d]; kv: device
     fp32 [B, H, d, d], updated in place.  Returns o [B, H, d] (q's dtype)."""
@@ -333,25 +393,7 @@ def decode_pool(q, k, v, kv_pool, slots, decay, stream=None, out=None, slots_hos
         raise ValueError("kv_pool must be a contiguous fp32 device tensor [P, H, d, d]")
     P = kv_pool.shape[0]
     dev = q.device
-    if slots_host is not None:
-        sl_host = np.ascontiguousarray(
-            slots_host.cpu().numpy() if isinstance(slots_host, torch.Tensor) else slots_host,
-            dtype=np.int32)
-        if not (isinstance(slots, torch.Tensor) and slots.is_cuda and slots.dtype == torch.int32
-                and slots.is_contiguous()):
-            raise ValueError("slots_host needs slots as a contiguous int32 device tensor")
-        sl_dev = slots
-    elif isinstance(slots, torch.Tensor):
-        sl_host = slots.detach().to("cpu", torch.int32).contiguous().numpy()
-        sl_dev = slots if (slots.is_cuda and slots.dtype == torch.int32
-                           and slots.is_contiguous()) else torch.from_numpy(sl_host).to(dev)
-    else:
-        sl_host = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
-        sl_dev = torch.from_numpy(sl_host).to(dev)
-    if stream is not None and sl_dev is not slots:
-        sl_dev.record_stream(stream)
-    if sl_host.shape != (B,):
-        raise ValueError(f"slots has shape {sl_host.shape}, expected ({B},)")
+    sl_dev, sl_host = _marshal_slots(slots, slots_host, B, dev, stream)
     dec = _host_decay(decay, H)
     if out is None:
         out = torch.empty_like(q)

@@ -358,6 +358,68 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   return hip_status(e, "la_prefill launch");
 }
 
+la_status la_prefill_pool(const void* q, const void* k, const void* v,
+                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                          int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                          int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                          const float* decay, float* kv_pool, int32_t pool_size,
+                          const int32_t* slots_dev, const int32_t* slots_host, void* o,
+                          void* stream) {
+  if (in_dtype != LA_BF16 && valid_dtype(in_dtype))
+    return fail(LA_ERR_UNSUPPORTED, "the pool prefill takes bf16 inputs only");
+  if (pool_size < 0) return fail(LA_ERR_INVALID_ARG, "pool_size = %d < 0", pool_size);
+  // the pool stands in for kv_init / kv_final; its own checks follow
+  la_status st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                               num_heads, head_dim, in_dtype, out_dtype, decay, nullptr, o,
+                               nullptr, num_seqs);
+  if (st != LA_OK || num_seqs == 0) return st;
+  if (!kv_pool) return fail(LA_ERR_INVALID_ARG, "kv_pool is NULL");
+  if (!aligned16(kv_pool)) return fail(LA_ERR_INVALID_ARG, "kv_pool is not 16-byte aligned");
+  if (!slots_dev || !slots_host)
+    return fail(LA_ERR_INVALID_ARG, "slots_dev and slots_host must be non-NULL");
+  // every slot in range and used once (two sequences on one state would race)
+  std::vector<uint8_t> used((size_t)pool_size, 0);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t x = slots_host[s];
+    if (x < 0 || x >= pool_size)
+      return fail(LA_ERR_INVALID_ARG, "slots[%d] = %d is outside [0, %d)", s, x, pool_size);
+    if (used[(size_t)x]) return fail(LA_ERR_INVALID_ARG, "slot %d is used twice", x);
+    used[(size_t)x] = 1;
+  }
+  const size_t tok = (size_t)total_tokens * num_heads * head_dim;
+  const Range rp = range("kv_pool", kv_pool, (size_t)pool_size * num_heads * head_dim * head_dim * 4);
+  const Range others[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
+                          range("o", o, tok * dtype_size(out_dtype))};
+  for (const Range& r : others)
+    if (overlap(rp, r)) return fail(LA_ERR_INVALID_ARG, "kv_pool overlaps %s", r.name);
+
+  la::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seqlens_dev;
+  a.kv_init = kv_pool;
+  a.kv_final = kv_pool;
+  a.init_slot = slots_dev;
+  a.final_slot = slots_dev;
+  a.o = o;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_items = (int32_t)((int64_t)num_seqs * num_heads * (head_dim / la::kBf16Cols));
+  for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
+  set_order(a, cu_seqlens_host, num_seqs);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (use_wide((int64_t)num_seqs * num_heads, head_dim)) {
+    a.num_items = num_seqs * num_heads;
+    e = la::launch_prefill_wide(a, out_dtype, false, false, s);
+  } else {
+    e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
+  }
+  return hip_status(e, "la_prefill_pool launch");
+}
+
 la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
                                               int32_t num_heads, int32_t head_dim,
                                               int32_t segment_len, size_t* bytes) {

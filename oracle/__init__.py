@@ -37,6 +37,7 @@ from .lightning import (  # noqa: F401
     blockwise,
     decode_step,
     prefill_varlen,
+    prefill_pool,
     decode_batch,
     decode_pool,
     backward_quadratic,

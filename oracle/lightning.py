@@ -238,6 +238,38 @@ def prefill_varlen(q, k, v, cu_seqlens, decay, kv_init=None, form="blockwise",
     return o, kv
 
 
+def prefill_pool(q, k, v, cu_seqlens, decay, pool, slots, beta=64, heads=None):
+    """Packed variable-length prefill on a pool of states: sequence s starts
+    from ``pool[slots[s]]`` and its final state replaces that entry (a
+    serving engine keeps every live sequence's state in one pool, prefills
+    new chunks from it and decodes from it, [JVY] 二、计算优化).
+
+    q, k, v [T, H, d]; pool [P, H, d_k, d_v]; slots [S] distinct indices
+    into the pool, one per sequence of ``cu_seqlens``.  Each (sequence,
+    head) runs the blockwise chain from its pooled state.  Returns
+    (o [T, H, d_v], pool_new [P, H, d_k, d_v]); entries that no slot names
+    are copied unchanged and the input pool is not modified.
+    """
+    slots = [int(x) for x in np.asarray(slots).reshape(-1).tolist()]
+    cu = [int(x) for x in np.asarray(cu_seqlens).tolist()]
+    if len(slots) != len(cu) - 1:
+        raise ValueError("one slot per sequence")
+    if len(set(slots)) != len(slots):
+        raise ValueError("a slot is used twice")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    decay = _f64(decay)
+    heads = range(H) if heads is None else heads
+    pool_new = _f64(pool).copy()
+    o = np.zeros((T, H, dv))
+    for s, sl in enumerate(slots):
+        a, b = cu[s], cu[s + 1]
+        for h in heads:
+            o[a:b, h, :], pool_new[sl, h] = blockwise(q[a:b, h, :], k[a:b, h, :], v[a:b, h, :],
+                                                      decay[h], beta, _f64(pool[sl, h]))
+    return o, pool_new
+
+
 def decode_batch(q, k, v, kv, decay, heads=None):
     """Decode step for a batch: q, k, v [B, H, d], kv [B, H, d, d].
 

@@ -261,6 +261,23 @@ def pin_decode_pool(orc):
     _close(pool.reshape(-1), np.array([2.0, 3.0, 5.0]), 0.0, "input pool unchanged")
 
 
+def pin_prefill_pool(orc):
+    """Pool prefill, worked by hand with d = 1 and lambda = 1/2 (exact in
+    binary): pool [2, 3, 5]; sequence 0 (two tokens) on slot 2, sequence 1
+    (one token) on slot 0; q [1, 2 | 1], k [3, 1 | 4], v [1/2, 2 | 1].  Sequence 0 from S = 5: S = 5/2 + 3/2 = 4, o = 4; then
+    S = 2 + 2 = 4, o = 8.  Sequence 1 from S = 2: S = 1 + 4 = 5, o = 5.
+    Slot 1 is untouched: pool becomes [5, 3, 4]; every block size agrees."""
+    pool = np.array([2.0, 3.0, 5.0]).reshape(3, 1, 1, 1)
+    q = np.array([1.0, 2.0, 1.0]).reshape(3, 1, 1)
+    k = np.array([3.0, 1.0, 4.0]).reshape(3, 1, 1)
+    v = np.array([0.5, 2.0, 1.0]).reshape(3, 1, 1)
+    for beta in (1, 2, 64):
+        o, pool_new = orc.prefill_pool(q, k, v, [0, 2, 3], np.array([0.5]), pool, [2, 0], beta=beta)
+        _close(o.reshape(-1), np.array([4.0, 8.0, 5.0]), 0.0, f"pool prefill o beta={beta}")
+        _close(pool_new.reshape(-1), np.array([5.0, 3.0, 4.0]), 0.0, "pool prefill states")
+    _close(pool.reshape(-1), np.array([2.0, 3.0, 5.0]), 0.0, "input pool unchanged")
+
+
 def pin_backward_autograd(orc):
     """Backward against automatic differentiation: torch (float64, CPU)
     differentiates a token-by-token forward, S_t = lam S_(t-1) + k_t^T v_t,
@@ -324,4 +341,4 @@ def pin_backward_finite_difference(orc):
 
 ALL_PINS = [pin_golden, pin_exact_rational, pin_lfilter, pin_nodecay_library, pin_geometric,
             pin_three_way, pin_continuation, pin_decode_consistency, pin_packing, pin_decode_pool,
-            pin_backward_autograd, pin_backward_finite_difference]
+            pin_prefill_pool, pin_backward_autograd, pin_backward_finite_difference]

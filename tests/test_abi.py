@@ -29,7 +29,8 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
               "la_prefill_backward", "la_prefill_backward_workspace_size",
-              "la_decode", "la_decode_pool", "la_status_str", "la_last_error"):
+              "la_prefill_pool", "la_decode", "la_decode_pool", "la_status_str",
+              "la_last_error"):
         assert n in names
 
 
@@ -284,6 +285,54 @@ def test_decode_pool_rejects(name, kw, code):
 
 def test_decode_pool_zero_batch_is_noop():
     st, msg = _pool(B=0, slots=None, slots_dev=None, q=None, k=None, v=None, o=None)
+    assert st == la.LA_OK, msg
+
+
+def _prefill_pool(**kw):
+    args = dict(q=Q, k=K, v=V, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2, T=T,
+                H=H, d=D, in_dt=la.LA_BF16, out_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), pool=POOL, P=10,
+                slots=np.array([7, 2], np.int32), slots_dev=KVI, o=O)
+    args.update(kw)
+    cu, sl, dec = args["cu_host"], args["slots"], args["decay"]
+    st = la.la_prefill_pool(args["q"], args["k"], args["v"], args["cu_dev"],
+                            None if cu is None else cu.ctypes.data, args["S"], args["T"],
+                            args["H"], args["d"], args["in_dt"], args["out_dt"],
+                            None if dec is None else dec.ctypes.data, args["pool"], args["P"],
+                            args["slots_dev"], None if sl is None else sl.ctypes.data, args["o"],
+                            None)
+    return st, la.la_last_error()
+
+
+BAD_PREFILL_POOL = [
+    ("slot_out_of_range", dict(slots=np.array([7, 10], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("slot_negative", dict(slots=np.array([-1, 2], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("slot_repeated", dict(slots=np.array([2, 2], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("slots_host_null", dict(slots=None), la.LA_ERR_INVALID_ARG),
+    ("slots_dev_null", dict(slots_dev=None), la.LA_ERR_INVALID_ARG),
+    ("pool_null", dict(pool=None), la.LA_ERR_INVALID_ARG),
+    ("pool_misaligned", dict(pool=POOL + 4), la.LA_ERR_INVALID_ARG),
+    ("pool_size_negative", dict(P=-1), la.LA_ERR_INVALID_ARG),
+    ("pool_empty", dict(P=0), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_pool", dict(o=POOL + 10 * 4 * 128 * 128 * 4 - 64), la.LA_ERR_INVALID_ARG),
+    ("pool_overlaps_k", dict(pool=K - 64), la.LA_ERR_INVALID_ARG),
+    ("fp32_inputs", dict(in_dt=la.LA_FP32, out_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
+    ("decay_null", dict(decay=None), la.LA_ERR_INVALID_ARG),
+    ("cu_last_mismatch", dict(cu_host=np.array([0, 40, 99], np.int32)), la.LA_ERR_INVALID_ARG),
+    ("head_dim_96", dict(d=96), la.LA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_PREFILL_POOL, ids=[b[0] for b in BAD_PREFILL_POOL])
+def test_prefill_pool_rejects(name, kw, code):
+    st, msg = _prefill_pool(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_prefill_pool_zero_sequences_is_noop():
+    st, msg = _prefill_pool(S=0, T=0, cu_host=np.array([0], np.int32), slots=None,
+                            slots_dev=None, q=None, k=None, v=None, o=None, pool=None)
     assert st == la.LA_OK, msg
 
 

@@ -47,6 +47,10 @@ MUTATIONS = {
                             "s0 = None\n            qs, ks"),
     "pool_writes_batch_index": ("o[b, h], pool_new[sl, h] = decode_step(", "o[b, h], pool_new[b, h] = decode_step("),
     "pool_reads_batch_index": ("v[b, h], pool[sl, h],", "v[b, h], pool[b, h],"),
+    "prefill_pool_writes_seq_index": ("o[a:b, h, :], pool_new[sl, h] = blockwise(",
+                                      "o[a:b, h, :], pool_new[s, h] = blockwise("),
+    "prefill_pool_reads_seq_index": ("decay[h], beta, _f64(pool[sl, h]))",
+                                     "decay[h], beta, _f64(pool[s, h]))"),
     "bwd_quad_dk_untransposed": ("    dk = a.T @ q\n", "    dk = a @ q\n"),
     "bwd_quad_dv_wrong_scores": ("    dv = b.T @ do\n", "    dv = a.T @ do\n"),
     "bwd_quad_ds0_exponent": ("    ds0 = (q * (lam ** (t + 1))[:, None]).T @ do",
