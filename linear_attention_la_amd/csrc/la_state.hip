@@ -18,9 +18,12 @@ struct StateArgs {
   float scale[LA_MAX_HEADS];
 };
 
-// Workgroup (state, tile row, tile column), 32 x 8 threads; each thread
-// moves 4 elements of a 32 x 32 tile.  The transposed path goes through a
-// padded LDS tile so that reads and writes stay row-contiguous.
+// Workgroup (state, tile row, tile column), 256 threads, one 32 x 32 tile:
+// thread t moves the 4 consecutive elements (4 (t % 8) .. + 3) of tile row
+// t / 8 with one 16-byte load and one 16-byte store.  The transposed path
+// goes through a padded LDS tile: a thread writes its input quad into 4 LDS
+// rows (one per column) and reads back 4 consecutive elements of one output
+// row.
 template <bool kTranspose>
 __global__ __launch_bounds__(256) void state_transform_kernel(StateArgs a, int d) {
   __shared__ float tile[kTile][kTile + 1];
@@ -31,23 +34,24 @@ __global__ __launch_bounds__(256) void state_transform_kernel(StateArgs a, int d
   const int h = sh % a.num_heads;
   const int64_t base = (int64_t)sh * d * d;
   const float f = a.scale[h];
-  const int x = threadIdx.x % kTile, y = threadIdx.x / kTile;  // y in [0, 8)
+  const int row = threadIdx.x / 8, q4 = 4 * (threadIdx.x % 8);  // row in [0, 32), quad start
+  const float4 x =
+      *reinterpret_cast<const float4*>(a.in + base + (int64_t)(tr * kTile + row) * d + tc * kTile + q4);
   if (!kTranspose) {
-#pragma unroll
-    for (int i = 0; i < kTile; i += 8) {
-      const int64_t idx = base + (int64_t)(tr * kTile + y + i) * d + tc * kTile + x;
-      a.out[idx] = f * a.in[idx];
-    }
+    *reinterpret_cast<float4*>(a.out + base + (int64_t)(tr * kTile + row) * d + tc * kTile + q4) =
+        make_float4(f * x.x, f * x.y, f * x.z, f * x.w);
     return;
   }
-#pragma unroll
-  for (int i = 0; i < kTile; i += 8)
-    tile[y + i][x] = a.in[base + (int64_t)(tr * kTile + y + i) * d + tc * kTile + x];
+  tile[q4][row] = x.x;
+  tile[q4 + 1][row] = x.y;
+  tile[q4 + 2][row] = x.z;
+  tile[q4 + 3][row] = x.w;
   __syncthreads();
-  // out[c][r] = in[r][c]: tile (tr, tc) of the input lands at tile (tc, tr)
-#pragma unroll
-  for (int i = 0; i < kTile; i += 8)
-    a.out[base + (int64_t)(tc * kTile + y + i) * d + tr * kTile + x] = f * tile[x][y + i];
+  // out[c][r] = in[r][c]: tile (tr, tc) of the input lands at tile (tc, tr);
+  // LDS row c of the tile now holds input column c
+  *reinterpret_cast<float4*>(a.out + base + (int64_t)(tc * kTile + row) * d + tr * kTile + q4) =
+      make_float4(f * tile[row][q4], f * tile[row][q4 + 1], f * tile[row][q4 + 2],
+                  f * tile[row][q4 + 3]);
 }
 
 }  // namespace
