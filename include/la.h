@@ -239,11 +239,16 @@ la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* c
  *                    (written), or NULL to skip.
  *   workspace        device scratch of la_prefill_backward_workspace_size
  *                    bytes, needed when kv_init or dkv_final is given (may be
- *                    NULL otherwise); 16-byte aligned.
+ *                    NULL otherwise); 16-byte aligned.  Only d = 64 writes
+ *                    it; the size contract is the same for both d.
  *
  * The outputs and the workspace may overlap nothing else.  Errors as
- * la_prefill.  Up to seven kernels are enqueued on `stream`; nothing
- * synchronises.  The three chains choose their kernel as la_prefill does.
+ * la_prefill.  Nothing synchronises.  d = 128: one kernel is enqueued on
+ * `stream`, running the three chains side by side (one workgroup per
+ * (chain, sequence, head)) and reading kv_init and dkv_final directly.
+ * d = 64: up to seven kernels -- the three chains one after the other, each
+ * on the kernel la_prefill would choose, with the states transposed and
+ * scaled into the workspace between them.
  */
 la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,

@@ -1,0 +1,35 @@
+// The backward pass as three runs of the one-workgroup-per-chain prefill
+// kernel in one launch (d = 128).  Internal, not part of the public ABI.
+#pragma once
+
+#include "la_internal.h"
+
+namespace la {
+
+// One of the three chains: queries, keys and values of the forward kernel,
+// the gradient it writes as its output, its direction in time, and how its
+// state enters and leaves: kv_init[s, h] (read transposed if
+// init_transposed) times lambda^init_pow, or zeros if kv_init is nullptr;
+// lambda^final_pow times the final state to kv_final[s, h] unless nullptr.
+struct BackwardPass {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const float* kv_init;
+  float* kv_final;
+  int32_t reverse;
+  int32_t init_transposed;
+  float init_pow;
+  float final_pow;
+};
+
+struct BackwardPasses {
+  BackwardPass pass[3];
+};
+
+// a.num_items = 3 * S * H; a carries the decays and the sequence order.
+hipError_t launch_backward_wide(const PrefillArgs& a, const BackwardPasses& bp,
+                                la_dtype grad_dtype, hipStream_t stream);
+
+}  // namespace la

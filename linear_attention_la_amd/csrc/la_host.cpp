@@ -13,6 +13,7 @@
 #include <vector>
 
 #include "la.h"
+#include "la_backward.h"
 #include "la_internal.h"
 
 namespace {
@@ -625,8 +626,23 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     lam[h] = decay[h];
   }
   set_order(a, cu_seqlens_host, num_seqs);
-  // Each pass runs the wide kernel when there are enough chains to fill the
-  // GPU, else the 32-column kernel.
+  if (head_dim == 128) {
+    // The three chains are independent: one launch of the wide kernel runs
+    // them side by side (3 S H workgroups), each reading its initial state
+    // straight from kv_init / dkv_final (transposed, scaled by 1/lambda) and
+    // writing dS0 = lambda x the dV chain's final state.  No workspace.
+    la::BackwardPasses bp;
+    memset(&bp, 0, sizeof(bp));
+    bp.pass[0] = {d_o, v, k, dq, kv_init, nullptr, 0, 1, 0.0f, 0.0f};          // dQ
+    bp.pass[1] = {v, d_o, q, dk, dkv_final, nullptr, 1, 1, -1.0f, 0.0f};       // dK
+    bp.pass[2] = {k, q, d_o, dv, dkv_final, dkv_init, 1, 0, -1.0f, 1.0f};      // dV, dS0
+    a.num_items = 3 * num_seqs * num_heads;
+    const hipError_t e = la::launch_backward_wide(a, bp, grad_dtype, s);
+    return e != hipSuccess ? hip_status(e, "la_prefill_backward launch") : ok();
+  }
+  // d = 64: three launches of the 32-column kernel (or of the wide kernel
+  // when there are enough chains to fill the GPU) with the states
+  // transformed in the workspace between them.
   const bool wide = use_wide((int64_t)num_seqs * num_heads, head_dim);
   auto pass = [&](bool reverse) {
     if (!wide) return la::launch_prefill_bf16(a, head_dim, grad_dtype, false, reverse, s);

@@ -43,6 +43,7 @@
 //                        32 kk2 + 4g + (0..3) and 32 kk2 + 16 + 4g + (0..3),
 //                        stored at unit u ^ (i mod 8)
 
+#include "la_backward.h"
 #include "la_internal.h"
 #include "la_mfma.h"
 
@@ -97,8 +98,25 @@ __device__ __forceinline__ void split4t(floatx4 x, uint2& hi, uint2& lo, uint32_
               __builtin_amdgcn_fdot2_f32_bf16(h1, n_hi, x[3], false));
 }
 
-template <bool kOutF32, bool kStateOnly, bool kReverse>
-__global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
+// One chain: its sequence and head, the tensors it reads and writes, its
+// direction in time and how its states enter and leave.  The state
+// starts from kv_init[s, h] (transposed if asked) times lambda^init_pow,
+// or from zeros; lambda^final_pow times the final state goes to
+// kv_final[s, h].  The prefill sets both powers to 0.
+struct Chain {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const float* kv_init;
+  float* kv_final;
+  int s, h;
+  bool reverse, init_transposed;
+  float init_pow, final_pow;
+};
+
+template <bool kOutF32, bool kStateOnly>
+__device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c) {
   __shared__ __attribute__((aligned(16))) uint16_t Qs[kStateOnly ? 8 : 2 * kTok];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kTok];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * kTok];
@@ -106,8 +124,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Pl[kStateOnly ? 8 : kBeta * kBeta];
 
   const int H = a.num_heads;
-  const int h = blockIdx.x % H;
-  const int s = seq_of(a, blockIdx.x / H);
+  const int h = c.h;
+  const int s = c.s;
   const int t = threadIdx.x;
   const int w = uniform(t >> 6);  // value-column tile of this wave
   const int c0 = 16 * w;
@@ -133,28 +151,31 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   };
   // Buffer resource over the valid rows (all heads) of block b: loads past
   // the end of the sequence return zero and stores there are dropped.
-  // With kReverse the chain runs backwards in time: logical token i of the
+  // A reverse chain runs backwards in time: logical token i of the
   // sequence is physical row end - 1 - i, so block b holds the physical rows
   // [end - 64b - ell, end - 64b) in decreasing order.  Rows are addressed
   // inside a block resource by prow(); logical rows past the end of the
   // sequence map outside the resource either way.
   auto block_rsrc = [&](const void* base, int b, int esize) {
     const int ell = block_len(b);
-    const int64_t row0 = kReverse ? end - (int64_t)b * kBeta - ell : start + (int64_t)b * kBeta;
+    const int64_t row0 = c.reverse ? end - (int64_t)b * kBeta - ell : start + (int64_t)b * kBeta;
     const char* p = static_cast<const char*>(base) + row0 * row_stride * (int64_t)esize;
     return buf_rsrc(p, ell * row_stride * esize);
   };
-  auto prow = [&](int r, int ell) { return kReverse ? ell - 1 - r : r; };
+  auto prow = [&](int r, int ell) { return c.reverse ? ell - 1 - r : r; };
 
   // ---- state: tile n holds key rows srow(n, g) + m, column c0 + li ----
   floatx4 st[8];
+  const float init_scale = c.init_pow == 0.0f ? 1.0f : exp2f(c.init_pow * l2);
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     st[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (a.kv_init) {
+    if (c.kv_init) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        st[n][m] = a.kv_init[init_off + (int64_t)(srow(n, g) + m) * kD + c0 + li];
+        st[n][m] = init_scale * (c.init_transposed
+                                     ? c.kv_init[init_off + (int64_t)(c0 + li) * kD + srow(n, g) + m]
+                                     : c.kv_init[init_off + (int64_t)(srow(n, g) + m) * kD + c0 + li]);
     }
   }
 
@@ -198,9 +219,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
     uint4 q[2], k[2], v[2];
   };
   auto load_stage = [&](Stage& r, int b) {
-    const __amdgpu_buffer_rsrc_t rq = block_rsrc(a.q, b, 2);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.k, b, 2);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.v, b, 2);
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc(c.q, b, 2);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(c.k, b, 2);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(c.v, b, 2);
     const int ell = block_len(b);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -297,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
     }
     if (!kStateOnly) {
       constexpr int ES = kOutF32 ? 4 : 2;
-      const __amdgpu_buffer_rsrc_t ro = block_rsrc(a.o, b, ES);
+      const __amdgpu_buffer_rsrc_t ro = block_rsrc(c.o, b, ES);
       floatx4 acc[4];
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) acc[qt] = oe[qt] * qdec[qt];
@@ -420,13 +441,59 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
     }
   }
 
-  if (a.kv_final) {
+  if (c.kv_final) {
+    const float final_scale = c.final_pow == 0.0f ? 1.0f : exp2f(c.final_pow * l2);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        a.kv_final[final_off + (int64_t)(srow(n, g) + m) * kD + c0 + li] = st[n][m];
+        c.kv_final[final_off + (int64_t)(srow(n, g) + m) * kD + c0 + li] = final_scale * st[n][m];
   }
+}
+
+// Prefill: workgroup i runs the chain of head i % H of the (i / H)-th
+// sequence in dispatch order, forwards in time (or backwards, kReverse).
+template <bool kOutF32, bool kStateOnly, bool kReverse>
+__global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
+  Chain c;
+  c.q = a.q;
+  c.k = a.k;
+  c.v = a.v;
+  c.o = a.o;
+  c.kv_init = a.kv_init;
+  c.kv_final = a.kv_final;
+  c.h = blockIdx.x % a.num_heads;
+  c.s = seq_of(a, blockIdx.x / a.num_heads);
+  c.reverse = kReverse;
+  c.init_transposed = false;
+  c.init_pow = 0.0f;
+  c.final_pow = 0.0f;
+  wide_chain<kOutF32, kStateOnly>(a, c);
+}
+
+// The three chains of the backward pass in one launch: item i runs pass
+// i % 3 of chain i / 3 (head chain % H of the (chain / H)-th sequence in
+// dispatch order).  The three passes of a chain go to one XCD, where the
+// two reverse-time passes read the same Q and dO rows at the same time.
+template <bool kOutF32>
+__global__ __launch_bounds__(kThreads) void backward_wide_kernel(PrefillArgs a, BackwardPasses bp) {
+  const int item = xcd_remap(blockIdx.x, a.num_items, 3);
+  const int chain = item / 3;
+  const BackwardPass& p = bp.pass[item % 3];
+  Chain c;
+  c.q = p.q;
+  c.k = p.k;
+  c.v = p.v;
+  c.o = p.o;
+  c.kv_init = p.kv_init;
+  c.kv_final = p.kv_final;
+  c.h = chain % a.num_heads;
+  c.s = seq_of(a, chain / a.num_heads);
+  c.reverse = p.reverse != 0;
+  c.init_transposed = p.init_transposed != 0;
+  c.init_pow = p.init_pow;
+  c.final_pow = p.final_pow;
+  wide_chain<kOutF32, false>(a, c);
 }
 
 }  // namespace
@@ -445,6 +512,16 @@ hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool st
     hipLaunchKernelGGL((prefill_wide_kernel<true, false, false>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((prefill_wide_kernel<false, false, false>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward_wide(const PrefillArgs& a, const BackwardPasses& bp,
+                                la_dtype grad_dtype, hipStream_t stream) {
+  const dim3 grid(a.num_items), block(kThreads);
+  if (grad_dtype == LA_FP32)
+    hipLaunchKernelGGL(backward_wide_kernel<true>, grid, block, 0, stream, a, bp);
+  else
+    hipLaunchKernelGGL(backward_wide_kernel<false>, grid, block, 0, stream, a, bp);
   return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ def _check(gpu, ref, f32_grads, heads=None, what=""):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("kv_init,dkv_final", [(False, False), (True, True), (False, True)])
+@pytest.mark.parametrize("kv_init,dkv_final", [(False, False), (True, True), (False, True),
+                                                (True, False)])
 def test_backward_ragged(dev, d, kv_init, dkv_final):
     """Ragged lengths around the 64-token block (empty, 1, 63..65, several
     blocks plus a tail), decays from none to strong, with and without an
@@ -82,9 +83,9 @@ def test_backward_n8k_sampled_heads(dev):
 @pytest.mark.parametrize("kv_init,dkv_final,f32_grads", [(False, False, False), (True, True, False),
                                                          (True, True, True)])
 def test_backward_wide_path(dev, kv_init, dkv_final, f32_grads):
-    """Eight ragged sequences x 64 heads (512 chains: at least one per CU),
-    so all three passes run the one-workgroup-per-chain kernel, the dK and
-    dV passes in reverse time; every head against the oracle."""
+    """Eight ragged sequences x 64 heads (512 chains: at least one per CU,
+    1536 workgroups in the one launch of the d = 128 backward); every head
+    against the oracle."""
     import torch
 
     lengths = [1, 63, 64, 65, 0, 300, 129, 17]
@@ -95,3 +96,11 @@ def test_backward_wide_path(dev, kv_init, dkv_final, f32_grads):
     gpu, ref = _run(dev, lengths, 64, 128, decay, 61 + kv_init + 2 * f32_grads, kv_init, dkv_final,
                     f32_grads=f32_grads)
     say("backward wide", _check(gpu, ref, f32_grads, what="wide"))
+
+
+def test_backward_single_chain(dev):
+    """One sequence, one head: three workgroups, none in a whole group of
+    XCD-placed items; a 64-token block boundary plus a tail."""
+    decay = np.array([0.95], np.float32)
+    gpu, ref = _run(dev, [130], 1, 128, decay, 141, True, True)
+    say("backward single chain", _check(gpu, ref, False, what="single chain"))
