@@ -61,8 +61,8 @@ __device__ __forceinline__ int v_woff(int r, int col) {
 __device__ __forceinline__ int p_off(int i, int u) { return i * kBeta + 8 * (u ^ (i & 7)); }
 
 // Score units: (query tile, 32-key step) pairs on or below the diagonal.
-__device__ __forceinline__ int unit_qt(int u) { return u < 2 ? u : u < 4 ? 2 : 3; }
-__device__ __forceinline__ int unit_kk2(int u) { return (u == 3 || u == 5) ? 1 : 0; }
+__device__ __forceinline__ int unit_qt(int u) { return (0x332120 >> (4 * u)) & 15; }
+__device__ __forceinline__ int unit_kk2(int u) { return (0x22 >> u) & 1; }
 
 // Element e of a bf16x8 as float.  The whole vector is reinterpreted before
 // indexing: a bit cast applied to one element of a vector value is lowered by
@@ -260,15 +260,24 @@ __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c)
       floatx4 sc[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) sc[e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-      const bool upper = 2 * skk2 + 1 > sqt;  // second key tile above the diagonal
+      // One loop per case of the (wave-uniform) test, so that each is a
+      // single basic block whose LDS reads the compiler can issue ahead of
+      // the MFMAs.
+      auto scores = [&](auto both_) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int qo = qk_off<kD>(16 * sqt + li, 4 * kk + g);
-        const bf16x8 qb = cat(*reinterpret_cast<const v4i16*>(&Qc[qo + hsw]),
-                              *reinterpret_cast<const v4i16*>(&Qc[qo + 4 - hsw]));
-        sc[0] = mfma(ld8(&Kc[qk_off<kD>(32 * skk2 + li, 4 * kk + g)]), qb, sc[0]);
-        if (!upper) sc[1] = mfma(ld8(&Kc[qk_off<kD>(32 * skk2 + 16 + li, 4 * kk + g)]), qb, sc[1]);
-      }
+        for (int kk = 0; kk < 4; ++kk) {
+          const int qo = qk_off<kD>(16 * sqt + li, 4 * kk + g);
+          const bf16x8 qb = cat(*reinterpret_cast<const v4i16*>(&Qc[qo + hsw]),
+                                *reinterpret_cast<const v4i16*>(&Qc[qo + 4 - hsw]));
+          sc[0] = mfma(ld8(&Kc[qk_off<kD>(32 * skk2 + li, 4 * kk + g)]), qb, sc[0]);
+          if (decltype(both_)::value)
+            sc[1] = mfma(ld8(&Kc[qk_off<kD>(32 * skk2 + 16 + li, 4 * kk + g)]), qb, sc[1]);
+        }
+      };
+      if (2 * skk2 + 1 > sqt)  // second key tile above the diagonal: stays zero
+        scores(std::false_type{});
+      else
+        scores(std::true_type{});
       uint2 h0, l0, h1, l1;
       split4t(sc[0] * fs[0], h0, l0, nlo);
       split4t(sc[1] * fs[1], h1, l1, nlo);
