@@ -35,6 +35,8 @@ def _status_name(s):
 
 
 def lib_path():
+    """The in-tree libla.so, or the build that the environment variable
+    LA_LIB names (to compare two builds of the library)."""
     return os.environ.get("LA_LIB", _DEFAULT_LIB)
 
 

@@ -1,7 +1,8 @@
 // Per-head scaled copy, optionally transposed, of fp32 d x d states.  The
-// backward pass feeds the forward kernel with transformed states: S0^T for
+// d = 64 backward feeds the forward kernel with transformed states: S0^T for
 // dQ, dS_L^T / lambda and dS_L / lambda for dK and dV, and scales the last
-// state by lambda to obtain dS0.
+// state by lambda to obtain dS0.  (For d = 128 the backward kernel reads and
+// writes the states in these forms itself.)
 
 #include "la_internal.h"
 
