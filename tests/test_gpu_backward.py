@@ -104,3 +104,13 @@ def test_backward_single_chain(dev):
     decay = np.array([0.95], np.float32)
     gpu, ref = _run(dev, [130], 1, 128, decay, 141, True, True)
     say("backward single chain", _check(gpu, ref, False, what="single chain"))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_extreme_decays(dev, d):
+    """Decays down to the smallest one allowed with a final-state gradient
+    (2^-64, whose 1/lambda = 2^64 scales dS_L into the reverse chains), next
+    to no decay and a moderate one."""
+    decay = np.array([1.0, 2.0 ** -64, 1e-10, 0.5, 0.999], np.float32)
+    gpu, ref = _run(dev, [1, 64, 130, 0, 257], 5, d, decay, 151 + d, True, True)
+    say("backward extreme decays", _check(gpu, ref, False, what="extreme decays"))
