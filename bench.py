@@ -401,6 +401,51 @@ def bench_segmented(dev, reps=3):
     return res
 
 
+def bench_backward_segmented(dev, reps=2):
+    """The backward in the same low-parallelism case as bench_segmented
+    (B=1, H=8, N=1,048,576, d=128, with S0 and dS_L): la_prefill_backward
+    runs 3 x 8 chains, la_prefill_backward_segmented cuts each of its three
+    chains into 32 segments of 32,768 tokens (256 chains a pass).
+    Algorithmic bytes as in bench_backward."""
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states, workload
+
+    decay = np.asarray(workload("n1m")["decay"][:SEG_H], np.float32)
+    q, k, v = device_qkv(SEG_N, SEG_H, D, 1007, dev)
+    do = device_qkv(SEG_N, SEG_H, D, 1008, dev)[0]
+    kv0 = device_states(1, SEG_H, D, 1009, dev, scale=0.1)
+    g = device_states(1, SEG_H, D, 1010, dev, scale=0.1)
+    cu = np.array([0, SEG_N], np.int32)
+    cu_dev = torch.from_numpy(cu).to(dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dkv0 = torch.empty_like(kv0)
+    ws = torch.empty(la.prefill_backward_segmented_workspace_size(cu, SEG_H, D, SEG_LEN),
+                     dtype=torch.uint8, device=dev)
+    wsp = torch.empty(la.la_prefill_backward_workspace_size(1, SEG_H, D)[1], dtype=torch.uint8,
+                      device=dev)
+    kw = dict(kv_init=kv0, dkv_final=g, cu_seqlens_host=cu, dq=dq, dk=dk, dv=dv, dkv_init=dkv0)
+    plain = lambda i: la.prefill_backward(q, k, v, do, cu_dev, decay, workspace=wsp,  # noqa
+                                          **kw)
+    seg = lambda i: la.prefill_backward_segmented(q, k, v, do, cu_dev, decay, SEG_LEN,  # noqa
+                                                  workspace=ws, **kw)
+    plain(0)
+    seg(0)
+    s = torch.cuda.current_stream()
+    tp = timed_launches(plain, reps, s)
+    ts = timed_launches(seg, reps, s)
+    by = SEG_N * SEG_H * 14 * D + 3 * SEG_H * D * D * 4
+    del q, k, v, do, dq, dk, dv, ws, wsp
+    torch.cuda.empty_cache()
+    return {"workload": f"la_prefill_backward B=1 H={SEG_H} N={SEG_N} d={D} bf16 "
+                        "(kv_init, dkv_final)",
+            "segment_len": SEG_LEN, "plain_us": round(tp * 1e6, 1),
+            "segmented_us": round(ts * 1e6, 1), "speedup": round(tp / ts, 2),
+            "segmented_tokens_per_s": round(SEG_N / ts, 0),
+            "segmented_frac_of_8TBs": round(by / ts / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -419,7 +464,8 @@ def main():
     ap.add_argument("--sweep-only", choices=SWEEP,
                     help="only time one workload of the length / batch sweep")
     ap.add_argument("--segmented-only", action="store_true",
-                    help="only time la_prefill vs la_prefill_segmented at B=1, H=8, N=1M")
+                    help="only time la_prefill vs la_prefill_segmented (and the two "
+                         "backwards) at B=1, H=8, N=1M")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
@@ -440,7 +486,8 @@ def main():
                           "backward_batch8": bench_backward(dev, name="batch8_n8k")}), flush=True)
         return
     if args.segmented_only:
-        print(json.dumps({"segmented": bench_segmented(dev)}), flush=True)
+        print(json.dumps({"segmented": bench_segmented(dev),
+                          "backward_segmented": bench_backward_segmented(dev)}), flush=True)
         return
     if args.sweep_only:
         print(json.dumps({"sweep": bench_sweep(dev, names=(args.sweep_only,))}), flush=True)
@@ -520,6 +567,7 @@ def main():
         line["peaks"] = peaks
         line["roofline"]["frac_of_measured_stream"] = round(achieved / peaks["stream_GB_per_s"], 4)
         line["segmented"] = bench_segmented(dev)
+        line["backward_segmented"] = bench_backward_segmented(dev)
         line["backward"] = bench_backward(dev)
         line["backward_batch8"] = bench_backward(dev, name="batch8_n8k")
     if not args.no_cpu:

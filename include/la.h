@@ -265,6 +265,46 @@ la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads
                                              int32_t head_dim, size_t* bytes);
 
 /*
+ * la_prefill_backward_segmented -- la_prefill_backward with every sequence
+ * cut into segments of segment_len tokens, for few long sequences (few
+ * (sequence, head) chains to spread over the GPU).
+ *
+ * Each of the backward's three chains (dQ forwards in time, dK and dV
+ * backwards) runs as la_prefill_segmented runs its chain: every segment's
+ * local state from a zero state, a prefix over the segments -- for the two
+ * reverse-time chains from the last segment to the first -- then every
+ * segment's outputs from the state at its start.  The one-exchange sequence
+ * split of LASP+ (mizuki blog "MiniMax-01：4M 上下文破局", 五) applied to
+ * the gradient chains.  The same result as la_prefill_backward up to the
+ * order of fp32 sums.
+ *
+ * Arguments as la_prefill_backward, except:
+ *   segment_len      tokens per segment, a positive multiple of 64.
+ *   workspace        device scratch of at least
+ *                    la_prefill_backward_segmented_workspace_size bytes
+ *                    (always needed), 16-byte aligned, overlapping no other
+ *                    argument.
+ * Errors as la_prefill_backward (LA_ERR_INVALID_ARG also for a bad
+ * segment_len).  Up to sixteen kernels are enqueued on `stream`; nothing
+ * synchronises.
+ */
+la_status la_prefill_backward_segmented(
+    const void* q, const void* k, const void* v, const void* d_o, const int32_t* cu_seqlens_dev,
+    const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+    int32_t head_dim, la_dtype in_dtype, la_dtype grad_dtype, const float* decay,
+    const float* kv_init, const float* dkv_final, void* dq, void* dk, void* dv, float* dkv_init,
+    int32_t segment_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace for la_prefill_backward_segmented (host only): the
+ * segment plan and states of la_prefill_segmented_workspace_size plus one
+ * set of S x H x d x d fp32 states.  Errors as
+ * la_prefill_segmented_workspace_size. */
+la_status la_prefill_backward_segmented_workspace_size(int32_t num_seqs,
+                                                       const int32_t* cu_seqlens_host,
+                                                       int32_t num_heads, int32_t head_dim,
+                                                       int32_t segment_len, size_t* bytes);
+
+/*
  * la_decode -- one decode token per sequence, updating fp32 states in place.
  *
  * The length-1 step that serving runs in its own kernel, apart from the

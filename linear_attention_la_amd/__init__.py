@@ -29,6 +29,8 @@ from ._binding import (  # noqa: F401
     la_prefill_segmented_workspace_size,
     la_prefill_backward,
     la_prefill_backward_workspace_size,
+    la_prefill_backward_segmented,
+    la_prefill_backward_segmented_workspace_size,
     la_decode,
     la_decode_pool,
     la_prefill_pool,
@@ -38,6 +40,8 @@ from ._binding import (  # noqa: F401
     prefill_segmented,
     prefill_segmented_workspace_size,
     prefill_backward,
+    prefill_backward_segmented,
+    prefill_backward_segmented_workspace_size,
     decode,
     decode_pool,
     prefill_pool,

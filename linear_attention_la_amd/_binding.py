@@ -71,6 +71,13 @@ def lib():
     L.la_prefill_backward_workspace_size.restype = ctypes.c_int
     L.la_prefill_backward_workspace_size.argtypes = [i32, i32, i32,
                                                      ctypes.POINTER(ctypes.c_size_t)]
+    L.la_prefill_backward_segmented.restype = ctypes.c_int
+    L.la_prefill_backward_segmented.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                                ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp,
+                                                vp, vp, i32, vp, ctypes.c_size_t, vp]
+    L.la_prefill_backward_segmented_workspace_size.restype = ctypes.c_int
+    L.la_prefill_backward_segmented_workspace_size.argtypes = [i32, vp, i32, i32, i32,
+                                                               ctypes.POINTER(ctypes.c_size_t)]
     L.la_decode.restype = ctypes.c_int
     L.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
     L.la_decode_pool.restype = ctypes.c_int
@@ -136,6 +143,27 @@ def la_prefill_backward_workspace_size(num_seqs, num_heads, head_dim):
     """Returns (status, bytes)."""
     n = ctypes.c_size_t(0)
     st = lib().la_prefill_backward_workspace_size(num_seqs, num_heads, head_dim, ctypes.byref(n))
+    return st, n.value
+
+
+def la_prefill_backward_segmented(q, k, v, d_o, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                  total_tokens, num_heads, head_dim, in_dtype, grad_dtype, decay,
+                                  kv_init, dkv_final, dq, dk, dv, dkv_init, segment_len, workspace,
+                                  workspace_bytes, stream):
+    return lib().la_prefill_backward_segmented(q, k, v, d_o, cu_seqlens_dev, cu_seqlens_host,
+                                               num_seqs, total_tokens, num_heads, head_dim,
+                                               in_dtype, grad_dtype, decay, kv_init, dkv_final,
+                                               dq, dk, dv, dkv_init, segment_len, workspace,
+                                               workspace_bytes, stream)
+
+
+def la_prefill_backward_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
+                                                 segment_len):
+    """Returns (status, bytes); cu_seqlens_host: host address of int32 [S+1]."""
+    n = ctypes.c_size_t(0)
+    st = lib().la_prefill_backward_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads,
+                                                            head_dim, segment_len,
+                                                            ctypes.byref(n))
     return st, n.value
 
 
@@ -406,12 +434,8 @@ def decode_pool(q, k, v, kv_pool, slots, decay, stream=None, out=None, slots_hos
     return out
 
 
-def prefill_backward(q, k, v, d_o, cu_seqlens, decay, kv_init=None, dkv_final=None,
-                     grad_dtype=None, stream=None, init_grad=True, cu_seqlens_host=None,
-                     workspace=None, dq=None, dk=None, dv=None, dkv_init=None):
-    """Gradients of prefill().  q, k, v, d_o: device bf16 [T, H, d];
-    kv_init / dkv_final: device fp32 [S, H, d, d] or None.  Returns
-    (dq, dk, dv, dkv_init or None); grad_dtype defaults to the input dtype."""
+def _backward(q, k, v, d_o, cu_seqlens, decay, kv_init, dkv_final, grad_dtype, stream, init_grad,
+              cu_seqlens_host, workspace, dq, dk, dv, dkv_init, segment_len):
     torch = _torch()
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, grad_dtype, stream, False, dq,
                          None, cu_seqlens_host)
@@ -429,19 +453,61 @@ def prefill_backward(q, k, v, d_o, cu_seqlens, decay, kv_init=None, dkv_final=No
         dkv_init = torch.empty((m.S, m.H, m.d, m.d), dtype=torch.float32, device=m.dev)
     if not init_grad:
         dkv_init = None
-    st, need = la_prefill_backward_workspace_size(m.S, m.H, m.d)
+    if segment_len is None:
+        st, need = la_prefill_backward_workspace_size(m.S, m.H, m.d)
+        needed = kv_init is not None or dkv_final is not None
+    else:
+        st, need = la_prefill_backward_segmented_workspace_size(m.S, m.cu_host.data_ptr(), m.H,
+                                                                m.d, segment_len)
+        needed = True
     _check(st)
-    if workspace is None and (kv_init is not None or dkv_final is not None):
+    if workspace is None and needed:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
         if stream is not None:
             workspace.record_stream(stream)
+    elif workspace is not None and not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
+                                        and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     (qp, kp, vp_, cud, cuh, S, T, H, d, in_code, out_code, decp, kvip, dqp, _) = m.args
-    _check(la_prefill_backward(qp, kp, vp_, d_o.data_ptr(), cud, cuh, S, T, H, d, in_code,
-                               out_code, decp, kvip,
-                               None if dkv_final is None else dkv_final.data_ptr(), dqp,
-                               dk.data_ptr(), dv.data_ptr(),
-                               None if dkv_init is None else dkv_init.data_ptr(),
-                               None if workspace is None else workspace.data_ptr(), nbytes,
-                               m.stream))
+    common = (qp, kp, vp_, d_o.data_ptr(), cud, cuh, S, T, H, d, in_code, out_code, decp, kvip,
+              None if dkv_final is None else dkv_final.data_ptr(), dqp, dk.data_ptr(),
+              dv.data_ptr(), None if dkv_init is None else dkv_init.data_ptr())
+    ws = None if workspace is None else workspace.data_ptr()
+    if segment_len is None:
+        _check(la_prefill_backward(*common, ws, nbytes, m.stream))
+    else:
+        _check(la_prefill_backward_segmented(*common, segment_len, ws, nbytes, m.stream))
     return m.out, dk, dv, dkv_init
+
+
+def prefill_backward(q, k, v, d_o, cu_seqlens, decay, kv_init=None, dkv_final=None,
+                     grad_dtype=None, stream=None, init_grad=True, cu_seqlens_host=None,
+                     workspace=None, dq=None, dk=None, dv=None, dkv_init=None):
+    """Gradients of prefill().  q, k, v, d_o: device bf16 [T, H, d];
+    kv_init / dkv_final: device fp32 [S, H, d, d] or None.  Returns
+    (dq, dk, dv, dkv_init or None); grad_dtype defaults to the input dtype."""
+    return _backward(q, k, v, d_o, cu_seqlens, decay, kv_init, dkv_final, grad_dtype, stream,
+                     init_grad, cu_seqlens_host, workspace, dq, dk, dv, dkv_init, None)
+
+
+def prefill_backward_segmented(q, k, v, d_o, cu_seqlens, decay, segment_len, kv_init=None,
+                               dkv_final=None, grad_dtype=None, stream=None, init_grad=True,
+                               cu_seqlens_host=None, workspace=None, dq=None, dk=None, dv=None,
+                               dkv_init=None):
+    """prefill_backward() with every sequence cut into segments of
+    ``segment_len`` tokens (a multiple of 64) processed as parallel chains.
+    ``workspace``: a device tensor of at least
+    prefill_backward_segmented_workspace_size() bytes, or None to allocate
+    one.  Same returns as prefill_backward()."""
+    return _backward(q, k, v, d_o, cu_seqlens, decay, kv_init, dkv_final, grad_dtype, stream,
+                     init_grad, cu_seqlens_host, workspace, dq, dk, dv, dkv_init, segment_len)
+
+
+def prefill_backward_segmented_workspace_size(cu_seqlens_host, num_heads, head_dim, segment_len):
+    """Bytes of workspace that prefill_backward_segmented needs (host computation)."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32).reshape(-1))
+    st, n = la_prefill_backward_segmented_workspace_size(cu.shape[0] - 1, cu.ctypes.data,
+                                                         num_heads, head_dim, segment_len)
+    _check(st)
+    return n

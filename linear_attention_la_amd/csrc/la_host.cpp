@@ -213,6 +213,7 @@ la_status check_segment_len(int32_t segment_len) {
 // (int32), then fp32 states [(n + S), H, d, d], n = number of segments.
 struct SegmentLayout {
   int32_t num_segments;
+  int32_t segment_len;
   size_t cu_seg, init_slot, final_slot, seq_first, states, total;
 };
 
@@ -228,6 +229,7 @@ la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
   if (n + num_seqs >= ((int64_t)1 << 31))
     return fail(LA_ERR_UNSUPPORTED, "%lld segments exceed the int32 range", (long long)n);
   lay->num_segments = (int32_t)n;
+  lay->segment_len = segment_len;
   size_t off = 0;
   lay->cu_seg = off;
   off = align256(off + (size_t)(n + 1) * 4);
@@ -421,6 +423,65 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   return hip_status(e, "la_prefill_pool launch");
 }
 
+// One chain of every (sequence, head), cut into segments: the plan, every
+// segment's local state from a zero state, the prefix over the segments, and
+// every segment's outputs from the state at its start.  `reverse` runs the
+// chain backwards in time: the segments are then taken from the last, so the
+// slots of a segment's start state and of its local state trade places (see
+// launch_segment_prefix).  Arguments have been validated; ws holds the
+// layout `lay`; kv_init / kv_final may be NULL.
+la_status segmented_chain(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
+                          int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                          la_dtype out_dtype, const float* l2, const float* kv_init, void* o,
+                          float* kv_final, const SegmentLayout& lay, char* ws, bool reverse,
+                          hipStream_t s) {
+  int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + lay.cu_seg);
+  int32_t* init_slot = reinterpret_cast<int32_t*>(ws + lay.init_slot);
+  int32_t* final_slot = reinterpret_cast<int32_t*>(ws + lay.final_slot);
+  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + lay.seq_first);
+  float* states = reinterpret_cast<float*>(ws + lay.states);
+  int32_t* start_slot = reverse ? final_slot : init_slot;  // state entering a segment
+  int32_t* local_slot = reverse ? init_slot : final_slot;  // its local state
+
+  hipError_t e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, lay.segment_len, cu_seg,
+                                         init_slot, final_slot, seq_first, s);
+  if (e != hipSuccess) return hip_status(e, "segmented plan launch");
+
+  // pass 1: local decayed state of every segment, from a zero state
+  la::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seg;
+  a.kv_final = states;
+  a.final_slot = local_slot;
+  a.num_seqs = lay.num_segments;
+  a.num_heads = num_heads;
+  a.num_items = lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
+  for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
+  const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
+  if (wide) a.num_items = lay.num_segments * num_heads;
+  e = wide ? la::launch_prefill_wide(a, LA_BF16, true, reverse, s)
+           : la::launch_prefill_bf16(a, head_dim, LA_BF16, true, reverse, s);
+  if (e != hipSuccess) return hip_status(e, "segmented state pass launch");
+
+  // pass 2: states at every segment start (and the final states)
+  e = la::launch_segment_prefix(cu_seg, seq_first, num_seqs, num_heads, head_dim, l2, kv_init,
+                                states, kv_final, reverse, s);
+  if (e != hipSuccess) return hip_status(e, "segmented prefix launch");
+
+  // pass 3: outputs of every segment from its start state
+  a.kv_init = states;
+  a.init_slot = start_slot;
+  a.kv_final = nullptr;
+  a.final_slot = nullptr;
+  a.o = o;
+  e = wide ? la::launch_prefill_wide(a, out_dtype, false, reverse, s)
+           : la::launch_prefill_bf16(a, head_dim, out_dtype, false, reverse, s);
+  return hip_status(e, "segmented output pass launch");
+}
+
 la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
                                               int32_t num_heads, int32_t head_dim,
                                               int32_t segment_len, size_t* bytes) {
@@ -480,54 +541,11 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
       (int64_t)num_seqs * num_heads * (head_dim * head_dim / 1024) >= ((int64_t)1 << 31))
     return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
 
-  char* ws = static_cast<char*>(workspace);
-  int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + lay.cu_seg);
-  int32_t* init_slot = reinterpret_cast<int32_t*>(ws + lay.init_slot);
-  int32_t* final_slot = reinterpret_cast<int32_t*>(ws + lay.final_slot);
-  int32_t* seq_first = reinterpret_cast<int32_t*>(ws + lay.seq_first);
-  float* states = reinterpret_cast<float*>(ws + lay.states);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-
   float l2[LA_MAX_HEADS];
   for (int32_t h = 0; h < num_heads; ++h) l2[h] = (float)log2((double)decay[h]);
-
-  hipError_t e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, segment_len, cu_seg, init_slot,
-                                         final_slot, seq_first, s);
-  if (e != hipSuccess) return hip_status(e, "la_prefill_segmented plan launch");
-
-  // pass 1: local decayed state of every segment, from a zero state
-  la::PrefillArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.cu_seqlens = cu_seg;
-  a.kv_final = states;
-  a.final_slot = final_slot;
-  a.num_seqs = lay.num_segments;
-  a.num_heads = num_heads;
-  a.num_items = (int32_t)items;
-  for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
-  const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
-  if (wide) a.num_items = lay.num_segments * num_heads;
-  e = wide ? la::launch_prefill_wide(a, LA_BF16, true, false, s)
-           : la::launch_prefill_bf16(a, head_dim, LA_BF16, true, false, s);
-  if (e != hipSuccess) return hip_status(e, "la_prefill_segmented state pass launch");
-
-  // pass 2: states at every segment start (and the final states)
-  e = la::launch_segment_prefix(cu_seg, seq_first, num_seqs, num_heads, head_dim, l2, kv_init,
-                                states, kv_final, s);
-  if (e != hipSuccess) return hip_status(e, "la_prefill_segmented prefix launch");
-
-  // pass 3: outputs of every segment from its start state
-  a.kv_init = states;
-  a.init_slot = init_slot;
-  a.kv_final = nullptr;
-  a.final_slot = nullptr;
-  a.o = o;
-  e = wide ? la::launch_prefill_wide(a, out_dtype, false, false, s)
-           : la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
-  return hip_status(e, "la_prefill_segmented output pass launch");
+  return segmented_chain(q, k, v, cu_seqlens_dev, num_seqs, num_heads, head_dim, out_dtype, l2,
+                         kv_init, o, kv_final, lay, static_cast<char*>(workspace), false,
+                         static_cast<hipStream_t>(stream));
 }
 
 la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads,
@@ -541,13 +559,12 @@ la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads
   return ok();
 }
 
-la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
-                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
-                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+// Checks shared by the backward entry points, up to the point where a call
+// without sequences has nothing left to do.
+la_status check_backward_args(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                               int32_t head_dim, la_dtype in_dtype, la_dtype grad_dtype,
-                              const float* decay, const float* kv_init, const float* dkv_final,
-                              void* dq, void* dk, void* dv, float* dkv_init, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              const float* decay, const float* dkv_final,
+                              const int32_t* cu_seqlens_host) {
   if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
   if (total_tokens < 0 || total_tokens >= (int64_t)1 << 31)
     return fail(LA_ERR_INVALID_ARG, "total_tokens = %lld out of range", (long long)total_tokens);
@@ -571,16 +588,28 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
   if ((int64_t)cu_seqlens_host[num_seqs] != total_tokens)
     return fail(LA_ERR_INVALID_ARG, "cu_seqlens[%d] = %d != total_tokens = %lld", num_seqs,
                 cu_seqlens_host[num_seqs], (long long)total_tokens);
-  if (num_seqs == 0) return ok();
+  return LA_OK;
+}
+
+// The buffers of a backward call with sequences: present where needed,
+// 16-byte aligned, the grid within its limits, and the outputs and ws_bytes
+// of workspace (0: none needed, it may be NULL) overlapping nothing else.
+la_status check_backward_buffers(const void* q, const void* k, const void* v, const void* d_o,
+                                 const int32_t* cu_seqlens_dev, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t num_heads, int32_t head_dim,
+                                 la_dtype grad_dtype, const float* kv_init,
+                                 const float* dkv_final, void* dq, void* dk, void* dv,
+                                 float* dkv_init, void* workspace, size_t workspace_bytes,
+                                 size_t ws_bytes) {
   if (!cu_seqlens_dev) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_dev is NULL");
   if (total_tokens > 0 && (!q || !k || !v || !d_o || !dq || !dk || !dv))
     return fail(LA_ERR_INVALID_ARG,
                 "q, k, v, d_o, dq, dk and dv must be non-NULL when total_tokens > 0");
   const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
-  const bool need_ws = kv_init || dkv_final;
-  if (need_ws && !workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
-  if (need_ws && workspace_bytes < sb)
-    return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes, sb);
+  if (ws_bytes > 0 && !workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes > 0 && workspace_bytes < ws_bytes)
+    return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes,
+                ws_bytes);
   const void* ptrs[] = {q, k, v, d_o, dq, dk, dv, kv_init, dkv_final, dkv_init, workspace};
   const char* names[] = {"q", "k", "v", "d_o", "dq", "dk", "dv", "kv_init", "dkv_final",
                          "dkv_init", "workspace"};
@@ -591,24 +620,43 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
   if (items >= ((int64_t)1 << 31) || (int64_t)num_seqs * num_heads * 16 >= ((int64_t)1 << 31))
     return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
   // Outputs and the workspace overlap nothing else.
-  {
-    const size_t tok = (size_t)total_tokens * num_heads * head_dim;
-    const Range ins[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
-                         range("d_o", d_o, tok * 2), range("kv_init", kv_init, kv_init ? sb : 0),
-                         range("dkv_final", dkv_final, dkv_final ? sb : 0)};
-    const Range outs[] = {range("dq", dq, tok * dtype_size(grad_dtype)),
-                          range("dk", dk, tok * dtype_size(grad_dtype)),
-                          range("dv", dv, tok * dtype_size(grad_dtype)),
-                          range("dkv_init", dkv_init, dkv_init ? sb : 0),
-                          range("workspace", workspace, need_ws ? sb : 0)};
-    for (int i = 0; i < 5; ++i) {
-      for (const Range& r : ins)
-        if (overlap(outs[i], r)) return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, r.name);
-      for (int j = i + 1; j < 5; ++j)
-        if (overlap(outs[i], outs[j]))
-          return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
-    }
+  const size_t tok = (size_t)total_tokens * num_heads * head_dim;
+  const Range ins[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
+                       range("d_o", d_o, tok * 2), range("kv_init", kv_init, kv_init ? sb : 0),
+                       range("dkv_final", dkv_final, dkv_final ? sb : 0)};
+  const Range outs[] = {range("dq", dq, tok * dtype_size(grad_dtype)),
+                        range("dk", dk, tok * dtype_size(grad_dtype)),
+                        range("dv", dv, tok * dtype_size(grad_dtype)),
+                        range("dkv_init", dkv_init, dkv_init ? sb : 0),
+                        range("workspace", workspace, ws_bytes)};
+  for (int i = 0; i < 5; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, r.name);
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(LA_ERR_INVALID_ARG, "%s overlaps %s", outs[i].name, outs[j].name);
   }
+  return LA_OK;
+}
+
+la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
+                              const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                              int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                              int32_t head_dim, la_dtype in_dtype, la_dtype grad_dtype,
+                              const float* decay, const float* kv_init, const float* dkv_final,
+                              void* dq, void* dk, void* dv, float* dkv_init, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  la_status st = check_backward_args(num_seqs, total_tokens, num_heads, head_dim, in_dtype,
+                                     grad_dtype, decay, dkv_final, cu_seqlens_host);
+  if (st != LA_OK || num_seqs == 0) return st == LA_OK ? ok() : st;
+  const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  const bool need_ws = kv_init || dkv_final;
+  if ((st = check_backward_buffers(q, k, v, d_o, cu_seqlens_dev, num_seqs, total_tokens,
+                                   num_heads, head_dim, grad_dtype, kv_init, dkv_final, dq, dk,
+                                   dv, dkv_init, workspace, workspace_bytes,
+                                   need_ws ? sb : 0)) != LA_OK)
+    return st;
+  const int64_t items = (int64_t)num_seqs * num_heads * (head_dim / la::kBf16Cols);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
@@ -692,6 +740,89 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
   if (dkv_init) {
     e = la::launch_state_transform(dkv_init, dkv_init, num_seqs, num_heads, head_dim, false, lam, s);
     if (e != hipSuccess) return hip_status(e, "la_prefill_backward state launch");
+  }
+  return ok();
+}
+
+la_status la_prefill_backward_segmented_workspace_size(int32_t num_seqs,
+                                                       const int32_t* cu_seqlens_host,
+                                                       int32_t num_heads, int32_t head_dim,
+                                                       int32_t segment_len, size_t* bytes) {
+  la_status st = la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads,
+                                                     head_dim, segment_len, bytes);
+  if (st != LA_OK) return st;
+  // the segment layout, then one set of S initial states
+  *bytes = align256(*bytes) + (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  return ok();
+}
+
+la_status la_prefill_backward_segmented(
+    const void* q, const void* k, const void* v, const void* d_o, const int32_t* cu_seqlens_dev,
+    const int32_t* cu_seqlens_host, int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+    int32_t head_dim, la_dtype in_dtype, la_dtype grad_dtype, const float* decay,
+    const float* kv_init, const float* dkv_final, void* dq, void* dk, void* dv, float* dkv_init,
+    int32_t segment_len, void* workspace, size_t workspace_bytes, void* stream) {
+  la_status st = check_segment_len(segment_len);
+  if (st != LA_OK) return st;
+  if ((st = check_backward_args(num_seqs, total_tokens, num_heads, head_dim, in_dtype,
+                                grad_dtype, decay, dkv_final, cu_seqlens_host)) != LA_OK)
+    return st;
+  if (num_seqs == 0) return ok();
+  SegmentLayout lay;
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
+    return st;
+  const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  const size_t init_off = align256(lay.total);
+  if ((st = check_backward_buffers(q, k, v, d_o, cu_seqlens_dev, num_seqs, total_tokens,
+                                   num_heads, head_dim, grad_dtype, kv_init, dkv_final, dq, dk,
+                                   dv, dkv_init, workspace, workspace_bytes, init_off + sb)) != LA_OK)
+    return st;
+  const int64_t items = (int64_t)lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
+  if (items >= ((int64_t)1 << 31) ||
+      (int64_t)num_seqs * num_heads * (head_dim * head_dim / 1024) >= ((int64_t)1 << 31))
+    return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* init = reinterpret_cast<float*>(ws + init_off);  // a chain's initial states
+  float l2[LA_MAX_HEADS], one[LA_MAX_HEADS], inv[LA_MAX_HEADS], lam[LA_MAX_HEADS];
+  for (int32_t h = 0; h < num_heads; ++h) {
+    l2[h] = (float)log2((double)decay[h]);
+    one[h] = 1.0f;
+    inv[h] = (float)(1.0 / (double)decay[h]);
+    lam[h] = decay[h];
+  }
+  // The three chains of la_prefill_backward one after the other, each cut
+  // into segments; the chains share the segment workspace and the region of
+  // initial states, in stream order.
+  hipError_t e;
+  // dQ: forwards with dO, V, K and initial state S0^T
+  if (kv_init) {
+    e = la::launch_state_transform(kv_init, init, num_seqs, num_heads, head_dim, true, one, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
+  }
+  st = segmented_chain(d_o, v, k, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
+                       kv_init ? init : nullptr, dq, nullptr, lay, ws, false, s);
+  if (st != LA_OK) return st;
+  // dK: backwards with V, dO, Q and dS_L^T / lambda
+  if (dkv_final) {
+    e = la::launch_state_transform(dkv_final, init, num_seqs, num_heads, head_dim, true, inv, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
+  }
+  st = segmented_chain(v, d_o, q, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
+                       dkv_final ? init : nullptr, dk, nullptr, lay, ws, true, s);
+  if (st != LA_OK) return st;
+  // dV: backwards with K, Q, dO and dS_L / lambda; its final state is dS0 / lambda
+  if (dkv_final) {
+    e = la::launch_state_transform(dkv_final, init, num_seqs, num_heads, head_dim, false, inv, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
+  }
+  st = segmented_chain(k, q, d_o, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
+                       dkv_final ? init : nullptr, dv, dkv_init, lay, ws, true, s);
+  if (st != LA_OK) return st;
+  if (dkv_init) {
+    e = la::launch_state_transform(dkv_init, dkv_init, num_seqs, num_heads, head_dim, false, lam, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
   }
   return ok();
 }

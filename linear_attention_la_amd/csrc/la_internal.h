@@ -92,12 +92,14 @@ hipError_t launch_segment_plan(const int32_t* cu_seqlens, int32_t num_seqs, int3
                                int32_t* seq_first, hipStream_t stream);
 // Prefix over segments: slot 0 of each sequence <- kv_init (or 0); slot i+1
 // <- lambda^len_i * slot i + slot i+1 (which holds segment i's local
-// state); the last slot is also written to kv_final (if not null).
-// log2_decay: host [H] (passed by value to the kernel).
+// state); the last slot is also written to kv_final (if not null).  With
+// `reverse` (a chain backwards in time) the same from the last slot down:
+// slot n <- kv_init, slot i <- lambda^len_i * slot i+1 + slot i, and slot 0
+// goes to kv_final.  log2_decay: host [H] (passed by value to the kernel).
 hipError_t launch_segment_prefix(const int32_t* cu_seg, const int32_t* seq_first, int32_t num_seqs,
                                  int32_t num_heads, int32_t head_dim, const float* log2_decay,
                                  const float* kv_init, float* states, float* kv_final,
-                                 hipStream_t stream);
+                                 bool reverse, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, la_dtype out_dtype,
                               hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, la_dtype in_dtype,

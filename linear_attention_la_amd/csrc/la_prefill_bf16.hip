@@ -525,7 +525,9 @@ template <int D>
 hipError_t launch_d(const PrefillArgs& a, la_dtype out_dtype, bool state_only, bool reverse,
                     hipStream_t stream) {
   const dim3 grid(a.num_items), block(kThreads);
-  if (state_only)
+  if (state_only && reverse)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, true>), grid, block, 0, stream, a);
+  else if (state_only)
     hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true, false>), grid, block, 0, stream, a);
   else if (reverse && out_dtype == LA_FP32)
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false, true>), grid, block, 0, stream, a);

@@ -511,7 +511,9 @@ hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool st
                                bool reverse, hipStream_t stream) {
   const dim3 grid(a.num_items), block(kThreads);
   const bool f32 = out_dtype == LA_FP32;
-  if (state_only)
+  if (state_only && reverse)
+    hipLaunchKernelGGL((prefill_wide_kernel<false, true, true>), grid, block, 0, stream, a);
+  else if (state_only)
     hipLaunchKernelGGL((prefill_wide_kernel<false, true, false>), grid, block, 0, stream, a);
   else if (reverse && f32)
     hipLaunchKernelGGL((prefill_wide_kernel<true, false, true>), grid, block, 0, stream, a);

@@ -7,6 +7,10 @@
 // segment, Shat_i = sum_{j in i} lambda^(len_i - 1 - j) k_j^T v_j (computed
 // by a state-only pass of the prefill kernel), chained in order:
 //   S_0 = S_init,   S_(i+1) = lambda^(len_i) S_i + Shat_i.
+// A chain that runs backwards in time (the backward pass) takes the
+// segments from the last to the first: with E_i the state entering segment
+// i and L_i its local state, E_(n-1) = S_init and E_(i-1) = lambda^(len_i)
+// E_i + L_i, the state after segment 0 being the final one.
 // This is the one-exchange sequence split of LASP+ (mizuki blog "MiniMax-01：
 // 4M 上下文破局", 五: local prefix sums, then an all-gather) carried out on
 // one device; it is exact: expanding the chain gives the same sum of decayed
@@ -71,11 +75,18 @@ struct PrefixArgs {
   float* kv_final;
   int32_t num_heads;
   int32_t chunks;  // float4 chunks of 256 threads per d x d state
+  int32_t reverse;
   float log2_decay[LA_MAX_HEADS];
 };
 
 // Workgroup (s, h, chunk): each thread carries 4 consecutive state elements
-// through the segments of sequence s.
+// through the segments of sequence s.  Sequence s owns slots first + s ..
+// first + s + n of `states` (n segments from segment index first): forwards,
+// slot first + s + i holds the state entering segment i and slot
+// first + s + i + 1 arrives holding its local state; backwards, slot
+// first + s + i + 1 holds the state entering segment i and slot first + s + i
+// arrives holding its local state.  Each local state is replaced in place by
+// the state the chain reaches after its segment.
 __global__ __launch_bounds__(256) void segment_prefix_kernel(PrefixArgs a, int64_t dd) {
   const int chunk = blockIdx.x % a.chunks;
   const int sh = blockIdx.x / a.chunks;
@@ -88,17 +99,22 @@ __global__ __launch_bounds__(256) void segment_prefix_kernel(PrefixArgs a, int64
   if (a.kv_init) x = *reinterpret_cast<const float4*>(a.kv_init + (int64_t)s * slot_stride + head_off);
   const int32_t first = a.seq_first[s];
   const int32_t n = a.seq_first[s + 1] - first;
-  float* slot = a.states + (int64_t)(first + s) * slot_stride + head_off;
-  *reinterpret_cast<float4*>(slot) = x;
+  float* base = a.states + (int64_t)(first + s) * slot_stride + head_off;
   const float l2 = a.log2_decay[h];
-  for (int i = 0; i < n; ++i) {
+  auto step = [&](int i, float* local) {
     const int32_t len = a.cu_seg[first + i + 1] - a.cu_seg[first + i];
     const float f = exp2f((float)len * l2);  // lambda^len
-    float* next = slot + (int64_t)(i + 1) * slot_stride;
-    const float4 loc = *reinterpret_cast<const float4*>(next);
+    const float4 loc = *reinterpret_cast<const float4*>(local);
     x = make_float4(fmaf(f, x.x, loc.x), fmaf(f, x.y, loc.y), fmaf(f, x.z, loc.z),
                     fmaf(f, x.w, loc.w));
-    *reinterpret_cast<float4*>(next) = x;
+    *reinterpret_cast<float4*>(local) = x;
+  };
+  if (!a.reverse) {
+    *reinterpret_cast<float4*>(base) = x;
+    for (int i = 0; i < n; ++i) step(i, base + (int64_t)(i + 1) * slot_stride);
+  } else {
+    *reinterpret_cast<float4*>(base + (int64_t)n * slot_stride) = x;
+    for (int i = n - 1; i >= 0; --i) step(i, base + (int64_t)i * slot_stride);
   }
   if (a.kv_final) *reinterpret_cast<float4*>(a.kv_final + (int64_t)s * slot_stride + head_off) = x;
 }
@@ -116,7 +132,7 @@ hipError_t launch_segment_plan(const int32_t* cu_seqlens, int32_t num_seqs, int3
 hipError_t launch_segment_prefix(const int32_t* cu_seg, const int32_t* seq_first, int32_t num_seqs,
                                  int32_t num_heads, int32_t head_dim, const float* log2_decay,
                                  const float* kv_init, float* states, float* kv_final,
-                                 hipStream_t stream) {
+                                 bool reverse, hipStream_t stream) {
   PrefixArgs a;
   a.cu_seg = cu_seg;
   a.seq_first = seq_first;
@@ -124,6 +140,7 @@ hipError_t launch_segment_prefix(const int32_t* cu_seg, const int32_t* seq_first
   a.states = states;
   a.kv_final = kv_final;
   a.num_heads = num_heads;
+  a.reverse = reverse ? 1 : 0;
   const int64_t dd = (int64_t)head_dim * head_dim;
   a.chunks = (int32_t)(dd / 1024);  // d = 64: 4, d = 128: 16
   for (int h = 0; h < num_heads; ++h) a.log2_decay[h] = log2_decay[h];

@@ -29,6 +29,7 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
               "la_prefill_backward", "la_prefill_backward_workspace_size",
+              "la_prefill_backward_segmented", "la_prefill_backward_segmented_workspace_size",
               "la_prefill_pool", "la_decode", "la_decode_pool", "la_status_str",
               "la_last_error"):
         assert n in names
@@ -394,4 +395,67 @@ def test_backward_no_states_needs_no_workspace():
     passes; nothing is launched because there are no sequences)."""
     st, msg = _bwd(S=0, T=0, cu_host=np.array([0], np.int32), kv_init=None, dkv_final=None,
                    ws=None, ws_bytes=0)
+    assert st == la.LA_OK, msg
+
+
+# ---- segmented backward (host-side checks only) ----
+
+def _bwd_seg(seg=64, **kw):
+    args = dict(q=Q, k=K, v=V, do=DO_, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2,
+                T=T, H=H, d=D, in_dt=la.LA_BF16, g_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), kv_init=KVI, dkv_final=KVF, dq=DQ, dk=DK,
+                dv=DV, dkv_init=DKV0, ws=BWS, ws_bytes=1 << 26)
+    args.update(kw)
+    cu = args["cu_host"]
+    st = la.la_prefill_backward_segmented(
+        args["q"], args["k"], args["v"], args["do"], args["cu_dev"],
+        None if cu is None else cu.ctypes.data, args["S"], args["T"], args["H"], args["d"],
+        args["in_dt"], args["g_dt"], args["decay"].ctypes.data, args["kv_init"],
+        args["dkv_final"], args["dq"], args["dk"], args["dv"], args["dkv_init"], seg, args["ws"],
+        args["ws_bytes"], None)
+    return st, la.la_last_error()
+
+
+def test_backward_segmented_workspace_size():
+    """The segmented forward's layout plus one set of S x H x d x d states
+    (256-byte aligned after it)."""
+    cu = np.array([0, 40, 100, 100], np.int32)
+    st, fwd = la.la_prefill_segmented_workspace_size(3, cu.ctypes.data, 4, 128, 64)
+    assert st == la.LA_OK
+    st, n = la.la_prefill_backward_segmented_workspace_size(3, cu.ctypes.data, 4, 128, 64)
+    assert st == la.LA_OK
+    assert n == ((fwd + 255) // 256) * 256 + 3 * 4 * 128 * 128 * 4
+    assert la.la_prefill_backward_segmented_workspace_size(3, cu.ctypes.data, 4, 128, 100)[0] == \
+        la.LA_ERR_INVALID_ARG
+    assert la.la_prefill_backward_segmented_workspace_size(3, None, 4, 128, 64)[0] == \
+        la.LA_ERR_INVALID_ARG
+    assert la.prefill_backward_segmented_workspace_size(cu, 4, 128, 64) == n
+
+
+BAD_BACKWARD_SEGMENTED = [
+    ("segment_len_not_multiple", dict(seg=96), la.LA_ERR_INVALID_ARG),
+    ("segment_len_zero", dict(seg=0), la.LA_ERR_INVALID_ARG),
+    ("fp32_inputs", dict(in_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
+    ("tiny_decay_with_final_grad", dict(decay=np.array([0.9, 1e-30, 0.9, 0.9], np.float32)),
+     la.LA_ERR_UNSUPPORTED),
+    ("workspace_null_without_states", dict(ws=None, kv_init=None, dkv_final=None),
+     la.LA_ERR_INVALID_ARG),
+    ("workspace_short", dict(ws_bytes=4096), la.LA_ERR_INVALID_ARG),
+    ("workspace_misaligned", dict(ws=BWS + 8), la.LA_ERR_INVALID_ARG),
+    ("workspace_overlaps_dk", dict(ws=DK - 4096), la.LA_ERR_INVALID_ARG),
+    ("dq_overlaps_q", dict(dq=Q + 64), la.LA_ERR_INVALID_ARG),
+    ("cu_decreasing", dict(cu_host=np.array([0, 60, 50], np.int32), T=50), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_BACKWARD_SEGMENTED,
+                         ids=[b[0] for b in BAD_BACKWARD_SEGMENTED])
+def test_backward_segmented_rejects(name, kw, code):
+    st, msg = _bwd_seg(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_backward_segmented_no_sequences():
+    st, msg = _bwd_seg(S=0, T=0, cu_host=np.array([0], np.int32), ws=None, ws_bytes=0)
     assert st == la.LA_OK, msg

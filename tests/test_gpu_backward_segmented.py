@@ -1,0 +1,126 @@
+"""GPU parity of la_prefill_backward_segmented (the backward with every
+sequence cut into segments) against the fp64 oracle backward and against
+la_prefill_backward (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import cu_seqlens, host_qkv, random_states
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _inputs(dev, lengths, H, d, seed, kv_init, dkv_final):
+    import torch
+
+    T, S = int(sum(lengths)), len(lengths)
+    q, k, v = host_qkv(T, H, d, seed, "bf16")
+    do = host_qkv(T, H, d, seed + 1, "bf16")[0]
+    kv0 = random_states(S, H, d, seed + 7, scale=0.1) if kv_init else None
+    g = random_states(S, H, d, seed + 9, scale=0.1) if dkv_final else None
+    dv_ = [to_dev(x, torch.bfloat16, dev) for x in (q, k, v, do)]
+    kv0d = to_dev(kv0, torch.float32, dev) if kv_init else None
+    gd = to_dev(g, torch.float32, dev) if dkv_final else None
+    return (q, k, v, do, kv0, g), (*dv_, kv0d, gd)
+
+
+def _check(gpu, ref, f32, heads=None, what=""):
+    sel = (lambda x: x) if heads is None else (lambda x: x[:, list(heads)])
+    stats = [parity.check(sel(to_np(a)), sel(b), 1, 1e-2, out_bf16=not f32, what=f"{what} {n}")
+             for n, a, b in zip(("dq", "dk", "dv"), gpu[:3], ref[:3])]
+    stats.append(parity.check(sel(to_np(gpu[3])), sel(ref[3]), 1, 1e-2, what=f"{what} dkv_init"))
+    return stats
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("segment_len", [64, 128])
+@pytest.mark.parametrize("kv_init,dkv_final", [(True, True), (False, True), (True, False),
+                                                (False, False)])
+def test_segmented_backward_ragged(dev, d, segment_len, kv_init, dkv_final):
+    """Lengths around the segment and block edges (empty, 1, 63..65, 127..129,
+    several segments plus a tail) against the oracle's backward."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [1, 63, 64, 65, 129, 0, 300, 127, 17]
+    decay = np.array([1.0, 0.99, 0.9, 0.5], np.float32)
+    say(f"case segmented backward d={d} segment_len={segment_len} kv_init={kv_init} "
+        f"dkv_final={dkv_final}")
+    host, devs = _inputs(dev, lengths, 4, d, 301 + d + segment_len, kv_init, dkv_final)
+    cu = cu_seqlens(lengths)
+    out = la.prefill_backward_segmented(*devs[:4], cu, decay, segment_len, kv_init=devs[4],
+                                        dkv_final=devs[5])
+    torch.cuda.synchronize()
+    ref = oracle.backward_varlen(*host[:4], cu, decay, kv_init=host[4], dkv_final=host[5])
+    say("  ", _check(out, ref, False, what="ragged"))
+
+
+def test_segmented_backward_fp32_grads(dev):
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [700, 0, 130]
+    decay = np.array([0.999, 0.97, 0.8], np.float32)
+    say("case segmented backward fp32 grads")
+    host, devs = _inputs(dev, lengths, 3, 128, 331, True, True)
+    cu = cu_seqlens(lengths)
+    out = la.prefill_backward_segmented(*devs[:4], cu, decay, 192, kv_init=devs[4],
+                                        dkv_final=devs[5], grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.backward_varlen(*host[:4], cu, decay, kv_init=host[4], dkv_final=host[5])
+    say("  ", _check(out, ref, True, what="fp32 grads"))
+
+
+def test_segmented_backward_wide_path(dev):
+    """One sequence of 16K tokens x 16 heads in segments of 1024: 256
+    (segment, head) chains, so every pass runs the one-workgroup-per-chain
+    kernel (reverse-time state pass included); three heads against the
+    oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    H, N = 16, 16384
+    rng = np.random.default_rng(17)
+    decay = np.exp(-rng.uniform(0.001, 0.1, H)).astype(np.float32)
+    decay[0] = 1.0
+    heads = [0, int(np.argmin(decay)), 7]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert (N // 1024) * H >= cus
+    say("case segmented backward wide path")
+    host, devs = _inputs(dev, [N], H, 128, 341, True, True)
+    cu = cu_seqlens([N])
+    out = la.prefill_backward_segmented(*devs[:4], cu, decay, 1024, kv_init=devs[4],
+                                        dkv_final=devs[5])
+    torch.cuda.synchronize()
+    ref = oracle.backward_varlen(*host[:4], cu, decay, kv_init=host[4], dkv_final=host[5],
+                                 heads=heads)
+    say("  ", _check(out, ref, False, heads=heads, what="wide"))
+
+
+def test_segmented_backward_matches_plain(dev):
+    """Against la_prefill_backward on the same inputs (every head): the two
+    differ only in the order of fp32 sums."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [3000, 1100, 64]
+    decay = np.array([1.0, 0.995, 0.95, 0.8, 0.6, 0.9], np.float32)
+    say("case segmented backward vs plain")
+    _, devs = _inputs(dev, lengths, 6, 128, 351, True, True)
+    cu = cu_seqlens(lengths)
+    seg = la.prefill_backward_segmented(*devs[:4], cu, decay, 256, kv_init=devs[4],
+                                        dkv_final=devs[5], grad_dtype=torch.float32)
+    plain = la.prefill_backward(*devs[:4], cu, decay, kv_init=devs[4], dkv_final=devs[5],
+                                grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    stats = [parity.check(to_np(a), to_np(b).astype(np.float64), 1, 1e-4, what=n)
+             for n, a, b in zip(("dq", "dk", "dv", "dkv_init"), seg, plain)]
+    say("  ", stats)
