@@ -124,3 +124,32 @@ def test_segmented_backward_matches_plain(dev):
     stats = [parity.check(to_np(a), to_np(b).astype(np.float64), 1, 1e-4, what=n)
              for n, a, b in zip(("dq", "dk", "dv", "dkv_init"), seg, plain)]
     say("  ", stats)
+
+
+def test_segmented_backward_side_stream_workspace_reuse(dev):
+    """Two calls on a side stream sharing one workspace (a different batch
+    each time, the second one smaller) give exactly what fresh calls on the
+    default stream give."""
+    import torch
+    import linear_attention_la_amd as la
+
+    decay = np.array([0.98, 0.9], np.float32)
+    side = torch.cuda.Stream()
+    cases = [([500, 64, 1], 371), ([200, 3], 381)]
+    cu0 = cu_seqlens(cases[0][0])
+    ws = torch.empty(la.prefill_backward_segmented_workspace_size(cu0, 2, 128, 128),
+                     dtype=torch.uint8, device=dev)
+    for lengths, seed in cases:
+        say(f"case segmented backward side stream lengths={lengths}")
+        _, devs = _inputs(dev, lengths, 2, 128, seed, True, True)
+        cu = cu_seqlens(lengths)
+        ref = la.prefill_backward_segmented(*devs[:4], cu, decay, 128, kv_init=devs[4],
+                                            dkv_final=devs[5])
+        torch.cuda.synchronize()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            out = la.prefill_backward_segmented(*devs[:4], cu, decay, 128, kv_init=devs[4],
+                                                dkv_final=devs[5], stream=side, workspace=ws)
+        side.synchronize()
+        for a, b in zip(out, ref):
+            assert torch.equal(a, b)
