@@ -1,9 +1,9 @@
 """Seeded randomized GPU parity (needs an MI355X): many small configurations
 of la_prefill (both bf16 kernels and the fp32 path), la_prefill_segmented
-and la_prefill_backward against the fp64 oracle.  Each case draws its batch
-shape, lengths (block edges 0, 1, 63, 64, 65 included often), head count,
-d, decays, initial states and output dtype from its own seed, and prints
-them before it runs."""
+and la_prefill_backward (plain and segmented) against the fp64 oracle.
+Each case draws its batch shape, lengths (block edges 0, 1, 63, 64, 65
+included often), head count, d, decays, initial states and output dtype
+from its own seed, and prints them before it runs."""
 
 import numpy as np
 import pytest
@@ -132,6 +132,39 @@ def test_random_backward(dev, case):
                               kv_init=to_dev(kv0, torch.float32, dev) if kv_init else None,
                               dkv_final=to_dev(g, torch.float32, dev) if dkv_final else None,
                               grad_dtype=torch.float32 if f32 else None)
+    torch.cuda.synchronize()
+    ref = oracle.backward_varlen(q, k, v, do, cu, decay, kv_init=kv0, dkv_final=g)
+    stats = [parity.check(to_np(a), b, 1, 1e-2, out_bf16=not f32, what=f"case {case} {n}")
+             for n, a, b in zip(("dq", "dk", "dv"), out[:3], ref[:3])]
+    stats.append(parity.check(to_np(out[3]), ref[3], 1, 1e-2, what=f"case {case} dkv_init"))
+    say("  ", stats)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_backward_segmented(dev, case):
+    import torch
+    import linear_attention_la_amd as la
+
+    rng, lengths, H, d, decay = _case(7300 + case, wide=case == 7)
+    segment_len = int(rng.choice([64, 128, 192, 320]))
+    kv_init = bool(rng.random() < 0.5)
+    dkv_final = bool(rng.random() < 0.5)
+    f32 = bool(rng.random() < 0.5)
+    say(f"random segmented backward case {case}: lengths={lengths} H={H} d={d} "
+        f"segment_len={segment_len} kv_init={kv_init} dkv_final={dkv_final} f32_grads={f32}")
+    T = sum(lengths)
+    S = len(lengths)
+    q, k, v = host_qkv(T, H, d, 8400 + case, "bf16")
+    do = host_qkv(T, H, d, 8500 + case, "bf16")[0]
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(S, H, d, 9400 + case, scale=0.1) if kv_init else None
+    g = random_states(S, H, d, 9500 + case, scale=0.1) if dkv_final else None
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v, do))
+    out = la.prefill_backward_segmented(
+        qd, kd, vd, dod, cu, decay, segment_len,
+        kv_init=to_dev(kv0, torch.float32, dev) if kv_init else None,
+        dkv_final=to_dev(g, torch.float32, dev) if dkv_final else None,
+        grad_dtype=torch.float32 if f32 else None)
     torch.cuda.synchronize()
     ref = oracle.backward_varlen(q, k, v, do, cu, decay, kv_init=kv0, dkv_final=g)
     stats = [parity.check(to_np(a), b, 1, 1e-2, out_bf16=not f32, what=f"case {case} {n}")
