@@ -1,5 +1,6 @@
-// The backward pass as three runs of the one-workgroup-per-chain prefill
-// kernel in one launch (d = 128).  Internal, not part of the public ABI.
+// Internal pieces of the backward pass (not part of the public ABI): its
+// three chains in one launch of the one-workgroup-per-chain prefill kernel
+// (d = 128), and an in-place state transpose for the segmented backward.
 #pragma once
 
 #include "la_internal.h"
@@ -31,5 +32,11 @@ struct BackwardPasses {
 // a.num_items = 3 * S * H; a carries the decays and the sequence order.
 hipError_t launch_backward_wide(const PrefillArgs& a, const BackwardPasses& bp,
                                 la_dtype grad_dtype, hipStream_t stream);
+
+// x[i] <- scale[h] * x[i]^T in place for num_states fp32 d x d states
+// (state i belongs to head i % num_heads); scale: host [H].
+hipError_t launch_state_transpose_inplace(float* x, int32_t num_states, int32_t num_heads,
+                                          int32_t head_dim, const float* scale,
+                                          hipStream_t stream);
 
 }  // namespace la

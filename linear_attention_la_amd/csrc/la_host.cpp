@@ -429,12 +429,14 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
 // chain backwards in time: the segments are then taken from the last, so the
 // slots of a segment's start state and of its local state trade places (see
 // launch_segment_prefix).  Arguments have been validated; ws holds the
-// layout `lay`; kv_init / kv_final may be NULL.
+// layout `lay`; kv_init / kv_final may be NULL.  With outputs_only the plan
+// and the segment start states already in ws are used as they are (only the
+// output pass runs; kv_init and kv_final are then unused).
 la_status segmented_chain(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                           la_dtype out_dtype, const float* l2, const float* kv_init, void* o,
                           float* kv_final, const SegmentLayout& lay, char* ws, bool reverse,
-                          hipStream_t s) {
+                          hipStream_t s, bool outputs_only = false) {
   int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + lay.cu_seg);
   int32_t* init_slot = reinterpret_cast<int32_t*>(ws + lay.init_slot);
   int32_t* final_slot = reinterpret_cast<int32_t*>(ws + lay.final_slot);
@@ -443,33 +445,36 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
   int32_t* start_slot = reverse ? final_slot : init_slot;  // state entering a segment
   int32_t* local_slot = reverse ? init_slot : final_slot;  // its local state
 
-  hipError_t e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, lay.segment_len, cu_seg,
-                                         init_slot, final_slot, seq_first, s);
-  if (e != hipSuccess) return hip_status(e, "segmented plan launch");
-
-  // pass 1: local decayed state of every segment, from a zero state
   la::PrefillArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
   a.k = k;
   a.v = v;
   a.cu_seqlens = cu_seg;
-  a.kv_final = states;
-  a.final_slot = local_slot;
   a.num_seqs = lay.num_segments;
   a.num_heads = num_heads;
   a.num_items = lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
   const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
   if (wide) a.num_items = lay.num_segments * num_heads;
-  e = wide ? la::launch_prefill_wide(a, LA_BF16, true, reverse, s)
-           : la::launch_prefill_bf16(a, head_dim, LA_BF16, true, reverse, s);
-  if (e != hipSuccess) return hip_status(e, "segmented state pass launch");
+  hipError_t e;
+  if (!outputs_only) {
+    e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, lay.segment_len, cu_seg, init_slot,
+                                final_slot, seq_first, s);
+    if (e != hipSuccess) return hip_status(e, "segmented plan launch");
 
-  // pass 2: states at every segment start (and the final states)
-  e = la::launch_segment_prefix(cu_seg, seq_first, num_seqs, num_heads, head_dim, l2, kv_init,
-                                states, kv_final, reverse, s);
-  if (e != hipSuccess) return hip_status(e, "segmented prefix launch");
+    // pass 1: local decayed state of every segment, from a zero state
+    a.kv_final = states;
+    a.final_slot = local_slot;
+    e = wide ? la::launch_prefill_wide(a, LA_BF16, true, reverse, s)
+             : la::launch_prefill_bf16(a, head_dim, LA_BF16, true, reverse, s);
+    if (e != hipSuccess) return hip_status(e, "segmented state pass launch");
+
+    // pass 2: states at every segment start (and the final states)
+    e = la::launch_segment_prefix(cu_seg, seq_first, num_seqs, num_heads, head_dim, l2, kv_init,
+                                  states, kv_final, reverse, s);
+    if (e != hipSuccess) return hip_status(e, "segmented prefix launch");
+  }
 
   // pass 3: outputs of every segment from its start state
   a.kv_init = states;
@@ -804,24 +809,30 @@ la_status la_prefill_backward_segmented(
   st = segmented_chain(d_o, v, k, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
                        kv_init ? init : nullptr, dq, nullptr, lay, ws, false, s);
   if (st != LA_OK) return st;
-  // dK: backwards with V, dO, Q and dS_L^T / lambda
+  // dK: backwards with V, dO, Q and dS_L^T / lambda; its final state is
+  // (dS0 / lambda)^T
   if (dkv_final) {
     e = la::launch_state_transform(dkv_final, init, num_seqs, num_heads, head_dim, true, inv, s);
     if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
   }
   st = segmented_chain(v, d_o, q, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
-                       dkv_final ? init : nullptr, dk, nullptr, lay, ws, true, s);
+                       dkv_final ? init : nullptr, dk, dkv_init, lay, ws, true, s);
   if (st != LA_OK) return st;
-  // dV: backwards with K, Q, dO and dS_L / lambda; its final state is dS0 / lambda
-  if (dkv_final) {
-    e = la::launch_state_transform(dkv_final, init, num_seqs, num_heads, head_dim, false, inv, s);
-    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
-  }
+  // dV: backwards with K, Q, dO and dS_L / lambda.  Its keys and values are
+  // the dK chain's values and keys, with the same decays and the transposed
+  // initial state, so each of its states is the transpose of the dK chain's
+  // state at the same point: the dK chain's segment start states, transposed
+  // in place, are the dV chain's, and only its output pass runs.
+  float* states = reinterpret_cast<float*>(ws + lay.states);
+  e = la::launch_state_transpose_inplace(states, (lay.num_segments + num_seqs) * num_heads,
+                                         num_heads, head_dim, one, s);
+  if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
   st = segmented_chain(k, q, d_o, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
-                       dkv_final ? init : nullptr, dv, dkv_init, lay, ws, true, s);
+                       nullptr, dv, nullptr, lay, ws, true, s, true);
   if (st != LA_OK) return st;
-  if (dkv_init) {
-    e = la::launch_state_transform(dkv_init, dkv_init, num_seqs, num_heads, head_dim, false, lam, s);
+  if (dkv_init) {  // dS0: lambda times the transpose of the dK chain's final state
+    e = la::launch_state_transpose_inplace(dkv_init, num_seqs * num_heads, num_heads, head_dim,
+                                           lam, s);
     if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
   }
   return ok();

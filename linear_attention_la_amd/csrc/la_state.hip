@@ -4,6 +4,7 @@
 // state by lambda to obtain dS0.  (For d = 128 the backward kernel reads and
 // writes the states in these forms itself.)
 
+#include "la_backward.h"
 #include "la_internal.h"
 
 namespace la {
@@ -55,6 +56,42 @@ __global__ __launch_bounds__(256) void state_transform_kernel(StateArgs a, int d
                   f * tile[row][q4 + 3]);
 }
 
+// In-place transpose with a per-head scale: workgroup (state, tile pair)
+// with tile row tr <= tile column tc loads tiles (tr, tc) and (tc, tr) into
+// LDS before writing either, then writes each, transposed, over the other
+// (a diagonal tile over itself).  Different workgroups touch disjoint tiles.
+__global__ __launch_bounds__(256) void state_transpose_inplace_kernel(StateArgs a, int d) {
+  __shared__ float tile[2][kTile][kTile + 1];
+  const int pairs = a.tiles * (a.tiles + 1) / 2;
+  const int sh = blockIdx.x / pairs;
+  int p = blockIdx.x % pairs, tr = 0;
+  while (p >= a.tiles - tr) {  // pairs of tile row tr: tc = tr .. tiles - 1
+    p -= a.tiles - tr;
+    ++tr;
+  }
+  const int tc = tr + p;
+  const int h = sh % a.num_heads;
+  float* x = a.out + (int64_t)sh * d * d;
+  const float f = a.scale[h];
+  const int row = threadIdx.x / 8, q4 = 4 * (threadIdx.x % 8);
+  const int nt = tr == tc ? 1 : 2;
+  for (int i = 0; i < nt; ++i) {  // tile 0 = (tr, tc), tile 1 = (tc, tr)
+    const int r0 = i ? tc : tr, c0 = i ? tr : tc;
+    const float4 v = *reinterpret_cast<const float4*>(x + (int64_t)(r0 * kTile + row) * d + c0 * kTile + q4);
+    tile[i][q4][row] = v.x;
+    tile[i][q4 + 1][row] = v.y;
+    tile[i][q4 + 2][row] = v.z;
+    tile[i][q4 + 3][row] = v.w;
+  }
+  __syncthreads();
+  for (int i = 0; i < nt; ++i) {  // the transpose of tile (r0, c0) goes to (c0, r0)
+    const int r0 = i ? tc : tr, c0 = i ? tr : tc;
+    *reinterpret_cast<float4*>(x + (int64_t)(c0 * kTile + row) * d + r0 * kTile + q4) =
+        make_float4(f * tile[i][row][q4], f * tile[i][row][q4 + 1], f * tile[i][row][q4 + 2],
+                    f * tile[i][row][q4 + 3]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_state_transform(const float* in, float* out, int32_t num_states,
@@ -73,6 +110,21 @@ hipError_t launch_state_transform(const float* in, float* out, int32_t num_state
   else
     hipLaunchKernelGGL(state_transform_kernel<false>, dim3((unsigned)blocks), dim3(256), 0,
                        stream, a, head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_transpose_inplace(float* x, int32_t num_states, int32_t num_heads,
+                                          int32_t head_dim, const float* scale,
+                                          hipStream_t stream) {
+  StateArgs a;
+  a.in = x;
+  a.out = x;
+  a.num_heads = num_heads;
+  a.tiles = head_dim / kTile;
+  for (int h = 0; h < num_heads; ++h) a.scale[h] = scale[h];
+  const int64_t blocks = (int64_t)num_states * (a.tiles * (a.tiles + 1) / 2);
+  hipLaunchKernelGGL(state_transpose_inplace_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     a, head_dim);
   return hipGetLastError();
 }
 
