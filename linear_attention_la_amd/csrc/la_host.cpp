@@ -783,8 +783,11 @@ la_status la_prefill_backward_segmented(
                                    dv, dkv_init, workspace, workspace_bytes, init_off + sb)) != LA_OK)
     return st;
   const int64_t items = (int64_t)lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
+  const int64_t tiles = head_dim / 32;  // the in-place transpose: one workgroup per tile pair
   if (items >= ((int64_t)1 << 31) ||
-      (int64_t)num_seqs * num_heads * (head_dim * head_dim / 1024) >= ((int64_t)1 << 31))
+      (int64_t)num_seqs * num_heads * (head_dim * head_dim / 1024) >= ((int64_t)1 << 31) ||
+      ((int64_t)lay.num_segments + num_seqs) * num_heads * (tiles * (tiles + 1) / 2) >=
+          ((int64_t)1 << 31))
     return fail(LA_ERR_UNSUPPORTED, "%lld work items exceed the grid limit", (long long)items);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
