@@ -114,3 +114,29 @@ def test_backward_extreme_decays(dev, d):
     decay = np.array([1.0, 2.0 ** -64, 1e-10, 0.5, 0.999], np.float32)
     gpu, ref = _run(dev, [1, 64, 130, 0, 257], 5, d, decay, 151 + d, True, True)
     say("backward extreme decays", _check(gpu, ref, False, what="extreme decays"))
+
+
+@pytest.mark.parametrize("segmented", [False, True])
+def test_backward_without_initial_state_gradient(dev, segmented):
+    """init_grad=False (dkv_init NULL): dq, dk and dv are exactly those of
+    the call that also returns dS0."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [200, 70]
+    decay = np.array([0.97, 0.8], np.float32)
+    say(f"case backward without dS0 segmented={segmented}")
+    T = sum(lengths)
+    q, k, v = host_qkv(T, 2, 128, 161, "bf16")
+    do = host_qkv(T, 2, 128, 162, "bf16")[0]
+    cu = cu_seqlens(lengths)
+    qd, kd, vd, dod = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v, do))
+    g = to_dev(random_states(2, 2, 128, 163, scale=0.1), torch.float32, dev)
+    call = ((lambda **kw: la.prefill_backward_segmented(qd, kd, vd, dod, cu, decay, 128, **kw))
+            if segmented else (lambda **kw: la.prefill_backward(qd, kd, vd, dod, cu, decay, **kw)))
+    full = call(dkv_final=g)
+    part = call(dkv_final=g, init_grad=False)
+    torch.cuda.synchronize()
+    assert part[3] is None
+    for a, b in zip(full[:3], part[:3]):
+        assert torch.equal(a, b)
