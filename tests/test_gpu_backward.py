@@ -140,3 +140,31 @@ def test_backward_without_initial_state_gradient(dev, segmented):
     assert part[3] is None
     for a, b in zip(full[:3], part[:3]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("segmented", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_all_sequences_empty(dev, segmented, d):
+    """Sequences of length 0 only: no gradient rows, and dS0 = dS_L (its
+    1/lambda and lambda scalings cancel up to rounding), against the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [0, 0, 0]
+    decay = np.array([1.0, 0.9, 0.3], np.float32)
+    say(f"case backward all empty d={d} segmented={segmented}")
+    q = np.zeros((0, 3, d), np.float32)
+    qd = torch.zeros((0, 3, d), dtype=torch.bfloat16, device=dev)
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(3, 3, d, 171, scale=0.1)
+    g = random_states(3, 3, d, 173, scale=0.1)
+    kv0d, gd = to_dev(kv0, torch.float32, dev), to_dev(g, torch.float32, dev)
+    if segmented:
+        out = la.prefill_backward_segmented(qd, qd, qd, qd, cu, decay, 64, kv_init=kv0d,
+                                            dkv_final=gd)
+    else:
+        out = la.prefill_backward(qd, qd, qd, qd, cu, decay, kv_init=kv0d, dkv_final=gd)
+    torch.cuda.synchronize()
+    assert all(x.shape[0] == 0 for x in out[:3])
+    ref = oracle.backward_varlen(q, q, q, q, cu, decay, kv_init=kv0, dkv_final=g)
+    parity.check(to_np(out[3]), ref[3], 1, 1e-5, what="all empty dkv_init")
