@@ -339,6 +339,58 @@ def pin_backward_finite_difference(orc):
         _close(grads[which], num, 1e-6, f"finite difference input {which}")
 
 
+def pin_backward_varlen(orc):
+    """Packed-batch backward against automatic differentiation of the packed
+    forward: torch (float64, CPU) runs the token recurrence of every
+    (sequence, head) of a packed batch -- per-head decays, per-sequence
+    initial states, a zero-length sequence -- and differentiates
+    sum(O * dO) + sum(S_final * dS_final).  Both backward forms of the varlen
+    wrapper must give the same gradients, the zero-length sequence passes its
+    final-state gradient straight to its initial state, and packing the
+    sequences in reverse order permutes the gradients accordingly."""
+    import torch
+
+    rng = _rng(41)
+    H, d = 3, 3
+    lens = [4, 0, 7, 1]
+    decay = np.array([0.9, 1.0, 0.6])
+    S = len(lens)
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, do = (rng.standard_normal((T, H, d)) for _ in range(4))
+    kv0 = rng.standard_normal((S, H, d, d))
+    g = rng.standard_normal((S, H, d, d))
+
+    tq, tk, tv, tkv0 = (torch.tensor(x, dtype=torch.float64, requires_grad=True)
+                        for x in (q, k, v, kv0))
+    loss = 0.0
+    for s in range(S):
+        for h in range(H):
+            St = tkv0[s, h]
+            for t in range(int(cu[s]), int(cu[s + 1])):
+                St = float(decay[h]) * St + torch.outer(tk[t, h], tv[t, h])
+                loss = loss + (tq[t, h] @ St * torch.tensor(do[t, h])).sum()
+            loss = loss + (St * torch.tensor(g[s, h])).sum()
+    loss.backward()
+    ref = [x.grad.numpy() for x in (tq, tk, tv, tkv0)]
+    for form in ("recurrent", "quadratic"):
+        got = orc.backward_varlen(q, k, v, do, cu, decay, kv_init=kv0, dkv_final=g, form=form)
+        for name, a, b in zip(("dq", "dk", "dv", "dkv_init"), got, ref):
+            _close(a, b, 1e-12, f"backward_varlen {form} {name}")
+        _close(got[3][1], g[1], 0.0, f"backward_varlen {form} zero-length sequence")
+    # reverse packing order: gradients move with their tokens and sequences
+    order = list(range(S))[::-1]
+    lens_r = [lens[i] for i in order]
+    cu_r = np.concatenate([[0], np.cumsum(lens_r)])
+    idx = np.concatenate([np.arange(cu[i], cu[i + 1]) for i in order]).astype(int)
+    got_r = orc.backward_varlen(q[idx], k[idx], v[idx], do[idx], cu_r, decay,
+                                kv_init=kv0[order], dkv_final=g[order])
+    for name, a, b in zip(("dq", "dk", "dv"), got_r[:3], ref[:3]):
+        _close(a, b[idx], 1e-12, f"backward_varlen reversed packing {name}")
+    _close(got_r[3], ref[3][order], 1e-12, "backward_varlen reversed packing dkv_init")
+
+
 ALL_PINS = [pin_golden, pin_exact_rational, pin_lfilter, pin_nodecay_library, pin_geometric,
             pin_three_way, pin_continuation, pin_decode_consistency, pin_packing, pin_decode_pool,
-            pin_prefill_pool, pin_backward_autograd, pin_backward_finite_difference]
+            pin_prefill_pool, pin_backward_autograd, pin_backward_finite_difference,
+            pin_backward_varlen]

@@ -61,6 +61,12 @@ MUTATIONS = {
                                     "        dq[t] = S @ do[t]\n        S = lam * S + np.outer(k[t], v[t])"),
     "bwd_rec_no_reverse_decay": ("        if j < L - 1:\n            R = lam * R\n", ""),
     "bwd_rec_dv_untransposed": ("        dv[j] = R.T @ k[j]", "        dv[j] = R @ k[j]"),
+    "bwd_varlen_first_head_decay": ("r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[h], s0, g)",
+                                    "r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[0], s0, g)"),
+    "bwd_varlen_swapped_state_args": ("r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[h], s0, g)",
+                                      "r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[h], g, s0)"),
+    "bwd_varlen_swapped_dk_dv": ("dq[a:b, h], dk[a:b, h], dv[a:b, h], dkv0[s, h] = r",
+                                 "dq[a:b, h], dv[a:b, h], dk[a:b, h], dkv0[s, h] = r"),
 }
 
 
