@@ -23,6 +23,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    # only the C ABI is exported (la_host.cpp gives the declarations of la.h
+    # default visibility)
+    "-fvisibility=hidden",
     # packed fp32 VALU ops stay off (v_pk_{add,mul,fma}_f32 are not emitted)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",

@@ -12,7 +12,11 @@
 
 #include <vector>
 
+// The entry points declared in la.h are the library's only exported symbols
+// (everything else is built with hidden visibility).
+#pragma GCC visibility push(default)
 #include "la.h"
+#pragma GCC visibility pop
 #include "la_backward.h"
 #include "la_internal.h"
 
@@ -423,6 +427,10 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   return hip_status(e, "la_prefill_pool launch");
 }
 
+}  // extern "C"
+
+namespace {
+
 // One chain of every (sequence, head), cut into segments: the plan, every
 // segment's local state from a zero state, the prefix over the segments, and
 // every segment's outputs from the state at its start.  `reverse` runs the
@@ -486,6 +494,10 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
            : la::launch_prefill_bf16(a, head_dim, out_dtype, false, reverse, s);
   return hip_status(e, "segmented output pass launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
                                               int32_t num_heads, int32_t head_dim,
@@ -563,6 +575,10 @@ la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads
   *bytes = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
   return ok();
 }
+
+}  // extern "C"
+
+namespace {
 
 // Checks shared by the backward entry points, up to the point where a call
 // without sequences has nothing left to do.
@@ -643,6 +659,10 @@ la_status check_backward_buffers(const void* q, const void* k, const void* v, co
   }
   return LA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 la_status la_prefill_backward(const void* q, const void* k, const void* v, const void* d_o,
                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,

@@ -41,6 +41,18 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), f"libla.so does not export {name}"
 
 
+def test_library_exports_only_the_c_abi():
+    """Every exported la_* symbol is declared in the header, and no internal
+    helper (kernel launchers, host checks) is exported."""
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", la.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert {n for n in names if n.startswith("la_")} == set(_declared_functions())
+    assert not [n for n in names if "launch_" in n or "segmented_chain" in n or "check_" in n]
+
+
 def test_status_strings():
     assert la.la_status_str(la.LA_OK) == "LA_OK"
     assert la.la_status_str(la.LA_ERR_INVALID_ARG) == "LA_ERR_INVALID_ARG"
