@@ -31,8 +31,9 @@
  *
  * Ownership.  The caller allocates and owns every buffer.  The library
  * allocates no device memory, keeps no pointer after a call returns and
- * holds no global state; calls on different streams with disjoint outputs
- * may run concurrently.  Work is enqueued on `stream` (a hipStream_t passed
+ * holds no global state (apart from the static device scratch of
+ * la_prefill_segmented_noalloc); calls on different streams with disjoint
+ * outputs may run concurrently (la_prefill_segmented_noalloc excepted).  Work is enqueued on `stream` (a hipStream_t passed
  * as void*, NULL = the default stream) and is asynchronous: device buffers
  * must stay valid until the stream has passed the kernel.  Host arrays
  * (decay, cu_seqlens_host) are read only during the call.  The device that
@@ -196,6 +197,41 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
                                const float* decay, const float* kv_init, void* o,
                                float* kv_final, int32_t segment_len, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* Size in bytes of the static device scratch of
+ * la_prefill_segmented_noalloc (each device the library runs on holds one
+ * such array until the process ends). */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * la_prefill_segmented_noalloc -- la_prefill_segmented without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * calls no hipMalloc, hipFree or allocating library routine: the workspace
+ * is a static device array of LA_NOALLOC_SCRATCH_BYTES bytes (64 MiB) that
+ * the library holds on every device it runs on; its device address is
+ * looked up once per device (hipGetSymbolAddress) on the first call there.
+ *
+ * Arguments, results and errors as la_prefill_segmented, without workspace
+ * and workspace_bytes.  A call whose workspace
+ * (la_prefill_segmented_workspace_size) would exceed the scratch returns
+ * LA_ERR_UNSUPPORTED before anything is enqueued; at H = 64, d = 128 the
+ * scratch holds (segments + sequences) <= 15.  Failing to look up the
+ * scratch address is LA_ERR_HIP.
+ *
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents (nothing in it needs to start at zero).  Calls that
+ * overlap in time on one device -- on different streams, or from different
+ * host threads -- race on the scratch and give undefined results; calls on
+ * one stream are ordered by the stream and are safe.
+ */
+la_status la_prefill_segmented_noalloc(const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens_dev,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       int64_t total_tokens, int32_t num_heads,
+                                       int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                                       const float* decay, const float* kv_init, void* o,
+                                       float* kv_final, int32_t segment_len, void* stream);
 
 /*
  * la_prefill_segmented_workspace_size -- bytes of workspace that

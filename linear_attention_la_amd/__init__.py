@@ -7,6 +7,7 @@ library is missing, every call raises.
 
     o, kv = prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None)
     o, kv = prefill_segmented(q, k, v, cu_seqlens, decay, segment_len)
+    o, kv = prefill_segmented_noalloc(q, k, v, cu_seqlens, decay, segment_len)  # static scratch
     dq, dk, dv, dkv0 = prefill_backward(q, k, v, do, cu_seqlens, decay, kv_init, dkv_final)
     o = decode(q, k, v, kv, decay)          # kv updated in place
     o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     la_prefill,
     la_prefill_segmented,
+    la_prefill_segmented_noalloc,
     la_prefill_segmented_workspace_size,
     la_prefill_backward,
     la_prefill_backward_workspace_size,
@@ -38,6 +40,7 @@ from ._binding import (  # noqa: F401
     la_last_error,
     prefill,
     prefill_segmented,
+    prefill_segmented_noalloc,
     prefill_segmented_workspace_size,
     prefill_backward,
     prefill_backward_segmented,

@@ -61,6 +61,10 @@ def lib():
     L.la_prefill_segmented.restype = ctypes.c_int
     L.la_prefill_segmented.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
                                        ctypes.c_int, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
+    L.la_prefill_segmented_noalloc.restype = ctypes.c_int
+    L.la_prefill_segmented_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32,
+                                               ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i32,
+                                               vp]
     L.la_prefill_segmented_workspace_size.restype = ctypes.c_int
     L.la_prefill_segmented_workspace_size.argtypes = [i32, vp, i32, i32, i32,
                                                       ctypes.POINTER(ctypes.c_size_t)]
@@ -107,6 +111,15 @@ def la_prefill_segmented(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, tot
                                       total_tokens, num_heads, head_dim, in_dtype, out_dtype,
                                       decay, kv_init, o, kv_final, segment_len, workspace,
                                       workspace_bytes, stream)
+
+
+def la_prefill_segmented_noalloc(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                 total_tokens, num_heads, head_dim, in_dtype, out_dtype, decay,
+                                 kv_init, o, kv_final, segment_len, stream):
+    return lib().la_prefill_segmented_noalloc(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                              total_tokens, num_heads, head_dim, in_dtype,
+                                              out_dtype, decay, kv_init, o, kv_final,
+                                              segment_len, stream)
 
 
 def la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
@@ -332,6 +345,20 @@ def prefill_segmented(q, k, v, cu_seqlens, decay, segment_len, kv_init=None, out
         raise ValueError("workspace must be a contiguous device tensor")
     nbytes = workspace.numel() * workspace.element_size()
     _check(la_prefill_segmented(*m.args, segment_len, workspace.data_ptr(), nbytes, m.stream))
+    return m.out, m.kv_final
+
+
+def prefill_segmented_noalloc(q, k, v, cu_seqlens, decay, segment_len, kv_init=None,
+                              out_dtype=None, stream=None, final_state=True, out=None,
+                              kv_final=None, cu_seqlens_host=None):
+    """prefill_segmented() whose workspace is the library's static device
+    scratch (la_prefill_segmented_noalloc): the library allocates nothing.
+    Pass ``out`` (and ``kv_final``) to allocate nothing on the Python side
+    either.  Calls that overlap in time on one device race on the scratch.
+    Same returns as prefill()."""
+    m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
+                         out, kv_final, cu_seqlens_host)
+    _check(la_prefill_segmented_noalloc(*m.args, segment_len, m.stream))
     return m.out, m.kv_final
 
 

@@ -427,6 +427,24 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   return hip_status(e, "la_prefill_pool launch");
 }
 
+la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                              int32_t num_heads, int32_t head_dim,
+                                              int32_t segment_len, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if ((st = check_segment_len(segment_len)) != LA_OK) return st;
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  SegmentLayout lay;
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
+    return st;
+  *bytes = lay.total;
+  return ok();
+}
+
 }  // extern "C"
 
 namespace {
@@ -495,47 +513,16 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
   return hip_status(e, "segmented output pass launch");
 }
 
-}  // namespace
-
-extern "C" {
-
-la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
-                                              int32_t num_heads, int32_t head_dim,
-                                              int32_t segment_len, size_t* bytes) {
-  if (!bytes) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = 0;
-  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
-  la_status st = check_heads_dim(num_heads, head_dim);
-  if (st != LA_OK) return st;
-  if ((st = check_segment_len(segment_len)) != LA_OK) return st;
-  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
-  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
-  SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
-    return st;
-  *bytes = lay.total;
-  return ok();
-}
-
-la_status la_prefill_segmented(const void* q, const void* k, const void* v,
-                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
-                               int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
-                               int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
-                               const float* decay, const float* kv_init, void* o,
-                               float* kv_final, int32_t segment_len, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  la_status st = check_segment_len(segment_len);
-  if (st != LA_OK) return st;
-  if (in_dtype != LA_BF16 && valid_dtype(in_dtype))
-    return fail(LA_ERR_UNSUPPORTED, "the segmented prefill takes bf16 inputs only");
-  if ((st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
-                          num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
-                          num_seqs)) != LA_OK)
-    return st;
-  if (num_seqs == 0) return ok();
-  SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
-    return st;
+// la_prefill_segmented with its workspace given: the checks that involve the
+// workspace, then the segmented chain.  `who` names the entry point in
+// error messages.
+la_status segmented_prefill(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                            int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                            const float* decay, const float* kv_init, void* o, float* kv_final,
+                            int32_t segment_len, const SegmentLayout& lay, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   if (!workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL");
   if (!aligned16(workspace)) return fail(LA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   if (workspace_bytes < lay.total)
@@ -553,6 +540,9 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
     for (const Range& r : others)
       if (overlap(rw, r)) return fail(LA_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
   }
+  (void)in_dtype;
+  (void)cu_seqlens_host;
+  (void)segment_len;
   const int64_t items = (int64_t)lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
   if (items >= ((int64_t)1 << 31) ||
       (int64_t)num_seqs * num_heads * (head_dim * head_dim / 1024) >= ((int64_t)1 << 31))
@@ -563,6 +553,114 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
   return segmented_chain(q, k, v, cu_seqlens_dev, num_seqs, num_heads, head_dim, out_dtype, l2,
                          kv_init, o, kv_final, lay, static_cast<char*>(workspace), false,
                          static_cast<hipStream_t>(stream));
+}
+
+// Arguments of la_prefill_segmented other than the workspace: checked, and
+// the workspace layout computed.  *done is set when there is nothing to run.
+la_status segmented_args(const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                         int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                         int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                         const float* decay, const float* kv_init, const void* o,
+                         const float* kv_final, int32_t segment_len, SegmentLayout* lay,
+                         bool* done) {
+  *done = false;
+  la_status st = check_segment_len(segment_len);
+  if (st != LA_OK) return st;
+  if (in_dtype != LA_BF16 && valid_dtype(in_dtype))
+    return fail(LA_ERR_UNSUPPORTED, "the segmented prefill takes bf16 inputs only");
+  if ((st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                          num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
+                          num_seqs)) != LA_OK)
+    return st;
+  if (num_seqs == 0) {
+    *done = true;
+    return ok();
+  }
+  return segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, lay);
+}
+
+// Scratch of la_prefill_segmented_noalloc: a static device array, so that
+// the entry point allocates nothing.  Each device that runs the library
+// holds its own copy until the process ends.  In host code the array's name
+// is not a device address: its address on each device comes from
+// hipGetSymbolAddress (scratch_on_device), and only that pointer is passed
+// to kernels.
+__device__ __attribute__((aligned(256))) char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (NULL with *st set on failure).
+char* scratch_on_device(la_status* st) {
+  static std::atomic<char*> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "la_prefill_segmented_noalloc: hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= 64) {
+    *st = fail(LA_ERR_UNSUPPORTED, "device %d: at most 64 devices are supported", dev);
+    return nullptr;
+  }
+  char* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    *st = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                     "la_prefill_segmented_noalloc: hipGetSymbolAddress(scratch)");
+    return nullptr;
+  }
+  p = static_cast<char*>(ptr);
+  cache[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_prefill_segmented(const void* q, const void* k, const void* v,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                               int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                               int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                               const float* decay, const float* kv_init, void* o,
+                               float* kv_final, int32_t segment_len, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  SegmentLayout lay;
+  bool done = false;
+  la_status st = segmented_args(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                                num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o,
+                                kv_final, segment_len, &lay, &done);
+  if (st != LA_OK || done) return st;
+  return segmented_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                           num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
+                           segment_len, lay, workspace, workspace_bytes, stream);
+}
+
+la_status la_prefill_segmented_noalloc(const void* q, const void* k, const void* v,
+                                       const int32_t* cu_seqlens_dev,
+                                       const int32_t* cu_seqlens_host, int32_t num_seqs,
+                                       int64_t total_tokens, int32_t num_heads,
+                                       int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                                       const float* decay, const float* kv_init, void* o,
+                                       float* kv_final, int32_t segment_len, void* stream) {
+  SegmentLayout lay;
+  bool done = false;
+  la_status st = segmented_args(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                                num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o,
+                                kv_final, segment_len, &lay, &done);
+  if (st != LA_OK || done) return st;
+  if (lay.total > (size_t)LA_NOALLOC_SCRATCH_BYTES)
+    return fail(LA_ERR_UNSUPPORTED,
+                "la_prefill_segmented_noalloc needs %zu bytes of scratch; its static scratch "
+                "holds %zu (use la_prefill_segmented with a workspace)",
+                lay.total, (size_t)LA_NOALLOC_SCRATCH_BYTES);
+  char* ws = scratch_on_device(&st);
+  if (!ws) return st;
+  return segmented_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                           num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
+                           segment_len, lay, ws, (size_t)LA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads,

@@ -28,6 +28,7 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
+              "la_prefill_segmented_noalloc",
               "la_prefill_backward", "la_prefill_backward_workspace_size",
               "la_prefill_backward_segmented", "la_prefill_backward_segmented_workspace_size",
               "la_prefill_pool", "la_decode", "la_decode_pool", "la_status_str",
@@ -255,6 +256,46 @@ def test_segmented_rejects(name, kw, code):
     st, msg = _seg(**kw)
     assert st == code, (st, msg)
     assert msg
+
+
+# ---- segmented prefill without allocation (host-side checks only) ----
+
+def _seg_noalloc(**kw):
+    args = dict(q=Q, k=K, v=V, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2, T=T,
+                H=H, d=D, in_dt=la.LA_BF16, out_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), kv_init=None, o=O, kv_final=KVF, seg=64)
+    args.update(kw)
+    cu = args["cu_host"]
+    st = la.la_prefill_segmented_noalloc(args["q"], args["k"], args["v"], args["cu_dev"],
+                                         None if cu is None else cu.ctypes.data, args["S"],
+                                         args["T"], args["H"], args["d"], args["in_dt"],
+                                         args["out_dt"], args["decay"].ctypes.data,
+                                         args["kv_init"], args["o"], args["kv_final"],
+                                         args["seg"], None)
+    return st, la.la_last_error()
+
+
+BAD_SEGMENTED_NOALLOC = [b for b in BAD_SEGMENTED if not b[0].startswith("workspace")] + [
+    # 64 heads, d = 128: 1024 tokens in segments of 64 need 16 + 1 state sets
+    # of 4 MiB, above the 64 MiB scratch
+    ("scratch_too_small", dict(H=64, decay=np.full(64, 0.9, np.float32), T=1024, S=1,
+                               cu_host=np.array([0, 1024], np.int32)), la.LA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_SEGMENTED_NOALLOC,
+                         ids=[b[0] for b in BAD_SEGMENTED_NOALLOC])
+def test_segmented_noalloc_rejects(name, kw, code):
+    st, msg = _seg_noalloc(**kw)
+    assert st == code, (st, msg)
+    assert msg
+    if name == "scratch_too_small":
+        assert "scratch" in msg
+
+
+def test_segmented_noalloc_no_sequences():
+    st, _ = _seg_noalloc(S=0, T=0, cu_host=np.array([0], np.int32))
+    assert st == la.LA_OK
 
 
 # ---- decode on a state pool (host-side checks only) ----
