@@ -215,9 +215,11 @@ la_status la_prefill_segmented(const void* q, const void* k, const void* v,
  * Arguments, results and errors as la_prefill_segmented, without workspace
  * and workspace_bytes.  A call whose workspace
  * (la_prefill_segmented_workspace_size) would exceed the scratch returns
- * LA_ERR_UNSUPPORTED before anything is enqueued; at H = 64, d = 128 the
- * scratch holds (segments + sequences) <= 15.  Failing to look up the
- * scratch address is LA_ERR_HIP.
+ * LA_ERR_UNSUPPORTED before anything is enqueued; with d = 128 the scratch
+ * holds up to 511 (sequence, head) pairs whatever the segment count (e.g.
+ * 7 sequences of 64 heads), with d = 64 up to about 4000 (segment or
+ * sequence, head) pairs.  Failing to look up the scratch address is
+ * LA_ERR_HIP.
  *
  * Every call on one device shares that device's scratch, which keeps the
  * last call's contents (nothing in it needs to start at zero).  Calls that

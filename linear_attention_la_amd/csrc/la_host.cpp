@@ -213,18 +213,32 @@ la_status check_segment_len(int32_t segment_len) {
 }
 
 // Byte offsets of the segmented-prefill workspace sections (each 256 B
-// aligned): cu_seg [n+1], init_slot [n], final_slot [n], seq_first [S+1]
-// (int32), then fp32 states [(n + S), H, d, d], n = number of segments.
+// aligned): cu_seg [n+1], init_slot [n], final_slot [n], seq_first [S+1],
+// the control words of a chained-scan launch [2 + 2 S H] (int32), then fp32
+// states: [(n + S), H, d, d] for the four-kernel path (n = number of
+// segments), or the scan's exchange ring [2 S H, d, d] when `scan` is set.
 struct SegmentLayout {
   int32_t num_segments;
   int32_t segment_len;
-  size_t cu_seg, init_slot, final_slot, seq_first, states, total;
+  size_t cu_seg, init_slot, final_slot, seq_first, ctrl, states, total;
+  int64_t ctrl_words;
 };
+
+// The forward segmented prefill runs the chained scan (one launch of the
+// one-workgroup-per-item kernel) for d = 128 and the four-kernel path for
+// d = 64.
+bool scan_path(int32_t head_dim) { return head_dim == 128; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Polls of one chained-scan wait before it gives up (each poll reads the
+// flag from memory and sleeps ~64 cycles: about a second in all).  A wait
+// only ever waits for a workgroup that has already started, so in a correct
+// run it ends long before this.
+constexpr int32_t kScanSpinLimit = 1 << 21;
+
 la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
-                         int32_t head_dim, int32_t segment_len, SegmentLayout* lay) {
+                         int32_t head_dim, int32_t segment_len, bool scan, SegmentLayout* lay) {
   int64_t n = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int64_t len = (int64_t)cu[s + 1] - cu[s];
@@ -243,8 +257,12 @@ la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
   off = align256(off + (size_t)n * 4);
   lay->seq_first = off;
   off = align256(off + (size_t)(num_seqs + 1) * 4);
+  lay->ctrl = off;
+  lay->ctrl_words = la::scan_ctrl_words((int64_t)num_seqs * num_heads);
+  off = align256(off + (size_t)lay->ctrl_words * 4);
   lay->states = off;
-  off += (size_t)(n + num_seqs) * num_heads * head_dim * head_dim * 4;
+  const int64_t slots = scan ? 2 * (int64_t)num_seqs : n + num_seqs;
+  off += (size_t)slots * num_heads * head_dim * head_dim * 4;
   lay->total = off;
   return LA_OK;
 }
@@ -439,7 +457,8 @@ la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* c
   if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
   if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
   SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len,
+                           scan_path(head_dim), &lay)) != LA_OK)
     return st;
   *bytes = lay.total;
   return ok();
@@ -471,6 +490,8 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
   int32_t* start_slot = reverse ? final_slot : init_slot;  // state entering a segment
   int32_t* local_slot = reverse ? init_slot : final_slot;  // its local state
 
+  int32_t* ctrl = reinterpret_cast<int32_t*>(ws + lay.ctrl);
+
   la::PrefillArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
@@ -481,12 +502,31 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
   a.num_heads = num_heads;
   a.num_items = lay.num_segments * num_heads * (head_dim / la::kBf16Cols);
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
+  hipError_t e;
+  if (scan_path(head_dim) && !reverse && !outputs_only) {
+    // the plan (which zeroes the control words), then one launch of the
+    // chained scan
+    e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, lay.segment_len, cu_seg, init_slot,
+                                final_slot, seq_first, ctrl, lay.ctrl_words, s);
+    if (e != hipSuccess) return hip_status(e, "segmented plan launch");
+    la::ScanArgs sa;
+    sa.init_slot = init_slot;
+    sa.seq_first = seq_first;
+    sa.kv_init = kv_init;
+    sa.kv_final = kv_final;
+    sa.ctrl = ctrl;
+    sa.ring = states;
+    sa.spin_limit = kScanSpinLimit;
+    a.o = o;
+    a.num_items = lay.num_segments * num_heads;
+    e = la::launch_prefill_scan(a, sa, out_dtype, s);
+    return hip_status(e, "segmented scan launch");
+  }
   const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
   if (wide) a.num_items = lay.num_segments * num_heads;
-  hipError_t e;
   if (!outputs_only) {
     e = la::launch_segment_plan(cu_seqlens_dev, num_seqs, lay.segment_len, cu_seg, init_slot,
-                                final_slot, seq_first, s);
+                                final_slot, seq_first, nullptr, 0, s);
     if (e != hipSuccess) return hip_status(e, "segmented plan launch");
 
     // pass 1: local decayed state of every segment, from a zero state
@@ -577,7 +617,8 @@ la_status segmented_args(const void* q, const void* k, const void* v,
     *done = true;
     return ok();
   }
-  return segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, lay);
+  return segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len,
+                        scan_path(head_dim), lay);
 }
 
 // Scratch of la_prefill_segmented_noalloc: a static device array, so that
@@ -871,11 +912,21 @@ la_status la_prefill_backward_segmented_workspace_size(int32_t num_seqs,
                                                        const int32_t* cu_seqlens_host,
                                                        int32_t num_heads, int32_t head_dim,
                                                        int32_t segment_len, size_t* bytes) {
-  la_status st = la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads,
-                                                     head_dim, segment_len, bytes);
+  if (!bytes) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  la_status st = check_heads_dim(num_heads, head_dim);
   if (st != LA_OK) return st;
-  // the segment layout, then one set of S initial states
-  *bytes = align256(*bytes) + (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+  if ((st = check_segment_len(segment_len)) != LA_OK) return st;
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  // the four-kernel layout (the reverse-time chains need a state per segment
+  // boundary), then one set of S initial states
+  SegmentLayout lay;
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, false,
+                           &lay)) != LA_OK)
+    return st;
+  *bytes = align256(lay.total) + (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
   return ok();
 }
 
@@ -892,7 +943,8 @@ la_status la_prefill_backward_segmented(
     return st;
   if (num_seqs == 0) return ok();
   SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, &lay)) != LA_OK)
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, false,
+                           &lay)) != LA_OK)
     return st;
   const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
   const size_t init_off = align256(lay.total);

@@ -62,6 +62,27 @@ struct DecodeArgs {
   float decay[LA_MAX_HEADS];
 };
 
+// Chained-scan prefill (la_prefill_wide.hip, d = 128, bf16): one launch over
+// the segments of a segment plan (see launch_segment_plan), a.cu_seqlens
+// being the plan's cu_seg and a.num_items = segments * H.  Workgroup items
+// (segment, head) compute their segment's local state, take the state
+// entering the segment from the item of the previous segment (a chained
+// exchange through `ring`, two slots of d x d fp32 per (sequence, head)),
+// publish the state entering the next one, then write their outputs.
+struct ScanArgs {
+  const int32_t* init_slot;  // plan: init_slot[g] = g + (sequence of g)
+  const int32_t* seq_first;  // plan: first segment of each sequence, [S+1]
+  const float* kv_init;      // [S, H, d, d] or nullptr (zeros)
+  float* kv_final;           // [S, H, d, d] or nullptr
+  int32_t* ctrl;             // ticket, error word, 2 flags per chain; zero on entry
+  float* ring;               // [S * H * 2][d * d]
+  int32_t spin_limit;        // polls before a wait gives up (sets the error word)
+};
+
+// Control words of a scan launch: the ticket, the error word and 2 flags per
+// (sequence, head) chain.
+inline int64_t scan_ctrl_words(int64_t chains) { return 2 + 2 * chains; }
+
 // Each returns hipSuccess or the launch error.  The caller has validated
 // every argument.
 // state_only: compute and write only the final states (no O): K and V are
@@ -76,6 +97,9 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, la_dtype out_
 hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool state_only,
                                bool reverse, hipStream_t stream);
 
+hipError_t launch_prefill_scan(const PrefillArgs& a, const ScanArgs& sa, la_dtype out_dtype,
+                               hipStream_t stream);
+
 // out[s,h] = scale[h] * (transpose ? in[s,h]^T : in[s,h]) for num_states x H
 // fp32 d x d states (la_state.hip); out may be in only without transpose.
 hipError_t launch_state_transform(const float* in, float* out, int32_t num_states,
@@ -87,9 +111,12 @@ hipError_t launch_state_transform(const float* in, float* out, int32_t num_state
 // seq_first [S+1] (first segment of each sequence) for a state workspace
 // holding n_seg + S slots: sequence s owns slots seq_first[s] + s ..
 // seq_first[s] + s + n_s.
+// The plan also zeroes ctrl[0 .. ctrl_words) (the control words of a scan
+// launch; ctrl may be nullptr).
 hipError_t launch_segment_plan(const int32_t* cu_seqlens, int32_t num_seqs, int32_t segment_len,
                                int32_t* cu_seg, int32_t* init_slot, int32_t* final_slot,
-                               int32_t* seq_first, hipStream_t stream);
+                               int32_t* seq_first, int32_t* ctrl, int64_t ctrl_words,
+                               hipStream_t stream);
 // Prefix over segments: slot 0 of each sequence <- kv_init (or 0); slot i+1
 // <- lambda^len_i * slot i + slot i+1 (which holds segment i's local
 // state); the last slot is also written to kv_final (if not null).  With

@@ -115,13 +115,38 @@ struct Chain {
   float init_pow, final_pow;
 };
 
+// The LDS arrays of one chain (declared by each kernel, so that two passes
+// of one kernel can share them); a state-only pass uses Ks and Vs alone.
+struct Lds {
+  uint16_t* Qs;  // [2][64][128]
+  uint16_t* Ks;  // [2][64][128]
+  uint16_t* Vs;  // [2][64][128]
+  uint16_t* Ph;  // [64][64]
+  uint16_t* Pl;  // [64][64]
+};
+
+// Thread t's place in the state: wave w owns value columns [16w, 16w+16) and
+// tile n of its eight 16 x 16 accumulator tiles holds key rows srow(n, g) + m
+// (m = 0..3) of column 16w + li, with li = lane % 16 and g = lane / 16.
+struct StatePos {
+  int c0, li, g;
+  __device__ explicit StatePos(int t) : c0(16 * uniform(t >> 6)), li(t & 15), g((t & 63) >> 4) {}
+  __device__ int row(int n, int m) const { return srow(n, g) + m; }
+  __device__ int col() const { return c0 + li; }
+};
+
+// Runs the blocks of chain c with the state st (fp32, held in registers;
+// updated in place): with kStateOnly only the state advances (K and V are
+// read, Q is not, O is not written).  Starts with an LDS write, so a caller
+// that used the LDS arrays before must have passed a workgroup barrier.
 template <bool kOutF32, bool kStateOnly>
-__device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c) {
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kStateOnly ? 8 : 2 * kTok];
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * kTok];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * kTok];
-  __shared__ __attribute__((aligned(16))) uint16_t Ph[kStateOnly ? 8 : kBeta * kBeta];
-  __shared__ __attribute__((aligned(16))) uint16_t Pl[kStateOnly ? 8 : kBeta * kBeta];
+__device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c, const Lds& sm,
+                                            floatx4 (&st)[8]) {
+  uint16_t* const Qs = sm.Qs;
+  uint16_t* const Ks = sm.Ks;
+  uint16_t* const Vs = sm.Vs;
+  uint16_t* const Ph = sm.Ph;
+  uint16_t* const Pl = sm.Pl;
 
   const int H = a.num_heads;
   const int h = c.h;
@@ -142,8 +167,6 @@ __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c)
   const int row_stride = H * kD;
   const float l2 = a.log2_decay[h];
   const float lam_beta = exp2f((float)kBeta * l2);
-  const int64_t init_off = ((int64_t)(a.init_slot ? a.init_slot[s] : s) * H + h) * kD * kD;
-  const int64_t final_off = ((int64_t)(a.final_slot ? a.final_slot[s] : s) * H + h) * kD * kD;
 
   auto block_len = [&](int b) -> int {
     const int64_t rem = end - (start + (int64_t)b * kBeta);
@@ -163,21 +186,6 @@ __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c)
     return buf_rsrc(p, ell * row_stride * esize);
   };
   auto prow = [&](int r, int ell) { return c.reverse ? ell - 1 - r : r; };
-
-  // ---- state: tile n holds key rows srow(n, g) + m, column c0 + li ----
-  floatx4 st[8];
-  const float init_scale = c.init_pow == 0.0f ? 1.0f : exp2f(c.init_pow * l2);
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    st[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (c.kv_init) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        st[n][m] = init_scale * (c.init_transposed
-                                     ? c.kv_init[init_off + (int64_t)(c0 + li) * kD + srow(n, g) + m]
-                                     : c.kv_init[init_off + (int64_t)(srow(n, g) + m) * kD + c0 + li]);
-    }
-  }
 
   // ---- per-lane decay factors ----
   // Score unit of this wave (waves 0..5): query tile qt, keys 32 kk2 .. +31
@@ -450,15 +458,55 @@ __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c)
     }
   }
 
+}
+
+// One whole chain: the state from kv_init[s, h] (slot map, transposition
+// and scale as the chain asks) or zeros, the blocks, then the final state to
+// kv_final[s, h].
+template <bool kOutF32, bool kStateOnly>
+__device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c, const Lds& sm) {
+  const int H = a.num_heads;
+  const int h = c.h;
+  const int s = c.s;
+  const StatePos sp(threadIdx.x);
+  const float l2 = a.log2_decay[h];
+  const int64_t init_off = ((int64_t)(a.init_slot ? a.init_slot[s] : s) * H + h) * kD * kD;
+  const int64_t final_off = ((int64_t)(a.final_slot ? a.final_slot[s] : s) * H + h) * kD * kD;
+
+  floatx4 st[8];
+  const float init_scale = c.init_pow == 0.0f ? 1.0f : exp2f(c.init_pow * l2);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    st[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (c.kv_init) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        st[n][m] = init_scale * (c.init_transposed
+                                     ? c.kv_init[init_off + (int64_t)sp.col() * kD + sp.row(n, m)]
+                                     : c.kv_init[init_off + (int64_t)sp.row(n, m) * kD + sp.col()]);
+    }
+  }
+
+  wide_blocks<kOutF32, kStateOnly>(a, c, sm, st);
+
   if (c.kv_final) {
     const float final_scale = c.final_pow == 0.0f ? 1.0f : exp2f(c.final_pow * l2);
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        c.kv_final[final_off + (int64_t)(srow(n, g) + m) * kD + c0 + li] = final_scale * st[n][m];
+        c.kv_final[final_off + (int64_t)sp.row(n, m) * kD + sp.col()] = final_scale * st[n][m];
   }
 }
+
+// LDS of a full chain (kStateOnly: of a state-only chain).
+#define LA_WIDE_LDS(kStateOnly)                                                       \
+  __shared__ __attribute__((aligned(16))) uint16_t Qs_[(kStateOnly) ? 8 : 2 * kTok];  \
+  __shared__ __attribute__((aligned(16))) uint16_t Ks_[2 * kTok];                     \
+  __shared__ __attribute__((aligned(16))) uint16_t Vs_[2 * kTok];                     \
+  __shared__ __attribute__((aligned(16))) uint16_t Ph_[(kStateOnly) ? 8 : kBeta * kBeta]; \
+  __shared__ __attribute__((aligned(16))) uint16_t Pl_[(kStateOnly) ? 8 : kBeta * kBeta]; \
+  const Lds sm{Qs_, Ks_, Vs_, Ph_, Pl_}
 
 // Prefill: workgroup i runs the chain of head i % H of the (i / H)-th
 // sequence in dispatch order, forwards in time (or backwards, kReverse).
@@ -477,7 +525,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   c.init_transposed = false;
   c.init_pow = 0.0f;
   c.final_pow = 0.0f;
-  wide_chain<kOutF32, kStateOnly>(a, c);
+  LA_WIDE_LDS(kStateOnly);
+  wide_chain<kOutF32, kStateOnly>(a, c, sm);
 }
 
 // The three chains of the backward pass in one launch: item i runs pass
@@ -502,7 +551,172 @@ __global__ __launch_bounds__(kThreads) void backward_wide_kernel(PrefillArgs a, 
   c.init_transposed = p.init_transposed != 0;
   c.init_pow = p.init_pow;
   c.final_pow = p.final_pow;
-  wide_chain<kOutF32, false>(a, c);
+  LA_WIDE_LDS(false);
+  wide_chain<kOutF32, false>(a, c, sm);
+}
+
+// ---- the chained scan over segments (one launch) ----
+//
+// A sequence cut into segments runs as independent (segment, head) items,
+// so that few long sequences still fill the GPU.  Item (segment i of a
+// sequence, head h), one workgroup:
+//   A  the local decayed state of the segment, Shat_i = sum_j
+//      lambda^(len_i - 1 - j) k_j^T v_j, by a state-only pass from zero
+//      (skipped for the last segment, whose state no later segment needs);
+//   B  the state entering the segment, E_i: kv_init (or zero) for i = 0, else
+//      read from item i - 1, which publishes E_(i-1) ... as
+//      P_(i-1) = lambda^(len_(i-1)) E_(i-1) + Shat_(i-1) = E_i; the item then
+//      publishes its own P_i;
+//   C  the full blocks of the segment from E_i (O written), and for the last
+//      segment the final state.
+// This is the local-prefix-sum exchange of the LASP+ sequence split (mizuki
+// blog "MiniMax-01：4M 上下文破局", 五) chained inside one launch: only the
+// small step B is serial, and an item waits in it only for its predecessor.
+//
+// Progress.  Items are handed out in the order in which workgroups start (a
+// ticket counter), item (g, h) of global segment g being ticket g H + h, and
+// an item waits only for the item of the previous segment of its sequence,
+// ticket g H + h - H: a workgroup that has already started, whose own wait
+// is for a smaller ticket again.  So every wait ends whatever order the
+// hardware starts workgroups in and however many of them are resident.  A
+// wait is also bounded (spin_limit polls); a wait that runs out sets the
+// error word, after which every wait ends at once (results are then
+// invalid).
+//
+// Exchange.  P_i goes to one of two ring slots of its chain (sequence, head),
+// slot i % 2, in register order; the flag of the slot then receives i + 1.
+// Item i + 1 polls that flag for i + 1, then reads the slot.  Every access to
+// the ring and the flags is a device-scope access (sc1 buffer loads and
+// stores, agent-scope atomics for the flags: they read from and write to the
+// device's coherence point, past the per-XCD L2), and the flag store is
+// issued only after every wave's
+// ring stores have completed (a wait for the wave's stores, then a workgroup
+// barrier).  No cache-wide maintenance is needed: an agent-scope release or
+// acquire fence would write back or invalidate a whole L2 per wave, which on
+// 32 workgroups of one XCD publishing at once serialises into tens of
+// microseconds.  Two slots suffice: item i writes slot i % 2 only after
+// reading P_(i-1), which item i - 1 published only after it had read
+// P_(i-2) from the slot being overwritten.  The plan kernel zeroes the
+// ticket, the error word and the flags before each launch.
+
+// Cache policy of a buffer access at device scope (sc1): it reads from and
+// writes to the device's coherence point rather than one XCD's L2.
+constexpr int kCpolSc1 = 16;
+
+// Control words of the scan workspace.
+constexpr int kCtrlTicket = 0;
+constexpr int kCtrlError = 1;
+constexpr int kCtrlFlags = 2;  // then 2 flags per (sequence, head) chain
+
+template <bool kOutF32>
+__global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a, ScanArgs sa) {
+  LA_WIDE_LDS(false);
+  __shared__ int32_t ticket_s;
+  const int t = threadIdx.x;
+  if (t == 0)
+    ticket_s = __hip_atomic_fetch_add(sa.ctrl + kCtrlTicket, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int item = uniform(ticket_s);
+  const int H = a.num_heads;
+  const int g = item / H;                 // global segment
+  const int h = item - g * H;
+  const int s = sa.init_slot[g] - g;      // its sequence (the plan's slot of g is g + s)
+  const int i = g - sa.seq_first[s];      // its index in the sequence
+  const bool last = g + 1 == sa.seq_first[s + 1];
+  const int chain = s * H + h;
+  const float l2 = a.log2_decay[h];
+  const StatePos sp(t);
+
+  Chain c;
+  c.q = a.q;
+  c.k = a.k;
+  c.v = a.v;
+  c.o = a.o;
+  c.kv_init = nullptr;
+  c.kv_final = nullptr;
+  c.s = g;  // rows of segment g: a.cu_seqlens is the plan's cu_seg
+  c.h = h;
+  c.reverse = false;
+  c.init_transposed = false;
+  c.init_pow = 0.0f;
+  c.final_pow = 0.0f;
+
+  // A: the segment's local state
+  floatx4 loc[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) loc[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (!last) wide_blocks<false, true>(a, c, sm, loc);
+
+  // B: the state entering the segment
+  floatx4 st[8];
+  // ring slot x of this chain (d x d fp32, thread t's tile n at float4
+  // n * 512 + t), accessed at device scope
+  auto slot_rsrc = [&](int x) {
+    return buf_rsrc(sa.ring + ((int64_t)chain * 2 + x) * (kD * kD), kD * kD * 4);
+  };
+  if (i == 0) {
+    const int64_t off = (int64_t)chain * kD * kD;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      st[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (sa.kv_init) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) st[n][m] = sa.kv_init[off + (int64_t)sp.row(n, m) * kD + sp.col()];
+      }
+    }
+  } else {
+    int32_t* flag = sa.ctrl + kCtrlFlags + 2 * chain + ((i - 1) & 1);
+    if (t == 0) {
+      for (int polls = 0;; ++polls) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == i) break;
+        if ((polls & 255) == 255 &&
+            (polls > sa.spin_limit ||
+             __hip_atomic_load(sa.ctrl + kCtrlError, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+          __hip_atomic_store(sa.ctrl + kCtrlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    // the ring is read only after the flag was seen (a workgroup-scope
+    // acquire keeps the loads below the barrier)
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const __amdgpu_buffer_rsrc_t src = slot_rsrc((i - 1) & 1);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      st[n] = __builtin_bit_cast(
+          floatx4, __builtin_amdgcn_raw_buffer_load_b128(src, 16 * (n * kThreads + t), 0, kCpolSc1));
+  }
+  if (!last) {
+    const int len = a.cu_seqlens[g + 1] - a.cu_seqlens[g];
+    const float f = exp2f((float)len * l2);  // lambda^len
+    const __amdgpu_buffer_rsrc_t dst = slot_rsrc(i & 1);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st[n] * f + loc[n]), dst,
+                                             16 * (n * kThreads + t), 0, kCpolSc1);
+    // every wave waits for its ring stores to complete (a workgroup-scope
+    // release does not wait for them on this target), then one flag store
+    // for the workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t == 0)
+      __hip_atomic_store(sa.ctrl + kCtrlFlags + 2 * chain + (i & 1), i + 1, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+
+  // C: the segment's outputs from its start state
+  wide_blocks<kOutF32, false>(a, c, sm, st);
+  if (last && sa.kv_final) {
+    const int64_t off = (int64_t)chain * kD * kD;
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sa.kv_final[off + (int64_t)sp.row(n, m) * kD + sp.col()] = st[n][m];
+  }
 }
 
 }  // namespace
@@ -533,6 +747,16 @@ hipError_t launch_backward_wide(const PrefillArgs& a, const BackwardPasses& bp,
     hipLaunchKernelGGL(backward_wide_kernel<true>, grid, block, 0, stream, a, bp);
   else
     hipLaunchKernelGGL(backward_wide_kernel<false>, grid, block, 0, stream, a, bp);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_scan(const PrefillArgs& a, const ScanArgs& sa, la_dtype out_dtype,
+                               hipStream_t stream) {
+  const dim3 grid(a.num_items), block(kThreads);
+  if (out_dtype == LA_FP32)
+    hipLaunchKernelGGL(prefill_scan_kernel<true>, grid, block, 0, stream, a, sa);
+  else
+    hipLaunchKernelGGL(prefill_scan_kernel<false>, grid, block, 0, stream, a, sa);
   return hipGetLastError();
 }
 

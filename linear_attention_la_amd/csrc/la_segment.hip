@@ -31,9 +31,12 @@ __device__ __forceinline__ int segments_of(int32_t len, int32_t segment_len) {
 // sum of the per-thread segment counts gives each thread its first segment.
 __global__ __launch_bounds__(kPlanThreads) void segment_plan_kernel(
     const int32_t* __restrict__ cu, int32_t num_seqs, int32_t segment_len, int32_t* cu_seg,
-    int32_t* init_slot, int32_t* final_slot, int32_t* seq_first) {
+    int32_t* init_slot, int32_t* final_slot, int32_t* seq_first, int32_t* ctrl,
+    int64_t ctrl_words) {
   __shared__ int32_t part[kPlanThreads];
   const int t = threadIdx.x;
+  if (ctrl)
+    for (int64_t x = t; x < ctrl_words; x += kPlanThreads) ctrl[x] = 0;
   const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
   const int s0 = min(num_seqs, t * per);
   const int s1 = min(num_seqs, s0 + per);
@@ -123,9 +126,11 @@ __global__ __launch_bounds__(256) void segment_prefix_kernel(PrefixArgs a, int64
 
 hipError_t launch_segment_plan(const int32_t* cu_seqlens, int32_t num_seqs, int32_t segment_len,
                                int32_t* cu_seg, int32_t* init_slot, int32_t* final_slot,
-                               int32_t* seq_first, hipStream_t stream) {
+                               int32_t* seq_first, int32_t* ctrl, int64_t ctrl_words,
+                               hipStream_t stream) {
   hipLaunchKernelGGL(segment_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_seqlens,
-                     num_seqs, segment_len, cu_seg, init_slot, final_slot, seq_first);
+                     num_seqs, segment_len, cu_seg, init_slot, final_slot, seq_first, ctrl,
+                     ctrl_words);
   return hipGetLastError();
 }
 

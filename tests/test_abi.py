@@ -195,15 +195,27 @@ def _ws_size(cu, H=4, d=128, seg=64):
 
 
 def test_segmented_workspace_size_layout():
-    """8 segments (lengths 100, 0, 300 at 64 tokens each: 2 + 1 + 5), 4
-    sections of int32 padded to 256 B, then (8 + 3) fp32 states of 4 x 128^2."""
+    """8 segments (lengths 100, 0, 300 at 64 tokens each: 2 + 1 + 5): 4
+    sections of int32 and the control words (2 + 2 S H) padded to 256 B,
+    then fp32 states: d = 128 runs the chained scan, whose exchange ring holds
+    2 states per (sequence, head) (2 x 3 x 4 of 128^2); d = 64 runs the
+    four-kernel path with (8 + 3) states per head."""
     st, n = _ws_size([0, 100, 100, 400])
     assert st == la.LA_OK
-    assert n == 4 * 256 + 11 * 4 * 128 * 128 * 4
+    assert n == 5 * 256 + 2 * 3 * 4 * 128 * 128 * 4
+    st, n = _ws_size([0, 100, 100, 400], d=64)
+    assert st == la.LA_OK
+    assert n == 5 * 256 + 11 * 4 * 64 * 64 * 4
     st, n = _ws_size([0, 64], seg=64)       # exactly one segment
-    assert st == la.LA_OK and n == 4 * 256 + 2 * 4 * 128 * 128 * 4
+    assert st == la.LA_OK and n == 5 * 256 + 2 * 4 * 128 * 128 * 4
     st, n = _ws_size([0], seg=64)           # no sequences: the empty slot sections take no space
-    assert st == la.LA_OK and n == 2 * 256
+    assert st == la.LA_OK and n == 3 * 256
+    # 64 sequences of one segment x 64 heads: cu_seg and seq_first (65 words)
+    # take 512 B each, the slot maps 256 B, 8194 control words 33,024 B
+    cu = np.arange(0, 65 * 64, 64, dtype=np.int32)
+    st, n = _ws_size(cu, H=64, seg=64)
+    assert st == la.LA_OK
+    assert n == 2 * 512 + 2 * 256 + 33024 + 2 * 64 * 64 * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("seg", [0, -64, 100, 63])
@@ -276,10 +288,15 @@ def _seg_noalloc(**kw):
 
 
 BAD_SEGMENTED_NOALLOC = [b for b in BAD_SEGMENTED if not b[0].startswith("workspace")] + [
-    # 64 heads, d = 128: 1024 tokens in segments of 64 need 16 + 1 state sets
-    # of 4 MiB, above the 64 MiB scratch
-    ("scratch_too_small", dict(H=64, decay=np.full(64, 0.9, np.float32), T=1024, S=1,
-                               cu_host=np.array([0, 1024], np.int32)), la.LA_ERR_UNSUPPORTED),
+    # d = 128 (the chained scan): 9 sequences x 64 heads need 2 exchange
+    # states per (sequence, head), 72 MiB, above the 64 MiB scratch
+    ("scratch_too_small", dict(H=64, decay=np.full(64, 0.9, np.float32), T=9, S=9,
+                               cu_host=np.arange(10, dtype=np.int32)), la.LA_ERR_UNSUPPORTED),
+    # d = 64 (four-kernel path): 16,384 tokens in segments of 64 need
+    # (256 + 1) x 64 states of 16 KiB, 257 MiB
+    ("scratch_too_small_d64", dict(H=64, d=64, decay=np.full(64, 0.9, np.float32), T=16384,
+                                   S=1, cu_host=np.array([0, 16384], np.int32)),
+     la.LA_ERR_UNSUPPORTED),
 ]
 
 
@@ -289,7 +306,7 @@ def test_segmented_noalloc_rejects(name, kw, code):
     st, msg = _seg_noalloc(**kw)
     assert st == code, (st, msg)
     assert msg
-    if name == "scratch_too_small":
+    if name.startswith("scratch_too_small"):
         assert "scratch" in msg
 
 
