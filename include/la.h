@@ -167,9 +167,6 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
  *   segment_len      tokens per segment, a positive multiple of 64; the last
  *                    segment of a sequence may be shorter.  A sequence of L
  *                    tokens gives max(1, ceil(L / segment_len)) segments.
- *                    With d = 128, a length that makes segments x heads at
- *                    least the device's compute-unit count runs both passes
- *                    one workgroup per (segment, head) (see la_prefill).
  *   workspace        device scratch of at least the size that
  *                    la_prefill_segmented_workspace_size reports for the same
  *                    num_seqs, cu_seqlens_host, num_heads, head_dim and
@@ -186,9 +183,18 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
  * the prefill from its start state.  K and V are read twice.  in_dtype must
  * be LA_BF16 (LA_FP32 is LA_ERR_UNSUPPORTED).  Errors as la_prefill, plus
  * LA_ERR_INVALID_ARG for a bad segment_len or a NULL, misaligned, short or
- * overlapping workspace.  Four kernels are enqueued on `stream`; nothing
- * synchronises.  The two passes over the segments choose their kernel as
- * la_prefill does, counting (segment, head) pairs.
+ * overlapping workspace.  Nothing synchronises.
+ *
+ * d = 128: two kernels are enqueued on `stream` -- a one-workgroup plan, then
+ * one launch in which every (segment, head) item computes its segment's local
+ * state, receives the state entering the segment from the item of the
+ * previous segment of its sequence (through the workspace, at device scope),
+ * passes the state entering the next segment on, and writes its outputs.
+ * An item only ever waits for an item that has already started, so the
+ * launch always completes; its workspace holds 2 states per (sequence, head)
+ * whatever the segment count.  d = 64: four kernels (plan, a state-only pass
+ * over all segments, the prefix over them, the output pass); the workspace
+ * holds one state per segment and per sequence.
  */
 la_status la_prefill_segmented(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
