@@ -232,7 +232,19 @@ def bench_decode_pool(dev, reps=20, pool_size=1024):
             "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def bench_mixed(dev, dec_state, reps=10):
+def bench_mixed(dev, dec_state, reps=10, warmup=2):
+    """The mixed serving step: the 256 x 64 decode batch (la_decode) and a
+    packed prefill of 8 sequences of U[1K, 32K] tokens (la_prefill, the
+    one-workgroup-per-chain kernel) on two streams.  Run with either kernel
+    submitted first, and with the decode arriving ~0.2 ms after the prefill
+    has started (``prefill_running``), on plain streams and on streams
+    restricted to disjoint compute units (decode 1/8 or 1/4 of them, prefill
+    the rest).  Per variant:
+    ``warmup`` untimed steps, then ``reps`` steps timed by HIP events on the
+    two streams against one start event both wait for: each kernel's time
+    from its submission point, and the step's time to the later of the two
+    ends.  ``step_frac_of_8TBs`` is the step's algorithmic bytes (decode and
+    prefill together) over its time."""
     import torch
 
     import linear_attention_la_amd as la
@@ -243,37 +255,116 @@ def bench_mixed(dev, dec_state, reps=10):
     wp = workload("mixed_prefill")
     cu = cu_seqlens(wp["lengths"])
     T = int(cu[-1])
+    S = len(wp["lengths"])
     qp, kp, vp = device_qkv(T, H, D, wp["seed"], dev)
     cu_dev = torch.from_numpy(cu).to(dev)
     op = torch.empty_like(qp)
-    kvp = torch.empty((len(wp["lengths"]), H, D, D), dtype=torch.float32, device=dev)
-    sp, sd = torch.cuda.Stream(), torch.cuda.Stream()
-    ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-          for n in ("p0", "p1", "d0", "d1")}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    # The decode step is submitted first: it is the short, latency-bound
-    # kernel of a serving step, and submitted first it takes the CUs before
-    # the prefill's workgroups fill them (submitted second it waits for
-    # prefill workgroups to drain and runs ~5x slower; the prefill's time is
-    # the same either way).
-    for i in range(reps):
-        ev["d0"][i].record(sd)
+    kvp = torch.empty((S, H, D, D), dtype=torch.float32, device=dev)
+    step_bytes = decode_bytes(B) + prefill_bytes(T, S)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    full = (1 << n_cu) - 1
+    dec8, dec4 = (1 << (n_cu // 8)) - 1, (1 << (n_cu // 4)) - 1
+    streams = {"plain": (torch.cuda.Stream(), torch.cuda.Stream()),
+               "cu_masked_8th": (la.cu_masked_stream(full & ~dec8), la.cu_masked_stream(dec8)),
+               "cu_masked_4th": (la.cu_masked_stream(full & ~dec4), la.cu_masked_stream(dec4))}
+    main = torch.cuda.current_stream()
+
+    def dec(sd):
         la.decode(q, k, v, kv, wd["decay"], stream=sd, out=out)
-        ev["d1"][i].record(sd)
-        ev["p0"][i].record(sp)
+
+    def pre(sp):
         la.prefill(qp, kp, vp, cu_dev, wp["decay"], stream=sp, out=op, kv_final=kvp,
                    cu_seqlens_host=cu)
-        ev["p1"][i].record(sp)
-        torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / reps
-    tp = sum(a.elapsed_time(b) for a, b in zip(ev["p0"], ev["p1"])) / reps / 1e3
-    td = sum(a.elapsed_time(b) for a, b in zip(ev["d0"], ev["d1"])) / reps / 1e3
-    return {"prefill_seqs": len(wp["lengths"]), "prefill_tokens": T, "decode_batch": B,
-            "prefill_us": round(tp * 1e6, 1), "decode_us_under_load": round(td * 1e6, 1),
-            "decode_GB_per_s_under_load": round(decode_bytes(B) / td / 1e9, 1),
-            "prefill_tokens_per_s_under_load": round(T / tp, 0),
-            "step_wall_us": round(wall * 1e6, 1)}
+
+    # each kernel alone, same protocol
+    alone = {}
+    for name, fn in (("decode", dec), ("prefill", pre)):
+        for _ in range(warmup):
+            fn(main)
+        alone[name] = timed_launches(lambda i: fn(main), reps, main)
+    res = {"prefill_seqs": S, "prefill_tokens": T, "decode_batch": B,
+           "step_bytes": step_bytes, "compute_units": n_cu,
+           "decode_alone_us": round(alone["decode"] * 1e6, 1),
+           "prefill_alone_us": round(alone["prefill"] * 1e6, 1),
+           "serial_sum_us": round((alone["decode"] + alone["prefill"]) * 1e6, 1)}
+    # cycles of torch's spin kernel that hold the decode back until the
+    # prefill's workgroups occupy the GPU (about 0.2 ms)
+    late_cycles = 400_000
+    for sname, (sp, sd) in streams.items():
+        for first in ("decode", "prefill", "prefill_running"):
+            if first == "decode":
+                order = lambda: (dec(sd), pre(sp))  # noqa: E731
+            elif first == "prefill":
+                order = lambda: (pre(sp), dec(sd))  # noqa: E731
+            else:
+                order = None
+            decode_first = first == "decode"
+            ev = {n: [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+                  for n in ("s", "d0", "d1", "p0", "p1")}
+            for it in range(warmup + reps):
+                i = it - warmup
+                if i >= 0:
+                    ev["s"][i].record(main)
+                    sd.wait_event(ev["s"][i])
+                    sp.wait_event(ev["s"][i])
+                else:
+                    sd.wait_stream(main)
+                    sp.wait_stream(main)
+                if order is not None:
+                    if i >= 0:
+                        ev["d0"][i].record(sd)
+                        ev["p0"][i].record(sp)
+                    order()
+                else:  # the decode arrives while the prefill runs
+                    if i >= 0:
+                        ev["p0"][i].record(sp)
+                    pre(sp)
+                    with torch.cuda.stream(sd):
+                        torch.cuda._sleep(late_cycles)
+                    if i >= 0:
+                        ev["d0"][i].record(sd)
+                    dec(sd)
+                if i >= 0:
+                    ev["d1"][i].record(sd)
+                    ev["p1"][i].record(sp)
+                main.wait_stream(sd)
+                main.wait_stream(sp)
+            torch.cuda.synchronize()
+            t = {n: np.array([ev["s"][i].elapsed_time(ev[n][i]) for i in range(reps)]) * 1e3
+                 for n in ("d0", "d1", "p0", "p1")}
+            step = np.maximum(t["d1"], t["p1"])
+            dec_us = float(np.median(t["d1"] - t["d0"]))
+            del decode_first
+            res[f"{sname}_{first}" + ("" if first == "prefill_running" else "_first")] = {
+                "decode_us": round(dec_us, 1),
+                "prefill_us": round(float(np.median(t["p1"] - t["p0"])), 1),
+                "step_us": round(float(np.median(step)), 1),
+                "decode_vs_alone": round(dec_us / (alone["decode"] * 1e6), 3),
+                "step_frac_of_8TBs": round(step_bytes / float(np.median(step)) / 1e3 / HBM_PEAK_GBS,
+                                           4)}
+    # one stream, decode then prefill: the decode runs alone and the step is
+    # the serial sum
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for it in range(warmup + reps):
+        e = ev[it - warmup] if it >= warmup else None
+        if e:
+            e[0].record(main)
+        dec(main)
+        if e:
+            e[1].record(main)
+        pre(main)
+        if e:
+            e[2].record(main)
+    torch.cuda.synchronize()
+    d_us = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    st_us = float(np.median([e[0].elapsed_time(e[2]) for e in ev])) * 1e3
+    res["one_stream_decode_then_prefill"] = {
+        "decode_us": round(d_us, 1), "step_us": round(st_us, 1),
+        "decode_vs_alone": round(d_us / (alone["decode"] * 1e6), 3),
+        "step_frac_of_8TBs": round(step_bytes / st_us / 1e3 / HBM_PEAK_GBS, 4)}
+    del qp, kp, vp, op, kvp, streams
+    torch.cuda.empty_cache()
+    return res
 
 
 SWEEP = ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodecay", "n1m",
@@ -457,6 +548,8 @@ def main():
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time la_decode on the 256 x 64-head serving batch")
+    ap.add_argument("--mixed-only", action="store_true",
+                    help="only time the mixed serving step (decode beside a packed prefill)")
     ap.add_argument("--pool-only", action="store_true",
                     help="only time la_decode_pool (256 sequences on a pool of 1024)")
     ap.add_argument("--backward-only", action="store_true",
@@ -499,6 +592,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}))
+        return
+    if args.mixed_only:
+        la.lib()
+        _, dec_state = bench_decode(dev, reps=3)
+        print(json.dumps({"mixed": bench_mixed(dev, dec_state)}), flush=True)
         return
     if args.decode_only:
         la.lib()

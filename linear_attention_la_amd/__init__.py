@@ -12,6 +12,7 @@ library is missing, every call raises.
     o = decode(q, k, v, kv, decay)          # kv updated in place
     o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
     o = prefill_pool(q, k, v, cu_seqlens, decay, pool, slots)   # continues from pool[slots]
+    s = cu_masked_stream(mask)   # a stream restricted to some compute units (two-stream serving)
 """
 
 from ._binding import (  # noqa: F401
@@ -25,6 +26,7 @@ from ._binding import (  # noqa: F401
     LA_MAX_HEADS,
     lib,
     lib_path,
+    cu_masked_stream,
     la_prefill,
     la_prefill_segmented,
     la_prefill_segmented_noalloc,

@@ -222,6 +222,60 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_hip = None
+
+
+def _hip_runtime():
+    """The HIP runtime already loaded in this process (torch's, which libla
+    uses too: both name it by its soname)."""
+    global _hip
+    if _hip is None:
+        _torch()
+        _hip = ctypes.CDLL("libamdhip64.so.7")
+        _hip.hipExtStreamCreateWithCUMask.restype = ctypes.c_int
+        _hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint32,
+                                                     ctypes.POINTER(ctypes.c_uint32)]
+    return _hip
+
+
+_masked_streams = {}
+
+
+def cu_masked_stream(cu_mask, device=None):
+    """A HIP stream (default priority) whose kernels run only on the compute
+    units set in ``cu_mask`` (an int, bit i = compute unit i as the HIP
+    runtime numbers them), wrapped as a torch ExternalStream usable as
+    ``stream=`` of every call here.  Serving can give the latency-bound decode
+    and the prefill disjoint sets of compute units, so that neither waits for
+    the other's workgroups to drain.  One stream is created per (device,
+    mask) and reused; it lives until the process ends (it is never destroyed:
+    destroying it from a finaliser at interpreter exit would race the HIP
+    runtime's own teardown)."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None \
+        else torch.device(device)
+    m = int(cu_mask)
+    if m <= 0:
+        raise ValueError("cu_mask must select at least one compute unit")
+    key = (dev.index, m)
+    if key in _masked_streams:
+        return _masked_streams[key]
+    words = []
+    while m:
+        words.append(m & 0xFFFFFFFF)
+        m >>= 32
+    arr = (ctypes.c_uint32 * len(words))(*words)
+    handle = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        st = _hip_runtime().hipExtStreamCreateWithCUMask(ctypes.byref(handle), len(words), arr)
+    if st != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed with HIP error {st}")
+    stream = torch.cuda.ExternalStream(handle.value, device=dev)
+    _masked_streams[key] = stream
+    return stream
+
+
 def _host_decay(decay, num_heads):
     torch = _torch()
     if isinstance(decay, torch.Tensor):

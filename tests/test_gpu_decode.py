@@ -135,3 +135,72 @@ def test_two_streams_bitwise(dev):
         assert torch.equal(kv_a, kv_b)
         assert torch.equal(o_pre_a, o_pre_b)
         assert torch.equal(kv_pre_a, kv_pre_b)
+
+
+def test_serving_step_two_streams_oracle(dev):
+    """The mixed serving step -- the 256 x 64 decode batch beside a packed
+    prefill of 8 sequences of U[1K, 32K] tokens (the one-workgroup-per-chain
+    kernel) -- run concurrently on two streams, with either kernel submitted
+    first, on plain streams and on streams restricted to disjoint sets of
+    compute units: every run equals the solo run bit for bit, and the solo
+    run matches the oracle (three heads over all 8 prefill sequences, with
+    their final states; 50 sampled decode pairs)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    wp = workload("mixed_prefill")
+    wd = workload("mixed_decode")
+    B, H, d = wd["batch"], wd["H"], wd["d"]
+    cu = cu_seqlens(wp["lengths"])
+    T = int(cu[-1])
+    qp, kp, vp = device_qkv(T, H, d, wp["seed"], dev)
+    qd, kd, vd = (x.view(B, H, d) for x in device_qkv(B, H, d, wd["seed"] + 1, dev))
+    kv_init = device_states(B, H, d, wd["seed"], dev, scale=0.5)
+    cu_dev = torch.from_numpy(cu).to(dev)
+
+    kv_solo = kv_init.clone()
+    o_dec = la.decode(qd, kd, vd, kv_solo, wd["decay"])
+    o_pre, kv_pre = la.prefill(qp, kp, vp, cu_dev, wp["decay"])
+    torch.cuda.synchronize()
+
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_dec = max(1, n_cu // 8)
+    dec_mask = (1 << n_dec) - 1
+    pre_mask = ((1 << n_cu) - 1) & ~dec_mask
+    plain = (torch.cuda.Stream(), torch.cuda.Stream())
+    masked = (la.cu_masked_stream(pre_mask), la.cu_masked_stream(dec_mask))
+    for name, (sp, sd) in (("plain", plain), ("cu-masked", masked)):
+        for decode_first in (True, False):
+            say(f"serving step: {name} streams, decode first={decode_first}")
+            kv_b = kv_init.clone()
+            o_pre_b, kv_pre_b = torch.empty_like(o_pre), torch.empty_like(kv_pre)
+            o_dec_b = torch.empty_like(o_dec)
+            torch.cuda.synchronize()
+            run_pre = lambda: la.prefill(qp, kp, vp, cu_dev, wp["decay"], stream=sp,  # noqa
+                                         out=o_pre_b, kv_final=kv_pre_b, cu_seqlens_host=cu)
+            run_dec = lambda: la.decode(qd, kd, vd, kv_b, wd["decay"], stream=sd,  # noqa
+                                        out=o_dec_b)
+            (run_dec, run_pre)[0 if decode_first else 1]()
+            (run_pre, run_dec)[0 if decode_first else 1]()
+            torch.cuda.synchronize()
+            assert torch.equal(o_dec_b, o_dec) and torch.equal(kv_b, kv_solo)
+            assert torch.equal(o_pre_b, o_pre) and torch.equal(kv_pre_b, kv_pre)
+
+    heads = [0, 31, 63]
+    q_h, k_h, v_h = (to_np(x[:, heads]) for x in (qp, kp, vp))
+    dec_h = np.asarray(wp["decay"], np.float32)[heads]
+    o_ref, kv_ref = oracle.prefill_varlen(q_h, k_h, v_h, cu, dec_h, beta=64)
+    s1 = parity.check(to_np(o_pre[:, heads]), o_ref, 1, 1e-2, out_bf16=True,
+                      what="serving prefill o")
+    s2 = parity.check(to_np(kv_pre[:, heads]), kv_ref, 1, 1e-2, what="serving prefill kv")
+    say("serving prefill", s1, s2)
+    rng = np.random.Generator(np.random.PCG64(11))
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 48), rng.integers(0, H, 48))]
+    pairs += [(0, 0), (B - 1, H - 1)]
+    for b, h in pairs:
+        od_ref, sd_ref = oracle.decode_step(to_np(qd[b, h]), to_np(kd[b, h]), to_np(vd[b, h]),
+                                            to_np(kv_init[b, h]), wd["decay"][h])
+        parity.check(to_np(o_dec[b, h])[None], od_ref[None], 0, 1e-2, out_bf16=True,
+                     what=f"serving decode ({b},{h}) o")
+        parity.check(to_np(kv_solo[b, h])[None], sd_ref[None], 0, 1e-5,
+                     what=f"serving decode ({b},{h}) kv")
