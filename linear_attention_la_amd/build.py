@@ -22,7 +22,7 @@ OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-function",
     # only the C ABI is exported (la_host.cpp gives the declarations of la.h
     # default visibility)
     "-fvisibility=hidden",

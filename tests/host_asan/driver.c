@@ -1,0 +1,172 @@
+/*
+ * Host-side driver for the AddressSanitizer build of libla (CPU only): runs
+ * every entry point's host code -- argument validation, workspace sizes,
+ * error strings, dispatch order of long batches, argument packing -- with
+ * fake device addresses that no kernel ever touches.  Calls that pass
+ * validation reach the HIP launch, which fails without a GPU (LA_ERR_HIP) or
+ * enqueues nothing.  Exit status 0 when every status matches; ASan aborts the
+ * run on any memory error in the library's host code.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "la.h"
+
+static int failures = 0;
+
+static void expect(const char* what, la_status got, la_status want) {
+  const char* msg = la_last_error();
+  if (got != want) {
+    printf("FAIL %s: %s (%s), expected %s\n", what, la_status_str(got), msg, la_status_str(want));
+    ++failures;
+  }
+  if (got != LA_OK && strlen(msg) == 0 && got != LA_ERR_HIP) {
+    printf("FAIL %s: no error text\n", what);
+    ++failures;
+  }
+}
+
+static void expect_not(const char* what, la_status got, la_status bad) {
+  if (got == bad) {
+    printf("FAIL %s: %s (%s)\n", what, la_status_str(got), la_last_error());
+    ++failures;
+  }
+}
+
+#define Q ((void*)0x10000000)
+#define K ((void*)0x20000000)
+#define V ((void*)0x30000000)
+#define O ((void*)0x40000000)
+#define KVF ((float*)0x50000000)
+#define KVI ((float*)0x60000000)
+#define CUD ((int32_t*)0x70000000)
+#define WS ((void*)0x90000000)
+#define DO ((void*)0xA0000000)
+#define DQ ((void*)0xB0000000)
+#define DK ((void*)0xC0000000)
+#define DV ((void*)0xD0000000)
+
+int main(void) {
+  const int H = 4, D = 128;
+  float decay[LA_MAX_HEADS + 1];
+  for (int i = 0; i <= LA_MAX_HEADS; ++i) decay[i] = 0.9f;
+  int32_t cu[3] = {0, 40, 100};
+
+  /* prefill: invalid arguments */
+  expect("prefill negative seqs",
+         la_prefill(Q, K, V, CUD, cu, -1, 100, H, D, LA_BF16, LA_BF16, decay, NULL, O, KVF, NULL),
+         LA_ERR_INVALID_ARG);
+  expect("prefill too many heads",
+         la_prefill(Q, K, V, CUD, cu, 2, 100, LA_MAX_HEADS + 1, D, LA_BF16, LA_BF16, decay, NULL, O,
+                    KVF, NULL),
+         LA_ERR_UNSUPPORTED);
+  expect("prefill head_dim 96",
+         la_prefill(Q, K, V, CUD, cu, 2, 100, H, 96, LA_BF16, LA_BF16, decay, NULL, O, KVF, NULL),
+         LA_ERR_UNSUPPORTED);
+  expect("prefill NULL host cu",
+         la_prefill(Q, K, V, CUD, NULL, 2, 100, H, D, LA_BF16, LA_BF16, decay, NULL, O, KVF, NULL),
+         LA_ERR_INVALID_ARG);
+  expect("prefill o overlaps k",
+         la_prefill(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, NULL,
+                    (char*)K + 64, KVF, NULL),
+         LA_ERR_INVALID_ARG);
+  float bad_decay[4] = {0.9f, 1.5f, 0.9f, 0.9f};
+  expect("prefill decay > 1",
+         la_prefill(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, bad_decay, NULL, O, KVF, NULL),
+         LA_ERR_INVALID_ARG);
+  /* prefill: valid arguments reach the launch (no GPU here: a HIP error) */
+  expect_not("prefill valid",
+             la_prefill(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, KVI, O, KVF,
+                        NULL),
+             LA_ERR_INVALID_ARG);
+
+  /* a batch of 512 sequences: the longest-first dispatch order is built */
+  {
+    const int S = 512;
+    int32_t* cub = (int32_t*)malloc(sizeof(int32_t) * (S + 1));
+    cub[0] = 0;
+    for (int s = 0; s < S; ++s) cub[s + 1] = cub[s] + (s * 37) % 101;
+    expect_not("prefill 512 sequences",
+               la_prefill(Q, K, V, CUD, cub, S, cub[S], 2, 64, LA_BF16, LA_BF16, decay, NULL, O,
+                          NULL, NULL),
+               LA_ERR_INVALID_ARG);
+    size_t bytes = 0;
+    expect("segmented workspace 512 sequences",
+           la_prefill_segmented_workspace_size(S, cub, 2, 128, 64, &bytes), LA_OK);
+    expect("segmented workspace d = 64",
+           la_prefill_segmented_workspace_size(S, cub, 2, 64, 64, &bytes), LA_OK);
+    expect("backward segmented workspace",
+           la_prefill_backward_segmented_workspace_size(S, cub, 2, 128, 64, &bytes), LA_OK);
+    free(cub);
+  }
+
+  /* segmented */
+  size_t ws_bytes = 0;
+  expect("segmented workspace size", la_prefill_segmented_workspace_size(2, cu, H, D, 64, &ws_bytes),
+         LA_OK);
+  size_t bad_bytes = 1;
+  expect("segmented bad segment_len",
+         la_prefill_segmented_workspace_size(2, cu, H, D, 100, &bad_bytes), LA_ERR_INVALID_ARG);
+  if (bad_bytes != 0) {
+    printf("FAIL segmented bad segment_len: bytes not zeroed\n");
+    ++failures;
+  }
+  expect("segmented workspace too small",
+         la_prefill_segmented(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, NULL, O,
+                              KVF, 64, WS, 16, NULL),
+         LA_ERR_INVALID_ARG);
+  expect_not("segmented valid",
+             la_prefill_segmented(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, KVI, O,
+                                  KVF, 64, WS, ws_bytes, NULL),
+             LA_ERR_INVALID_ARG);
+  expect("segmented noalloc fp32 input",
+         la_prefill_segmented_noalloc(Q, K, V, CUD, cu, 2, 100, H, D, LA_FP32, LA_FP32, decay, NULL,
+                                      O, KVF, 64, NULL),
+         LA_ERR_UNSUPPORTED);
+
+  /* backward */
+  size_t bw = 0;
+  expect("backward workspace size", la_prefill_backward_workspace_size(2, H, D, &bw), LA_OK);
+  expect("backward fp32 input",
+         la_prefill_backward(Q, K, V, DO, CUD, cu, 2, 100, H, D, LA_FP32, LA_BF16, decay, NULL, NULL,
+                             DQ, DK, DV, NULL, NULL, 0, NULL),
+         LA_ERR_UNSUPPORTED);
+  expect("backward dq overlaps dk",
+         la_prefill_backward(Q, K, V, DO, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, NULL,
+                             NULL, DQ, (char*)DQ + 128, DV, NULL, NULL, 0, NULL),
+         LA_ERR_INVALID_ARG);
+  expect_not("backward valid",
+             la_prefill_backward(Q, K, V, DO, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, KVI,
+                                 KVF, DQ, DK, DV, (float*)0xE0000000, WS, bw, NULL),
+             LA_ERR_INVALID_ARG);
+
+  /* decode and the pools */
+  int32_t slots[3] = {3, 0, 7}, dup[3] = {3, 3, 7};
+  expect("decode negative batch",
+         la_decode(Q, K, V, KVF, decay, -1, H, D, LA_BF16, O, NULL), LA_ERR_INVALID_ARG);
+  expect_not("decode valid", la_decode(Q, K, V, KVF, decay, 3, H, D, LA_BF16, O, NULL),
+             LA_ERR_INVALID_ARG);
+  expect("decode pool repeated slot",
+         la_decode_pool(Q, K, V, KVF, 10, CUD, dup, decay, 3, H, D, LA_BF16, O, NULL),
+         LA_ERR_INVALID_ARG);
+  expect("decode pool slot out of range",
+         la_decode_pool(Q, K, V, KVF, 5, CUD, slots, decay, 3, H, D, LA_BF16, O, NULL),
+         LA_ERR_INVALID_ARG);
+  expect("prefill pool repeated slot",
+         la_prefill_pool(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, KVF, 10, CUD, dup,
+                         O, NULL),
+         LA_ERR_INVALID_ARG);
+
+  /* status strings */
+  for (int s = -1; s < 6; ++s) {
+    const char* name = la_status_str((la_status)s);
+    if (!name || !*name) {
+      printf("FAIL status string %d\n", s);
+      ++failures;
+    }
+  }
+  printf("%s: %d failure(s)\n", failures ? "FAILED" : "OK", failures);
+  return failures ? 1 : 0;
+}
