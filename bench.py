@@ -148,18 +148,41 @@ def measured_peaks(dev):
             "note": "1 GiB fp32 read+write stream (torch.mul out=); 8192^3 bf16 matmul (hipBLASLt)"}
 
 
-def cpu_baseline(budget_s=12.0):
-    """fp64 oracle over heads of the N=8192 workload (host inputs of the same
-    distribution), until budget_s of compute has been spent."""
-    import oracle
-    from la_inputs import decay_from_seed, host_qkv
-
+def _host_info():
+    """CPU model, usable host cores and the BLAS library numpy runs on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            b = libs[0]
+            blas = f"{b.get('internal_api')} {b.get('version')} ({os.path.basename(b.get('filepath', ''))})"
+            threads = int(b.get("num_threads", threads))
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(budget_s=12.0, decode_budget_s=4.0):
+    """The fp64 oracle on the host cores: prefill over (sequence, head)
+    chains of the N=8192 workload's shape (host inputs of the same
+    distribution) until budget_s of compute has been spent, reported as
+    tokens/s of the 64-head workload; and the decode step over states of the
+    256 x 64 serving batch until decode_budget_s, reported as GB/s of the
+    decode's algorithmic bytes."""
+    import oracle
+    from la_inputs import decay_from_seed, host_qkv, random_states
+
+    model, blas, threads = _host_info()
     N = 8192
     decay = decay_from_seed(H)
     heads_done, elapsed = 0, 0.0
@@ -172,13 +195,29 @@ def cpu_baseline(budget_s=12.0):
         elapsed += time.perf_counter() - t0
         heads_done += chunk
     tokens_equiv = N * heads_done / H
+    # decode: one step per (sequence, head) state, in batches of 64 heads
+    states_done, d_elapsed = 0, 0.0
+    while d_elapsed < decode_budget_s and states_done < 256 * H:
+        kv = random_states(1, H, D, 6000 + states_done)
+        q, k, v = (x.reshape(1, H, D) for x in host_qkv(H, 1, D, 7000 + states_done))
+        t0 = time.perf_counter()
+        oracle.decode_batch(q, k, v, kv, decay)
+        d_elapsed += time.perf_counter() - t0
+        states_done += H
+    dec_gbs = states_done * (8 * D * D + 8 * D) / d_elapsed / 1e9
+    cores = len(os.sched_getaffinity(0))
     return {"value": tokens_equiv / elapsed, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"fp64 blockwise oracle (beta={BETA}) on {heads_done} (sequence, head) "
                       f"chains of N={N}, d={D} ({heads_done / H:.2f}x the 64-head workload), "
-                      f"{elapsed:.1f} s of compute on {len(os.sched_getaffinity(0))} "
-                      f"visible host cores",
-            "seconds": round(elapsed, 2)}
+                      f"{elapsed:.1f} s of compute; decode: {states_done} (sequence, head) "
+                      f"states of d={D}, {d_elapsed:.1f} s; {cores} visible host cores",
+            "seconds": round(elapsed, 2),
+            "decode": {"GB_per_s": round(dec_gbs, 3), "states": states_done,
+                       "seconds": round(d_elapsed, 2),
+                       "bytes_per_state": 8 * D * D + 8 * D},
+            "cpu_model": model, "visible_cores": cores, "blas": blas,
+            "blas_threads": int(threads)}
 
 
 def bench_decode(dev, reps=20):
