@@ -43,4 +43,5 @@ from .lightning import (  # noqa: F401
     backward_quadratic,
     backward_recurrent,
     backward_varlen,
+    norm_gate,
 )

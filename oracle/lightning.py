@@ -414,3 +414,29 @@ def backward_varlen(q, k, v, do, cu_seqlens, decay, kv_init=None, dkv_final=None
             r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[h], s0, g)
             dq[a:b, h], dk[a:b, h], dv[a:b, h], dkv0[s, h] = r
     return dq, dk, dv, dkv0
+
+
+# ---------------------------------------------------------------------------
+# Output normalisation and gate (the memory-bound epilogue next to the core).
+# The pages say the model takes TransNormer's NormAttention ([CSDN] §2.1),
+# i.e. a normalisation of the linear-attention output in place of softmax's
+# scaling, and that memory-bound kernels around lightning attention are fused
+# so that intermediate results are not stored ([JVY] 二、计算优化, [CSDN]
+# §3.2).  They do not define the normalisation.  Reading taken: an RMS
+# normalisation of each head's output row over its d features with a
+# per-(head, feature) weight, y = w_h * o / sqrt(mean(o^2) + eps), optionally
+# multiplied element-wise by sigmoid(g) for a caller-supplied gate g of the
+# same shape (the gate is not on the pages; it is an option).
+# ---------------------------------------------------------------------------
+
+def norm_gate(o, weight, eps, gate=None):
+    """Per-head RMS normalisation of o [..., H, d] over its last axis, scaled
+    by weight [H, d], then, if gate [..., H, d] is given, multiplied by
+    sigmoid(gate).  Returns float64 of o's shape."""
+    o = _f64(o)
+    w = _f64(weight)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    y = o / np.sqrt(ms + float(eps)) * w
+    if gate is not None:
+        y = y * (1.0 / (1.0 + np.exp(-_f64(gate))))
+    return y

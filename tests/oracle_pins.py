@@ -390,7 +390,43 @@ def pin_backward_varlen(orc):
     _close(got_r[3], ref[3][order], 1e-12, "backward_varlen reversed packing dkv_init")
 
 
+def pin_norm_gate(orc):
+    """Output normalisation: hand-worked values (tests/golden), invariants
+    of an RMS normalisation (positive scale invariance at eps = 0, odd in o,
+    unit mean square with unit weights), each head its own weight and its
+    own rows, and the gate as the logistic function (sigmoid(-g) =
+    1 - sigmoid(g), limits 0 and 1)."""
+    g = json.load(open(GOLDEN))
+    for case in g["norm_gate"]:
+        o = np.array(case["o"], dtype=np.float64)
+        gate = None if case["gate"] is None else np.array(case["gate"], dtype=np.float64)
+        y = orc.norm_gate(o, np.array(case["weight"], dtype=np.float64), case["eps"], gate)
+        _close(y, case["y"], 1e-15, f"golden norm_gate {case['name']}")
+    rng = _rng(43)
+    T, H, d = 7, 3, 16
+    o = rng.standard_normal((T, H, d)) * rng.uniform(0.1, 10.0, (T, H, 1))
+    w1 = np.ones((H, d))
+    y = orc.norm_gate(o, w1, 0.0)
+    _close(np.mean(y * y, axis=-1), np.ones((T, H)), 1e-13, "norm_gate unit mean square")
+    _close(orc.norm_gate(3.7 * o, w1, 0.0), y, 1e-13, "norm_gate scale invariance")
+    _close(orc.norm_gate(-o, w1, 0.0), -y, 0.0, "norm_gate odd")
+    w = rng.standard_normal((H, d))
+    yw = orc.norm_gate(o, w, 1e-3)
+    for h in range(H):
+        row = o[:, h, :]
+        ref = row / np.sqrt(np.mean(row * row, axis=-1, keepdims=True) + 1e-3) * w[h]
+        _close(yw[:, h, :], ref, 1e-14, f"norm_gate head {h}")
+    gt = rng.standard_normal((T, H, d)) * 3.0
+    a = orc.norm_gate(o, w, 1e-3, gt) / yw
+    b = orc.norm_gate(o, w, 1e-3, -gt) / yw
+    _close(a + b, np.ones_like(a), 1e-12, "gate: sigmoid(g) + sigmoid(-g) = 1")
+    big = np.full((T, H, d), 800.0)
+    with np.errstate(over="ignore"):  # exp(800) is inf: sigmoid(-800) = 1 / inf = 0
+        _close(orc.norm_gate(o, w, 1e-3, big), yw, 1e-15, "gate limit 1")
+        _close(orc.norm_gate(o, w, 1e-3, -big), np.zeros_like(yw), 0.0, "gate limit 0")
+
+
 ALL_PINS = [pin_golden, pin_exact_rational, pin_lfilter, pin_nodecay_library, pin_geometric,
             pin_three_way, pin_continuation, pin_decode_consistency, pin_packing, pin_decode_pool,
             pin_prefill_pool, pin_backward_autograd, pin_backward_finite_difference,
-            pin_backward_varlen]
+            pin_backward_varlen, pin_norm_gate]

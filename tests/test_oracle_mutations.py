@@ -67,6 +67,15 @@ MUTATIONS = {
                                       "r = fn(q[a:b, h], k[a:b, h], v[a:b, h], do[a:b, h], decay[h], g, s0)"),
     "bwd_varlen_swapped_dk_dv": ("dq[a:b, h], dk[a:b, h], dv[a:b, h], dkv0[s, h] = r",
                                  "dq[a:b, h], dv[a:b, h], dk[a:b, h], dkv0[s, h] = r"),
+    "norm_sum_not_mean": ("ms = np.mean(o * o, axis=-1, keepdims=True)",
+                          "ms = np.sum(o * o, axis=-1, keepdims=True)"),
+    "norm_drops_eps": ("y = o / np.sqrt(ms + float(eps)) * w", "y = o / np.sqrt(ms) * w"),
+    "norm_first_head_weight": ("y = o / np.sqrt(ms + float(eps)) * w", "y = o / np.sqrt(ms + float(eps)) * w[0]"),
+    "norm_over_heads": ("ms = np.mean(o * o, axis=-1, keepdims=True)",
+                        "ms = np.mean(o * o, axis=-2, keepdims=True)"),
+    "gate_wrong_sign": ("y = y * (1.0 / (1.0 + np.exp(-_f64(gate))))",
+                        "y = y * (1.0 / (1.0 + np.exp(_f64(gate))))"),
+    "gate_ignored": ("        y = y * (1.0 / (1.0 + np.exp(-_f64(gate))))\n", "        pass\n"),
 }
 
 
