@@ -406,6 +406,83 @@ def bench_mixed(dev, dec_state, reps=10, warmup=2):
     return res
 
 
+def bench_normed(dev, reps=10):
+    """The output normalisation fused into the kernels that write O
+    (la_prefill_normed, la_decode_normed; weight [H, d], eps 1e-6, a bf16
+    gate) against the same result unfused: la_prefill / la_decode, then the
+    normalisation and gate as torch operations on the written output.  Two
+    prefill shapes: eight 8K sequences (one workgroup per chain) and the
+    headline B=1, N=8192 (fused: the chained scan; unfused: the 32-column
+    kernel); and the 256 x 64 decode batch.  Algorithmic bytes of the fused
+    prefill: the plain prefill's plus the gate read (2 B per element); the
+    unfused path also writes O and reads it back."""
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import cu_seqlens, device_qkv, device_states, workload
+
+    s = torch.cuda.current_stream()
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB cache flush
+    eps = 1e-6
+    w = torch.rand((H, D), dtype=torch.float32, device=dev) + 0.5
+
+    def epilogue(o, gate):
+        of = o.float()
+        y = of * torch.rsqrt(of.pow(2).mean(-1, keepdim=True) + eps) * w * torch.sigmoid(gate.float())
+        return y.to(o.dtype)
+
+    res = {}
+    for name in ("batch8_n8k", "n8k"):
+        wl = workload(name)
+        cu = cu_seqlens(wl["lengths"])
+        T, S = int(cu[-1]), len(wl["lengths"])
+        q, k, v = device_qkv(T, H, D, wl["seed"], dev)
+        gate = device_qkv(T, H, D, wl["seed"] + 21, dev)[0]
+        cu_dev = torch.from_numpy(cu).to(dev)
+        o = torch.empty_like(q)
+        kvf = torch.empty((S, H, D, D), dtype=torch.float32, device=dev)
+        need = la.prefill_normed_workspace_size(cu, H, D)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        fused = lambda i: la.prefill_normed(q, k, v, cu_dev, wl["decay"], w, eps, gate, out=o,  # noqa
+                                            kv_final=kvf, cu_seqlens_host=cu, workspace=ws)
+        unfused = lambda i: epilogue(la.prefill(q, k, v, cu_dev, wl["decay"], out=o,  # noqa
+                                                kv_final=kvf, cu_seqlens_host=cu)[0], gate)
+        fused_ng = lambda i: la.prefill_normed(q, k, v, cu_dev, wl["decay"], w, eps, None,  # noqa
+                                               out=o, kv_final=kvf, cu_seqlens_host=cu,
+                                               workspace=ws)
+        plain = lambda i: la.prefill(q, k, v, cu_dev, wl["decay"], out=o, kv_final=kvf,  # noqa
+                                     cu_seqlens_host=cu)
+        for fn in (fused, unfused, fused_ng, plain):
+            fn(0)
+        med = lambda fn: sorted(launch_times(fn, reps, s, flush=lambda: scratch.zero_()))[reps // 2]  # noqa
+        tf, tu, tn, tp = med(fused), med(unfused), med(fused_ng), med(plain)
+        by = prefill_bytes(T, S) + T * H * D * 2
+        res[name] = {"tokens": T, "seqs": S, "path": "one workgroup per chain" if need == 0
+                     else "chained scan", "fused_us": round(tf * 1e6, 1),
+                     "fused_no_gate_us": round(tn * 1e6, 1), "plain_prefill_us": round(tp * 1e6, 1),
+                     "unfused_us": round(tu * 1e6, 1), "speedup": round(tu / tf, 3),
+                     "fused_frac_of_8TBs": round(by / tf / 1e9 / HBM_PEAK_GBS, 4)}
+        del q, k, v, gate, o, kvf, ws
+        torch.cuda.empty_cache()
+    wd = workload("mixed_decode")
+    B = wd["batch"]
+    kv = device_states(B, H, D, wd["seed"], dev, scale=0.5)
+    q, k, v = (x.view(B, H, D) for x in device_qkv(B, H, D, wd["seed"] + 1, dev))
+    gate = device_qkv(B, H, D, wd["seed"] + 3, dev)[0].view(B, H, D)
+    out = torch.empty_like(q)
+    fused = lambda i: la.decode_normed(q, k, v, kv, wd["decay"], w, eps, gate, out=out)  # noqa
+    unfused = lambda i: epilogue(la.decode(q, k, v, kv, wd["decay"], out=out), gate)  # noqa
+    for fn in (fused, unfused):
+        fn(0)
+    tf = timed_launches(fused, 20, s)
+    tu = timed_launches(unfused, 20, s)
+    res["decode_b256"] = {"fused_us": round(tf * 1e6, 1), "unfused_us": round(tu * 1e6, 1),
+                          "speedup": round(tu / tf, 3)}
+    del scratch, kv
+    torch.cuda.empty_cache()
+    return res
+
+
 SWEEP = ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodecay", "n1m",
          "batch8_n8k", "varlen64")
 
@@ -587,6 +664,8 @@ def main():
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time la_decode on the 256 x 64-head serving batch")
+    ap.add_argument("--normed-only", action="store_true",
+                    help="only time the fused output normalisation against the unfused one")
     ap.add_argument("--mixed-only", action="store_true",
                     help="only time the mixed serving step (decode beside a packed prefill)")
     ap.add_argument("--pool-only", action="store_true",
@@ -631,6 +710,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}))
+        return
+    if args.normed_only:
+        la.lib()
+        print(json.dumps({"normed": bench_normed(dev)}), flush=True)
         return
     if args.mixed_only:
         la.lib()
@@ -697,6 +780,7 @@ def main():
         line["decode"] = dec
         line["decode_pool"] = bench_decode_pool(dev)
         line["mixed"] = bench_mixed(dev, dec_state)
+        line["normed"] = bench_normed(dev)
         del dec_state
         torch.cuda.empty_cache()
         line["sweep"] = bench_sweep(dev)

@@ -395,6 +395,83 @@ la_status la_decode_pool(const void* q, const void* k, const void* v, float* kv_
                          const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
                          la_dtype in_dtype, void* o, void* stream);
 
+/*
+ * la_norm -- the output normalisation that la_prefill_normed and
+ * la_decode_normed fuse into the kernels that write O.
+ *
+ * The pages say the model uses TransNormer's NormAttention, a normalisation
+ * of the linear-attention output (CSDN §2.1), and that the memory-bound
+ * kernels around lightning attention are fused so that intermediate results
+ * are not stored (jvyan.cn 二、计算优化; CSDN §3.2: batched kernel fusion).
+ * They do not define the normalisation; this library reads it as an RMS
+ * normalisation of each head's output row over its d features:
+ *
+ *     y[t,h,:] = weight[h,:] * o[t,h,:] / sqrt(mean_c(o[t,h,c]^2) + eps)
+ *                * sigmoid(gate[t,h,:])            (if gate is given)
+ *
+ * where o is the attention output of la_prefill / la_decode, computed in
+ * fp32 and normalised before its only rounding to the output dtype.  The
+ * gate is not on the pages; it is an option for a caller whose layer gates
+ * the attention output.
+ *
+ *   weight   device fp32 [H, d] (16-byte aligned).
+ *   eps      added to each row's mean square; finite and > 0.
+ *   gate     device [T, H, d] (prefill) or [B, H, d] (decode), the layout and
+ *            dtype of q, 16-byte aligned; or NULL (no gate).
+ */
+typedef struct la_norm {
+  const float* weight;
+  float eps;
+  const void* gate;
+} la_norm;
+
+/*
+ * la_prefill_normed -- la_prefill with the output normalisation of *norm
+ * applied to every output row before it is written: o receives y (see
+ * la_norm), the final states are those of la_prefill.  One pass; the
+ * unnormalised O never reaches memory.
+ *
+ * Arguments as la_prefill, plus norm, workspace and workspace_bytes.
+ * in_dtype must be LA_BF16 and head_dim 128 (else LA_ERR_UNSUPPORTED).
+ * With at least as many (sequence, head) pairs as the current device has
+ * compute units, one workgroup per pair runs the chain (as la_prefill) and
+ * the workspace is unused (may be NULL).  With fewer, the sequences are cut
+ * into segments (as la_prefill_segmented's chained scan, with a segment
+ * length the library chooses so that segments x heads reaches the compute
+ * units), which needs a workspace of la_prefill_normed_workspace_size
+ * bytes (16-byte aligned, overlapping no other buffer; contents ignored and
+ * left undefined).  o must not overlap the weight or the gate.  Errors as
+ * la_prefill, plus LA_ERR_INVALID_ARG for a NULL norm or weight, a bad eps,
+ * a misaligned or overlapping weight or gate, or a missing or short
+ * workspace.  Nothing synchronises.
+ */
+la_status la_prefill_normed(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                            int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                            const float* decay, const float* kv_init, const la_norm* norm,
+                            void* o, float* kv_final, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Bytes of workspace la_prefill_normed needs for these sequences and heads
+ * on the current device (0 when there are enough (sequence, head) pairs
+ * for one workgroup each).  Host only apart from reading the device's
+ * compute-unit count.  Errors as la_prefill_segmented_workspace_size. */
+la_status la_prefill_normed_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                           int32_t num_heads, int32_t head_dim, size_t* bytes);
+
+/*
+ * la_decode_normed -- la_decode with the output normalisation of *norm
+ * (la_norm) applied to o before it is written; the states are updated as
+ * by la_decode.  Arguments as la_decode plus norm (gate: [B, H, d] of
+ * in_dtype, or NULL).  Errors as la_decode, plus LA_ERR_INVALID_ARG for a
+ * NULL norm or weight, a bad eps, or a misaligned or overlapping weight or
+ * gate.
+ */
+la_status la_decode_normed(const void* q, const void* k, const void* v, float* kv,
+                           const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                           la_dtype in_dtype, const la_norm* norm, void* o, void* stream);
+
 /* Static, never-NULL name of a status code. */
 const char* la_status_str(la_status s);
 

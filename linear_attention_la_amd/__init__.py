@@ -10,6 +10,8 @@ library is missing, every call raises.
     o, kv = prefill_segmented_noalloc(q, k, v, cu_seqlens, decay, segment_len)  # static scratch
     dq, dk, dv, dkv0 = prefill_backward(q, k, v, do, cu_seqlens, decay, kv_init, dkv_final)
     o = decode(q, k, v, kv, decay)          # kv updated in place
+    y, kv = prefill_normed(q, k, v, cu_seqlens, decay, weight, eps, gate)  # fused output norm
+    y = decode_normed(q, k, v, kv, decay, weight, eps, gate)
     o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
     o = prefill_pool(q, k, v, cu_seqlens, decay, pool, slots)   # continues from pool[slots]
     s = cu_masked_stream(mask)   # a stream restricted to some compute units (two-stream serving)
@@ -17,6 +19,7 @@ library is missing, every call raises.
 
 from ._binding import (  # noqa: F401
     LAError,
+    LaNorm,
     LA_OK,
     LA_ERR_INVALID_ARG,
     LA_ERR_UNSUPPORTED,
@@ -36,6 +39,9 @@ from ._binding import (  # noqa: F401
     la_prefill_backward_segmented,
     la_prefill_backward_segmented_workspace_size,
     la_decode,
+    la_decode_normed,
+    la_prefill_normed,
+    la_prefill_normed_workspace_size,
     la_decode_pool,
     la_prefill_pool,
     la_status_str,
@@ -48,6 +54,9 @@ from ._binding import (  # noqa: F401
     prefill_backward_segmented,
     prefill_backward_segmented_workspace_size,
     decode,
+    decode_normed,
+    prefill_normed,
+    prefill_normed_workspace_size,
     decode_pool,
     prefill_pool,
 )

@@ -23,6 +23,12 @@ _DEFAULT_LIB = os.path.join(_HERE, "_lib", "libla.so")
 _lib = None
 
 
+class LaNorm(ctypes.Structure):
+    """struct la_norm of la.h: the output normalisation's weight (device fp32
+    [H, d]), epsilon and optional gate (device, layout and dtype of q)."""
+    _fields_ = [("weight", ctypes.c_void_p), ("eps", ctypes.c_float), ("gate", ctypes.c_void_p)]
+
+
 class LAError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"{_status_name(status)}: {msg}")
@@ -82,6 +88,16 @@ def lib():
     L.la_prefill_backward_segmented_workspace_size.restype = ctypes.c_int
     L.la_prefill_backward_segmented_workspace_size.argtypes = [i32, vp, i32, i32, i32,
                                                                ctypes.POINTER(ctypes.c_size_t)]
+    L.la_prefill_normed.restype = ctypes.c_int
+    L.la_prefill_normed.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
+                                    ctypes.c_int, vp, vp, ctypes.POINTER(LaNorm), vp, vp, vp,
+                                    ctypes.c_size_t, vp]
+    L.la_prefill_normed_workspace_size.restype = ctypes.c_int
+    L.la_prefill_normed_workspace_size.argtypes = [i32, vp, i32, i32,
+                                                   ctypes.POINTER(ctypes.c_size_t)]
+    L.la_decode_normed.restype = ctypes.c_int
+    L.la_decode_normed.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int,
+                                   ctypes.POINTER(LaNorm), vp, vp]
     L.la_decode.restype = ctypes.c_int
     L.la_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int, vp, vp]
     L.la_decode_pool.restype = ctypes.c_int
@@ -137,6 +153,29 @@ def la_prefill_pool(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_to
     return lib().la_prefill_pool(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs,
                                  total_tokens, num_heads, head_dim, in_dtype, out_dtype, decay,
                                  kv_pool, pool_size, slots_dev, slots_host, o, stream)
+
+
+def la_prefill_normed(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                      num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, norm, o, kv_final,
+                      workspace, workspace_bytes, stream):
+    """``norm``: a LaNorm (or None for a NULL pointer)."""
+    return lib().la_prefill_normed(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs,
+                                   total_tokens, num_heads, head_dim, in_dtype, out_dtype, decay,
+                                   kv_init, None if norm is None else ctypes.byref(norm), o,
+                                   kv_final, workspace, workspace_bytes, stream)
+
+
+def la_prefill_normed_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = lib().la_prefill_normed_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
+                                                ctypes.byref(n))
+    return st, n.value
+
+
+def la_decode_normed(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, norm, o, stream):
+    return lib().la_decode_normed(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype,
+                                  None if norm is None else ctypes.byref(norm), o, stream)
 
 
 def la_decode(q, k, v, kv, decay, batch, num_heads, head_dim, in_dtype, o, stream):
@@ -416,6 +455,60 @@ def prefill_segmented_noalloc(q, k, v, cu_seqlens, decay, segment_len, kv_init=N
     return m.out, m.kv_final
 
 
+def _marshal_norm(weight, eps, gate, H, d, dev, like):
+    """LaNorm for a weight [H, d] (device fp32 tensor, or host values copied
+    to the device) and an optional gate tensor shaped and typed as ``like``.
+    Returns (LaNorm, tensors to keep alive)."""
+    torch = _torch()
+    if not isinstance(weight, torch.Tensor):
+        weight = torch.as_tensor(np.asarray(weight, dtype=np.float32)).to(dev)
+    if (not weight.is_cuda or weight.dtype != torch.float32 or not weight.is_contiguous()
+            or tuple(weight.shape) != (H, d)):
+        raise ValueError("norm weight must be a contiguous fp32 device tensor [H, d]")
+    if gate is not None:
+        if (not isinstance(gate, torch.Tensor) or not gate.is_cuda or gate.dtype != like.dtype
+                or not gate.is_contiguous() or gate.shape != like.shape):
+            raise ValueError("gate must be a contiguous device tensor shaped and typed as q")
+    nm = LaNorm(weight.data_ptr(), float(eps), None if gate is None else gate.data_ptr())
+    return nm, (weight, gate)
+
+
+def prefill_normed(q, k, v, cu_seqlens, decay, weight, eps=1e-6, gate=None, kv_init=None,
+                   out_dtype=None, stream=None, final_state=True, out=None, kv_final=None,
+                   cu_seqlens_host=None, workspace=None):
+    """prefill() whose output rows are normalised before they are written:
+    out = weight[h] * o / sqrt(mean(o^2) + eps) (* sigmoid(gate)), o being
+    prefill()'s output (la_prefill_normed).  q, k, v bf16 [T, H, 128];
+    weight fp32 [H, 128]; gate None or like q.  ``workspace``: device bytes
+    of at least prefill_normed_workspace_size() (allocated here if None and
+    needed).  Returns (out, kv_final)."""
+    torch = _torch()
+    m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
+                         out, kv_final, cu_seqlens_host)
+    nm, keep = _marshal_norm(weight, eps, gate, m.H, m.d, m.dev, q)
+    st, need = la_prefill_normed_workspace_size(m.S, m.cu_host.data_ptr(), m.H, m.d)
+    _check(st)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=m.dev)
+        if stream is not None:
+            workspace.record_stream(stream)
+    wp = 0 if workspace is None else workspace.data_ptr()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a = m.args
+    _check(la_prefill_normed(*a[:13], nm, a[13], a[14], wp or None, nbytes, m.stream))
+    del keep
+    return m.out, m.kv_final
+
+
+def prefill_normed_workspace_size(cu_seqlens_host, num_heads, head_dim):
+    """Bytes of device workspace prefill_normed needs on the current device."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    st, n = la_prefill_normed_workspace_size(cu.shape[0] - 1, cu.ctypes.data, num_heads,
+                                             head_dim)
+    _check(st)
+    return n
+
+
 def _marshal_slots(slots, slots_host, n, dev, stream):
     """Pool slots as (device int32 tensor, host int32 array) of shape [n]."""
     torch = _torch()
@@ -484,6 +577,32 @@ def decode(q, k, v, kv, decay, stream=None, out=None):
     st = la_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(), dec.ctypes.data,
                    B, H, d, _dtype_code(q), out.data_ptr(), _stream_handle(stream, q.device))
     _check(st)
+    return out
+
+
+def decode_normed(q, k, v, kv, decay, weight, eps=1e-6, gate=None, stream=None, out=None):
+    """decode() whose output is normalised before it is written (la_decode_normed):
+    out = weight[h] * o / sqrt(mean(o^2) + eps) (* sigmoid(gate)).  weight:
+    fp32 [H, d]; gate None or like q.  kv is updated in place as by decode()."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("kv", kv)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype \
+            or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share shape [B, H, d] and dtype")
+    B, H, d = q.shape
+    if kv.dtype != torch.float32 or tuple(kv.shape) != (B, H, d, d):
+        raise ValueError("kv must be fp32 [B, H, d, d]")
+    dec = _host_decay(decay, H)
+    nm, keep = _marshal_norm(weight, eps, gate, H, d, q.device, q)
+    if out is None:
+        out = torch.empty_like(q)
+    st = la_decode_normed(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(),
+                          dec.ctypes.data, B, H, d, _dtype_code(q), nm, out.data_ptr(),
+                          _stream_handle(stream, q.device))
+    _check(st)
+    del keep
     return out
 
 

@@ -14,6 +14,12 @@
 // state slots[b] of the pool instead of state b (serving keeps the states of
 // all live sequences in one pool and decodes any subset of them).
 //
+// With kNorm the output row is normalised before it is written: the
+// normalisation of NormAttention (CSDN §2.1), read as an RMS normalisation
+// over the d features with a per-(head, feature) weight, times
+// sigmoid(gate) when a gate is given -- the memory-bound epilogue fused into
+// the kernel that produces o (jvyan.cn 二、计算优化).
+//
 // Layout: one workgroup per (b, h).  Thread t owns the column quad
 // 4*(t % (d/4)) and rows r = t / (d/4) + RP*n; each row of the state is read
 // with float4 loads by d/4 consecutive lanes (coalesced 512 B rows for
@@ -47,7 +53,7 @@ __device__ __forceinline__ void store_o<uint16_t>(uint16_t* p, int64_t i, floatx
   *reinterpret_cast<uint2*>(p + i) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
 }
 
-template <int D, typename InT>
+template <int D, typename InT, bool kNorm>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   constexpr int CQ = D / 4;         // column quads per row
   constexpr int RP = kThreads / CQ;  // rows handled concurrently
@@ -98,21 +104,42 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   }
   red[rp][cq] = acc;
   __syncthreads();
-  if (t < CQ) {
-    floatx4 o = red[0][t];
+  if (t < 64) {  // wave 0: lane t < CQ completes columns 4t .. 4t + 3
+    floatx4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (t < CQ) {
+      o = red[0][t];
 #pragma unroll
-    for (int p = 1; p < RP; ++p) o += red[p][t];
-    store_o(static_cast<InT*>(a.o), vec_off + 4 * t, o);
+      for (int p = 1; p < RP; ++p) o += red[p][t];
+    }
+    if constexpr (kNorm) {
+      float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];  // 0 past the row
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      const float inv = rsqrtf(ss * (1.0f / D) + a.norm_eps);
+      if (t < CQ) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float f = inv * a.norm_weight[h * D + 4 * t + m];
+          if (a.gate)
+            f *= __builtin_amdgcn_rcpf(
+                1.0f + __builtin_amdgcn_exp2f(
+                           -1.4426950408889634f *
+                           load_in(static_cast<const InT*>(a.gate), vec_off + 4 * t + m)));
+          o[m] *= f;
+        }
+      }
+    }
+    if (t < CQ) store_o(static_cast<InT*>(a.o), vec_off + 4 * t, o);
   }
 }
 
-template <int D>
+template <int D, bool kNorm>
 hipError_t launch_d(const DecodeArgs& a, la_dtype in_dtype, hipStream_t stream) {
   const dim3 grid((unsigned)a.batch * (unsigned)a.num_heads), block(kThreads);
   if (in_dtype == LA_FP32)
-    hipLaunchKernelGGL((decode_kernel<D, float>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, float, kNorm>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, uint16_t>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, uint16_t, kNorm>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -120,8 +147,10 @@ hipError_t launch_d(const DecodeArgs& a, la_dtype in_dtype, hipStream_t stream) 
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, la_dtype in_dtype,
                          hipStream_t stream) {
-  if (head_dim == 64) return launch_d<64>(a, in_dtype, stream);
-  return launch_d<128>(a, in_dtype, stream);
+  const bool norm = a.norm_weight != nullptr;
+  if (head_dim == 64)
+    return norm ? launch_d<64, true>(a, in_dtype, stream) : launch_d<64, false>(a, in_dtype, stream);
+  return norm ? launch_d<128, true>(a, in_dtype, stream) : launch_d<128, false>(a, in_dtype, stream);
 }
 
 }  // namespace la

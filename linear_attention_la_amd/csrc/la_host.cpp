@@ -272,17 +272,41 @@ la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
 la_status decode_common(const void* q, const void* k, const void* v, float* kv,
                         int32_t num_states, const int32_t* slots_dev, const int32_t* slots_host,
                         const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
-                        la_dtype in_dtype, void* o, void* stream);
+                        la_dtype in_dtype, void* o, void* stream, const la_norm* norm = nullptr);
+
+// The output normalisation's arguments: the struct, its weight and epsilon,
+// alignment, and no overlap between o (rows x H x d of out_bytes each) and
+// the weight or the gate (rows x H x d of gate_bytes each).
+la_status check_norm(const la_norm* norm, int64_t rows, int32_t num_heads, int32_t head_dim,
+                     size_t gate_bytes, const void* o, size_t out_bytes);
 
 la_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+la_status check_norm(const la_norm* norm, int64_t rows, int32_t num_heads, int32_t head_dim,
+                     size_t gate_bytes, const void* o, size_t out_bytes) {
+  if (!norm) return fail(LA_ERR_INVALID_ARG, "norm is NULL");
+  if (!norm->weight) return fail(LA_ERR_INVALID_ARG, "norm->weight is NULL");
+  if (!(norm->eps > 0.0f) || !isfinite(norm->eps))
+    return fail(LA_ERR_INVALID_ARG, "norm->eps = %g must be finite and > 0", (double)norm->eps);
+  if (!aligned16(norm->weight))
+    return fail(LA_ERR_INVALID_ARG, "norm->weight is not 16-byte aligned");
+  if (!aligned16(norm->gate)) return fail(LA_ERR_INVALID_ARG, "norm->gate is not 16-byte aligned");
+  const size_t n = (size_t)rows * num_heads * head_dim;
+  const Range ro = range("o", o, n * out_bytes);
+  const Range rw = range("norm->weight", norm->weight, (size_t)num_heads * head_dim * 4);
+  const Range rg = range("norm->gate", norm->gate, norm->gate ? n * gate_bytes : 0);
+  if (overlap(ro, rw)) return fail(LA_ERR_INVALID_ARG, "o overlaps norm->weight");
+  if (overlap(ro, rg)) return fail(LA_ERR_INVALID_ARG, "o overlaps norm->gate");
+  return LA_OK;
+}
+
 la_status decode_common(const void* q, const void* k, const void* v, float* kv,
                         int32_t num_states, const int32_t* slots_dev, const int32_t* slots_host,
                         const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
-                        la_dtype in_dtype, void* o, void* stream) {
+                        la_dtype in_dtype, void* o, void* stream, const la_norm* norm) {
   (void)slots_host;
   if (batch < 0) return fail(LA_ERR_INVALID_ARG, "batch = %d < 0", batch);
   la_status st = check_heads_dim(num_heads, head_dim);
@@ -311,12 +335,27 @@ la_status decode_common(const void* q, const void* k, const void* v, float* kv,
   for (const Range* x : vecs)
     if (overlap(rs, *x)) return fail(LA_ERR_INVALID_ARG, "kv overlaps %s", x->name);
 
+  if (norm) {
+    if ((st = check_norm(norm, batch, num_heads, head_dim, dtype_size(in_dtype), o,
+                         dtype_size(in_dtype))) != LA_OK)
+      return st;
+    const Range rw = range("norm->weight", norm->weight, (size_t)num_heads * head_dim * 4);
+    const Range rg = range("norm->gate", norm->gate, norm->gate ? vec_bytes : 0);
+    if (overlap(rs, rw) || overlap(rs, rg))
+      return fail(LA_ERR_INVALID_ARG, "kv overlaps the normalisation's weight or gate");
+  }
+
   la::DecodeArgs a;
   memset(&a, 0, sizeof(a));
   a.q = q;
   a.k = k;
   a.v = v;
   a.kv = kv;
+  if (norm) {
+    a.norm_weight = norm->weight;
+    a.gate = norm->gate;
+    a.norm_eps = norm->eps;
+  }
   a.slots = slots_dev;
   a.o = o;
   a.batch = batch;
@@ -481,7 +520,8 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                           la_dtype out_dtype, const float* l2, const float* kv_init, void* o,
                           float* kv_final, const SegmentLayout& lay, char* ws, bool reverse,
-                          hipStream_t s, bool outputs_only = false) {
+                          hipStream_t s, bool outputs_only = false,
+                          const la_norm* norm = nullptr) {
   int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + lay.cu_seg);
   int32_t* init_slot = reinterpret_cast<int32_t*>(ws + lay.init_slot);
   int32_t* final_slot = reinterpret_cast<int32_t*>(ws + lay.final_slot);
@@ -518,8 +558,13 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
     sa.ring = states;
     sa.spin_limit = kScanSpinLimit;
     a.o = o;
+    if (norm) {
+      a.norm_weight = norm->weight;
+      a.gate = norm->gate;
+      a.norm_eps = norm->eps;
+    }
     a.num_items = lay.num_segments * num_heads;
-    e = la::launch_prefill_scan(a, sa, out_dtype, s);
+    e = la::launch_prefill_scan(a, sa, out_dtype, a.norm_weight != nullptr, s);
     return hip_status(e, "segmented scan launch");
   }
   const bool wide = use_wide((int64_t)lay.num_segments * num_heads, head_dim);
@@ -702,6 +747,131 @@ la_status la_prefill_segmented_noalloc(const void* q, const void* k, const void*
   return segmented_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
                            num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,
                            segment_len, lay, ws, (size_t)LA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// la_prefill_normed with fewer (sequence, head) pairs than compute units cuts
+// the sequences into segments of this length: about one segment per compute
+// unit over all heads, at least one block.  Without a device to ask, the
+// compute units are taken as 256 (MI355X).
+int32_t normed_segment_len(int64_t total_tokens, int32_t num_heads) {
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t per = (total_tokens * num_heads + cus - 1) / cus;
+  const int64_t len = ((per + 63) / 64) * 64;
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(len, 64), (int64_t)1 << 30);
+}
+
+// Whether la_prefill_normed runs one workgroup per (sequence, head) pair
+// (else the chained scan over segments).
+bool normed_wide(int32_t num_seqs, int32_t num_heads) {
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  return (int64_t)num_seqs * num_heads >= cus;
+}
+
+}  // namespace
+
+extern "C" {
+
+la_status la_prefill_normed_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                           int32_t num_heads, int32_t head_dim, size_t* bytes) {
+  if (!bytes) return fail(LA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = 0;
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if (head_dim != 128)
+    return fail(LA_ERR_UNSUPPORTED, "the normed prefill takes head_dim 128 only");
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  if (num_seqs == 0 || normed_wide(num_seqs, num_heads)) return ok();
+  SegmentLayout lay;
+  const int32_t seg = normed_segment_len(cu_seqlens_host[num_seqs], num_heads);
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, seg, true, &lay)) !=
+      LA_OK)
+    return st;
+  *bytes = lay.total;
+  return ok();
+}
+
+la_status la_prefill_normed(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                            int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                            int32_t head_dim, la_dtype in_dtype, la_dtype out_dtype,
+                            const float* decay, const float* kv_init, const la_norm* norm,
+                            void* o, float* kv_final, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (valid_dtype(in_dtype) && in_dtype != LA_BF16)
+    return fail(LA_ERR_UNSUPPORTED, "the normed prefill takes bf16 inputs only");
+  if (head_dim == 64) return fail(LA_ERR_UNSUPPORTED, "the normed prefill takes head_dim 128 only");
+  la_status st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
+                               num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o,
+                               kv_final, num_seqs);
+  if (st != LA_OK) return st;
+  if ((st = check_norm(norm, total_tokens, num_heads, head_dim, 2, o, dtype_size(out_dtype))) !=
+      LA_OK)
+    return st;
+  if (kv_final) {
+    const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+    const Range rf = range("kv_final", kv_final, sb);
+    if (overlap(rf, range("norm->weight", norm->weight, (size_t)num_heads * head_dim * 4)) ||
+        overlap(rf, range("norm->gate", norm->gate,
+                          norm->gate ? (size_t)total_tokens * num_heads * head_dim * 2 : 0)))
+      return fail(LA_ERR_INVALID_ARG, "kv_final overlaps the normalisation's weight or gate");
+  }
+  if (num_seqs == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (normed_wide(num_seqs, num_heads)) {
+    la::PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_seqlens = cu_seqlens_dev;
+    a.kv_init = kv_init;
+    a.o = o;
+    a.kv_final = kv_final;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_items = num_seqs * num_heads;
+    for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
+    set_order(a, cu_seqlens_host, num_seqs);
+    a.norm_weight = norm->weight;
+    a.gate = norm->gate;
+    a.norm_eps = norm->eps;
+    return hip_status(la::launch_prefill_wide_normed(a, out_dtype, s), "la_prefill_normed launch");
+  }
+  // fewer pairs than compute units: the chained scan over segments
+  const int32_t seg = normed_segment_len(total_tokens, num_heads);
+  SegmentLayout lay;
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, seg, true, &lay)) !=
+      LA_OK)
+    return st;
+  if (!workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", lay.total);
+  if (!aligned16(workspace)) return fail(LA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes,
+                lay.total);
+  {
+    const size_t tok = (size_t)total_tokens * num_heads * head_dim;
+    const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
+    const Range rw = range("workspace", workspace, lay.total);
+    const Range others[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
+                            range("o", o, tok * dtype_size(out_dtype)),
+                            range("kv_init", kv_init, kv_init ? sb : 0),
+                            range("kv_final", kv_final, kv_final ? sb : 0),
+                            range("norm->weight", norm->weight, (size_t)num_heads * head_dim * 4),
+                            range("norm->gate", norm->gate, norm->gate ? tok * 2 : 0)};
+    for (const Range& r : others)
+      if (overlap(rw, r)) return fail(LA_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
+  }
+  float l2[LA_MAX_HEADS];
+  for (int32_t h = 0; h < num_heads; ++h) l2[h] = (float)log2((double)decay[h]);
+  return segmented_chain(q, k, v, cu_seqlens_dev, num_seqs, num_heads, head_dim, out_dtype, l2,
+                         kv_init, o, kv_final, lay, static_cast<char*>(workspace), false, s,
+                         false, norm);
 }
 
 la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads,
@@ -1016,6 +1186,14 @@ la_status la_decode(const void* q, const void* k, const void* v, float* kv,
                     la_dtype in_dtype, void* o, void* stream) {
   return decode_common(q, k, v, kv, batch, nullptr, nullptr, decay, batch, num_heads, head_dim,
                        in_dtype, o, stream);
+}
+
+la_status la_decode_normed(const void* q, const void* k, const void* v, float* kv,
+                           const float* decay, int32_t batch, int32_t num_heads, int32_t head_dim,
+                           la_dtype in_dtype, const la_norm* norm, void* o, void* stream) {
+  if (!norm) return fail(LA_ERR_INVALID_ARG, "norm is NULL");
+  return decode_common(q, k, v, kv, batch, nullptr, nullptr, decay, batch, num_heads, head_dim,
+                       in_dtype, o, stream, norm);
 }
 
 la_status la_decode_pool(const void* q, const void* k, const void* v, float* kv_pool,

@@ -38,6 +38,12 @@ struct PrefillArgs {
   // chains start in the first wave of workgroups); else sequence i.
   int32_t ordered;
   uint16_t seq_order[kMaxOrder];
+  // Output normalisation (kernels launched with it only): per-(head, feature)
+  // weight [H, d] fp32, the epsilon added to each row's mean square, and an
+  // optional gate [T, H, d] bf16 whose sigmoid multiplies the output.
+  const float* norm_weight;
+  const void* gate;
+  float norm_eps;
 };
 
 // Sequence index of the idx-th sequence in dispatch order.
@@ -60,6 +66,12 @@ struct DecodeArgs {
   // are streamed at the same time over memory.
   int32_t b_step;
   float decay[LA_MAX_HEADS];
+  // Output normalisation (norm_weight non-null): per-(head, feature) weight
+  // [H, d] fp32, the epsilon added to the row's mean square, and an
+  // optional gate [B, H, d] of the input dtype whose sigmoid multiplies o.
+  const float* norm_weight;
+  const void* gate;
+  float norm_eps;
 };
 
 // Chained-scan prefill (la_prefill_wide.hip, d = 128, bf16): one launch over
@@ -98,7 +110,13 @@ hipError_t launch_prefill_wide(const PrefillArgs& a, la_dtype out_dtype, bool st
                                bool reverse, hipStream_t stream);
 
 hipError_t launch_prefill_scan(const PrefillArgs& a, const ScanArgs& sa, la_dtype out_dtype,
-                               hipStream_t stream);
+                               bool norm, hipStream_t stream);
+
+// The one-workgroup-per-chain prefill (forwards, d = 128) with the output
+// normalisation of a.norm_weight / a.norm_eps / a.gate fused into its
+// output write.
+hipError_t launch_prefill_wide_normed(const PrefillArgs& a, la_dtype out_dtype,
+                                      hipStream_t stream);
 
 // out[s,h] = scale[h] * (transpose ? in[s,h]^T : in[s,h]) for num_states x H
 // fp32 d x d states (la_state.hip); out may be in only without transpose.

@@ -123,6 +123,7 @@ struct Lds {
   uint16_t* Vs;  // [2][64][128]
   uint16_t* Ph;  // [64][64]
   uint16_t* Pl;  // [64][64]
+  float* Ob;     // [64][128] fp32: a block's output rows (normed output only)
 };
 
 // Thread t's place in the state: wave w owns value columns [16w, 16w+16) and
@@ -137,9 +138,11 @@ struct StatePos {
 
 // Runs the blocks of chain c with the state st (fp32, held in registers;
 // updated in place): with kStateOnly only the state advances (K and V are
-// read, Q is not, O is not written).  Starts with an LDS write, so a caller
-// that used the LDS arrays before must have passed a workgroup barrier.
-template <bool kOutF32, bool kStateOnly>
+// read, Q is not, O is not written).  With kNorm each output row is
+// normalised before it is written (see the output epilogue below).  Starts
+// with an LDS write, so a caller that used the LDS arrays before must have
+// passed a workgroup barrier.
+template <bool kOutF32, bool kStateOnly, bool kNorm = false>
 __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c, const Lds& sm,
                                             floatx4 (&st)[8]) {
   uint16_t* const Qs = sm.Qs;
@@ -147,6 +150,7 @@ __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c
   uint16_t* const Vs = sm.Vs;
   uint16_t* const Ph = sm.Ph;
   uint16_t* const Pl = sm.Pl;
+  float* const Ob = sm.Ob;
 
   const int H = a.num_heads;
   const int h = c.h;
@@ -220,6 +224,89 @@ __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c
   };
   float wfull[2][8];
   vweights(wfull, kBeta);
+
+  // ---- output epilogue (kNorm): the normalisation of NormAttention (CSDN
+  // §2.1), read as an RMS normalisation of each head's output row over its
+  // d features with a per-(head, feature) weight, times sigmoid(gate) when a
+  // gate is given.  Phase 2 writes the block's fp32 output to Ob instead of
+  // storing it; after the block's closing barrier, wave w takes rows
+  // 8w .. 8w+7 whole: lane l holds row 8w + l / 8, columns 8j .. 8j+7 and
+  // 64 + 8j .. 64 + 8j+7 (j = l % 8: each of its two 16-byte accesses of a
+  // row then covers, with the other 7 lanes of the row, 128 contiguous
+  // bytes), so a row's sum of squares is a reduction over 8 consecutive lanes (three
+  // DPP steps within the VALU), and its gate values are loaded and its
+  // outputs stored as whole 256-byte rows.  Ob chunk q (16 B) of row r sits
+  // at chunk q ^ (r % 16), which keeps the tile writes (16 rows, one chunk)
+  // free of bank conflicts.  The head's weights are staged in LDS once; the
+  // gate rows of a block are loaded at the top of its step.
+  auto ob_off = [](int r, int q) { return r * kD + 4 * (q ^ (r & 15)); };
+  const int er = 8 * w + (l >> 3);  // epilogue row of this lane
+  const int ec = 8 * (l & 7);       // its first column (and ec + 64)
+  // sum over the 8 consecutive lanes of x's group: quad xor 1, quad xor 2,
+  // then each lane with lane 7 - l of its half row
+  auto sum8 = [](float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+    return x;
+  };
+  if constexpr (kNorm) {
+    if (t < kD) Ob[kBeta * kD + t] = a.norm_weight[h * kD + t];  // weights after the rows
+    // (published by the first block's barriers before the first epilogue)
+  }
+  auto load_gate = [&](uint4 (&gt)[2], int b) {
+    if constexpr (kNorm) {
+      if (a.gate) {
+        const __amdgpu_buffer_rsrc_t rg = block_rsrc(a.gate, b, 2);
+        const int off = 2 * (prow(er, block_len(b)) * row_stride + h * kD + ec);
+        gt[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+        gt[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off + 128, 0, 0));
+      }
+    }
+  };
+  auto epilogue = [&](int b, const uint4 (&gt)[2]) {
+    constexpr int ES = kOutF32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t ro = block_rsrc(c.o, b, ES);
+    floatx4 x[4];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = *reinterpret_cast<const floatx4*>(&Ob[ob_off(er, (ec >> 2) + (i & 1) + 16 * (i >> 1))]);
+      ss += x[i][0] * x[i][0] + x[i][1] * x[i][1] + x[i][2] * x[i][2] + x[i][3] * x[i][3];
+    }
+    ss = sum8(ss);
+    const float inv = rsqrtf(ss * (1.0f / kD) + a.norm_eps);
+    const float* wb = &Ob[kBeta * kD + ec];
+    const uint32_t* gw = reinterpret_cast<const uint32_t*>(&gt[0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      floatx4 f = *reinterpret_cast<const floatx4*>(wb + 4 * (i & 1) + 64 * (i >> 1)) * inv;
+      if (a.gate) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t pw = gw[2 * i + (m >> 1)];
+          const float gv = (m & 1) ? bf16_hi(pw) : bf16_lo(pw);
+          // sigmoid(gv) = 1 / (1 + 2^(-gv log2 e)), hardware exp2 and reciprocal
+          f[m] *= __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gv));
+        }
+      }
+      x[i] *= f;
+    }
+    const int off = ES * (prow(er, block_len(b)) * row_stride + h * kD + ec);
+    if constexpr (kOutF32) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x[i]), ro,
+                                               off + 16 * (i & 1) + 256 * (i >> 1), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{cvt2(x[2 * i][0], x[2 * i][1]), cvt2(x[2 * i][2], x[2 * i][3]),
+                  cvt2(x[2 * i + 1][0], x[2 * i + 1][1]), cvt2(x[2 * i + 1][2], x[2 * i + 1][3])},
+            ro, off + 128 * i, 0, 0);
+    }
+  };
 
   // ---- staging: thread t moves 16 B chunks t and t + 512 of each block
   // (row id / 16, chunk id % 16) of Q, K and V ----
@@ -347,6 +434,11 @@ __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c
 #pragma unroll
           for (int qt = 2 * kk2; qt < 4; ++qt)
             acc[qt] = mfma(va[kk2], ld8(&(hl ? Pl : Ph)[p_off(16 * qt + li, 4 * kk2 + g)]), acc[qt]);
+      if constexpr (kNorm) {  // to Ob; the epilogue stores the normalised rows
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt)
+          *reinterpret_cast<floatx4*>(&Ob[ob_off(16 * qt + li, 4 * w + g)]) = acc[qt];
+      } else {
 #pragma unroll
       for (int qt = 0; qt < 4; ++qt) {
         // lane (li, g): query 16 qt + li, value columns c0 + 4g + (0..3)
@@ -357,6 +449,7 @@ __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c
           __builtin_amdgcn_raw_buffer_store_b64(
               u32x2{cvt2(acc[qt][0], acc[qt][1]), cvt2(acc[qt][2], acc[qt][3])}, ro, off, 0, 0);
         }
+      }
       }
     }
     // decayed values lambda^(ell-1-j) V as hi/lo operands; only the last
@@ -445,12 +538,15 @@ __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c
       constexpr int cur = decltype(cur_)::value;
       Stage r;
       load_stage(r, b + 1);  // empty range past the last block
+      uint4 gt[2] = {};
+      load_gate(gt, b);
       asm volatile("" ::: "memory");
       phase1(cur_);
       lds_barrier();
       phase2(cur_, b);
       if (b + 1 < nblocks) store_stage(r, cur ^ 1);
       lds_barrier();
+      if constexpr (kNorm) epilogue(b, gt);
     };
     for (int b = 0; b < nblocks; b += 2) {
       step(b, IC<0>{});
@@ -463,7 +559,7 @@ __device__ __forceinline__ void wide_blocks(const PrefillArgs& a, const Chain& c
 // One whole chain: the state from kv_init[s, h] (slot map, transposition
 // and scale as the chain asks) or zeros, the blocks, then the final state to
 // kv_final[s, h].
-template <bool kOutF32, bool kStateOnly>
+template <bool kOutF32, bool kStateOnly, bool kNorm = false>
 __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c, const Lds& sm) {
   const int H = a.num_heads;
   const int h = c.h;
@@ -487,7 +583,7 @@ __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c,
     }
   }
 
-  wide_blocks<kOutF32, kStateOnly>(a, c, sm, st);
+  wide_blocks<kOutF32, kStateOnly, kNorm>(a, c, sm, st);
 
   if (c.kv_final) {
     const float final_scale = c.final_pow == 0.0f ? 1.0f : exp2f(c.final_pow * l2);
@@ -499,18 +595,21 @@ __device__ __forceinline__ void wide_chain(const PrefillArgs& a, const Chain& c,
   }
 }
 
-// LDS of a full chain (kStateOnly: of a state-only chain).
-#define LA_WIDE_LDS(kStateOnly)                                                       \
+// LDS of a full chain (kStateOnly: of a state-only chain; kNorm: with the
+// output rows of a block for the normalisation).
+#define LA_WIDE_LDS(kStateOnly, kNorm)                                                \
   __shared__ __attribute__((aligned(16))) uint16_t Qs_[(kStateOnly) ? 8 : 2 * kTok];  \
   __shared__ __attribute__((aligned(16))) uint16_t Ks_[2 * kTok];                     \
   __shared__ __attribute__((aligned(16))) uint16_t Vs_[2 * kTok];                     \
   __shared__ __attribute__((aligned(16))) uint16_t Ph_[(kStateOnly) ? 8 : kBeta * kBeta]; \
   __shared__ __attribute__((aligned(16))) uint16_t Pl_[(kStateOnly) ? 8 : kBeta * kBeta]; \
-  const Lds sm{Qs_, Ks_, Vs_, Ph_, Pl_}
+  __shared__ __attribute__((aligned(16))) float Ob_[(kNorm) ? kBeta * kD + kD : 4];   \
+  const Lds sm{Qs_, Ks_, Vs_, Ph_, Pl_, Ob_}
 
 // Prefill: workgroup i runs the chain of head i % H of the (i / H)-th
-// sequence in dispatch order, forwards in time (or backwards, kReverse).
-template <bool kOutF32, bool kStateOnly, bool kReverse>
+// sequence in dispatch order, forwards in time (or backwards, kReverse);
+// kNorm: with the output normalisation (forwards, full chains only).
+template <bool kOutF32, bool kStateOnly, bool kReverse, bool kNorm = false>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   Chain c;
   c.q = a.q;
@@ -525,8 +624,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   c.init_transposed = false;
   c.init_pow = 0.0f;
   c.final_pow = 0.0f;
-  LA_WIDE_LDS(kStateOnly);
-  wide_chain<kOutF32, kStateOnly>(a, c, sm);
+  LA_WIDE_LDS(kStateOnly, kNorm);
+  wide_chain<kOutF32, kStateOnly, kNorm>(a, c, sm);
 }
 
 // The three chains of the backward pass in one launch: item i runs pass
@@ -551,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void backward_wide_kernel(PrefillArgs a, 
   c.init_transposed = p.init_transposed != 0;
   c.init_pow = p.init_pow;
   c.final_pow = p.final_pow;
-  LA_WIDE_LDS(false);
+  LA_WIDE_LDS(false, false);
   wide_chain<kOutF32, false>(a, c, sm);
 }
 
@@ -608,9 +707,9 @@ constexpr int kCtrlTicket = 0;
 constexpr int kCtrlError = 1;
 constexpr int kCtrlFlags = 2;  // then 2 flags per (sequence, head) chain
 
-template <bool kOutF32>
+template <bool kOutF32, bool kNorm>
 __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a, ScanArgs sa) {
-  LA_WIDE_LDS(false);
+  LA_WIDE_LDS(false, kNorm);
   __shared__ int32_t ticket_s;
   const int t = threadIdx.x;
   if (t == 0)
@@ -709,7 +808,7 @@ __global__ __launch_bounds__(kThreads) void prefill_scan_kernel(PrefillArgs a, S
   __syncthreads();
 
   // C: the segment's outputs from its start state
-  wide_blocks<kOutF32, false>(a, c, sm, st);
+  wide_blocks<kOutF32, false, kNorm>(a, c, sm, st);
   if (last && sa.kv_final) {
     const int64_t off = (int64_t)chain * kD * kD;
 #pragma unroll
@@ -751,12 +850,27 @@ hipError_t launch_backward_wide(const PrefillArgs& a, const BackwardPasses& bp,
 }
 
 hipError_t launch_prefill_scan(const PrefillArgs& a, const ScanArgs& sa, la_dtype out_dtype,
-                               hipStream_t stream) {
+                               bool norm, hipStream_t stream) {
+  const dim3 grid(a.num_items), block(kThreads);
+  const bool f32 = out_dtype == LA_FP32;
+  if (norm && f32)
+    hipLaunchKernelGGL((prefill_scan_kernel<true, true>), grid, block, 0, stream, a, sa);
+  else if (norm)
+    hipLaunchKernelGGL((prefill_scan_kernel<false, true>), grid, block, 0, stream, a, sa);
+  else if (f32)
+    hipLaunchKernelGGL((prefill_scan_kernel<true, false>), grid, block, 0, stream, a, sa);
+  else
+    hipLaunchKernelGGL((prefill_scan_kernel<false, false>), grid, block, 0, stream, a, sa);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_wide_normed(const PrefillArgs& a, la_dtype out_dtype,
+                                      hipStream_t stream) {
   const dim3 grid(a.num_items), block(kThreads);
   if (out_dtype == LA_FP32)
-    hipLaunchKernelGGL(prefill_scan_kernel<true>, grid, block, 0, stream, a, sa);
+    hipLaunchKernelGGL((prefill_wide_kernel<true, false, false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_scan_kernel<false>, grid, block, 0, stream, a, sa);
+    hipLaunchKernelGGL((prefill_wide_kernel<false, false, false, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

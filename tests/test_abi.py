@@ -28,7 +28,8 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("la_prefill", "la_prefill_segmented", "la_prefill_segmented_workspace_size",
-              "la_prefill_segmented_noalloc",
+              "la_prefill_segmented_noalloc", "la_prefill_normed",
+              "la_prefill_normed_workspace_size", "la_decode_normed",
               "la_prefill_backward", "la_prefill_backward_workspace_size",
               "la_prefill_backward_segmented", "la_prefill_backward_segmented_workspace_size",
               "la_prefill_pool", "la_decode", "la_decode_pool", "la_status_str",
@@ -313,6 +314,94 @@ def test_segmented_noalloc_rejects(name, kw, code):
 def test_segmented_noalloc_no_sequences():
     st, _ = _seg_noalloc(S=0, T=0, cu_host=np.array([0], np.int32))
     assert st == la.LA_OK
+
+
+# ---- output normalisation (host-side checks only) ----
+
+NW, GT = 0xB0000000, 0xC0000000
+
+
+def _prefill_normed(norm="default", **kw):
+    args = dict(q=Q, k=K, v=V, cu_dev=CUD, cu_host=np.array([0, 40, 100], np.int32), S=2, T=T,
+                H=H, d=D, in_dt=la.LA_BF16, out_dt=la.LA_BF16,
+                decay=np.full(H, 0.9, np.float32), kv_init=None, o=O, kv_final=KVF, ws=WS,
+                ws_bytes=1 << 30)
+    args.update(kw)
+    nm = la.LaNorm(NW, 1e-6, GT) if norm == "default" else norm
+    cu = args["cu_host"]
+    st = la.la_prefill_normed(args["q"], args["k"], args["v"], args["cu_dev"], cu.ctypes.data,
+                              args["S"], args["T"], args["H"], args["d"], args["in_dt"],
+                              args["out_dt"], args["decay"].ctypes.data, args["kv_init"], nm,
+                              args["o"], args["kv_final"], args["ws"], args["ws_bytes"], None)
+    return st, la.la_last_error()
+
+
+BAD_NORMED = [
+    ("norm_null", dict(norm=None), la.LA_ERR_INVALID_ARG),
+    ("weight_null", dict(norm=la.LaNorm(None, 1e-6, GT)), la.LA_ERR_INVALID_ARG),
+    ("eps_zero", dict(norm=la.LaNorm(NW, 0.0, None)), la.LA_ERR_INVALID_ARG),
+    ("eps_negative", dict(norm=la.LaNorm(NW, -1.0, None)), la.LA_ERR_INVALID_ARG),
+    ("eps_nan", dict(norm=la.LaNorm(NW, float("nan"), None)), la.LA_ERR_INVALID_ARG),
+    ("eps_inf", dict(norm=la.LaNorm(NW, float("inf"), None)), la.LA_ERR_INVALID_ARG),
+    ("weight_misaligned", dict(norm=la.LaNorm(NW + 4, 1e-6, None)), la.LA_ERR_INVALID_ARG),
+    ("gate_misaligned", dict(norm=la.LaNorm(NW, 1e-6, GT + 8)), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_gate", dict(o=GT + 256), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_weight", dict(o=NW - 256), la.LA_ERR_INVALID_ARG),
+    ("fp32_input", dict(in_dt=la.LA_FP32, out_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
+    ("head_dim_64", dict(d=64), la.LA_ERR_UNSUPPORTED),
+    ("workspace_null", dict(ws=None), la.LA_ERR_INVALID_ARG),
+    ("workspace_short", dict(ws_bytes=256), la.LA_ERR_INVALID_ARG),
+    ("workspace_overlaps_gate", dict(ws=GT - 4096), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_NORMED, ids=[b[0] for b in BAD_NORMED])
+def test_prefill_normed_rejects(name, kw, code):
+    st, msg = _prefill_normed(**kw)
+    assert st == code, (st, msg)
+    assert msg
+
+
+def test_prefill_normed_workspace_size():
+    """Without a GPU the compute-unit count is taken as 256: 2 sequences x 4
+    heads use the chained scan, whose ring holds 2 states per pair; 64
+    sequences x 4 heads (256 pairs) need no workspace."""
+    cu = np.array([0, 40, 100], np.int32)
+    st, n = la.la_prefill_normed_workspace_size(2, cu.ctypes.data, 4, 128)
+    assert st == la.LA_OK and n >= 2 * 2 * 4 * 128 * 128 * 4
+    cu64 = np.arange(0, 65 * 10, 10, dtype=np.int32)
+    st, n = la.la_prefill_normed_workspace_size(64, cu64.ctypes.data, 4, 128)
+    assert st == la.LA_OK and n == 0
+    assert la.la_prefill_normed_workspace_size(2, cu.ctypes.data, 4, 64)[0] == la.LA_ERR_UNSUPPORTED
+    assert la.la_prefill_normed_workspace_size(2, None, 4, 128)[0] == la.LA_ERR_INVALID_ARG
+
+
+def _decode_normed(norm="default", **kw):
+    args = dict(q=Q, k=K, v=V, kv=KVF, decay=np.full(H, 0.9, np.float32), B=3, H=H, d=D,
+                dt=la.LA_BF16, o=O)
+    args.update(kw)
+    nm = la.LaNorm(NW, 1e-6, GT) if norm == "default" else norm
+    st = la.la_decode_normed(args["q"], args["k"], args["v"], args["kv"],
+                             args["decay"].ctypes.data, args["B"], args["H"], args["d"],
+                             args["dt"], nm, args["o"], None)
+    return st, la.la_last_error()
+
+
+BAD_DECODE_NORMED = [
+    ("norm_null", dict(norm=None), la.LA_ERR_INVALID_ARG),
+    ("eps_zero", dict(norm=la.LaNorm(NW, 0.0, None)), la.LA_ERR_INVALID_ARG),
+    ("gate_misaligned", dict(norm=la.LaNorm(NW, 1e-6, GT + 2)), la.LA_ERR_INVALID_ARG),
+    ("o_overlaps_gate", dict(o=GT), la.LA_ERR_INVALID_ARG),
+    ("kv_overlaps_weight", dict(kv=NW - 64), la.LA_ERR_INVALID_ARG),
+    ("negative_batch", dict(B=-1), la.LA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD_DECODE_NORMED, ids=[b[0] for b in BAD_DECODE_NORMED])
+def test_decode_normed_rejects(name, kw, code):
+    st, msg = _decode_normed(**kw)
+    assert st == code, (st, msg)
+    assert msg
 
 
 # ---- decode on a state pool (host-side checks only) ----

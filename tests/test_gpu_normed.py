@@ -1,0 +1,132 @@
+"""GPU parity of the fused output normalisation (la_prefill_normed,
+la_decode_normed) against the fp64 oracle: the oracle's prefill or decode
+output passed through oracle.norm_gate (needs an MI355X)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from la_inputs import cu_seqlens, host_qkv, random_states
+from tests import parity
+from tests.gpu_util import device, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _weights(H, d, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.uniform(0.5, 1.5, (H, d)).astype(np.float32)
+
+
+def _prefill_case(dev, lengths, H, decay, seed, gate, out_f32, kv_init, heads):
+    import torch
+    import linear_attention_la_amd as la
+
+    d = 128
+    say(f"case normed prefill lengths={lengths[:6]} H={H} gate={gate} out_f32={out_f32} "
+        f"kv_init={kv_init}")
+    T = int(sum(lengths))
+    q, k, v = host_qkv(T, H, d, seed, "bf16")
+    g = host_qkv(T, H, d, seed + 1, "bf16")[0] * 20.0 if gate else None  # gate logits ~ N(0, 3)
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(len(lengths), H, d, seed + 2, scale=0.1) if kv_init else None
+    w = _weights(H, d, seed + 3)
+    eps = 1e-5
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    gd = to_dev(g, torch.bfloat16, dev) if gate else None
+    g_exact = to_np(gd) if gate else None  # the gate values as the GPU sees them
+    kv0d = to_dev(kv0, torch.float32, dev) if kv_init else None
+    y, kv = la.prefill_normed(qd, kd, vd, cu, decay, to_dev(w, torch.float32, dev), eps, gd,
+                              kv_init=kv0d, out_dtype=torch.float32 if out_f32 else None)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.prefill_varlen(q[:, heads], k[:, heads], v[:, heads], cu,
+                                          np.asarray(decay)[heads],
+                                          kv_init=None if kv0 is None else kv0[:, heads])
+    y_ref = oracle.norm_gate(o_ref, w[heads], eps, None if g_exact is None else g_exact[:, heads])
+    s1 = parity.check(to_np(y)[:, heads], y_ref, 1, 1e-2, out_bf16=not out_f32,
+                      what="normed prefill y")
+    s2 = parity.check(to_np(kv)[:, heads], kv_ref, 1, 1e-2, what="normed prefill kv")
+    say("normed prefill", s1, s2)
+    return y
+
+
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_prefill_normed_wide(dev, gate, out_f32):
+    """320 (sequence, head) pairs: one workgroup per pair, epilogue fused into
+    its output write; ragged lengths incl. empty, 1 and block edges."""
+    H = 64
+    lengths = [1, 63, 300, 0, 129]
+    decay = np.exp(-np.linspace(0.001, 0.1, H)).astype(np.float32)
+    decay[0] = 1.0
+    _prefill_case(dev, lengths, H, decay, 301 + gate + 2 * out_f32, gate, out_f32, kv_init=True,
+                  heads=[0, 1, 31, 63])
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_prefill_normed_scan(dev, gate):
+    """Few pairs (3 sequences x 4 heads): the chained scan over segments of
+    a length the library picks, epilogue fused into the output pass."""
+    decay = np.array([1.0, 0.99, 0.9, 0.5], np.float32)
+    _prefill_case(dev, [700, 0, 333], 4, decay, 311 + gate, gate, False, kv_init=True,
+                  heads=[0, 1, 2, 3])
+
+
+def test_prefill_normed_long_single(dev):
+    """One 8192-token sequence x 16 heads (the scan, 16 segments a head)."""
+    decay = np.exp(-np.linspace(0.001, 0.1, 16)).astype(np.float32)
+    _prefill_case(dev, [8192], 16, decay, 321, True, False, kv_init=False, heads=[0, 7, 15])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("gate", [False, True])
+def test_decode_normed(dev, d, dtype, gate):
+    import torch
+    import linear_attention_la_amd as la
+
+    B, H = 5, 3
+    decay = np.array([1.0, 0.97, 0.5], np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say(f"case normed decode d={d} dtype={dtype} gate={gate}")
+    kv = random_states(B, H, d, 331 + d)
+    kvd = to_dev(kv, torch.float32, dev)
+    q, k, v = (x[:B * H].reshape(B, H, d) for x in host_qkv(B * H, 1, d, 332 + d, dtype))
+    g = host_qkv(B * H, 1, d, 333 + d, dtype)[0][:B * H].reshape(B, H, d) * 20.0 if gate else None
+    w = _weights(H, d, 334)
+    gd = to_dev(g, tdt, dev) if gate else None
+    y = la.decode_normed(to_dev(q, tdt, dev), to_dev(k, tdt, dev), to_dev(v, tdt, dev), kvd, decay,
+                         to_dev(w, torch.float32, dev), 1e-5, gd)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.decode_batch(to_np(to_dev(q, tdt, dev)), to_np(to_dev(k, tdt, dev)),
+                                        to_np(to_dev(v, tdt, dev)), kv, decay)
+    y_ref = oracle.norm_gate(o_ref, w, 1e-5, to_np(gd) if gate else None)
+    tol = 1e-5 if dtype == "fp32" else 1e-2
+    parity.check(to_np(y), y_ref, 1, tol, out_bf16=(dtype == "bf16"), what="normed decode y")
+    parity.check(to_np(kvd), kv_ref, 1, 1e-5, what="normed decode kv")
+
+
+def test_prefill_normed_unit_weight_matches_plain(dev):
+    """With unit weights and no gate, the normed output of the wide path is
+    the plain output normalised: checked against la_prefill's output rows
+    normalised on the host (both from the same kernel's fp32 sums, so they
+    agree to the output rounding)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    H, d, lengths = 64, 128, [200, 100, 57, 90]
+    T = sum(lengths)
+    q, k, v = (to_dev(x, torch.bfloat16, dev) for x in host_qkv(T, H, d, 341, "bf16"))
+    decay = np.full(H, 0.95, np.float32)
+    o, _ = la.prefill(q, k, v, cu_seqlens(lengths), decay, out_dtype=torch.float32)
+    y, _ = la.prefill_normed(q, k, v, cu_seqlens(lengths), decay,
+                             torch.ones((H, d), dtype=torch.float32, device=dev), 1e-6,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.norm_gate(to_np(o), np.ones((H, d)), 1e-6)
+    parity.check(to_np(y), ref, 1, 1e-5, what="normed vs plain")
