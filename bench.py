@@ -7,12 +7,17 @@ bf16 Q/K/V ~ N(0,1)/sqrt(d), per-head decay exp(-U[0.001, 0.1]) (the
 MiniMax-Text-01 lightning-layer shape at its 8192-token pretraining length).
 Inputs are resident in HBM before timing starts; two input sets alternate
 (1.08 GB together, four times the 256 MB Infinity Cache) so no step reads
-inputs left in cache by the step before.  W untimed warmup steps, then K
-timed steps bracketed by torch.cuda.synchronize().
+inputs left in cache by the step before.  The step first runs untimed for
+--settle-ms (200 ms: the GPU raises its clocks only after tens of ms of
+sustained load), then W untimed warmup steps, then K timed steps back to
+back, bracketed by torch.cuda.synchronize() and by one HIP event pair on
+the launch stream.  Every other timed region below is preceded by the same
+untimed settle of the operation it times.
 
 One JSON line is printed with the contract fields plus:
   roofline      the prefill kernel's algorithmic HBM bytes per launch over
-                its average launch time (HIP events on its stream), against
+                its average launch time (one HIP event pair on its stream
+                around the K timed steps), against
                 8 TB/s; `traffic` is the counter-measured bytes per launch
                 from profiles/ if it was taken on the current kernel source.
   cpu_baseline  the fp64 oracle (blockwise, beta=64) timed on the host cores
@@ -24,9 +29,10 @@ One JSON line is printed with the contract fields plus:
   peaks         measured on the GPU: a 1 GiB read+write stream (HBM) and an 8192^3
                 bf16 matmul; roofline.frac_of_measured_stream relates the
                 prefill kernel to that stream.
-  sweep         cold tokens/s (median, min) at N = 1K ... 1M, for eight 8K sequences in one
-                call and for a packed varlen batch (the last two have enough
-                (sequence, head) chains for the one-workgroup-per-chain kernel).
+  sweep         tokens/s at N = 1K ... 1M, for eight 8K sequences in one call and
+                for a packed varlen batch (the last two have enough (sequence,
+                head) chains for the one-workgroup-per-chain kernel): back-to-back
+                launches over input sets that together exceed 1 GiB.
 """
 
 import argparse
@@ -115,6 +121,29 @@ def timed_launches(fn, reps, stream, flush=None):
     """Average duration (s) of `fn` over `reps` launches (see launch_times)."""
     t = launch_times(fn, reps, stream, flush)
     return sum(t) / len(t)
+
+
+SETTLE_S = 0.2  # set from --settle-ms
+
+
+def settle(fn, seconds=None):
+    """Run ``fn`` back to back, untimed, for ``seconds`` (default: the
+    --settle-ms setting) and wait for it: the GPU raises its clocks only
+    after tens of milliseconds of sustained load and lowers them again after
+    an idle gap, so every timed region is preceded by this.  Returns the
+    number of launches."""
+    import torch
+
+    seconds = SETTLE_S if seconds is None else seconds
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(i)
+        i += 1
+        if i % 8 == 0:  # keep the queue short so the host clock tracks the GPU
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return i
 
 
 def measured_peaks(dev):
@@ -234,6 +263,7 @@ def bench_decode(dev, reps=20):
     s = torch.cuda.current_stream()
     for _ in range(3):
         la.decode(q, k, v, kv, w["decay"], out=out)
+    settle(lambda i: la.decode(q, k, v, kv, w["decay"], out=out))
     t = timed_launches(lambda i: la.decode(q, k, v, kv, w["decay"], out=out), reps, s)
     gbs = decode_bytes(B) / t / 1e9
     return {"batch": B, "heads": H, "head_dim": D, "us": round(t * 1e6, 2),
@@ -262,6 +292,7 @@ def bench_decode_pool(dev, reps=20, pool_size=1024):
                                    slots_host=slots_h)
     for _ in range(3):
         run(0)
+    settle(run)
     t = timed_launches(run, reps, s)
     gbs = decode_bytes(B) / t / 1e9
     del pool
@@ -454,6 +485,7 @@ def bench_normed(dev, reps=10):
                                      cu_seqlens_host=cu)
         for fn in (fused, unfused, fused_ng, plain):
             fn(0)
+        settle(fused)
         med = lambda fn: sorted(launch_times(fn, reps, s, flush=lambda: scratch.zero_()))[reps // 2]  # noqa
         tf, tu, tn, tp = med(fused), med(unfused), med(fused_ng), med(plain)
         by = prefill_bytes(T, S) + T * H * D * 2
@@ -474,6 +506,7 @@ def bench_normed(dev, reps=10):
     unfused = lambda i: epilogue(la.decode(q, k, v, kv, wd["decay"], out=out), gate)  # noqa
     for fn in (fused, unfused):
         fn(0)
+    settle(fused)
     tf = timed_launches(fused, 20, s)
     tu = timed_launches(unfused, 20, s)
     res["decode_b256"] = {"fused_us": round(tf * 1e6, 1), "unfused_us": round(tu * 1e6, 1),
@@ -487,7 +520,16 @@ SWEEP = ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodec
          "batch8_n8k", "varlen64")
 
 
-def bench_sweep(dev, reps=20, names=SWEEP):
+def bench_sweep(dev, reps=20, names=SWEEP, footprint=1 << 30):
+    """Tokens/s per workload of the length / batch sweep.  Several input sets
+    are generated so that together they exceed ``footprint`` (1 GiB, four
+    times the 256 MB Infinity Cache; one set when a set alone is larger), and
+    ``reps`` launches (5 for the 1M-token workloads) run back to back over
+    them in turn, so no launch finds its inputs in cache; one event pair on
+    the stream around them gives the average launch time (``us``).  For
+    comparison with earlier records, ``us_single`` is the median of single
+    launches each bracketed by its own events after a 1 GiB cache flush
+    (events between launches add ~20 us to each)."""
     import torch
 
     import linear_attention_la_amd as la
@@ -500,23 +542,37 @@ def bench_sweep(dev, reps=20, names=SWEEP):
         w = workload(name)
         cu = cu_seqlens(w["lengths"])
         T = int(cu[-1])
-        q, k, v = device_qkv(T, H, D, w["seed"], dev)
+        S = len(w["lengths"])
+        set_bytes = T * H * D * 2 * 3
+        n_sets = 1 if set_bytes >= footprint else -(-footprint // set_bytes)
+        sets = [device_qkv(T, H, D, w["seed"] + 100 * i, dev) for i in range(n_sets)]
         cu_dev = torch.from_numpy(cu).to(dev)
-        o = torch.empty_like(q)
-        kvf = torch.empty((len(w["lengths"]), H, D, D), dtype=torch.float32, device=dev)
-        run = lambda i: la.prefill(q, k, v, cu_dev, w["decay"], out=o, kv_final=kvf,  # noqa
-                                   cu_seqlens_host=cu)
-        run(0)
-        n = reps if T <= 1 << 17 else 5  # >= 20 repeats, 5 for the 1M-token workloads
+        o = torch.empty_like(sets[0][0])
+        kvf = torch.empty((S, H, D, D), dtype=torch.float32, device=dev)
+
+        def run(i):
+            q, k, v = sets[i % n_sets]
+            la.prefill(q, k, v, cu_dev, w["decay"], out=o, kv_final=kvf, cu_seqlens_host=cu)
+
+        n = reps if T <= 1 << 17 else 5
+        for i in range(min(n, 3)):
+            run(i)
+        settle(run)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for i in range(n):
+            run(i)
+        e1.record(s)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / n / 1e3
         ts = sorted(launch_times(run, n, s, flush=lambda: scratch.zero_()))
-        t = ts[len(ts) // 2]
-        by = prefill_bytes(T, len(w["lengths"]))
-        res[name] = {"tokens": T, "seqs": len(w["lengths"]), "us": round(t * 1e6, 1),
-                     "us_min": round(ts[0] * 1e6, 1),
+        by = prefill_bytes(T, S)
+        res[name] = {"tokens": T, "seqs": S, "us": round(t * 1e6, 1),
+                     "us_single": round(ts[len(ts) // 2] * 1e6, 1), "input_sets": n_sets,
                      "tokens_per_s": round(T / t, 0), "GB_per_s": round(by / t / 1e9, 1),
                      "frac_of_8TBs": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
                      "tflops_beta64": round(prefill_flops(T) / t / 1e12, 1)}
-        del q, k, v, o, kvf
+        del sets, o, kvf
         torch.cuda.empty_cache()
     return res
 
@@ -550,6 +606,7 @@ def bench_backward(dev, reps=10, name="n8k"):
                                         dk=dk, dv=dv, dkv_init=dkv0)
     for _ in range(3):
         run(0)
+    settle(run)
     t = timed_launches(run, reps, torch.cuda.current_stream())
     by = N * H * 14 * D + 3 * S * H * D * D * 4
     del q, k, v, do, dq, dk, dv, ws
@@ -592,7 +649,9 @@ def bench_segmented(dev, reps=3):
                                          kv_final=kvf, cu_seqlens_host=cu, workspace=ws)
     plain(0)
     seg(0)
+    settle(plain)
     tp = timed_launches(plain, reps, s, flush=lambda: scratch.zero_())
+    settle(seg)
     ts = timed_launches(seg, reps, s, flush=lambda: scratch.zero_())
     by = prefill_bytes(SEG_N, 1, heads=SEG_H)
     res = {"workload": f"B=1 H={SEG_H} N={SEG_N} d={D} bf16, one sequence",
@@ -640,7 +699,9 @@ def bench_backward_segmented(dev, reps=2):
     plain(0)
     seg(0)
     s = torch.cuda.current_stream()
+    settle(plain)
     tp = timed_launches(plain, reps, s)
+    settle(seg)
     ts = timed_launches(seg, reps, s)
     by = SEG_N * SEG_H * 14 * D + 3 * SEG_H * D * D * 4
     del q, k, v, do, dq, dk, dv, ws, wsp
@@ -659,6 +720,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true", help="skip decode/mixed/sweep")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps for this long before the warm-up steps (clock ramp)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
@@ -678,6 +741,8 @@ def main():
                     help="only time la_prefill vs la_prefill_segmented (and the two "
                          "backwards) at B=1, H=8, N=1M")
     args = ap.parse_args()
+    global SETTLE_S
+    SETTLE_S = args.settle_ms / 1e3
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
@@ -740,20 +805,27 @@ def main():
         q, k, v = sets[i & 1]
         la.prefill(q, k, v, cu_dev, decay, out=o, kv_final=kvf, cu_seqlens_host=cu_host)
 
+    # Settle: the GPU raises its clocks only after tens of milliseconds of
+    # sustained load (measured on this workload: 201 us a launch after 5
+    # launches, 172-174 us after 150, and 206 us again after 0.5 s idle), so
+    # the step runs untimed for --settle-ms before the W warm-up steps.
+    settle_steps = settle(step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # One event pair around the K back-to-back steps (events between steps
+    # would serialise the stream and add ~20 us to every launch): the
+    # kernel's average launch duration over the timed region.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        ev0[i].record(stream)
         step(i)
-        ev1[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_s = sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / args.steps / 1e3
+    kern_s = ev0.elapsed_time(ev1) / args.steps / 1e3
 
     tokens_per_s = N * args.steps / elapsed
     by = prefill_bytes(N, 1)
@@ -772,6 +844,7 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "prefill_bf16_kernel<128, false, false, false>",
                      "kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes": by},
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "mfma": {"tflops_algorithmic_beta64": round(tflops, 2),
                  "frac_of_2500": round(tflops / BF16_PEAK_TFLOPS, 4)},
     }
