@@ -1,6 +1,7 @@
 // Internal pieces of the backward pass (not part of the public ABI): its
-// three chains in one launch of the one-workgroup-per-chain prefill kernel
-// (d = 128), and an in-place state transpose for the segmented backward.
+// chains side by side in one launch of the one-workgroup-per-chain prefill
+// kernel (d = 128), and an in-place state transpose for the segmented
+// backward.
 #pragma once
 
 #include "la_internal.h"
@@ -25,11 +26,16 @@ struct BackwardPass {
   float final_pow;
 };
 
+// num_passes (2 or 3) passes of every chain; item i runs pass
+// i % num_passes of chain i / num_passes, and the passes of a chain go to
+// one XCD.
 struct BackwardPasses {
   BackwardPass pass[3];
+  int32_t num_passes;
 };
 
-// a.num_items = 3 * S * H; a carries the decays and the sequence order.
+// a.num_items = num_passes * S * H; a carries the decays, the sequence order
+// and the slot map of the initial states.
 hipError_t launch_backward_wide(const PrefillArgs& a, const BackwardPasses& bp,
                                 la_dtype grad_dtype, hipStream_t stream);
 

@@ -515,13 +515,15 @@ namespace {
 // launch_segment_prefix).  Arguments have been validated; ws holds the
 // layout `lay`; kv_init / kv_final may be NULL.  With outputs_only the plan
 // and the segment start states already in ws are used as they are (only the
-// output pass runs; kv_init and kv_final are then unused).
+// output pass runs; kv_init and kv_final are then unused); with states_only
+// the output pass is left out (the segment start states and kv_final are
+// written; o is unused).
 la_status segmented_chain(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_dev,
                           int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                           la_dtype out_dtype, const float* l2, const float* kv_init, void* o,
                           float* kv_final, const SegmentLayout& lay, char* ws, bool reverse,
                           hipStream_t s, bool outputs_only = false,
-                          const la_norm* norm = nullptr) {
+                          const la_norm* norm = nullptr, bool states_only = false) {
   int32_t* cu_seg = reinterpret_cast<int32_t*>(ws + lay.cu_seg);
   int32_t* init_slot = reinterpret_cast<int32_t*>(ws + lay.init_slot);
   int32_t* final_slot = reinterpret_cast<int32_t*>(ws + lay.final_slot);
@@ -585,6 +587,7 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
     e = la::launch_segment_prefix(cu_seg, seq_first, num_seqs, num_heads, head_dim, l2, kv_init,
                                   states, kv_final, reverse, s);
     if (e != hipSuccess) return hip_status(e, "segmented prefix launch");
+    if (states_only) return ok();
   }
 
   // pass 3: outputs of every segment from its start state
@@ -1018,6 +1021,7 @@ la_status la_prefill_backward(const void* q, const void* k, const void* v, const
     bp.pass[0] = {d_o, v, k, dq, kv_init, nullptr, 0, 1, 0.0f, 0.0f};          // dQ
     bp.pass[1] = {v, d_o, q, dk, dkv_final, nullptr, 1, 1, -1.0f, 0.0f};       // dK
     bp.pass[2] = {k, q, d_o, dv, dkv_final, dkv_init, 1, 0, -1.0f, 1.0f};      // dV, dS0
+    bp.num_passes = 3;
     a.num_items = 3 * num_seqs * num_heads;
     const hipError_t e = la::launch_backward_wide(a, bp, grad_dtype, s);
     return e != hipSuccess ? hip_status(e, "la_prefill_backward launch") : ok();
@@ -1158,21 +1162,46 @@ la_status la_prefill_backward_segmented(
     e = la::launch_state_transform(dkv_final, init, num_seqs, num_heads, head_dim, true, inv, s);
     if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
   }
-  st = segmented_chain(v, d_o, q, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
-                       dkv_final ? init : nullptr, dk, dkv_init, lay, ws, true, s);
-  if (st != LA_OK) return st;
   // dV: backwards with K, Q, dO and dS_L / lambda.  Its keys and values are
   // the dK chain's values and keys, with the same decays and the transposed
   // initial state, so each of its states is the transpose of the dK chain's
-  // state at the same point: the dK chain's segment start states, transposed
-  // in place, are the dV chain's, and only its output pass runs.
+  // state at the same point: the dK chain's segment start states, read
+  // transposed, are the dV chain's, and only its output pass runs.
   float* states = reinterpret_cast<float*>(ws + lay.states);
-  e = la::launch_state_transpose_inplace(states, (lay.num_segments + num_seqs) * num_heads,
-                                         num_heads, head_dim, one, s);
-  if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
-  st = segmented_chain(k, q, d_o, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype, l2,
-                       nullptr, dv, nullptr, lay, ws, true, s, true);
-  if (st != LA_OK) return st;
+  if (use_wide((int64_t)lay.num_segments * num_heads, head_dim)) {
+    // The dK chain's local states and prefix, then the output passes of dK
+    // and dV side by side in one launch: the two items of a (segment, head)
+    // run on one XCD and read the same Q and dO rows at the same time.
+    st = segmented_chain(v, d_o, q, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype,
+                         l2, dkv_final ? init : nullptr, dk, dkv_init, lay, ws, true, s, false,
+                         nullptr, true);
+    if (st != LA_OK) return st;
+    la::PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.cu_seqlens = reinterpret_cast<const int32_t*>(ws + lay.cu_seg);
+    a.num_seqs = lay.num_segments;
+    a.num_heads = num_heads;
+    a.num_items = 2 * lay.num_segments * num_heads;
+    a.init_slot = reinterpret_cast<const int32_t*>(ws + lay.final_slot);  // start states (reverse)
+    for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = l2[h];
+    la::BackwardPasses bp;
+    memset(&bp, 0, sizeof(bp));
+    bp.pass[0] = {v, d_o, q, dk, states, nullptr, 1, 0, 0.0f, 0.0f};  // dK
+    bp.pass[1] = {k, q, d_o, dv, states, nullptr, 1, 1, 0.0f, 0.0f};  // dV: states transposed
+    bp.num_passes = 2;
+    e = la::launch_backward_wide(a, bp, grad_dtype, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented output launch");
+  } else {
+    st = segmented_chain(v, d_o, q, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype,
+                         l2, dkv_final ? init : nullptr, dk, dkv_init, lay, ws, true, s);
+    if (st != LA_OK) return st;
+    e = la::launch_state_transpose_inplace(states, (lay.num_segments + num_seqs) * num_heads,
+                                           num_heads, head_dim, one, s);
+    if (e != hipSuccess) return hip_status(e, "la_prefill_backward_segmented state launch");
+    st = segmented_chain(k, q, d_o, cu_seqlens_dev, num_seqs, num_heads, head_dim, grad_dtype,
+                         l2, nullptr, dv, nullptr, lay, ws, true, s, true);
+    if (st != LA_OK) return st;
+  }
   if (dkv_init) {  // dS0: lambda times the transpose of the dK chain's final state
     e = la::launch_state_transpose_inplace(dkv_init, num_seqs * num_heads, num_heads, head_dim,
                                            lam, s);

@@ -628,15 +628,18 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(PrefillArgs a) {
   wide_chain<kOutF32, kStateOnly, kNorm>(a, c, sm);
 }
 
-// The three chains of the backward pass in one launch: item i runs pass
-// i % 3 of chain i / 3 (head chain % H of the (chain / H)-th sequence in
-// dispatch order).  The three passes of a chain go to one XCD, where the
-// two reverse-time passes read the same Q and dO rows at the same time.
+// The chains of the backward pass in one launch: item i runs pass i % np
+// of chain i / np (head chain % H of the (chain / H)-th sequence in dispatch
+// order), np = bp.num_passes: all three chains, or the two reverse-time
+// output passes of the segmented backward.  The passes of a chain go to one
+// XCD, where the two reverse-time passes read the same Q and dO rows at the
+// same time.
 template <bool kOutF32>
 __global__ __launch_bounds__(kThreads) void backward_wide_kernel(PrefillArgs a, BackwardPasses bp) {
-  const int item = xcd_remap(blockIdx.x, a.num_items, 3);
-  const int chain = item / 3;
-  const BackwardPass& p = bp.pass[item % 3];
+  const int np = bp.num_passes;
+  const int item = xcd_remap(blockIdx.x, a.num_items, np);
+  const int chain = item / np;
+  const BackwardPass& p = bp.pass[item - chain * np];
   Chain c;
   c.q = p.q;
   c.k = p.k;

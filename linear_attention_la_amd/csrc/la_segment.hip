@@ -27,14 +27,29 @@ __device__ __forceinline__ int segments_of(int32_t len, int32_t segment_len) {
   return len <= 0 ? 1 : (int)((len + (int64_t)segment_len - 1) / segment_len);
 }
 
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+// Inclusive prefix sum over the 64 lanes of a wave (six shuffle steps).
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // One workgroup.  Thread t owns a contiguous range of sequences; a prefix
-// sum of the per-thread segment counts gives each thread its first segment.
+// sum of the per-thread segment counts (within each wave, then over the
+// wave totals) gives each thread its first segment.
 __global__ __launch_bounds__(kPlanThreads) void segment_plan_kernel(
     const int32_t* __restrict__ cu, int32_t num_seqs, int32_t segment_len, int32_t* cu_seg,
     int32_t* init_slot, int32_t* final_slot, int32_t* seq_first, int32_t* ctrl,
     int64_t ctrl_words) {
-  __shared__ int32_t part[kPlanThreads];
+  __shared__ int32_t wave_total[kPlanWaves];
   const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
   if (ctrl)
     for (int64_t x = t; x < ctrl_words; x += kPlanThreads) ctrl[x] = 0;
   const int per = (num_seqs + kPlanThreads - 1) / kPlanThreads;
@@ -42,20 +57,21 @@ __global__ __launch_bounds__(kPlanThreads) void segment_plan_kernel(
   const int s1 = min(num_seqs, s0 + per);
   int32_t count = 0;
   for (int s = s0; s < s1; ++s) count += segments_of(cu[s + 1] - cu[s], segment_len);
-  part[t] = count;
+  const int32_t incl = wave_inclusive_scan(count, lane);
+  if (lane == 63) wave_total[wave] = incl;
   __syncthreads();
+  int32_t before = 0, run = 0;  // segments of earlier waves; of all waves
+#pragma unroll
+  for (int i = 0; i < kPlanWaves; ++i) {
+    const int32_t c = wave_total[i];
+    before += i < wave ? c : 0;
+    run += c;
+  }
   if (t == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < kPlanThreads; ++i) {
-      const int32_t c = part[i];
-      part[i] = run;  // exclusive prefix
-      run += c;
-    }
     seq_first[num_seqs] = run;
     cu_seg[run] = cu[num_seqs];
   }
-  __syncthreads();
-  int32_t g = part[t];
+  int32_t g = before + incl - count;  // exclusive prefix of thread t
   for (int s = s0; s < s1; ++s) {
     seq_first[s] = g;
     const int32_t start = cu[s];

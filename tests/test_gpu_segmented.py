@@ -111,3 +111,17 @@ def test_caller_workspace_reused(dev):
         o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay)
         parity.check(to_np(o), o_ref, 1, 1e-2, out_bf16=True, what="workspace reuse o")
         parity.check(to_np(kv), kv_ref, 1, 1e-2, what="workspace reuse kv")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_sequences(dev, d):
+    """1,100 sequences of 0..160 tokens: the plan spreads more than 1,024
+    sequences over its threads (two per thread) and every wave of its
+    prefix sum carries segments."""
+    rng = np.random.default_rng(1234 + d)
+    lengths = [int(x) for x in rng.integers(0, 161, size=1100)]
+    decay = np.array([0.97], np.float32)
+    o, kv, o_ref, kv_ref = _run(dev, lengths, 1, d, decay, 41 + d, 64)
+    s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="segmented many o")
+    s2 = parity.check(kv, kv_ref, 1, 1e-2, what="segmented many kv")
+    say("segmented many sequences", s1, s2)
