@@ -130,3 +130,64 @@ def test_prefill_normed_unit_weight_matches_plain(dev):
     torch.cuda.synchronize()
     ref = oracle.norm_gate(to_np(o), np.ones((H, d)), 1e-6)
     parity.check(to_np(y), ref, 1, 1e-5, what="normed vs plain")
+
+
+@pytest.mark.parametrize("name", ["n8k", "batch8_n8k"])
+def test_prefill_normed_bench_shapes(dev, name):
+    """The launches the bench times, at full size with a gate: B=1, H=64,
+    N=8192 (the chained scan, segments of 2048) and eight 8K sequences
+    (one workgroup per chain); three heads of every sequence against the
+    oracle, on the bench's own device-generated inputs."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, workload
+
+    w = workload(name)
+    H, d = 64, 128
+    cu = cu_seqlens(w["lengths"])
+    T = int(cu[-1])
+    say(f"case normed bench shape {name} T={T}")
+    q, k, v = device_qkv(T, H, d, w["seed"], dev)
+    g = device_qkv(T, H, d, w["seed"] + 21, dev)[0]
+    wt = _weights(H, d, 351)
+    y, kv = la.prefill_normed(q, k, v, cu, w["decay"], to_dev(wt, torch.float32, dev), 1e-6, g)
+    torch.cuda.synchronize()
+    heads = [0, 37, 63]
+    qh, kh, vh, gh = (to_np(x[:, heads]) for x in (q, k, v, g))
+    o_ref, kv_ref = oracle.prefill_varlen(qh, kh, vh, cu, np.asarray(w["decay"])[heads])
+    y_ref = oracle.norm_gate(o_ref, wt[heads], 1e-6, gh)
+    s1 = parity.check(to_np(y[:, heads]), y_ref, 1, 1e-2, out_bf16=True, what=f"normed {name} y")
+    s2 = parity.check(to_np(kv[:, heads]), kv_ref, 1, 1e-2, what=f"normed {name} kv")
+    say(f"normed {name}", s1, s2)
+
+
+def test_decode_normed_full_batch_sampled(dev):
+    """la_decode_normed on the serving batch the bench times (256 sequences x
+    64 heads x d=128, bf16, with a gate): sampled (sequence, head) pairs
+    checked one by one against the oracle's decode step and norm_gate."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states, workload
+
+    w = workload("mixed_decode")
+    B, H, d = w["batch"], w["H"], w["d"]
+    say(f"case normed decode full batch B={B} H={H}")
+    kvd = device_states(B, H, d, w["seed"], dev, scale=0.5)
+    kv0 = kvd.clone()
+    qd, kd, vd = (x.view(B, H, d) for x in device_qkv(B, H, d, w["seed"] + 1, dev))
+    gd = device_qkv(B, H, d, w["seed"] + 3, dev)[0].view(B, H, d)
+    wt = _weights(H, d, 361)
+    y = la.decode_normed(qd, kd, vd, kvd, w["decay"], to_dev(wt, torch.float32, dev), 1e-6, gd)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(19))
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 32), rng.integers(0, H, 32))]
+    pairs += [(0, 0), (B - 1, H - 1)]
+    for b, h in pairs:
+        o_ref, s_ref = oracle.decode_step(to_np(qd[b, h]), to_np(kd[b, h]), to_np(vd[b, h]),
+                                          to_np(kv0[b, h]), w["decay"][h])
+        y_ref = oracle.norm_gate(o_ref[None, None], wt[h][None], 1e-6,
+                                 to_np(gd[b, h])[None, None])[0]
+        parity.check(to_np(y[b, h])[None], y_ref, 0, 1e-2, out_bf16=True,
+                     what=f"normed decode ({b},{h}) y")
+        parity.check(to_np(kvd[b, h])[None], s_ref[None], 0, 1e-5,
+                     what=f"normed decode ({b},{h}) kv")
