@@ -319,8 +319,12 @@ la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads
  * reverse-time chains from the last segment to the first -- then every
  * segment's outputs from the state at its start.  The one-exchange sequence
  * split of LASP+ (mizuki blog "MiniMax-01：4M 上下文破局", 五) applied to
- * the gradient chains.  The same result as la_prefill_backward up to the
- * order of fp32 sums.
+ * the gradient chains.  The dV chain's states are the transposes of the dK
+ * chain's, so only its output pass runs, from the dK chain's segment start
+ * states read transposed; at d = 128, with at least as many (segment, head)
+ * pairs as compute units, the dK and dV output passes run side by side in
+ * one launch.  The same result as la_prefill_backward up to the order of
+ * fp32 sums.
  *
  * Arguments as la_prefill_backward, except:
  *   segment_len      tokens per segment, a positive multiple of 64.
