@@ -153,3 +153,55 @@ def test_segmented_backward_side_stream_workspace_reuse(dev):
         side.synchronize()
         for a, b in zip(out, ref):
             assert torch.equal(a, b)
+
+
+def test_bench_config_one_million_tokens(dev):
+    """The segmented backward the bench times: B=1, H=8, N=1,048,576, d=128,
+    segments of 32,768, with S0 and dS_L.  dQ at a token depends only on the
+    tokens up to it and S0, and dK, dV only on the tokens from it on and
+    dS_L, so the oracle backward of the first 8192 tokens (with S0) gives dQ
+    there and that of the last 8192 tokens (with dS_L) gives dK and dV there,
+    for the heads of strongest and weakest decay; every output of every head
+    is also compared with la_prefill_backward (fp32 gradients: the two differ
+    only in the order of fp32 sums)."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states, workload
+
+    w = workload("n1m")
+    N, H, d, P = w["lengths"][0], 8, 128, 8192
+    decay = np.asarray(w["decay"][:H], np.float32)
+    say("case segmented backward bench config H=8 N=1M")
+    q, k, v = device_qkv(N, H, d, 1007, dev)
+    do = device_qkv(N, H, d, 1008, dev)[0]
+    kv0 = device_states(1, H, d, 1009, dev, scale=0.1)
+    g = device_states(1, H, d, 1010, dev, scale=0.1)
+    cu = np.array([0, N], np.int32)
+    seg = la.prefill_backward_segmented(q, k, v, do, cu, decay, 32768, kv_init=kv0, dkv_final=g,
+                                        grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    heads = sorted({int(np.argmin(decay)), int(np.argmax(decay))})
+    pre = [to_np(x[:P][:, heads]) for x in (q, k, v, do)]
+    ref = oracle.backward_varlen(*pre, [0, P], decay[heads], kv_init=to_np(kv0[:, heads]))
+    s1 = parity.check(to_np(seg[0][:P][:, heads]), ref[0], 1, 1e-2, what="1M dq (first 8K)")
+    suf = [to_np(x[N - P:][:, heads]) for x in (q, k, v, do)]
+    ref = oracle.backward_varlen(*suf, [0, P], decay[heads], dkv_final=to_np(g[:, heads]))
+    s2 = parity.check(to_np(seg[1][N - P:][:, heads]), ref[1], 1, 1e-2, what="1M dk (last 8K)")
+    s3 = parity.check(to_np(seg[2][N - P:][:, heads]), ref[2], 1, 1e-2, what="1M dv (last 8K)")
+    say("  oracle", s1, s2, s3)
+    plain = la.prefill_backward(q, k, v, do, cu, decay, kv_init=kv0, dkv_final=g,
+                                grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # per head on the device (1M x 8 x 128 is too large to move to the host
+    # in float64): relative L2 and largest element over the head's rms
+    for n, a, b in zip(("dq", "dk", "dv", "dkv_init"), seg, plain):
+        a64 = a.double().transpose(0, 1).reshape(H, -1)
+        b64 = b.double().transpose(0, 1).reshape(H, -1)
+        nb = torch.linalg.vector_norm(b64, dim=1)
+        rel = torch.linalg.vector_norm(a64 - b64, dim=1) / nb
+        worst = (a64 - b64).abs().amax(dim=1) / (nb / b64.shape[1] ** 0.5)
+        say("  vs plain", n, float(rel.max()), float(worst.max()))
+        assert bool(torch.isfinite(rel).all()) and float(rel.max()) <= 1e-4, n
+        assert float(worst.max()) <= 2e-2, n
+    del q, k, v, do, seg, plain
+    torch.cuda.empty_cache()

@@ -125,3 +125,33 @@ def test_many_sequences(dev, d):
     s1 = parity.check(o, o_ref, 1, 1e-2, out_bf16=True, what="segmented many o")
     s2 = parity.check(kv, kv_ref, 1, 1e-2, what="segmented many kv")
     say("segmented many sequences", s1, s2)
+
+
+def test_bench_config_one_million_tokens(dev):
+    """The segmented launch the bench times: B=1, H=8, N=1,048,576, d=128,
+    segments of 32,768 (256 (segment, head) items of the chained scan); the
+    heads of strongest and weakest decay checked over all 1M tokens, and the
+    final states of all heads."""
+    import torch
+    import linear_attention_la_amd as la
+
+    w = workload("n1m")
+    N, H = w["lengths"][0], 8
+    decay = np.asarray(w["decay"][:H], np.float32)
+    say("case segmented bench config H=8 N=1M")
+    qd, kd, vd = device_qkv(N, H, 128, 1006, dev)
+    cu = np.array([0, N], np.int32)
+    o, kv = la.prefill_segmented(qd, kd, vd, cu, decay, 32768)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    heads = sorted({int(np.argmin(decay)), int(np.argmax(decay))})
+    for h in heads:
+        sl = lambda x: to_np(x[:, h, :])[:, None, :]  # noqa: E731
+        o_ref, kv_ref = oracle.prefill_varlen(sl(qd), sl(kd), sl(vd), cu, decay[h:h + 1], beta=256)
+        s1 = parity.check(to_np(o[:, h, :])[:, None, :], o_ref, 1, 1e-2, out_bf16=True,
+                          what=f"segmented 1M o head {h}")
+        s2 = parity.check(to_np(kv[:, h])[:, None], kv_ref, 1, 1e-2,
+                          what=f"segmented 1M kv head {h}")
+        say("segmented 1M head", h, s1, s2)
+    del qd, kd, vd, o, kv
+    torch.cuda.empty_cache()
