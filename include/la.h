@@ -191,8 +191,12 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
  * previous segment of its sequence (through the workspace, at device scope),
  * passes the state entering the next segment on, and writes its outputs.
  * An item only ever waits for an item that has already started, so the
- * launch always completes; its workspace holds 2 states per (sequence, head)
- * whatever the segment count.  d = 64: four kernels (plan, a state-only pass
+ * launch always completes.  Each wait is also bounded (a poll count that
+ * grows with the segment length and the segment count, far beyond what a
+ * correct run needs); a wait that reached it would end the remaining waits
+ * at once and leave the outputs undefined -- it exists so that a fault
+ * cannot hang the GPU, and no correct call reaches it.  The workspace holds
+ * 2 states per (sequence, head) whatever the segment count.  d = 64: four kernels (plan, a state-only pass
  * over all segments, the prefix over them, the output pass); the workspace
  * holds one state per segment and per sequence.
  */

@@ -232,10 +232,18 @@ bool scan_path(int32_t head_dim) { return head_dim == 128; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Polls of one chained-scan wait before it gives up (each poll reads the
-// flag from memory and sleeps ~64 cycles: about a second in all).  A wait
-// only ever waits for a workgroup that has already started, so in a correct
-// run it ends long before this.
-constexpr int32_t kScanSpinLimit = 1 << 21;
+// flag from memory and sleeps ~64 cycles, so a poll takes at least ~30 ns).
+// A wait only ever waits for a workgroup that has already started: for its
+// local-state pass over one segment (~2 us a 64-token block) and for the
+// hops of the segments before it (~3 us each).  The limit allows 2^21 polls
+// (about a second) plus 4096 polls (over 100 us) per block of a segment and
+// per segment of the launch, so a correct run ends long before it however
+// long the segments are.
+int32_t scan_spin_limit(const SegmentLayout& lay) {
+  const int64_t blocks = (lay.segment_len + 63) / 64;
+  const int64_t polls = ((int64_t)1 << 21) + 4096 * (blocks + (int64_t)lay.num_segments);
+  return (int32_t)std::min<int64_t>(polls, (int64_t)1 << 30);
+}
 
 la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
                          int32_t head_dim, int32_t segment_len, bool scan, SegmentLayout* lay) {
@@ -558,7 +566,7 @@ la_status segmented_chain(const void* q, const void* k, const void* v, const int
     sa.kv_final = kv_final;
     sa.ctrl = ctrl;
     sa.ring = states;
-    sa.spin_limit = kScanSpinLimit;
+    sa.spin_limit = scan_spin_limit(lay);
     a.o = o;
     if (norm) {
       a.norm_weight = norm->weight;
