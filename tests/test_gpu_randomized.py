@@ -1,6 +1,8 @@
 """Seeded randomized GPU parity (needs an MI355X): many small configurations
 of la_prefill (both bf16 kernels and the fp32 path), la_prefill_segmented
-and la_prefill_backward (plain and segmented) against the fp64 oracle.
+(and its no-allocation form), la_prefill_backward (plain and segmented),
+la_prefill_normed and the state pool (prefill then decode) against the fp64
+oracle.
 Each case draws its batch shape, lengths (block edges 0, 1, 63, 64, 65
 included often), head count, d, decays, initial states and output dtype
 from its own seed, and prints them before it runs."""
@@ -171,3 +173,119 @@ def test_random_backward_segmented(dev, case):
              for n, a, b in zip(("dq", "dk", "dv"), out[:3], ref[:3])]
     stats.append(parity.check(to_np(out[3]), ref[3], 1, 1e-2, what=f"case {case} dkv_init"))
     say("  ", stats)
+
+
+def _weights(rng, H, d):
+    return rng.uniform(0.5, 1.5, (H, d)).astype(np.float32)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_prefill_normed(dev, case):
+    """la_prefill_normed: the one-workgroup-per-chain path (every second case)
+    or the chained scan, random gate, eps, kv_init and output dtype."""
+    import torch
+    import linear_attention_la_amd as la
+
+    wide = case % 2 == 1
+    rng = np.random.Generator(np.random.PCG64(7400 + case))
+    if wide:
+        S, H = int(rng.integers(5, 9)), int(rng.integers(48, 65))
+        lengths = _lengths(rng, S, 200)
+    else:
+        S, H = int(rng.integers(1, 5)), int(rng.integers(1, 9))
+        lengths = _lengths(rng, S, 900)
+    d = 128
+    decay = _decays(rng, H)
+    gate = bool(rng.random() < 0.6)
+    kv_init = bool(rng.random() < 0.5)
+    out_f32 = bool(rng.random() < 0.5)
+    eps = float(10.0 ** rng.uniform(-6, -3))
+    heads = sorted({0, H - 1, int(rng.integers(0, H))})
+    say(f"random normed prefill case {case}: lengths={lengths} H={H} gate={gate} "
+        f"kv_init={kv_init} out_f32={out_f32} eps={eps:.2e}")
+    T = sum(lengths)
+    q, k, v = host_qkv(T, H, d, 8600 + case, "bf16")
+    g = host_qkv(T, H, d, 8700 + case, "bf16")[0] * 30.0 if gate else None
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(S, H, d, 9600 + case, scale=0.1) if kv_init else None
+    w = _weights(rng, H, d)
+    gd = to_dev(g, torch.bfloat16, dev) if gate else None
+    y, kv = la.prefill_normed(*(to_dev(x, torch.bfloat16, dev) for x in (q, k, v)), cu, decay,
+                              to_dev(w, torch.float32, dev), eps, gd,
+                              kv_init=to_dev(kv0, torch.float32, dev) if kv_init else None,
+                              out_dtype=torch.float32 if out_f32 else None)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.prefill_varlen(q[:, heads], k[:, heads], v[:, heads], cu,
+                                          decay[heads],
+                                          kv_init=None if kv0 is None else kv0[:, heads])
+    y_ref = oracle.norm_gate(o_ref, w[heads], eps, to_np(gd)[:, heads] if gate else None)
+    s1 = parity.check(to_np(y)[:, heads], y_ref, 1, 1e-2, out_bf16=not out_f32,
+                      what=f"case {case} y")
+    s2 = parity.check(to_np(kv)[:, heads], kv_ref, 1, 1e-2, what=f"case {case} kv")
+    say("  ", s1, s2)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_pool_prefill_then_decode(dev, case):
+    """A chunk of la_prefill_pool on random slots, then la_decode_pool on a
+    random subset of those slots: every output and every pool entry against
+    the oracle's pool functions."""
+    import torch
+    import linear_attention_la_amd as la
+
+    rng = np.random.Generator(np.random.PCG64(7500 + case))
+    S, H, d = int(rng.integers(1, 9)), int(rng.integers(1, 9)), int(rng.choice([64, 128]))
+    P = S + int(rng.integers(0, 6))
+    lengths = _lengths(rng, S, 300)
+    decay = _decays(rng, H)
+    slots = rng.permutation(P)[:S].astype(np.int32)
+    say(f"random pool case {case}: lengths={lengths} H={H} d={d} P={P} slots={slots.tolist()}")
+    T = sum(lengths)
+    q, k, v = host_qkv(T, H, d, 8800 + case, "bf16")
+    cu = cu_seqlens(lengths)
+    pool = random_states(P, H, d, 9800 + case, scale=0.1)
+    pool_d = to_dev(pool, torch.float32, dev)
+    o = la.prefill_pool(*(to_dev(x, torch.bfloat16, dev) for x in (q, k, v)), cu, decay, pool_d,
+                        slots)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = oracle.prefill_pool(q, k, v, cu, decay, pool, slots)
+    s1 = parity.check(to_np(o), o_ref, 1, 1e-2, out_bf16=True, what=f"case {case} prefill o")
+    s2 = parity.check(to_np(pool_d), pool_ref, 1, 1e-2, what=f"case {case} pool after prefill")
+    B = int(rng.integers(1, S + 1))
+    dslots = rng.permutation(slots)[:B].astype(np.int32)
+    q1, k1, v1 = (x[:B * H].reshape(B, H, d)
+                  for x in host_qkv(B * H, 1, d, 8900 + case, "bf16"))
+    pool_host = to_np(pool_d)
+    o1 = la.decode_pool(*(to_dev(x, torch.bfloat16, dev) for x in (q1, k1, v1)), pool_d, dslots,
+                        decay)
+    torch.cuda.synchronize()
+    o1_ref, pool1_ref = oracle.decode_pool(q1, k1, v1, pool_host, dslots, decay)
+    s3 = parity.check(to_np(o1), o1_ref, 1, 1e-2, out_bf16=True, what=f"case {case} decode o")
+    s4 = parity.check(to_np(pool_d), pool1_ref, 1, 1e-5, what=f"case {case} pool after decode")
+    say("  ", s1, s2, s3, s4)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_segmented_noalloc(dev, case):
+    """la_prefill_segmented_noalloc on random batches (its static scratch
+    reused from call to call) against the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    rng, lengths, H, d, decay = _case(7600 + case, wide=case == 5)
+    segment_len = int(rng.choice([64, 128, 256]))
+    kv_init = bool(rng.random() < 0.5)
+    say(f"random noalloc case {case}: lengths={lengths} H={H} d={d} segment_len={segment_len} "
+        f"kv_init={kv_init}")
+    T = sum(lengths)
+    q, k, v = host_qkv(T, H, d, 8950 + case, "bf16")
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(len(lengths), H, d, 9900 + case, scale=0.1) if kv_init else None
+    o, kv = la.prefill_segmented_noalloc(
+        *(to_dev(x, torch.bfloat16, dev) for x in (q, k, v)), cu, decay, segment_len,
+        kv_init=to_dev(kv0, torch.float32, dev) if kv_init else None)
+    torch.cuda.synchronize()
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0)
+    s1 = parity.check(to_np(o), o_ref, 1, 1e-2, out_bf16=True, what=f"case {case} o")
+    s2 = parity.check(to_np(kv), kv_ref, 1, 1e-2, what=f"case {case} kv")
+    say("  ", s1, s2)
