@@ -32,7 +32,8 @@ One JSON line is printed with the contract fields plus:
   sweep         tokens/s at N = 1K ... 1M, for eight 8K sequences in one call and
                 for a packed varlen batch (the last two have enough (sequence,
                 head) chains for the one-workgroup-per-chain kernel): back-to-back
-                launches over input sets that together exceed 1 GiB.
+                launches over input sets that together exceed 1 GiB;
+                sweep_flatness gives max/min tokens/s over 1K ... 1M.
 """
 
 import argparse
@@ -577,6 +578,19 @@ def bench_sweep(dev, reps=20, names=SWEEP, footprint=1 << 30):
     return res
 
 
+def sweep_flatness(sweep):
+    """max / min of tokens/s over the single-sequence length sweep (B=1,
+    H=64: 1K ... 1M tokens, with and without decay), and over 4K ... 1M."""
+    single = {k: v["tokens_per_s"] for k, v in sweep.items()
+              if k.startswith("sweep") or k == "n1m"}
+    if not single:
+        return None
+    no1k = {k: v for k, v in single.items() if k != "sweep1024"}
+    ratio = lambda d: round(max(d.values()) / min(d.values()), 3) if d else None  # noqa: E731
+    return {"max_over_min_1k_1m": ratio(single), "max_over_min_4k_1m": ratio(no1k),
+            "workloads": sorted(single)}
+
+
 def bench_backward(dev, reps=10, name="n8k"):
     """la_prefill_backward on the n8k workload (B=1, H=64, N=8192, d=128,
     bf16; the 32-column kernel) or on batch8_n8k (eight such sequences: the
@@ -857,6 +871,7 @@ def main():
         del dec_state
         torch.cuda.empty_cache()
         line["sweep"] = bench_sweep(dev)
+        line["sweep_flatness"] = sweep_flatness(line["sweep"])
         peaks = measured_peaks(dev)
         line["peaks"] = peaks
         line["roofline"]["frac_of_measured_stream"] = round(achieved / peaks["stream_GB_per_s"], 4)
