@@ -118,6 +118,22 @@ def launch_times(fn, reps, stream, flush=None):
     return [s.elapsed_time(e) / 1e3 for s, e in zip(starts, ends)]
 
 
+def region_time(fn, reps, stream):
+    """Average duration (s) of `fn` over `reps` launches run back to back
+    inside one HIP event pair on `stream` (events between launches would
+    serialise the stream and add ~20 us to each)."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps / 1e3
+
+
 def timed_launches(fn, reps, stream, flush=None):
     """Average duration (s) of `fn` over `reps` launches (see launch_times)."""
     t = launch_times(fn, reps, stream, flush)
@@ -251,6 +267,9 @@ def cpu_baseline(budget_s=12.0, decode_budget_s=4.0):
 
 
 def bench_decode(dev, reps=20):
+    """la_decode on the 256 x 64 serving batch (d = 128, bf16, fp32 states
+    updated in place): settled, then `reps` launches back to back in one
+    event pair.  Returns the record and the inputs (for bench_mixed)."""
     import torch
 
     import linear_attention_la_amd as la
@@ -265,7 +284,7 @@ def bench_decode(dev, reps=20):
     for _ in range(3):
         la.decode(q, k, v, kv, w["decay"], out=out)
     settle(lambda i: la.decode(q, k, v, kv, w["decay"], out=out))
-    t = timed_launches(lambda i: la.decode(q, k, v, kv, w["decay"], out=out), reps, s)
+    t = region_time(lambda i: la.decode(q, k, v, kv, w["decay"], out=out), reps, s)
     gbs = decode_bytes(B) / t / 1e9
     return {"batch": B, "heads": H, "head_dim": D, "us": round(t * 1e6, 2),
             "GB_per_s": round(gbs, 1), "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4),
@@ -294,7 +313,7 @@ def bench_decode_pool(dev, reps=20, pool_size=1024):
     for _ in range(3):
         run(0)
     settle(run)
-    t = timed_launches(run, reps, s)
+    t = region_time(run, reps, s)
     gbs = decode_bytes(B) / t / 1e9
     del pool
     torch.cuda.empty_cache()
@@ -593,9 +612,10 @@ def sweep_flatness(sweep):
 
 def bench_backward(dev, reps=10, name="n8k"):
     """la_prefill_backward on the n8k workload (B=1, H=64, N=8192, d=128,
-    bf16; the 32-column kernel) or on batch8_n8k (eight such sequences: the
-    one-workgroup-per-chain kernel), with initial states and final-state
-    gradients.  Algorithmic bytes: q, k, v, dO read and dq, dk, dv written
+    bf16: its three chains in one launch, 192 workgroups) or on batch8_n8k
+    (eight such sequences, 1536 workgroups), with initial states and
+    final-state gradients; settled, then `reps` calls back to back in one
+    event pair.  Algorithmic bytes: q, k, v, dO read and dq, dk, dv written
     (14 d B per token and head) plus kv_init and dkv_final read and dkv_init
     written."""
     import torch
@@ -621,7 +641,7 @@ def bench_backward(dev, reps=10, name="n8k"):
     for _ in range(3):
         run(0)
     settle(run)
-    t = timed_launches(run, reps, torch.cuda.current_stream())
+    t = region_time(run, reps, torch.cuda.current_stream())
     by = N * H * 14 * D + 3 * S * H * D * D * 4
     del q, k, v, do, dq, dk, dv, ws
     torch.cuda.empty_cache()
