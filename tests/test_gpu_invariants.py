@@ -1,0 +1,119 @@
+"""Scaling invariants of the GPU path at full size (needs an MI355X).
+
+The method is multilinear in its inputs: O(a q, b k, c v) = abc O(q, k, v)
+and the state scales by bc (with an initial state scaled by bc).  For powers
+of two every product, sum and rounding of the computation scales exactly --
+the bf16 hi/lo splits, the fp32 accumulations and the final rounding commute
+with the scale while nothing overflows or becomes subnormal -- so the scaled
+call must return the unscaled result times the scale bit for bit.  This
+holds at any size, so it is checked on the launches the bench times (no
+oracle needed): both prefill kernels, the chained scan, decode and the
+backward."""
+
+import numpy as np
+import pytest
+
+from tests.gpu_util import device, say
+
+pytestmark = pytest.mark.gpu
+
+A, B, C = 8.0, 4.0, 2.0  # scales of q, k, v (powers of two)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+def _inputs(name, dev, H=64):
+    import torch
+    from la_inputs import cu_seqlens, device_qkv, device_states, workload
+
+    w = workload(name)
+    cu_h = cu_seqlens(w["lengths"])
+    T, S = int(cu_h[-1]), len(w["lengths"])
+    q, k, v = device_qkv(T, H, 128, w["seed"], dev)
+    kv0 = device_states(S, H, 128, w["seed"] + 5, dev, scale=0.1)
+    return q, k, v, kv0, cu_h, torch.from_numpy(cu_h).to(dev), np.asarray(w["decay"][:H])
+
+
+@pytest.mark.parametrize("name", ["n8k", "batch8_n8k"])
+def test_prefill_scaling(dev, name):
+    """la_prefill on the 32-column kernel (B=1, H=64, N=8192) and on the
+    one-workgroup-per-chain kernel (8 x 8192)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    say(f"case prefill scaling {name}")
+    q, k, v, kv0, cu_h, cu, decay = _inputs(name, dev)
+    o1, s1 = la.prefill(q, k, v, cu, decay, kv_init=kv0, cu_seqlens_host=cu_h)
+    o2, s2 = la.prefill(q * A, k * B, v * C, cu, decay, kv_init=kv0 * (B * C),
+                        cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and torch.isfinite(s1).all()
+    assert torch.equal(o2, o1 * (A * B * C)), "output"
+    assert torch.equal(s2, s1 * (B * C)), "final state"
+
+
+def test_segmented_scan_scaling(dev):
+    """la_prefill_segmented (the chained scan) on one 64K-token sequence x 8
+    heads in 4K segments (128 items)."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, workload
+
+    say("case segmented scaling")
+    w = workload("sweep65536")
+    N, H = 65536, 8
+    q, k, v = device_qkv(N, H, 128, w["seed"], dev)
+    cu_h = np.array([0, N], np.int32)
+    cu = torch.from_numpy(cu_h).to(dev)
+    decay = np.asarray(w["decay"][:H])
+    o1, s1 = la.prefill_segmented(q, k, v, cu, decay, 4096, cu_seqlens_host=cu_h)
+    o2, s2 = la.prefill_segmented(q * A, k * B, v * C, cu, decay, 4096, cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1 * (A * B * C)), "output"
+    assert torch.equal(s2, s1 * (B * C)), "final state"
+
+
+def test_decode_scaling(dev):
+    """la_decode on the 256 x 64 serving batch."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states, workload
+
+    say("case decode scaling")
+    w = workload("mixed_decode")
+    Bt, H, d = w["batch"], w["H"], w["d"]
+    kv = device_states(Bt, H, d, w["seed"], dev, scale=0.5)
+    q, k, v = (x.view(Bt, H, d) for x in device_qkv(Bt, H, d, w["seed"] + 1, dev))
+    kv2 = kv * (B * C)
+    o1 = la.decode(q, k, v, kv, w["decay"])
+    o2 = la.decode(q * A, k * B, v * C, kv2, w["decay"])
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1 * (A * B * C)), "output"
+    assert torch.equal(kv2, kv * (B * C)), "updated state"
+
+
+def test_backward_scaling(dev):
+    """la_prefill_backward at B=1, H=64, N=8192 with S0 and dS_L: with dO
+    scaled by E, S0 by BC and dS_L by AE, dQ scales by EBC, dK by EAC, dV by
+    ABE and dS0 by AE."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states
+
+    E = 16.0
+    say("case backward scaling")
+    q, k, v, kv0, cu_h, cu, decay = _inputs("n8k", dev)
+    do = device_qkv(8192, 64, 128, 77, dev)[0]
+    g = device_states(1, 64, 128, 78, dev, scale=0.1)
+    r1 = la.prefill_backward(q, k, v, do, cu, decay, kv_init=kv0, dkv_final=g,
+                             cu_seqlens_host=cu_h)
+    r2 = la.prefill_backward(q * A, k * B, v * C, do * E, cu, decay, kv_init=kv0 * (B * C),
+                             dkv_final=g * (A * E), cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    for name, x1, x2, f in zip(("dq", "dk", "dv", "dkv_init"), r1, r2,
+                               (E * B * C, E * A * C, A * B * E, A * E)):
+        assert torch.isfinite(x1).all(), name
+        assert torch.equal(x2, x1 * f), name
