@@ -1,4 +1,5 @@
-"""Scaling invariants of the GPU path at full size (needs an MI355X).
+"""Invariants of the GPU path at full size (needs an MI355X): scaling,
+continuation and packing order, each bit for bit.
 
 The method is multilinear in its inputs: O(a q, b k, c v) = abc O(q, k, v)
 and the state scales by bc (with an initial state scaled by bc).  For powers
@@ -8,7 +9,8 @@ with the scale while nothing overflows or becomes subnormal -- so the scaled
 call must return the unscaled result times the scale bit for bit.  This
 holds at any size, so it is checked on the launches the bench times (no
 oracle needed): both prefill kernels, the chained scan, decode and the
-backward."""
+backward.  Continuation at a block boundary and the order in which
+sequences are packed also leave every result bit-identical."""
 
 import numpy as np
 import pytest
@@ -117,3 +119,54 @@ def test_backward_scaling(dev):
                                (E * B * C, E * A * C, A * B * E, A * E)):
         assert torch.isfinite(x1).all(), name
         assert torch.equal(x2, x1 * f), name
+
+
+@pytest.mark.parametrize("name", ["n8k", "batch8_n8k"])
+def test_continuation_bitwise(dev, name):
+    """Prefilling the first 4096 tokens of every sequence, then the rest from
+    the returned states (kv_final written over kv_init in place), gives the
+    one-call result bit for bit: the split falls on a block boundary, the
+    state crosses it in fp32 either way, and each call runs the same kernel."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import cu_seqlens
+
+    say(f"case continuation bitwise {name}")
+    q, k, v, kv0, cu_h, cu, decay = _inputs(name, dev)
+    S = len(cu_h) - 1
+    o_full, s_full = la.prefill(q, k, v, cu, decay, kv_init=kv0, cu_seqlens_host=cu_h)
+    first = np.concatenate([np.arange(cu_h[s], cu_h[s] + 4096) for s in range(S)])
+    rest = np.concatenate([np.arange(cu_h[s] + 4096, cu_h[s + 1]) for s in range(S)])
+    fi, ri = (torch.from_numpy(x).to(dev) for x in (first, rest))
+    half = cu_seqlens([4096] * S)
+    st = kv0.clone()
+    o1, _ = la.prefill(q[fi].contiguous(), k[fi].contiguous(), v[fi].contiguous(), half, decay,
+                       kv_init=st, kv_final=st)
+    o2, _ = la.prefill(q[ri].contiguous(), k[ri].contiguous(), v[ri].contiguous(),
+                       cu_seqlens([int(cu_h[s + 1] - cu_h[s] - 4096) for s in range(S)]), decay,
+                       kv_init=st, kv_final=st)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o_full[fi]), "first part"
+    assert torch.equal(o2, o_full[ri]), "continued part"
+    assert torch.equal(st, s_full), "final state"
+
+
+def test_packing_order_bitwise(dev):
+    """Eight 8K sequences packed in reverse order give, for every sequence,
+    the same rows and final state bit for bit (one workgroup per chain either
+    way; a chain's result does not depend on where its sequence sits)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    say("case packing order bitwise")
+    q, k, v, kv0, cu_h, cu, decay = _inputs("batch8_n8k", dev)
+    S = len(cu_h) - 1
+    o1, s1 = la.prefill(q, k, v, cu, decay, kv_init=kv0, cu_seqlens_host=cu_h)
+    order = list(range(S))[::-1]
+    rows = np.concatenate([np.arange(cu_h[s], cu_h[s + 1]) for s in order])
+    idx = torch.from_numpy(rows).to(dev)
+    o2, s2 = la.prefill(q[idx].contiguous(), k[idx].contiguous(), v[idx].contiguous(), cu_h,
+                        decay, kv_init=kv0[order].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o1[idx]), "outputs"
+    assert torch.equal(s2, s1[order]), "final states"
