@@ -170,3 +170,35 @@ def test_packing_order_bitwise(dev):
     torch.cuda.synchronize()
     assert torch.equal(o2, o1[idx]), "outputs"
     assert torch.equal(s2, s1[order]), "final states"
+
+
+def test_backward_chains_are_forward_runs(dev):
+    """Without S0 and dS_L the backward's three chains are forward runs of
+    the same one-workgroup-per-chain kernel body: dQ = prefill(dO, V, K),
+    dK = flip(prefill(flip V, flip dO, flip Q)) and dV = flip(prefill(flip K,
+    flip Q, flip dO)), flip reversing the tokens of every sequence.  Checked
+    bit for bit on eight 8K sequences x 64 heads (512 chains: la_prefill and
+    la_prefill_backward both take that kernel)."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv
+
+    say("case backward chains vs forward runs")
+    q, k, v, _, cu_h, cu, decay = _inputs("batch8_n8k", dev)
+    do = device_qkv(int(cu_h[-1]), 64, 128, 91, dev)[0]
+    dq, dk, dv, _ = la.prefill_backward(q, k, v, do, cu, decay, cu_seqlens_host=cu_h)
+    rows = np.concatenate([np.arange(cu_h[s + 1] - 1, cu_h[s] - 1, -1)
+                           for s in range(len(cu_h) - 1)])
+    fl = torch.from_numpy(rows).to(dev)  # token reversal within each sequence (an involution)
+
+    def fwd(a, b, c):
+        return la.prefill(a.contiguous(), b.contiguous(), c.contiguous(), cu, decay,
+                          cu_seqlens_host=cu_h, final_state=False)[0]
+
+    ref_dq = fwd(do, v, k)
+    ref_dk = fwd(v[fl], do[fl], q[fl])[fl]
+    ref_dv = fwd(k[fl], q[fl], do[fl])[fl]
+    torch.cuda.synchronize()
+    assert torch.equal(dq, ref_dq), "dq"
+    assert torch.equal(dk, ref_dk), "dk"
+    assert torch.equal(dv, ref_dv), "dv"
