@@ -191,3 +191,27 @@ def test_decode_normed_full_batch_sampled(dev):
                      what=f"normed decode ({b},{h}) y")
         parity.check(to_np(kvd[b, h])[None], s_ref[None], 0, 1e-5,
                      what=f"normed decode ({b},{h}) kv")
+
+
+@pytest.mark.parametrize("name", ["n8k", "batch8_n8k"])
+def test_gate_limits_bitwise(dev, name):
+    """At the bench's launches: a gate of 0 gives sigmoid 1/2, so exactly half
+    the ungated output, and a gate of 64 gives sigmoid 1 in fp32, so exactly
+    the ungated output (both bit for bit: the scale 1/2 and the rounding
+    commute)."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, workload
+
+    w = workload(name)
+    cu = cu_seqlens(w["lengths"])
+    T, H, d = int(cu[-1]), 64, 128
+    say(f"case gate limits {name}")
+    q, k, v = device_qkv(T, H, d, w["seed"], dev)
+    wt = to_dev(_weights(H, d, 371), torch.float32, dev)
+    y0, _ = la.prefill_normed(q, k, v, cu, w["decay"], wt, 1e-6, None)
+    yz, _ = la.prefill_normed(q, k, v, cu, w["decay"], wt, 1e-6, torch.zeros_like(q))
+    y1, _ = la.prefill_normed(q, k, v, cu, w["decay"], wt, 1e-6, torch.full_like(q, 64.0))
+    torch.cuda.synchronize()
+    assert torch.equal(yz, y0 * 0.5), "gate 0"
+    assert torch.equal(y1, y0), "gate 64"
