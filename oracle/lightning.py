@@ -16,7 +16,9 @@ q_t, k_t, v_t in R^d and a decay lambda in (0, 1]:
   diagonal (t = j) is included with weight lambda^0 = 1.  There is no
   softmax, no 1/sqrt(d) scale and no normaliser inside the attention core;
   the normalisation of TransNormer's NormAttention ([CSDN] §2.1) belongs
-  to the surrounding layer and is not part of this core.
+  to the surrounding layer and is not part of this core (``norm_gate`` at
+  the end of this file is that normalisation as an optional epilogue, under
+  the reading stated there).
 * The carried state is the d x d matrix S (rows: key dimension, columns:
   value dimension), the fixed-size "state note" of linear attention
   ([MZK] 三).  An optional initial state S0 continues an earlier prefix.
