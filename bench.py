@@ -268,16 +268,22 @@ def cpu_baseline(budget_s=12.0, decode_budget_s=4.0):
 
 def bench_decode(dev, reps=20):
     """la_decode on the 256 x 64 serving batch (d = 128, bf16, fp32 states
-    updated in place): settled, then `reps` launches back to back in one
-    event pair.  Returns the record and the inputs (for bench_mixed)."""
+    updated in place, made by a seeded prefill of 256 sequences of U[256,
+    2048] tokens): settled, then `reps` launches back to back in one event
+    pair.  Returns the record and the inputs (for bench_mixed)."""
     import torch
 
     import linear_attention_la_amd as la
-    from la_inputs import device_qkv, device_states, workload
+    from la_inputs import cu_seqlens, device_qkv, workload
 
     w = workload("mixed_decode")
     B = w["batch"]
-    kv = device_states(B, H, D, w["seed"], dev, scale=0.5)
+    cu_s = cu_seqlens(w["state_lengths"])
+    qs, ks, vs = device_qkv(int(cu_s[-1]), H, D, w["seed"] + 7, dev)
+    kv = la.prefill(qs, ks, vs, torch.from_numpy(cu_s).to(dev), w["decay"],
+                    cu_seqlens_host=cu_s)[1]
+    del qs, ks, vs
+    torch.cuda.empty_cache()
     q, k, v = (x.view(B, H, D) for x in device_qkv(B, H, D, w["seed"] + 1, dev))
     out = torch.empty_like(q)
     s = torch.cuda.current_stream()

@@ -111,7 +111,10 @@ def test_two_streams_bitwise(dev):
     say(f"two streams: prefill T={T}, decode B={B}")
     qp, kp, vp = device_qkv(T, H, d, wp["seed"], dev)
     qd, kd, vd = (x.view(B, H, d) for x in device_qkv(B, H, d, wd["seed"] + 1, dev))
-    kv_init = device_states(B, H, d, wd["seed"], dev, scale=0.5)
+    cu_s = cu_seqlens(wd["state_lengths"])
+    qs, ks, vs = device_qkv(int(cu_s[-1]), H, d, wd["seed"] + 7, dev)
+    _, kv_init = la.prefill(qs, ks, vs, torch.from_numpy(cu_s).to(dev), wd["decay"],
+                            cu_seqlens_host=cu_s)
     cu_dev = torch.from_numpy(cu).to(dev)
 
     kv_a = kv_init.clone()
@@ -138,13 +141,15 @@ def test_two_streams_bitwise(dev):
 
 
 def test_serving_step_two_streams_oracle(dev):
-    """The mixed serving step -- the 256 x 64 decode batch beside a packed
+    """The mixed serving step -- the 256 x 64 decode batch, its states made by
+    a seeded prefill of 256 sequences of U[256, 2048] tokens, beside a packed
     prefill of 8 sequences of U[1K, 32K] tokens (the one-workgroup-per-chain
     kernel) -- run concurrently on two streams, with either kernel submitted
     first, on plain streams and on streams restricted to disjoint sets of
     compute units: every run equals the solo run bit for bit, and the solo
     run matches the oracle (three heads over all 8 prefill sequences, with
-    their final states; 50 sampled decode pairs)."""
+    their final states; 50 sampled decode pairs, each from the oracle's own
+    prefill of its state's sequence)."""
     import torch
     import linear_attention_la_amd as la
 
@@ -155,7 +160,10 @@ def test_serving_step_two_streams_oracle(dev):
     T = int(cu[-1])
     qp, kp, vp = device_qkv(T, H, d, wp["seed"], dev)
     qd, kd, vd = (x.view(B, H, d) for x in device_qkv(B, H, d, wd["seed"] + 1, dev))
-    kv_init = device_states(B, H, d, wd["seed"], dev, scale=0.5)
+    cu_s = cu_seqlens(wd["state_lengths"])
+    qs, ks, vs = device_qkv(int(cu_s[-1]), H, d, wd["seed"] + 7, dev)
+    _, kv_init = la.prefill(qs, ks, vs, torch.from_numpy(cu_s).to(dev), wd["decay"],
+                            cu_seqlens_host=cu_s)
     cu_dev = torch.from_numpy(cu).to(dev)
 
     kv_solo = kv_init.clone()
@@ -198,8 +206,14 @@ def test_serving_step_two_streams_oracle(dev):
     pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, B, 48), rng.integers(0, H, 48))]
     pairs += [(0, 0), (B - 1, H - 1)]
     for b, h in pairs:
+        rows = slice(int(cu_s[b]), int(cu_s[b + 1]))
+        _, s0_ref = oracle.prefill_varlen(*(to_np(x[rows, h:h + 1]) for x in (qs, ks, vs)),
+                                          [0, rows.stop - rows.start],
+                                          np.asarray(wd["decay"])[h:h + 1])
+        parity.check(to_np(kv_init[b, h])[None], s0_ref[0], 0, 1e-2,
+                     what=f"serving state prefill ({b},{h})")
         od_ref, sd_ref = oracle.decode_step(to_np(qd[b, h]), to_np(kd[b, h]), to_np(vd[b, h]),
-                                            to_np(kv_init[b, h]), wd["decay"][h])
+                                            s0_ref[0, 0], wd["decay"][h])
         parity.check(to_np(o_dec[b, h])[None], od_ref[None], 0, 1e-2, out_bf16=True,
                      what=f"serving decode ({b},{h}) o")
         parity.check(to_np(kv_solo[b, h])[None], sd_ref[None], 0, 1e-5,
