@@ -60,14 +60,24 @@
 extern "C" {
 #endif
 
-typedef enum la_status {
+/* The enums are int-sized.  A C caller may pass any int where one is
+ * expected (unknown values are rejected); in C++ the enums take int32_t as
+ * their underlying type, so that every such value is a valid value of the
+ * type and the library's checks of it are well defined. */
+#ifdef __cplusplus
+#define LA_ENUM_BASE : int32_t
+#else
+#define LA_ENUM_BASE
+#endif
+
+typedef enum la_status LA_ENUM_BASE {
   LA_OK = 0,
   LA_ERR_INVALID_ARG = 1,
   LA_ERR_UNSUPPORTED = 2,
   LA_ERR_HIP = 3
 } la_status;
 
-typedef enum la_dtype { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
+typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
 
 /* Largest number of heads one call accepts (per-head decay travels in the
  * kernel arguments). */

@@ -37,6 +37,8 @@ la_status ok() {
   return LA_OK;
 }
 
+// Any int32 is a value of la_dtype (the ABI's enums have int32_t as their
+// base in C++), so an unknown dtype from a C caller is simply rejected here.
 bool valid_dtype(la_dtype d) { return d == LA_BF16 || d == LA_FP32; }
 // Kernels use 16 B vector loads and stores at row granularity.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -437,7 +439,7 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
                           const float* decay, float* kv_pool, int32_t pool_size,
                           const int32_t* slots_dev, const int32_t* slots_host, void* o,
                           void* stream) {
-  if (in_dtype != LA_BF16 && valid_dtype(in_dtype))
+  if (valid_dtype(in_dtype) && in_dtype != LA_BF16)
     return fail(LA_ERR_UNSUPPORTED, "the pool prefill takes bf16 inputs only");
   if (pool_size < 0) return fail(LA_ERR_INVALID_ARG, "pool_size = %d < 0", pool_size);
   // the pool stands in for kv_init / kv_final; its own checks follow
@@ -663,7 +665,7 @@ la_status segmented_args(const void* q, const void* k, const void* v,
   *done = false;
   la_status st = check_segment_len(segment_len);
   if (st != LA_OK) return st;
-  if (in_dtype != LA_BF16 && valid_dtype(in_dtype))
+  if (valid_dtype(in_dtype) && in_dtype != LA_BF16)
     return fail(LA_ERR_UNSUPPORTED, "the segmented prefill takes bf16 inputs only");
   if ((st = check_prefill(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_seqs, total_tokens,
                           num_heads, head_dim, in_dtype, out_dtype, decay, kv_init, o, kv_final,

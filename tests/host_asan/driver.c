@@ -159,6 +159,52 @@ int main(void) {
                          O, NULL),
          LA_ERR_INVALID_ARG);
 
+  /* dtype arguments outside the enumerators (a C caller may pass any int):
+     rejected, and never read as the enum type before they are checked */
+  const la_dtype bad_dtypes[2] = {(la_dtype)7, (la_dtype)-1};
+  la_norm nrm = {(const float*)0xF0000000, 1e-6f, NULL};
+  int32_t ok_slots[2] = {0, 1};
+  for (int i = 0; i < 2; ++i) {
+    const la_dtype bd = bad_dtypes[i];
+    expect("prefill bad in_dtype",
+           la_prefill(Q, K, V, CUD, cu, 2, 100, H, D, bd, LA_BF16, decay, NULL, O, KVF, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("prefill bad out_dtype",
+           la_prefill(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, bd, decay, NULL, O, KVF, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("segmented bad in_dtype",
+           la_prefill_segmented(Q, K, V, CUD, cu, 2, 100, H, D, bd, LA_BF16, decay, NULL, O, KVF,
+                                64, WS, 1 << 20, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("segmented noalloc bad out_dtype",
+           la_prefill_segmented_noalloc(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, bd, decay, NULL,
+                                        O, KVF, 64, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("pool prefill bad in_dtype",
+           la_prefill_pool(Q, K, V, CUD, cu, 2, 100, H, D, bd, LA_BF16, decay, KVF, 4, CUD,
+                           ok_slots, O, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("normed bad in_dtype",
+           la_prefill_normed(Q, K, V, CUD, cu, 2, 100, H, D, bd, LA_BF16, decay, NULL, &nrm, O,
+                             KVF, WS, 1 << 20, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("backward bad grad_dtype",
+           la_prefill_backward(Q, K, V, DO, CUD, cu, 2, 100, H, D, LA_BF16, bd, decay, NULL, NULL,
+                               DQ, DK, DV, NULL, NULL, 0, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("backward segmented bad in_dtype",
+           la_prefill_backward_segmented(Q, K, V, DO, CUD, cu, 2, 100, H, D, bd, LA_BF16, decay,
+                                         NULL, NULL, DQ, DK, DV, NULL, 64, WS, 1 << 20, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("decode bad in_dtype", la_decode(Q, K, V, KVF, decay, 3, H, D, bd, O, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("decode pool bad in_dtype",
+           la_decode_pool(Q, K, V, KVF, 4, CUD, ok_slots, decay, 2, H, D, bd, O, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("decode normed bad in_dtype",
+           la_decode_normed(Q, K, V, KVF, decay, 3, H, D, bd, &nrm, O, NULL), LA_ERR_INVALID_ARG);
+  }
+
   /* status strings */
   for (int s = -1; s < 6; ++s) {
     const char* name = la_status_str((la_status)s);

@@ -1,11 +1,13 @@
-"""libla's host code under AddressSanitizer (CPU only).
+"""libla's host code under AddressSanitizer and UndefinedBehaviorSanitizer
+(CPU only).
 
-Every source is built with AddressSanitizer on its host code alone (the flag
+Every source is built with both sanitizers on its host code alone (each flag
 follows -Xarch_host, so no GPU code is instrumented), linked into a small C
 driver (tests/host_asan/driver.c) that runs each entry point's host paths --
 validation, workspace sizes, long-batch dispatch order, argument packing --
-with fake device addresses.  Any out-of-bounds access or use after free in
-that code aborts the driver."""
+with fake device addresses.  Any out-of-bounds access, use after free,
+signed overflow, misaligned access or other undefined behaviour in that code
+aborts the driver."""
 
 import os
 import subprocess
@@ -20,7 +22,8 @@ sys.path.insert(0, ROOT)
 from linear_attention_la_amd import build as labuild  # noqa: E402
 
 OUT = os.path.join(ROOT, "_build", "host_asan")
-ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+        "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 
 def _compile(src):
@@ -48,8 +51,10 @@ def test_host_code_under_address_sanitizer():
            "-x", "c", drv, "-x", "none", *objs, "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1")
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:halt_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     out = r.stdout + r.stderr
     assert "ERROR: AddressSanitizer" not in out, out[-4000:]
+    assert "runtime error:" not in out, out[-4000:]  # UndefinedBehaviorSanitizer
     assert r.returncode == 0 and "OK: 0 failure(s)" in out, out[-4000:]
