@@ -127,7 +127,11 @@ typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * another stream gets fewer of them while it runs.  Calls of 2 to 512
  * sequences hand the sequences to the grid longest first (read from
  * cu_seqlens_host), so that when the grid runs in several waves of
- * workgroups the longest chains start in the first.
+ * workgroups the longest chains start in the first.  With fewer than about
+ * a quarter as many (sequence, head) pairs as compute units (e.g. a few
+ * heads of one long sequence), most compute units stay idle: there
+ * la_prefill_segmented, which cuts the sequences into parallel segments, is
+ * several times faster (it needs a workspace, which la_prefill does not).
  */
 la_status la_prefill(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
