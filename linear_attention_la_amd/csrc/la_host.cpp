@@ -133,12 +133,12 @@ la_status check_prefill(const void* q, const void* k, const void* v,
 
   // Aliasing: o and kv_final are written; they may overlap no input, except
   // that kv_final may be exactly kv_init.
-  const size_t tok_bytes = (size_t)total_tokens * num_heads * head_dim;
+  const size_t tok_elems = (size_t)total_tokens * num_heads * head_dim;
   const size_t state_bytes = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
-  const Range rq = range("q", q, tok_bytes * dtype_size(in_dtype));
-  const Range rk = range("k", k, tok_bytes * dtype_size(in_dtype));
-  const Range rv = range("v", v, tok_bytes * dtype_size(in_dtype));
-  const Range ro = range("o", o, tok_bytes * dtype_size(out_dtype));
+  const Range rq = range("q", q, tok_elems * dtype_size(in_dtype));
+  const Range rk = range("k", k, tok_elems * dtype_size(in_dtype));
+  const Range rv = range("v", v, tok_elems * dtype_size(in_dtype));
+  const Range ro = range("o", o, tok_elems * dtype_size(out_dtype));
   const Range ri = range("kv_init", kv_init, kv_init ? state_bytes : 0);
   const Range rf = range("kv_final", kv_final, kv_final ? state_bytes : 0);
   const Range* ins[] = {&rq, &rk, &rv, &ri};
