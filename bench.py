@@ -20,6 +20,8 @@ One JSON line is printed with the contract fields plus:
                 around the K timed steps), against
                 8 TB/s; `traffic` is the counter-measured bytes per launch
                 from profiles/ if it was taken on the current kernel source.
+                config.la_ndv records the LA_NDV override of the library's
+                kernel choice (null: unset, the 32-column kernel here).
   cpu_baseline  the fp64 oracle (blockwise, beta=64) timed on the host cores
                 over heads of the same workload.
   mfma          algorithmic TFLOP/s at beta=64 against 2.5 PFLOP/s bf16.
@@ -871,7 +873,12 @@ def main():
     by = prefill_bytes(N, 1)
     achieved = by / kern_s / 1e9
     tflops = prefill_flops(N) / kern_s / 1e12
-    traffic = measured_traffic()
+    # LA_NDV (sweep override of the library's kernel choice) is recorded;
+    # unset, this workload (64 chains) runs the 32-column kernel
+    ndv = os.environ.get("LA_NDV") or None
+    kernel = ("prefill_wide_kernel<false, false, false>" if ndv == "1"
+              else "prefill_bf16_kernel<128, false, false, false>")
+    traffic = measured_traffic() if ndv in (None, "4") else None
     line = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
@@ -879,10 +886,11 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "la_prefill B=1 H=64 N=8192 d=128 bf16 in/out, fp32 state, "
                                "seeded per-head decay", "global_batch": 1, "seq_len": N,
-                   "heads": H, "head_dim": D, "beta": BETA, "parallelism": "single GPU"},
+                   "heads": H, "head_dim": D, "beta": BETA, "parallelism": "single GPU",
+                   "la_ndv": ndv},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "prefill_bf16_kernel<128, false, false, false>",
+                     "traffic": traffic, "kernel": kernel,
                      "kernel_us": round(kern_s * 1e6, 2), "algorithmic_bytes": by},
         "settle": {"ms": args.settle_ms, "steps": settle_steps},
         "mfma": {"tflops_algorithmic_beta64": round(tflops, 2),

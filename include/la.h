@@ -132,6 +132,13 @@ typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * heads of one long sequence), most compute units stay idle: there
  * la_prefill_segmented, which cuts the sequences into parallel segments, is
  * several times faster (it needs a workspace, which la_prefill does not).
+ *
+ * Sweep override (bf16 inputs): the environment variable LA_NDV, read on
+ * every call that has sequences, forces the kernel -- "1" one workgroup per
+ * pair (d = 128 only), "4" (d = 128) or "2" (d = 64) the 32-column slices.
+ * Unset or empty: the choice above.  Any other value is LA_ERR_UNSUPPORTED
+ * (after the argument checks, before anything is enqueued).  The block
+ * length is not an option: both kernels tile by 64 tokens.
  */
 la_status la_prefill(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -161,9 +168,10 @@ la_status la_prefill(const void* q, const void* k, const void* v,
  *                in_dtype must be LA_BF16; o must not overlap the pool and
  *                the pool must not overlap q, k or v.
  *
- * A zero-length sequence leaves its slot unchanged.  Errors as la_prefill,
- * plus LA_ERR_INVALID_ARG for a NULL pool or slot array, a slot out of range
- * or a repeated slot, and LA_ERR_UNSUPPORTED for fp32 inputs.
+ * A zero-length sequence leaves its slot unchanged.  Kernels, and the
+ * LA_NDV override, as in la_prefill.  Errors as la_prefill, plus
+ * LA_ERR_INVALID_ARG for a NULL pool or slot array, a slot out of range or a
+ * repeated slot, and LA_ERR_UNSUPPORTED for fp32 inputs.
  */
 la_status la_prefill_pool(const void* q, const void* k, const void* v,
                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,

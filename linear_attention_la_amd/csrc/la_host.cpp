@@ -8,6 +8,7 @@
 #include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -171,6 +172,27 @@ int device_cus() {
 bool use_wide(int64_t chains, int32_t head_dim) {
   const int cus = device_cus();
   return head_dim == 128 && cus > 0 && chains >= cus;
+}
+
+// The sweep override of that choice for la_prefill and la_prefill_pool with
+// bf16 inputs: the environment variable LA_NDV, read on every call, names
+// the workgroups per (sequence, head) chain -- 1 (one workgroup per chain,
+// d = 128 only) or d / 32 (32-column slices).  Unset or empty: the choice
+// by chain count above.  Any other value is LA_ERR_UNSUPPORTED, before
+// anything is enqueued.  Sets *wide to the kernel to run.
+la_status choose_wide(int64_t chains, int32_t head_dim, bool* wide) {
+  *wide = false;
+  const char* s = getenv("LA_NDV");
+  if (!s || !*s) {
+    *wide = use_wide(chains, head_dim);
+    return LA_OK;
+  }
+  const bool slices = strcmp(s, head_dim == 128 ? "4" : "2") == 0;
+  if (!slices && !(head_dim == 128 && strcmp(s, "1") == 0))
+    return fail(LA_ERR_UNSUPPORTED, "LA_NDV = \"%.32s\": expected %s%d (d = %d)", s,
+                head_dim == 128 ? "1 or " : "", head_dim / 32, head_dim);
+  *wide = !slices;
+  return LA_OK;
 }
 
 // Longest sequences first: a grid with more chains than compute units runs
@@ -419,11 +441,15 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
   set_order(a, cu_seqlens_host, num_seqs);
 
+  bool wide = false;
+  if (in_dtype == LA_BF16 &&
+      (st = choose_wide((int64_t)num_seqs * num_heads, head_dim, &wide)) != LA_OK)
+    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (in_dtype != LA_BF16) {
     e = la::launch_prefill_f32(a, head_dim, out_dtype, s);
-  } else if (use_wide((int64_t)num_seqs * num_heads, head_dim)) {
+  } else if (wide) {
     a.num_items = num_seqs * num_heads;
     e = la::launch_prefill_wide(a, out_dtype, false, false, s);
   } else {
@@ -483,9 +509,11 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   a.num_items = (int32_t)((int64_t)num_seqs * num_heads * (head_dim / la::kBf16Cols));
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
   set_order(a, cu_seqlens_host, num_seqs);
+  bool wide = false;
+  if ((st = choose_wide((int64_t)num_seqs * num_heads, head_dim, &wide)) != LA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  if (use_wide((int64_t)num_seqs * num_heads, head_dim)) {
+  if (wide) {
     a.num_items = num_seqs * num_heads;
     e = la::launch_prefill_wide(a, out_dtype, false, false, s);
   } else {

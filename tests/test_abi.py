@@ -496,6 +496,28 @@ def test_prefill_pool_zero_sequences_is_noop():
     assert st == la.LA_OK, msg
 
 
+# LA_NDV: the sweep override of the kernel choice (1 or d/32 workgroups per
+# chain).  Only rejected values are tried here: an accepted one would launch.
+BAD_NDV = [("2", 128), ("8", 128), ("0", 128), ("1", 64), ("4", 64), ("four", 128),
+           ("4 ", 128), ("-4", 128)]
+
+
+@pytest.mark.parametrize("value,d", BAD_NDV, ids=[f"{v!r}-d{d}" for v, d in BAD_NDV])
+def test_ndv_override_rejects(monkeypatch, value, d):
+    monkeypatch.setenv("LA_NDV", value)
+    st, msg = _prefill(d=d)
+    assert st == la.LA_ERR_UNSUPPORTED and "LA_NDV" in msg, (st, msg)
+    st, msg = _prefill_pool(d=d)
+    assert st == la.LA_ERR_UNSUPPORTED and "LA_NDV" in msg, (st, msg)
+
+
+def test_ndv_override_checked_after_arguments(monkeypatch):
+    """An argument error is still reported as such with LA_NDV set."""
+    monkeypatch.setenv("LA_NDV", "2")
+    st, msg = _prefill(decay=None)
+    assert st == la.LA_ERR_INVALID_ARG, (st, msg)
+
+
 # ---- backward (host-side checks only) ----
 
 DO_, DQ, DK, DV, DKV0, BWS = (0xB0000000 + 0x10000000 * i for i in range(6))

@@ -212,3 +212,68 @@ def _compare_on_device(a, b, bf16, what, rel_tol=1e-2, elem_tol=2e-2):
         bad = over & (diff.abs() > ulp)
         assert not bool(bad.any()), f"{what}: {int(bad.sum().item())} elements over the bound"
     return {"max_rel_l2": float(rel.max().item()), "format_explained": n_over}
+
+
+def test_ndv_override_forces_either_kernel(dev, monkeypatch):
+    """LA_NDV forces the kernel of la_prefill and la_prefill_pool.  A chain's
+    result does not depend on the other chains of its call, so each kernel
+    is recognised bit for bit: two sequences x 64 heads (128 chains, fewer
+    than the compute units: 32-column slices by default) run with LA_NDV=1
+    must equal those sequences inside a call padded to 384 chains (one
+    workgroup per chain by default), and the padded call with LA_NDV=4 must
+    equal the unpadded default.  The two kernels differ in their last bits
+    on these inputs (fp32 output), and both match the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths, pad = [300, 77], [64, 64, 64, 64]
+    say(f"case LA_NDV override lengths={lengths} pad={pad}")
+    _assert_wide(len(lengths + pad) * H)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert len(lengths) * H < cus
+    decay = _decay()
+    T, Tp = sum(lengths), sum(lengths + pad)
+    q, k, v = host_qkv(Tp, H, D, 131, "bf16")
+    kv0 = random_states(len(lengths + pad), H, D, 132, scale=0.1)
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    kv0d = to_dev(kv0, torch.float32, dev)
+    S = len(lengths)
+
+    def run(n, ndv):
+        if ndv is None:
+            monkeypatch.delenv("LA_NDV", raising=False)
+        else:
+            monkeypatch.setenv("LA_NDV", ndv)
+        cu = cu_seqlens((lengths + pad)[:n])
+        tt = int(cu[-1])
+        o, kv = la.prefill(qd[:tt], kd[:tt], vd[:tt], cu, decay, kv_init=kv0d[:n].contiguous(),
+                           out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return o[:T], kv[:S]
+
+    o_slices, kv_slices = run(S, None)
+    o_wide, kv_wide = run(S, "1")
+    o_pad_wide, kv_pad_wide = run(S + len(pad), None)
+    o_pad_slices, kv_pad_slices = run(S + len(pad), "4")
+    assert torch.equal(o_wide, o_pad_wide) and torch.equal(kv_wide, kv_pad_wide), \
+        "LA_NDV=1 did not run the one-workgroup-per-chain kernel"
+    assert torch.equal(o_pad_slices, o_slices) and torch.equal(kv_pad_slices, kv_slices), \
+        "LA_NDV=4 did not run the 32-column kernel"
+    assert not torch.equal(o_wide, o_slices), "the two kernels gave identical results"
+    o_ref, kv_ref = oracle.prefill_varlen(q[:T], k[:T], v[:T], cu_seqlens(lengths), decay,
+                                          kv_init=kv0[:S], beta=64)
+    for name, o, kv in (("slices", o_slices, kv_slices), ("wide", o_wide, kv_wide)):
+        parity.check(to_np(o), o_ref, 1, 1e-2, what=f"LA_NDV {name} o")
+        parity.check(to_np(kv), kv_ref, 1, 1e-2, what=f"LA_NDV {name} kv")
+
+    # la_prefill_pool takes the same override: its states sit in pool slots
+    monkeypatch.setenv("LA_NDV", "1")
+    pool = torch.zeros((5, H, D, D), dtype=torch.float32, device=dev)
+    slots = [3, 1]
+    pool[slots] = kv0d[:S]
+    o_pool = la.prefill_pool(qd[:T], kd[:T], vd[:T], cu_seqlens(lengths), decay, pool, slots,
+                             out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("LA_NDV")
+    assert torch.equal(o_pool, o_wide) and torch.equal(pool[slots], kv_wide), \
+        "la_prefill_pool with LA_NDV=1 differs from la_prefill with LA_NDV=1"
