@@ -118,10 +118,12 @@ typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * Zero-length sequences produce no rows; their final state is kv_init's (or
  * zero).
  *
- * Kernels: bf16 inputs with d = 128 and at least as many (sequence, head)
- * pairs as the current device has compute units run one workgroup per pair
+ * Kernels: bf16 inputs with d = 128 and more (sequence, head) pairs than
+ * half the compute units of the current device run one workgroup per pair
  * (each input row is read once); otherwise each pair is split by value
- * columns over d / 32 workgroups.  Both give results within the same
+ * columns over d / 32 workgroups (with at most half as many pairs as
+ * compute units these fill the GPU in two waves of workgroups, the faster
+ * choice there).  Both give results within the same
  * tolerance, not bitwise equal to each other; a given call is deterministic.
  * A one-workgroup-per-pair launch occupies whole compute units, so work on
  * another stream gets fewer of them while it runs.  Calls of 2 to 512
@@ -347,8 +349,8 @@ la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads
  * split of LASP+ (mizuki blog "MiniMax-01：4M 上下文破局", 五) applied to
  * the gradient chains.  The dV chain's states are the transposes of the dK
  * chain's, so only its output pass runs, from the dK chain's segment start
- * states read transposed; at d = 128, with at least as many (segment, head)
- * pairs as compute units, the dK and dV output passes run side by side in
+ * states read transposed; at d = 128, with more (segment, head) pairs than
+ * half the compute units, the dK and dV output passes run side by side in
  * one launch.  The same result as la_prefill_backward up to the order of
  * fp32 sums.
  *

@@ -166,12 +166,15 @@ int device_cus() {
 }
 
 // The wide bf16 kernel (one workgroup per chain, d = 128) reads every input
-// row once per chain instead of once per 32-column slice; it is chosen when
-// there are at least as many chains as compute units, so that it fills the
-// GPU.
+// row once per chain instead of once per 32-column slice, and takes 2.3-2.9
+// times as long per chain as one slice.  It is chosen when there are more
+// chains than half the compute units: the 32-column kernel (four workgroups
+// a chain, one workgroup per compute unit) then needs three or more waves of
+// workgroups where the wide kernel needs one; with fewer chains the slices'
+// two waves are faster.
 bool use_wide(int64_t chains, int32_t head_dim) {
   const int cus = device_cus();
-  return head_dim == 128 && cus > 0 && chains >= cus;
+  return head_dim == 128 && cus > 0 && 2 * chains > cus;
 }
 
 // The sweep override of that choice for la_prefill and la_prefill_pool with

@@ -12,8 +12,8 @@
 // Decomposition.  The 32-column kernel (la_prefill_bf16.hip) splits the state
 // over four workgroups per chain, each of which reads all Q and K rows and
 // forms Q K^T again.  Here one workgroup of 8 waves owns the whole chain, so
-// every input row crosses into the CU once and Q K^T is formed once; it
-// fills the GPU when there are at least as many chains as CUs (many
+// every input row crosses into the CU once and Q K^T is formed once; it is
+// the faster of the two when there are more chains than half the CUs (many
 // sequences, or a long sequence cut into segments).  Wave w owns value
 // columns [16w, 16w+16) of the fp32 d x d state -- all 128 key rows, eight
 // 16 x 16 accumulator tiles -- for the whole chain.  Per block:

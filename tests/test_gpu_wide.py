@@ -1,9 +1,9 @@
 """GPU parity of the wide bf16 prefill kernel (one workgroup per chain, d = 128)
 against the fp64 oracle (needs an MI355X).
 
-The library takes the wide kernel when a call has at least as many (sequence,
-head) chains -- or (segment, head) chains in the segmented prefill -- as the
-GPU has compute units; every case here is sized past that point (64 heads and
+The library takes the wide kernel when a call has more (sequence, head)
+chains -- or (segment, head) chains in the segmented prefill -- than half the
+GPU's compute units; every case here is sized past that point (64 heads and
 enough sequences or segments), which the tests assert."""
 
 import numpy as np
@@ -29,7 +29,7 @@ def _assert_wide(chains):
     import torch
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert chains >= cus, f"{chains} chains < {cus} compute units: the wide kernel is not used"
+    assert 2 * chains > cus, f"{chains} chains <= {cus} / 2 compute units: the wide kernel is not used"
 
 
 def _decay():
@@ -218,11 +218,13 @@ def test_ndv_override_forces_either_kernel(dev, monkeypatch):
     """LA_NDV forces the kernel of la_prefill and la_prefill_pool.  A chain's
     result does not depend on the other chains of its call, so each kernel
     is recognised bit for bit: two sequences x 64 heads (128 chains, fewer
-    than the compute units: 32-column slices by default) run with LA_NDV=1
-    must equal those sequences inside a call padded to 384 chains (one
-    workgroup per chain by default), and the padded call with LA_NDV=4 must
-    equal the unpadded default.  The two kernels differ in their last bits
-    on these inputs (fp32 output), and both match the oracle."""
+    than half the compute units: 32-column slices by default) run with
+    LA_NDV=1 must equal those sequences inside a call padded to 384 chains
+    (one workgroup per chain by default) and inside one of 192 chains (more
+    than half the compute units: also one workgroup per chain by default),
+    and the padded call with LA_NDV=4 must equal the unpadded default.  The
+    two kernels differ in their last bits on these inputs (fp32 output), and
+    both match the oracle."""
     import torch
     import linear_attention_la_amd as la
 
@@ -230,7 +232,7 @@ def test_ndv_override_forces_either_kernel(dev, monkeypatch):
     say(f"case LA_NDV override lengths={lengths} pad={pad}")
     _assert_wide(len(lengths + pad) * H)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert len(lengths) * H < cus
+    assert 2 * len(lengths) * H <= cus < 2 * (len(lengths) + 1) * H
     decay = _decay()
     T, Tp = sum(lengths), sum(lengths + pad)
     q, k, v = host_qkv(Tp, H, D, 131, "bf16")
@@ -255,8 +257,11 @@ def test_ndv_override_forces_either_kernel(dev, monkeypatch):
     o_wide, kv_wide = run(S, "1")
     o_pad_wide, kv_pad_wide = run(S + len(pad), None)
     o_pad_slices, kv_pad_slices = run(S + len(pad), "4")
+    o_mid, kv_mid = run(S + 1, None)
     assert torch.equal(o_wide, o_pad_wide) and torch.equal(kv_wide, kv_pad_wide), \
         "LA_NDV=1 did not run the one-workgroup-per-chain kernel"
+    assert torch.equal(o_mid, o_wide) and torch.equal(kv_mid, kv_wide), \
+        "192 chains did not take the one-workgroup-per-chain kernel"
     assert torch.equal(o_pad_slices, o_slices) and torch.equal(kv_pad_slices, kv_slices), \
         "LA_NDV=4 did not run the 32-column kernel"
     assert not torch.equal(o_wide, o_slices), "the two kernels gave identical results"
