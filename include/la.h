@@ -123,8 +123,13 @@ typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * (each input row is read once); otherwise each pair is split by value
  * columns over d / 32 workgroups (with at most half as many pairs as
  * compute units these fill the GPU in two waves of workgroups, the faster
- * choice there).  Both give results within the same
- * tolerance, not bitwise equal to each other; a given call is deterministic.
+ * choice there).  When the pairs fill whole waves of the first kind plus a
+ * remainder of at most half the compute units, and a model of the two plans
+ * finds it faster, the sequences of the remainder run in 32-column slices
+ * in a second launch on the stream instead of an extra wave.  Both kernels
+ * give results within the same tolerance, not bitwise equal to each other;
+ * each sequence's results come from one kernel, and a given call is
+ * deterministic.
  * A one-workgroup-per-pair launch occupies whole compute units, so work on
  * another stream gets fewer of them while it runs.  Calls of 2 to 512
  * sequences hand the sequences to the grid longest first (read from
@@ -136,9 +141,9 @@ typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * several times faster (it needs a workspace, which la_prefill does not).
  *
  * Sweep override (bf16 inputs): the environment variable LA_NDV, read on
- * every call that has sequences, forces the kernel -- "1" one workgroup per
- * pair (d = 128 only), "4" (d = 128) or "2" (d = 64) the 32-column slices.
- * Unset or empty: the choice above.  Any other value is LA_ERR_UNSUPPORTED
+ * every call that has sequences, forces one kernel for every pair -- "1"
+ * one workgroup per pair (d = 128 only), "4" (d = 128) or "2" (d = 64) the
+ * 32-column slices.  Unset or empty: the choice above.  Any other value is LA_ERR_UNSUPPORTED
  * (after the argument checks, before anything is enqueued).  The block
  * length is not an option: both kernels tile by 64 tokens.
  */

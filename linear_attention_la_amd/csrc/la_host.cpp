@@ -6,6 +6,8 @@
 #include <math.h>
 #include <algorithm>
 #include <atomic>
+#include <functional>
+#include <queue>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -177,25 +179,104 @@ bool use_wide(int64_t chains, int32_t head_dim) {
   return head_dim == 128 && cus > 0 && 2 * chains > cus;
 }
 
-// The sweep override of that choice for la_prefill and la_prefill_pool with
-// bf16 inputs: the environment variable LA_NDV, read on every call, names
-// the workgroups per (sequence, head) chain -- 1 (one workgroup per chain,
-// d = 128 only) or d / 32 (32-column slices).  Unset or empty: the choice
-// by chain count above.  Any other value is LA_ERR_UNSUPPORTED, before
-// anything is enqueued.  Sets *wide to the kernel to run.
-la_status choose_wide(int64_t chains, int32_t head_dim, bool* wide) {
-  *wide = false;
+// Time (us) to run jobs of the given durations, taken in order by `units`
+// compute units, each job starting on the first unit to become free: how
+// the GPU hands queued workgroups to compute units.
+double makespan(const std::vector<double>& jobs, int units) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < units; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (double j : jobs) {
+    const double t = free_at.top() + j;
+    free_at.pop();
+    free_at.push(t);
+    end = std::max(end, t);
+  }
+  return end;
+}
+
+// Time per 64-token block of a one-workgroup-per-chain workgroup and of a
+// 32-column slice workgroup with the GPU full (MI355X, d = 128), and the
+// cost of a second launch on the stream.
+constexpr double kWideBlockUs = 3.7;
+constexpr double kSliceBlockUs = 1.3;
+constexpr double kLaunchUs = 8.0;
+
+// With the wide kernel chosen, the number of leading sequences in dispatch
+// order that it runs; the others then run in 32-column slices in a second
+// launch.  Chains beyond whole waves of the wide kernel would run in an
+// extra wave of the wide kernel, which takes a whole chain's time however
+// few chains it holds; when those chains fill at most half the compute
+// units, their slices take at most two shorter waves.  Both plans are timed
+// with makespan() (blocks of each chain times the per-block costs above)
+// and the faster is taken.  Calls of more than four waves, or whose
+// remainder is larger, run on the wide kernel alone.
+int32_t wide_sequences(const la::PrefillArgs& a, const int32_t* cu_host, int cus) {
+  const int32_t S = a.num_seqs, H = a.num_heads;
+  const int64_t chains = (int64_t)S * H;
+  if (cus <= 0 || chains > 4 * (int64_t)cus) return S;
+  const int32_t seqs = (int32_t)(chains / cus * cus / H);  // whole sequences in whole waves
+  const int64_t rest = chains - (int64_t)seqs * H;
+  if (seqs == 0 || rest == 0 || 2 * rest > cus || S - seqs > la::kMaxOrder) return S;
+  auto blocks = [&](int32_t i) {  // blocks of the i-th sequence in dispatch order
+    const int32_t s = a.ordered ? a.seq_order[i] : i;
+    return (double)((cu_host[s + 1] - cu_host[s] + 63) / 64);
+  };
+  std::vector<double> all, wide, slices;
+  for (int32_t i = 0; i < S; ++i) {
+    const double b = blocks(i);
+    for (int32_t h = 0; h < H; ++h) {
+      all.push_back(b * kWideBlockUs);
+      if (i < seqs) wide.push_back(b * kWideBlockUs);
+      else slices.insert(slices.end(), 128 / la::kBf16Cols, b * kSliceBlockUs);
+    }
+  }
+  const double split = makespan(wide, cus) + kLaunchUs + makespan(slices, cus);
+  return split < makespan(all, cus) ? seqs : S;
+}
+
+// The kernels of a bf16 la_prefill or la_prefill_pool call, as the number of
+// leading sequences in dispatch order run one workgroup per chain (the
+// others run in 32-column slices): 0, num_seqs, or a split (d = 128).
+// The environment variable LA_NDV, read on every call, overrides the
+// choice for sweeps: 1 runs every chain on the wide kernel (d = 128 only),
+// d / 32 every chain in slices; unset or empty, use_wide and
+// wide_sequences decide.  Any other value is LA_ERR_UNSUPPORTED, before
+// anything is enqueued.
+la_status choose_kernels(const la::PrefillArgs& a, const int32_t* cu_host, int32_t head_dim,
+                         int32_t* wide_seqs) {
+  *wide_seqs = 0;
+  const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
   const char* s = getenv("LA_NDV");
   if (!s || !*s) {
-    *wide = use_wide(chains, head_dim);
+    if (use_wide(chains, head_dim)) *wide_seqs = wide_sequences(a, cu_host, device_cus());
     return LA_OK;
   }
   const bool slices = strcmp(s, head_dim == 128 ? "4" : "2") == 0;
   if (!slices && !(head_dim == 128 && strcmp(s, "1") == 0))
     return fail(LA_ERR_UNSUPPORTED, "LA_NDV = \"%.32s\": expected %s%d (d = %d)", s,
                 head_dim == 128 ? "1 or " : "", head_dim / 32, head_dim);
-  *wide = !slices;
+  *wide_seqs = slices ? 0 : a.num_seqs;
   return LA_OK;
+}
+
+// Enqueues a bf16 prefill: the first wide_seqs sequences of the dispatch
+// order on the wide kernel, the others on the 32-column kernel (as a
+// second launch, whose dispatch order lists just those sequences).
+hipError_t launch_bf16_prefill(la::PrefillArgs a, int32_t wide_seqs, int32_t head_dim,
+                               la_dtype out_dtype, hipStream_t s) {
+  const int32_t S = a.num_seqs, H = a.num_heads;
+  if (wide_seqs > 0) {
+    la::PrefillArgs w = a;
+    w.num_items = wide_seqs * H;
+    const hipError_t e = la::launch_prefill_wide(w, out_dtype, false, false, s);
+    if (e != hipSuccess || wide_seqs == S) return e;
+    for (int32_t i = wide_seqs; i < S; ++i)  // writes trail reads: in place
+      a.seq_order[i - wide_seqs] = a.ordered ? a.seq_order[i] : (uint16_t)i;
+    a.ordered = 1;
+  }
+  a.num_items = (S - wide_seqs) * H * (head_dim / la::kBf16Cols);
+  return la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
 }
 
 // Longest sequences first: a grid with more chains than compute units runs
@@ -444,21 +525,13 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
   set_order(a, cu_seqlens_host, num_seqs);
 
-  bool wide = false;
-  if (in_dtype == LA_BF16 &&
-      (st = choose_wide((int64_t)num_seqs * num_heads, head_dim, &wide)) != LA_OK)
-    return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (in_dtype != LA_BF16) {
-    e = la::launch_prefill_f32(a, head_dim, out_dtype, s);
-  } else if (wide) {
-    a.num_items = num_seqs * num_heads;
-    e = la::launch_prefill_wide(a, out_dtype, false, false, s);
-  } else {
-    e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
-  }
-  return hip_status(e, "la_prefill launch");
+  if (in_dtype != LA_BF16)
+    return hip_status(la::launch_prefill_f32(a, head_dim, out_dtype, s), "la_prefill launch");
+  int32_t wide_seqs = 0;
+  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, &wide_seqs)) != LA_OK) return st;
+  return hip_status(launch_bf16_prefill(a, wide_seqs, head_dim, out_dtype, s),
+                    "la_prefill launch");
 }
 
 la_status la_prefill_pool(const void* q, const void* k, const void* v,
@@ -512,17 +585,11 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   a.num_items = (int32_t)((int64_t)num_seqs * num_heads * (head_dim / la::kBf16Cols));
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
   set_order(a, cu_seqlens_host, num_seqs);
-  bool wide = false;
-  if ((st = choose_wide((int64_t)num_seqs * num_heads, head_dim, &wide)) != LA_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (wide) {
-    a.num_items = num_seqs * num_heads;
-    e = la::launch_prefill_wide(a, out_dtype, false, false, s);
-  } else {
-    e = la::launch_prefill_bf16(a, head_dim, out_dtype, false, false, s);
-  }
-  return hip_status(e, "la_prefill_pool launch");
+  int32_t wide_seqs = 0;
+  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, &wide_seqs)) != LA_OK) return st;
+  return hip_status(launch_bf16_prefill(a, wide_seqs, head_dim, out_dtype,
+                                        static_cast<hipStream_t>(stream)),
+                    "la_prefill_pool launch");
 }
 
 la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,

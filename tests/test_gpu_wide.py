@@ -282,3 +282,59 @@ def test_ndv_override_forces_either_kernel(dev, monkeypatch):
     monkeypatch.delenv("LA_NDV")
     assert torch.equal(o_pool, o_wide) and torch.equal(pool[slots], kv_wide), \
         "la_prefill_pool with LA_NDV=1 differs from la_prefill with LA_NDV=1"
+
+
+@pytest.mark.parametrize("lengths,wide_seqs", [([640] * 5, [0, 1, 2, 3]),
+                                               ([576, 640, 640, 640, 640], [1, 2, 3, 4])])
+def test_split_launch(dev, monkeypatch, lengths, wide_seqs):
+    """Five sequences x 64 heads (320 chains on 256 compute units): the four
+    longest sequences fill one wave of the one-workgroup-per-chain kernel and
+    the last one runs in 32-column slices in a second launch, rather than as
+    an extra wave of the wide kernel.  Each sequence's rows and final state
+    equal, bit for bit, those of the kernel it was given (forced for the
+    whole call with LA_NDV), also on a state pool; the call matches the
+    oracle.  The second case dispatches the sequences out of index order."""
+    import torch
+    import linear_attention_la_amd as la
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"the split planned here assumes 256 compute units, not {cus}")
+    say(f"case split launch lengths={lengths}")
+    decay = _decay()
+    cu = cu_seqlens(lengths)
+    T, S = int(cu[-1]), len(lengths)
+    q, k, v = host_qkv(T, H, D, 141, "bf16")
+    kv0 = random_states(S, H, D, 142, scale=0.1)
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    kv0d = to_dev(kv0, torch.float32, dev)
+
+    def run(ndv):
+        if ndv is None:
+            monkeypatch.delenv("LA_NDV", raising=False)
+        else:
+            monkeypatch.setenv("LA_NDV", ndv)
+        o, kv = la.prefill(qd, kd, vd, cu, decay, kv_init=kv0d, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return o, kv
+
+    o, kv = run(None)
+    o_wide, kv_wide = run("1")
+    o_slices, kv_slices = run("4")
+    monkeypatch.delenv("LA_NDV")
+    for s in range(S):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        ref_o, ref_kv = (o_wide, kv_wide) if s in wide_seqs else (o_slices, kv_slices)
+        assert torch.equal(o[rows], ref_o[rows]), f"sequence {s}: rows"
+        assert torch.equal(kv[s], ref_kv[s]), f"sequence {s}: final state"
+    assert not torch.equal(o, o_wide) and not torch.equal(o, o_slices)
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0, beta=64)
+    parity.check(to_np(o), o_ref, 1, 1e-2, what="split o")
+    parity.check(to_np(kv), kv_ref, 1, 1e-2, what="split kv")
+
+    pool = torch.zeros((7, H, D, D), dtype=torch.float32, device=dev)
+    slots = [6, 0, 3, 5, 1]
+    pool[slots] = kv0d
+    o_pool = la.prefill_pool(qd, kd, vd, cu, decay, pool, slots, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_pool, o) and torch.equal(pool[slots], kv), "pool prefill differs"
