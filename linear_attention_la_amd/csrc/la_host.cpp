@@ -6,8 +6,6 @@
 #include <math.h>
 #include <algorithm>
 #include <atomic>
-#include <functional>
-#include <queue>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -179,22 +177,6 @@ bool use_wide(int64_t chains, int32_t head_dim) {
   return head_dim == 128 && cus > 0 && 2 * chains > cus;
 }
 
-// Time (us) to run jobs of the given durations, taken in order by `units`
-// compute units, each job starting on the first unit to become free: how
-// the GPU hands queued workgroups to compute units.
-double makespan(const std::vector<double>& jobs, int units) {
-  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-  for (int i = 0; i < units; ++i) free_at.push(0.0);
-  double end = 0.0;
-  for (double j : jobs) {
-    const double t = free_at.top() + j;
-    free_at.pop();
-    free_at.push(t);
-    end = std::max(end, t);
-  }
-  return end;
-}
-
 // Time per 64-token block of a one-workgroup-per-chain workgroup and of a
 // 32-column slice workgroup with the GPU full (MI355X, d = 128), and the
 // cost of a second launch on the stream.
@@ -208,31 +190,53 @@ constexpr double kLaunchUs = 8.0;
 // extra wave of the wide kernel, which takes a whole chain's time however
 // few chains it holds; when those chains fill at most half the compute
 // units, their slices take at most two shorter waves.  Both plans are timed
-// with makespan() (blocks of each chain times the per-block costs above)
-// and the faster is taken.  Calls of more than four waves, or whose
-// remainder is larger, run on the wide kernel alone.
+// on a model of the GPU (each chain's blocks times the per-block costs
+// above) and the faster is taken.  Calls of more than four waves, of more
+// than kPlanSeqs sequences, or whose remainder is larger, run on the wide
+// kernel alone.
+constexpr int32_t kPlanSeqs = 128;
 int32_t wide_sequences(const la::PrefillArgs& a, const int32_t* cu_host, int cus) {
   const int32_t S = a.num_seqs, H = a.num_heads;
   const int64_t chains = (int64_t)S * H;
-  if (cus <= 0 || chains > 4 * (int64_t)cus) return S;
+  if (cus <= 0 || chains > 4 * (int64_t)cus || S > kPlanSeqs) return S;
   const int32_t seqs = (int32_t)(chains / cus * cus / H);  // whole sequences in whole waves
   const int64_t rest = chains - (int64_t)seqs * H;
-  if (seqs == 0 || rest == 0 || 2 * rest > cus || S - seqs > la::kMaxOrder) return S;
+  if (seqs == 0 || rest == 0 || 2 * rest > cus) return S;
   auto blocks = [&](int32_t i) {  // blocks of the i-th sequence in dispatch order
     const int32_t s = a.ordered ? a.seq_order[i] : i;
     return (double)((cu_host[s + 1] - cu_host[s] + 63) / 64);
   };
-  std::vector<double> all, wide, slices;
-  for (int32_t i = 0; i < S; ++i) {
-    const double b = blocks(i);
-    for (int32_t h = 0; h < H; ++h) {
-      all.push_back(b * kWideBlockUs);
-      if (i < seqs) wide.push_back(b * kWideBlockUs);
-      else slices.insert(slices.end(), 128 / la::kBf16Cols, b * kSliceBlockUs);
+  // Time of a launch of `per` workgroups for each sequence at dispatch
+  // positions [from, to), each lasting its sequence's blocks x block_us, the
+  // GPU handing every workgroup in turn to the compute unit that frees
+  // first.  The units are kept as groups (time they free, how many), in
+  // order of time: the workgroups of one sequence take the earliest groups.
+  std::vector<std::pair<double, int64_t>> groups;
+  auto launch_us = [&](int32_t from, int32_t to, int64_t per, double block_us) {
+    groups.assign(1, {0.0, (int64_t)cus});
+    double last = 0.0;
+    for (int32_t i = from; i < to; ++i) {
+      const double d = blocks(i) * block_us;
+      int64_t left = per;
+      while (left > 0) {
+        const double t = groups.front().first;
+        const int64_t take = std::min(left, groups.front().second);
+        if ((groups.front().second -= take) == 0) groups.erase(groups.begin());
+        left -= take;
+        last = std::max(last, t + d);
+        auto at = std::lower_bound(groups.begin(), groups.end(), t + d,
+                                   [](const std::pair<double, int64_t>& g, double x) {
+                                     return g.first < x;
+                                   });
+        if (at != groups.end() && at->first == t + d) at->second += take;
+        else groups.insert(at, {t + d, take});
+      }
     }
-  }
-  const double split = makespan(wide, cus) + kLaunchUs + makespan(slices, cus);
-  return split < makespan(all, cus) ? seqs : S;
+    return last;
+  };
+  const double split = launch_us(0, seqs, H, kWideBlockUs) + kLaunchUs +
+                       launch_us(seqs, S, 128 / la::kBf16Cols * H, kSliceBlockUs);
+  return split < launch_us(0, S, H, kWideBlockUs) ? seqs : S;
 }
 
 // The kernels of a bf16 la_prefill or la_prefill_pool call, as the number of
