@@ -470,8 +470,8 @@ typedef struct la_norm {
  *
  * Arguments as la_prefill, plus norm, workspace and workspace_bytes.
  * in_dtype must be LA_BF16 and head_dim 128 (else LA_ERR_UNSUPPORTED).
- * With at least as many (sequence, head) pairs as the current device has
- * compute units, one workgroup per pair runs the chain (as la_prefill) and
+ * With more (sequence, head) pairs than half the compute units of the
+ * current device, one workgroup per pair runs the chain (as la_prefill) and
  * the workspace is unused (may be NULL).  With fewer, the sequences are cut
  * into segments (as la_prefill_segmented's chained scan, with a segment
  * length the library chooses so that segments x heads reaches the compute

@@ -880,10 +880,12 @@ int32_t normed_segment_len(int64_t total_tokens, int32_t num_heads) {
 }
 
 // Whether la_prefill_normed runs one workgroup per (sequence, head) pair
-// (else the chained scan over segments).
+// (else the chained scan over segments): with more pairs than half the
+// compute units, where the one wave of whole chains is faster than the
+// scan's extra local-state pass over every segment.
 bool normed_wide(int32_t num_seqs, int32_t num_heads) {
   const int cus = device_cus() > 0 ? device_cus() : 256;
-  return (int64_t)num_seqs * num_heads >= cus;
+  return 2 * (int64_t)num_seqs * num_heads > cus;
 }
 
 }  // namespace
