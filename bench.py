@@ -31,9 +31,11 @@ One JSON line is printed with the contract fields plus:
   peaks         measured on the GPU: a 1 GiB read+write stream (HBM) and an 8192^3
                 bf16 matmul; roofline.frac_of_measured_stream relates the
                 prefill kernel to that stream.
-  sweep         tokens/s at N = 1K ... 1M, for eight 8K sequences in one call and
-                for a packed varlen batch (the last two have enough (sequence,
-                head) chains for the one-workgroup-per-chain kernel): back-to-back
+  sweep         tokens/s at N = 1K ... 1M, for three, five and eight 8K
+                sequences in one call (192, 320 and 512 chains: the
+                one-workgroup-per-chain kernel, for 320 chains followed by
+                the 32-column kernel on the fifth sequence) and for a packed
+                varlen batch (that kernel as well): back-to-back
                 launches over input sets that together exceed 1 GiB;
                 sweep_flatness gives max/min tokens/s over 1K ... 1M.
 """
@@ -545,7 +547,7 @@ def bench_normed(dev, reps=10):
 
 
 SWEEP = ("sweep1024", "sweep4096", "sweep16384", "sweep65536", "sweep65536_nodecay", "n1m",
-         "batch8_n8k", "varlen64")
+         "batch3_n8k", "batch5_n8k", "batch8_n8k", "varlen64")
 
 
 def bench_sweep(dev, reps=20, names=SWEEP, footprint=1 << 30):

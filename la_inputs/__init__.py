@@ -151,6 +151,11 @@ def workload(name):
         # the n8k sequence shape, eight sequences in one call (512 chains)
         return dict(name=name, lengths=[8192] * 8, H=64, d=128, dtype="bf16",
                     decay=decay_from_seed(64), seed=SEEDS[name])
+    if name in ("batch3_n8k", "batch5_n8k"):
+        # the same shape three or five times (192 or 320 chains)
+        b = int(name[5])
+        return dict(name=name, lengths=[8192] * b, H=64, d=128, dtype="bf16",
+                    decay=decay_from_seed(64), seed=SEEDS["batch8_n8k"] + 10 * b)
     if name == "n1m":
         return dict(name=name, lengths=[1 << 20], H=64, d=128, dtype="bf16",
                     decay=decay_from_seed(64), seed=SEEDS[name])

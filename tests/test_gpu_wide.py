@@ -155,20 +155,22 @@ def test_wide_determinism_bitwise(dev):
     assert torch.equal(kv1, kv2)
 
 
-def test_wide_batch8_n8k_benchmark_launch(dev):
-    """Eight 8192-token sequences x 64 heads (the bench's batch8_n8k launch):
-    three heads over all eight sequences against the oracle, and every
-    output and final state against the 32-column kernel run one sequence
-    at a time on the same inputs (64 chains per call)."""
+@pytest.mark.parametrize("name", ["batch3_n8k", "batch5_n8k", "batch8_n8k"])
+def test_wide_batch_n8k_benchmark_launch(dev, name):
+    """Three, five or eight 8192-token sequences x 64 heads (the bench's
+    launches; with five, the fifth sequence runs in 32-column slices after
+    one wave of the wide kernel): three heads over all sequences against the
+    oracle, and every output and final state against the 32-column kernel
+    run one sequence at a time on the same inputs (64 chains per call)."""
     import torch
     import linear_attention_la_amd as la
     from la_inputs import device_qkv
 
-    w = workload("batch8_n8k")
+    w = workload(name)
     cu = cu_seqlens(w["lengths"])
     T, S = int(cu[-1]), len(w["lengths"])
     _assert_wide(S * H)
-    say(f"case wide batch8_n8k T={T}")
+    say(f"case wide {name} T={T}")
     qd, kd, vd = device_qkv(T, H, D, w["seed"], dev)
     o, kv = la.prefill(qd, kd, vd, cu, w["decay"])
     parts = [la.prefill(qd[cu[i]:cu[i + 1]].contiguous(), kd[cu[i]:cu[i + 1]].contiguous(),
@@ -186,7 +188,7 @@ def test_wide_batch8_n8k_benchmark_launch(dev):
         s3 = parity.check(to_np(o[:, h, :])[:, None, :], o_ref, 1, 1e-2, out_bf16=True,
                           what=f"o head {h}")
         s4 = parity.check(to_np(kv[:, h])[:, None], kv_ref, 1, 1e-2, what=f"kv head {h}")
-        say("wide batch8 head", h, s3, s4)
+        say(f"wide {name} head", h, s3, s4)
 
 
 def _compare_on_device(a, b, bf16, what, rel_tol=1e-2, elem_tol=2e-2):
