@@ -191,14 +191,14 @@ constexpr double kLaunchUs = 8.0;
 // few chains it holds; when those chains fill at most half the compute
 // units, their slices take at most two shorter waves.  Both plans are timed
 // on a model of the GPU (each chain's blocks times the per-block costs
-// above) and the faster is taken.  Calls of more than four waves, of more
+// above) and the faster is taken.  Calls of more than 16 waves, of more
 // than kPlanSeqs sequences, or whose remainder is larger, run on the wide
 // kernel alone.
 constexpr int32_t kPlanSeqs = 128;
 int32_t wide_sequences(const la::PrefillArgs& a, const int32_t* cu_host, int cus) {
   const int32_t S = a.num_seqs, H = a.num_heads;
   const int64_t chains = (int64_t)S * H;
-  if (cus <= 0 || chains > 4 * (int64_t)cus || S > kPlanSeqs) return S;
+  if (cus <= 0 || chains > 16 * (int64_t)cus || S > kPlanSeqs) return S;
   const int32_t seqs = (int32_t)(chains / cus * cus / H);  // whole sequences in whole waves
   const int64_t rest = chains - (int64_t)seqs * H;
   if (seqs == 0 || rest == 0 || 2 * rest > cus) return S;
