@@ -2,7 +2,7 @@
 of la_prefill (both bf16 kernels and the fp32 path), la_prefill_segmented
 (and its no-allocation form), la_prefill_backward (plain and segmented),
 la_prefill_normed and the state pool (prefill then decode) against the fp64
-oracle.
+oracle, and la_prefill's choice of kernels across chain counts.
 Each case draws its batch shape, lengths (block edges 0, 1, 63, 64, 65
 included often), head count, d, decays, initial states and output dtype
 from its own seed, and prints them before it runs."""
@@ -82,6 +82,57 @@ def test_random_prefill(dev, case):
     tol = 1e-5 if fp32_in else 1e-2
     s1 = parity.check(to_np(o), o_ref, 1, tol, out_bf16=not out_f32, what=f"case {case} o")
     s2 = parity.check(to_np(kv), kv_ref, 1, tol, what=f"case {case} kv")
+    say("  ", s1, s2)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_kernel_choice(dev, monkeypatch, case):
+    """la_prefill at d = 128 over 32 to 1280 (sequence, head) chains, equal or
+    mixed lengths: the library picks the 32-column kernel, one workgroup per
+    chain, or whole waves of the latter with the remaining sequences in
+    slices.  Whatever it picks, every sequence's rows and final state equal,
+    bit for bit, those of one of the two kernels forced for the whole call
+    (LA_NDV), and the call matches the oracle."""
+    import torch
+    import linear_attention_la_amd as la
+
+    rng = np.random.Generator(np.random.PCG64(7600 + case))
+    S = int(rng.integers(2, 21))
+    H = int(rng.choice([16, 24, 32, 48, 64]))
+    if rng.random() < 0.5:
+        lengths = [int(rng.integers(1, 401))] * S
+    else:
+        lengths = _lengths(rng, S, 400)
+    decay = _decays(rng, H)
+    kv_init = bool(rng.random() < 0.5)
+    say(f"random kernel choice case {case}: chains={S * H} lengths={lengths} H={H} "
+        f"kv_init={kv_init}")
+    T = sum(lengths)
+    q, k, v = host_qkv(T, H, 128, 8600 + case, "bf16")
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(S, H, 128, 9600 + case, scale=0.1) if kv_init else None
+    qd, kd, vd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v))
+    kv0d = to_dev(kv0, torch.float32, dev) if kv_init else None
+
+    def run(ndv):
+        if ndv is None:
+            monkeypatch.delenv("LA_NDV", raising=False)
+        else:
+            monkeypatch.setenv("LA_NDV", ndv)
+        o, kv = la.prefill(qd, kd, vd, cu, decay, kv_init=kv0d, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return o, kv
+
+    o, kv = run(None)
+    forced = [run("1"), run("4")]
+    monkeypatch.delenv("LA_NDV")
+    for s in range(S):
+        rows = slice(int(cu[s]), int(cu[s + 1]))
+        assert any(torch.equal(o[rows], fo[rows]) and torch.equal(kv[s], fkv[s])
+                   for fo, fkv in forced), f"sequence {s} matches neither kernel"
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0)
+    s1 = parity.check(to_np(o), o_ref, 1, 1e-2, what=f"case {case} o")
+    s2 = parity.check(to_np(kv), kv_ref, 1, 1e-2, what=f"case {case} kv")
     say("  ", s1, s2)
 
 
