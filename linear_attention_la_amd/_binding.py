@@ -315,6 +315,27 @@ def cu_masked_stream(cu_mask, device=None):
     return stream
 
 
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output or workspace-like buffer: the library writes
+    exactly ``shape`` elements of ``dtype`` through its pointer and cannot
+    see the tensor's size, so anything else is rejected here."""
+    torch = _torch()
+    if not (isinstance(t, torch.Tensor) and t.device == device and t.dtype == dtype
+            and tuple(t.shape) == tuple(shape) and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}")
+    return t
+
+
+def _check_device_buffer(name, t, device):
+    """A caller-supplied workspace: a contiguous tensor on ``device`` (its
+    size in bytes is passed to the library, which checks it)."""
+    torch = _torch()
+    if not (isinstance(t, torch.Tensor) and t.device == device and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    return t
+
+
 def _host_decay(decay, num_heads):
     torch = _torch()
     if isinstance(decay, torch.Tensor):
@@ -337,13 +358,16 @@ def _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, fin
             raise TypeError(f"{name} must be a device tensor")
         if t.dim() != 3 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [T, H, d] tensor")
-    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype:
-        raise ValueError("q, k, v must share shape and dtype")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype \
+            or q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must share shape, dtype and device")
     T, H, d = q.shape
     dev = q.device
     in_code = _dtype_code(q)
     if out_dtype is None:
         out_dtype = q.dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported out_dtype {out_dtype} (bfloat16 or float32)")
     out_code = LA_BF16 if out_dtype == torch.bfloat16 else LA_FP32
     if cu_seqlens_host is not None:
         cu_host = torch.as_tensor(np.ascontiguousarray(
@@ -365,17 +389,22 @@ def _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, fin
     S = cu_host.numel() - 1
     if S < 0:
         raise ValueError("cu_seqlens must have at least one entry")
+    if cu_dev.numel() != cu_host.numel() or cu_dev.device != dev:
+        raise ValueError("cu_seqlens and cu_seqlens_host must have the same length, "
+                         "cu_seqlens on q's device")
     dec = _host_decay(decay, H)
     if kv_init is not None:
-        if (not kv_init.is_cuda or kv_init.dtype != torch.float32 or not kv_init.is_contiguous()
-                or tuple(kv_init.shape) != (S, H, d, d)):
-            raise ValueError("kv_init must be a contiguous fp32 device tensor [S, H, d, d]")
+        _check_out("kv_init", kv_init, (S, H, d, d), torch.float32, dev)
     if out is None:
         out = torch.empty((T, H, d), dtype=out_dtype, device=dev)
-    if final_state and kv_final is None:
-        kv_final = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    else:
+        _check_out("out", out, (T, H, d), out_dtype, dev)
     if not final_state:
         kv_final = None
+    elif kv_final is None:
+        kv_final = torch.empty((S, H, d, d), dtype=torch.float32, device=dev)
+    else:
+        _check_out("kv_final", kv_final, (S, H, d, d), torch.float32, dev)
     m = _Prefill()
     m.T, m.H, m.d, m.S, m.dev = T, H, d, S, dev
     m.in_code, m.out_code = in_code, out_code
@@ -433,9 +462,8 @@ def prefill_segmented(q, k, v, cu_seqlens, decay, segment_len, kv_init=None, out
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
         if stream is not None:
             workspace.record_stream(stream)
-    elif not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
-              and workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous device tensor")
+    else:
+        _check_device_buffer("workspace", workspace, m.dev)
     nbytes = workspace.numel() * workspace.element_size()
     _check(la_prefill_segmented(*m.args, segment_len, workspace.data_ptr(), nbytes, m.stream))
     return m.out, m.kv_final
@@ -462,11 +490,11 @@ def _marshal_norm(weight, eps, gate, H, d, dev, like):
     torch = _torch()
     if not isinstance(weight, torch.Tensor):
         weight = torch.as_tensor(np.asarray(weight, dtype=np.float32)).to(dev)
-    if (not weight.is_cuda or weight.dtype != torch.float32 or not weight.is_contiguous()
+    if (weight.device != dev or weight.dtype != torch.float32 or not weight.is_contiguous()
             or tuple(weight.shape) != (H, d)):
         raise ValueError("norm weight must be a contiguous fp32 device tensor [H, d]")
     if gate is not None:
-        if (not isinstance(gate, torch.Tensor) or not gate.is_cuda or gate.dtype != like.dtype
+        if (not isinstance(gate, torch.Tensor) or gate.device != dev or gate.dtype != like.dtype
                 or not gate.is_contiguous() or gate.shape != like.shape):
             raise ValueError("gate must be a contiguous device tensor shaped and typed as q")
     nm = LaNorm(weight.data_ptr(), float(eps), None if gate is None else gate.data_ptr())
@@ -492,6 +520,8 @@ def prefill_normed(q, k, v, cu_seqlens, decay, weight, eps=1e-6, gate=None, kv_i
         workspace = torch.empty(need, dtype=torch.uint8, device=m.dev)
         if stream is not None:
             workspace.record_stream(stream)
+    elif workspace is not None:
+        _check_device_buffer("workspace", workspace, m.dev)
     wp = 0 if workspace is None else workspace.data_ptr()
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a = m.args
@@ -529,8 +559,9 @@ def _marshal_slots(slots, slots_host, n, dev, stream):
         sl_dev = torch.from_numpy(sl_host).to(dev)
     if stream is not None and sl_dev is not slots:
         sl_dev.record_stream(stream)  # temporary read by a kernel on another stream
-    if sl_host.shape != (n,):
-        raise ValueError(f"slots has shape {sl_host.shape}, expected ({n},)")
+    if sl_host.shape != (n,) or sl_dev.numel() != n or sl_dev.device != dev:
+        raise ValueError(f"slots has shape {sl_host.shape} (device copy: {sl_dev.numel()} on "
+                         f"{sl_dev.device}), expected ({n},) on {dev}")
     return sl_dev, sl_host
 
 
@@ -546,7 +577,7 @@ def prefill_pool(q, k, v, cu_seqlens, decay, kv_pool, slots, out_dtype=None, str
     torch = _torch()
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, None, out_dtype, stream, False, out, None,
                          cu_seqlens_host)
-    if (not isinstance(kv_pool, torch.Tensor) or not kv_pool.is_cuda
+    if (not isinstance(kv_pool, torch.Tensor) or kv_pool.device != m.dev
             or kv_pool.dtype != torch.float32 or not kv_pool.is_contiguous()
             or kv_pool.dim() != 4 or tuple(kv_pool.shape[1:]) != (m.H, m.d, m.d)):
         raise ValueError("kv_pool must be a contiguous fp32 device tensor [P, H, d, d]")
@@ -566,14 +597,13 @@ def decode(q, k, v, kv, decay, stream=None, out=None):
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
     if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype \
-            or q.dtype != v.dtype:
-        raise ValueError("q, k, v must share shape [B, H, d] and dtype")
+            or q.dtype != v.dtype or q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must share shape [B, H, d], dtype and device")
     B, H, d = q.shape
-    if kv.dtype != torch.float32 or tuple(kv.shape) != (B, H, d, d):
-        raise ValueError("kv must be fp32 [B, H, d, d]")
+    _dtype_code(q)
+    _check_out("kv", kv, (B, H, d, d), torch.float32, q.device)
     dec = _host_decay(decay, H)
-    if out is None:
-        out = torch.empty_like(q)
+    out = torch.empty_like(q) if out is None else _check_out("out", out, q.shape, q.dtype, q.device)
     st = la_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(), dec.ctypes.data,
                    B, H, d, _dtype_code(q), out.data_ptr(), _stream_handle(stream, q.device))
     _check(st)
@@ -589,15 +619,14 @@ def decode_normed(q, k, v, kv, decay, weight, eps=1e-6, gate=None, stream=None, 
         if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
     if q.dim() != 3 or q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype \
-            or q.dtype != v.dtype:
-        raise ValueError("q, k, v must share shape [B, H, d] and dtype")
+            or q.dtype != v.dtype or q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must share shape [B, H, d], dtype and device")
     B, H, d = q.shape
-    if kv.dtype != torch.float32 or tuple(kv.shape) != (B, H, d, d):
-        raise ValueError("kv must be fp32 [B, H, d, d]")
+    _dtype_code(q)
+    _check_out("kv", kv, (B, H, d, d), torch.float32, q.device)
     dec = _host_decay(decay, H)
     nm, keep = _marshal_norm(weight, eps, gate, H, d, q.device, q)
-    if out is None:
-        out = torch.empty_like(q)
+    out = torch.empty_like(q) if out is None else _check_out("out", out, q.shape, q.dtype, q.device)
     st = la_decode_normed(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(),
                           dec.ctypes.data, B, H, d, _dtype_code(q), nm, out.data_ptr(),
                           _stream_handle(stream, q.device))
@@ -617,16 +646,20 @@ def decode_pool(q, k, v, kv_pool, slots, decay, stream=None, out=None, slots_hos
         if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dim() != 3 \
                 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [B, H, d] device tensor")
+    if q.shape != k.shape or q.shape != v.shape or q.dtype != k.dtype or q.dtype != v.dtype \
+            or q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must share shape [B, H, d], dtype and device")
     B, H, d = q.shape
-    if (not kv_pool.is_cuda or kv_pool.dtype != torch.float32 or not kv_pool.is_contiguous()
+    _dtype_code(q)
+    if (not isinstance(kv_pool, torch.Tensor) or kv_pool.device != q.device
+            or kv_pool.dtype != torch.float32 or not kv_pool.is_contiguous()
             or kv_pool.dim() != 4 or tuple(kv_pool.shape[1:]) != (H, d, d)):
         raise ValueError("kv_pool must be a contiguous fp32 device tensor [P, H, d, d]")
     P = kv_pool.shape[0]
     dev = q.device
     sl_dev, sl_host = _marshal_slots(slots, slots_host, B, dev, stream)
     dec = _host_decay(decay, H)
-    if out is None:
-        out = torch.empty_like(q)
+    out = torch.empty_like(q) if out is None else _check_out("out", out, q.shape, q.dtype, dev)
     st = la_decode_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_pool.data_ptr(), P,
                         sl_dev.data_ptr(), sl_host.ctypes.data, dec.ctypes.data, B, H, d,
                         _dtype_code(q), out.data_ptr(), _stream_handle(stream, dev))
@@ -639,20 +672,20 @@ def _backward(q, k, v, d_o, cu_seqlens, decay, kv_init, dkv_final, grad_dtype, s
     torch = _torch()
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, grad_dtype, stream, False, dq,
                          None, cu_seqlens_host)
-    if not (isinstance(d_o, torch.Tensor) and d_o.is_cuda and d_o.shape == q.shape
-            and d_o.dtype == q.dtype and d_o.is_contiguous()):
-        raise ValueError("d_o must be a contiguous device tensor like q")
-    if dkv_final is not None and (not dkv_final.is_cuda or dkv_final.dtype != torch.float32
-                                  or not dkv_final.is_contiguous()
-                                  or tuple(dkv_final.shape) != (m.S, m.H, m.d, m.d)):
-        raise ValueError("dkv_final must be a contiguous fp32 device tensor [S, H, d, d]")
-    gdt = q.dtype if grad_dtype is None else grad_dtype
-    dk = torch.empty(q.shape, dtype=gdt, device=m.dev) if dk is None else dk
-    dv = torch.empty(q.shape, dtype=gdt, device=m.dev) if dv is None else dv
-    if init_grad and dkv_init is None:
-        dkv_init = torch.empty((m.S, m.H, m.d, m.d), dtype=torch.float32, device=m.dev)
+    _check_out("d_o", d_o, q.shape, q.dtype, m.dev)
+    if dkv_final is not None:
+        _check_out("dkv_final", dkv_final, (m.S, m.H, m.d, m.d), torch.float32, m.dev)
+    gdt = m.out.dtype  # grad_dtype (default: q's), as checked for dq
+    dk = torch.empty(q.shape, dtype=gdt, device=m.dev) if dk is None else \
+        _check_out("dk", dk, q.shape, gdt, m.dev)
+    dv = torch.empty(q.shape, dtype=gdt, device=m.dev) if dv is None else \
+        _check_out("dv", dv, q.shape, gdt, m.dev)
     if not init_grad:
         dkv_init = None
+    elif dkv_init is None:
+        dkv_init = torch.empty((m.S, m.H, m.d, m.d), dtype=torch.float32, device=m.dev)
+    else:
+        _check_out("dkv_init", dkv_init, (m.S, m.H, m.d, m.d), torch.float32, m.dev)
     if segment_len is None:
         st, need = la_prefill_backward_workspace_size(m.S, m.H, m.d)
         needed = kv_init is not None or dkv_final is not None
@@ -665,9 +698,8 @@ def _backward(q, k, v, d_o, cu_seqlens, decay, kv_init, dkv_final, grad_dtype, s
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
         if stream is not None:
             workspace.record_stream(stream)
-    elif workspace is not None and not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
-                                        and workspace.is_contiguous()):
-        raise ValueError("workspace must be a contiguous device tensor")
+    elif workspace is not None:
+        _check_device_buffer("workspace", workspace, m.dev)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     (qp, kp, vp_, cud, cuh, S, T, H, d, in_code, out_code, decp, kvip, dqp, _) = m.args
     common = (qp, kp, vp_, d_o.data_ptr(), cud, cuh, S, T, H, d, in_code, out_code, decp, kvip,

@@ -266,3 +266,67 @@ def test_varlen_64_sequences(dev):
     _check_heads(dev, qd, kd, vd, cu, w["decay"], o, kv, [5, 50], beta=256, what="varlen64")
     del qd, kd, vd, o, kv
     torch.cuda.empty_cache()
+
+
+def test_binding_rejects_mismatched_outputs(dev):
+    """The torch wrappers reject caller-supplied outputs and buffers that do
+    not match what the library will write (shape, dtype, device, layout) and
+    output dtypes it does not produce, before any call into the library: it
+    writes through bare pointers and cannot see a tensor's size."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import cu_seqlens
+
+    say("case binding rejects mismatched outputs")
+    T, H, d = 130, 2, 64
+    q, k, v = (to_dev(x, torch.bfloat16, dev) for x in host_qkv(T, H, d, 5, "bf16"))
+    cu = cu_seqlens([100, 30])
+    decay = np.array([0.9, 0.8], np.float32)
+    bad_out = [torch.empty((T - 1, H, d), dtype=torch.bfloat16, device=dev),
+               torch.empty((T, H, d), dtype=torch.float32, device=dev),
+               torch.empty((T, H, 2 * d), dtype=torch.bfloat16, device=dev)[:, :, :d],
+               torch.empty((T, H, d), dtype=torch.bfloat16)]
+    for o in bad_out:
+        with pytest.raises(ValueError):
+            la.prefill(q, k, v, cu, decay, out=o)
+    with pytest.raises(ValueError):  # fp32 output into a bf16 buffer
+        la.prefill(q, k, v, cu, decay, out_dtype=torch.float32,
+                   out=torch.empty((T, H, d), dtype=torch.bfloat16, device=dev))
+    with pytest.raises(TypeError):
+        la.prefill(q, k, v, cu, decay, out_dtype=torch.float16)
+    with pytest.raises(ValueError):
+        la.prefill(q, k, v, cu, decay, kv_final=torch.empty((1, H, d, d), device=dev))
+    with pytest.raises(ValueError):
+        la.prefill(q, k, v, cu, decay, kv_init=torch.zeros((2, H, d, d), device=dev).double())
+    with pytest.raises(ValueError):  # host copy longer than the device cu_seqlens
+        la.prefill(q, k, v, torch.from_numpy(cu[:2].copy()).to(dev), decay,
+                   cu_seqlens_host=cu)
+    with pytest.raises(ValueError):
+        la.prefill_segmented(q, k, v, cu, decay, 64, workspace=torch.empty(1 << 20,
+                                                                            dtype=torch.uint8))
+    do = torch.empty_like(q)
+    with pytest.raises(ValueError):
+        la.prefill_backward(q, k, v, do, cu, decay,
+                            dk=torch.empty((T, H, d), dtype=torch.float32, device=dev))
+    with pytest.raises(ValueError):
+        la.prefill_backward(q, k, v, do, cu, decay,
+                            dkv_init=torch.empty((2, H, d, d), dtype=torch.bfloat16, device=dev))
+    q1, k1, v1 = q[:4].contiguous(), k[:4].contiguous(), v[:4].contiguous()
+    kv = torch.zeros((4, H, d, d), device=dev)
+    with pytest.raises(ValueError):
+        la.decode(q1, k1, v1, kv, decay, out=torch.empty((4, H, d), dtype=torch.float32,
+                                                          device=dev))
+    with pytest.raises(ValueError):
+        la.decode(q1, k1, v1, kv[:3].contiguous(), decay)
+    pool = torch.zeros((6, H, d, d), device=dev)
+    with pytest.raises(ValueError):
+        la.decode_pool(q1, k1, v1, pool, torch.tensor([0, 1, 2], dtype=torch.int32,
+                                                      device=dev), decay)
+    with pytest.raises(ValueError):
+        la.prefill_pool(q, k, v, cu, decay, pool, [0, 1],
+                        out=torch.empty((H, T, d), dtype=torch.bfloat16,
+                                        device=dev).transpose(0, 1))
+    # nothing was launched; a correct call still works
+    o, kv_f = la.prefill(q, k, v, cu, decay)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(kv_f).all()
