@@ -189,6 +189,33 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
                           void* stream);
 
 /*
+ * la_prefill_kernel_plan -- the kernels la_prefill and la_prefill_pool would
+ * run for a call with bf16 inputs and these sequences and heads (see
+ * "Kernels" at la_prefill).  Host only: nothing is enqueued and no device
+ * memory is touched.
+ *
+ *   num_seqs, cu_seqlens_host, num_heads, head_dim: as in la_prefill.
+ *   compute_units  compute units of the device to plan for (e.g. 256 for
+ *                  MI355X), or 0 for the current device.
+ *   wide_seqs      host int32, receives the number of leading sequences, in
+ *                  dispatch order, that run one workgroup per (sequence,
+ *                  head); the others run in 32-column slices (in a second
+ *                  launch when both kinds occur).  0: every sequence in
+ *                  slices; num_seqs: every sequence one workgroup per pair.
+ *   order          NULL, or host int32 [num_seqs], receives the dispatch
+ *                  order (longest first for 2 to 512 sequences, else the
+ *                  index order).
+ *
+ * LA_NDV is applied as in la_prefill.  Errors: LA_ERR_INVALID_ARG (NULL
+ * wide_seqs or cu_seqlens_host, num_seqs or compute_units < 0, bad
+ * cu_seqlens), LA_ERR_UNSUPPORTED (num_heads or head_dim as in la_prefill, an
+ * LA_NDV value la_prefill rejects, or compute_units 0 with no device).
+ */
+la_status la_prefill_kernel_plan(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                 int32_t num_heads, int32_t head_dim, int32_t compute_units,
+                                 int32_t* wide_seqs, int32_t* order);
+
+/*
  * la_prefill_segmented -- la_prefill with every sequence cut into segments of
  * segment_len tokens that run as parallel chains; same results (up to the
  * order of fp32 sums) and the same arguments, plus:

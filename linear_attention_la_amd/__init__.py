@@ -15,6 +15,7 @@ library is missing, every call raises.
     o = decode_pool(q, k, v, pool, slots, decay)   # pool[slots] updated in place
     o = prefill_pool(q, k, v, cu_seqlens, decay, pool, slots)   # continues from pool[slots]
     s = cu_masked_stream(mask)   # a stream restricted to some compute units (two-stream serving)
+    n, order = kernel_plan(cu_seqlens, num_heads)   # which prefill kernels a call would run
 """
 
 from ._binding import (  # noqa: F401
@@ -31,6 +32,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     cu_masked_stream,
     la_prefill,
+    la_prefill_kernel_plan,
     la_prefill_segmented,
     la_prefill_segmented_noalloc,
     la_prefill_segmented_workspace_size,
@@ -47,6 +49,7 @@ from ._binding import (  # noqa: F401
     la_status_str,
     la_last_error,
     prefill,
+    kernel_plan,
     prefill_segmented,
     prefill_segmented_noalloc,
     prefill_segmented_workspace_size,

@@ -64,6 +64,8 @@ def lib():
     L.la_prefill_pool.restype = ctypes.c_int
     L.la_prefill_pool.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
                                   ctypes.c_int, vp, vp, i32, vp, vp, vp, vp]
+    L.la_prefill_kernel_plan.restype = ctypes.c_int
+    L.la_prefill_kernel_plan.argtypes = [i32, vp, i32, i32, i32, ctypes.POINTER(i32), vp]
     L.la_prefill_segmented.restype = ctypes.c_int
     L.la_prefill_segmented.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i32, ctypes.c_int,
                                        ctypes.c_int, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
@@ -136,6 +138,15 @@ def la_prefill_segmented_noalloc(q, k, v, cu_seqlens_dev, cu_seqlens_host, num_s
                                               total_tokens, num_heads, head_dim, in_dtype,
                                               out_dtype, decay, kv_init, o, kv_final,
                                               segment_len, stream)
+
+
+def la_prefill_kernel_plan(num_seqs, cu_seqlens_host, num_heads, head_dim, compute_units,
+                           order):
+    """Returns (status, wide_seqs); ``order`` is a host int32 pointer or None."""
+    n = ctypes.c_int32(0)
+    st = lib().la_prefill_kernel_plan(num_seqs, cu_seqlens_host, num_heads, head_dim,
+                                      compute_units, ctypes.byref(n), order)
+    return st, n.value
 
 
 def la_prefill_segmented_workspace_size(num_seqs, cu_seqlens_host, num_heads, head_dim,
@@ -434,6 +445,20 @@ def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=Non
                          out, kv_final, cu_seqlens_host)
     _check(la_prefill(*m.args, m.stream))
     return m.out, m.kv_final
+
+
+def kernel_plan(cu_seqlens_host, num_heads, head_dim=128, compute_units=0):
+    """The kernels prefill() and prefill_pool() would run for bf16 inputs with
+    these sequences (la_prefill_kernel_plan): (wide_seqs, order) -- the first
+    ``wide_seqs`` sequences of ``order`` run one workgroup per (sequence,
+    head), the others in 32-column slices.  ``compute_units`` 0 plans for the
+    current device."""
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32).reshape(-1))
+    order = np.zeros(max(cu.shape[0] - 1, 0), dtype=np.int32)
+    st, n = la_prefill_kernel_plan(cu.shape[0] - 1, cu.ctypes.data, num_heads, head_dim,
+                                   compute_units, order.ctypes.data if order.size else None)
+    _check(st)
+    return n, order
 
 
 def prefill_segmented_workspace_size(cu_seqlens_host, num_heads, head_dim, segment_len):

@@ -172,10 +172,10 @@ int device_cus() {
 // a chain, one workgroup per compute unit) then needs three or more waves of
 // workgroups where the wide kernel needs one; with fewer chains the slices'
 // two waves are faster.
-bool use_wide(int64_t chains, int32_t head_dim) {
-  const int cus = device_cus();
+bool use_wide(int64_t chains, int32_t head_dim, int cus) {
   return head_dim == 128 && cus > 0 && 2 * chains > cus;
 }
+bool use_wide(int64_t chains, int32_t head_dim) { return use_wide(chains, head_dim, device_cus()); }
 
 // Time per 64-token block of a one-workgroup-per-chain workgroup and of a
 // 32-column slice workgroup with the GPU full (MI355X, d = 128), and the
@@ -248,12 +248,12 @@ int32_t wide_sequences(const la::PrefillArgs& a, const int32_t* cu_host, int cus
 // wide_sequences decide.  Any other value is LA_ERR_UNSUPPORTED, before
 // anything is enqueued.
 la_status choose_kernels(const la::PrefillArgs& a, const int32_t* cu_host, int32_t head_dim,
-                         int32_t* wide_seqs) {
+                         int cus, int32_t* wide_seqs) {
   *wide_seqs = 0;
   const int64_t chains = (int64_t)a.num_seqs * a.num_heads;
   const char* s = getenv("LA_NDV");
   if (!s || !*s) {
-    if (use_wide(chains, head_dim)) *wide_seqs = wide_sequences(a, cu_host, device_cus());
+    if (use_wide(chains, head_dim, cus)) *wide_seqs = wide_sequences(a, cu_host, cus);
     return LA_OK;
   }
   const bool slices = strcmp(s, head_dim == 128 ? "4" : "2") == 0;
@@ -533,7 +533,8 @@ la_status la_prefill(const void* q, const void* k, const void* v,
   if (in_dtype != LA_BF16)
     return hip_status(la::launch_prefill_f32(a, head_dim, out_dtype, s), "la_prefill launch");
   int32_t wide_seqs = 0;
-  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, &wide_seqs)) != LA_OK) return st;
+  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, device_cus(), &wide_seqs)) != LA_OK)
+    return st;
   return hip_status(launch_bf16_prefill(a, wide_seqs, head_dim, out_dtype, s),
                     "la_prefill launch");
 }
@@ -590,10 +591,37 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
   set_order(a, cu_seqlens_host, num_seqs);
   int32_t wide_seqs = 0;
-  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, &wide_seqs)) != LA_OK) return st;
+  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, device_cus(), &wide_seqs)) != LA_OK)
+    return st;
   return hip_status(launch_bf16_prefill(a, wide_seqs, head_dim, out_dtype,
                                         static_cast<hipStream_t>(stream)),
                     "la_prefill_pool launch");
+}
+
+la_status la_prefill_kernel_plan(int32_t num_seqs, const int32_t* cu_seqlens_host,
+                                 int32_t num_heads, int32_t head_dim, int32_t compute_units,
+                                 int32_t* wide_seqs, int32_t* order) {
+  if (!wide_seqs) return fail(LA_ERR_INVALID_ARG, "wide_seqs is NULL");
+  *wide_seqs = 0;
+  if (num_seqs < 0) return fail(LA_ERR_INVALID_ARG, "num_seqs = %d < 0", num_seqs);
+  la_status st = check_heads_dim(num_heads, head_dim);
+  if (st != LA_OK) return st;
+  if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+  if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
+  if (compute_units < 0)
+    return fail(LA_ERR_INVALID_ARG, "compute_units = %d < 0", compute_units);
+  const int cus = compute_units > 0 ? compute_units : device_cus();
+  if (cus <= 0) return fail(LA_ERR_UNSUPPORTED, "no device to read the compute units of");
+  la::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  set_order(a, cu_seqlens_host, num_seqs);
+  if (order)
+    for (int32_t i = 0; i < num_seqs; ++i) order[i] = a.ordered ? a.seq_order[i] : i;
+  if (num_seqs == 0) return ok();
+  if ((st = choose_kernels(a, cu_seqlens_host, head_dim, cus, wide_seqs)) != LA_OK) return st;
+  return ok();
 }
 
 la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,

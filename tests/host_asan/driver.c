@@ -205,6 +205,36 @@ int main(void) {
            la_decode_normed(Q, K, V, KVF, decay, 3, H, D, bd, &nrm, O, NULL), LA_ERR_INVALID_ARG);
   }
 
+  /* kernel plan: every branch of the planner on the host (256 compute units) */
+  {
+    static int32_t cuv[130], order[129];
+    int32_t n = -1;
+    for (int S = 0; S <= 129; S += 1) {
+      cuv[0] = 0;  /* mixed lengths, some empty */
+      for (int i = 1; i <= S; ++i) cuv[i] = cuv[i - 1] + (i % 7 == 0 ? 0 : 64 + 911 * (i % 5));
+      for (int h = 1; h <= 64; h *= 4) {
+        expect("plan mixed", la_prefill_kernel_plan(S, cuv, h, 128, 256, &n, order), LA_OK);
+        if (n < 0 || n > S) {
+          printf("FAIL plan range S=%d H=%d: %d\n", S, h, n);
+          ++failures;
+        }
+      }
+      for (int i = 0; i <= S; ++i) cuv[i] = i * 640;  /* equal lengths */
+      expect("plan equal", la_prefill_kernel_plan(S, cuv, 64, 128, 256, &n, NULL), LA_OK);
+      expect("plan d64", la_prefill_kernel_plan(S, cuv, 64, 64, 256, &n, order), LA_OK);
+      if (n != 0) {
+        printf("FAIL plan d64 S=%d: %d\n", S, n);
+        ++failures;
+      }
+    }
+    expect("plan NULL out", la_prefill_kernel_plan(2, cu, 64, 128, 256, NULL, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("plan negative units", la_prefill_kernel_plan(2, cu, 64, 128, -5, &n, NULL),
+           LA_ERR_INVALID_ARG);
+    expect("plan bad head_dim", la_prefill_kernel_plan(2, cu, 64, 80, 256, &n, NULL),
+           LA_ERR_UNSUPPORTED);
+  }
+
   /* status strings */
   for (int s = -1; s < 6; ++s) {
     const char* name = la_status_str((la_status)s);

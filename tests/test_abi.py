@@ -32,8 +32,8 @@ def test_header_declares_entry_points():
               "la_prefill_normed_workspace_size", "la_decode_normed",
               "la_prefill_backward", "la_prefill_backward_workspace_size",
               "la_prefill_backward_segmented", "la_prefill_backward_segmented_workspace_size",
-              "la_prefill_pool", "la_decode", "la_decode_pool", "la_status_str",
-              "la_last_error"):
+              "la_prefill_pool", "la_prefill_kernel_plan", "la_decode", "la_decode_pool",
+              "la_status_str", "la_last_error"):
         assert n in names
 
 
@@ -640,3 +640,67 @@ def test_backward_segmented_rejects(name, kw, code):
 def test_backward_segmented_no_sequences():
     st, msg = _bwd_seg(S=0, T=0, cu_host=np.array([0], np.int32), ws=None, ws_bytes=0)
     assert st == la.LA_OK, msg
+
+
+# ---- la_prefill_kernel_plan: the kernel choice of la_prefill on the host ----
+
+VARLEN40 = [8335, 8420, 3054, 1378, 617, 1933, 2109, 598, 606, 16337, 4911, 1154, 2311, 14981,
+            11492, 9549, 1994, 2827, 5343, 632, 3511, 1311, 10796, 639, 5389, 10444, 1125, 11403,
+            10520, 545, 5945, 514, 2930, 2325, 1035, 1578, 8370, 1533, 858, 5762]
+
+# (lengths, heads, head_dim, expected wide_seqs) on 256 compute units
+PLANS = [
+    ([8192], 64, 128, 0),                   # 64 chains: one wave of slices
+    ([8192] * 2, 64, 128, 0),               # 128: two waves of slices beat one wide wave
+    ([8192] * 3, 64, 128, 3),               # 192: one wave of the wide kernel
+    ([8192] * 4, 64, 128, 4),               # 256
+    ([8192] * 5, 64, 128, 4),               # 320: a wide wave, the fifth in slices
+    ([576, 640, 640, 640, 640], 64, 128, 4),  # the same, the short one dispatched last
+    ([8192] * 33, 8, 128, 32),              # 264: 32 sequences wide, one in slices
+    ([8192] * 8, 64, 128, 8),               # 512: two whole waves
+    ([8192] * 17, 64, 128, 16),             # 1088
+    ([10356, 8478, 4478, 13501, 13513], 64, 128, 5),  # leftover chains fit the idle CUs
+    (VARLEN40, 8, 128, 40),                 # likewise
+    ([8192] * 200, 8, 128, 200),            # more sequences than the model plans for
+    ([8192] * 5, 64, 64, 0),                # d = 64: slices only
+    ([], 64, 128, 0),                       # no sequences
+]
+
+
+@pytest.mark.parametrize("lengths,H,d,expected", PLANS,
+                         ids=[f"{len(p[0])}x{p[1]}h-d{p[2]}-{i}" for i, p in enumerate(PLANS)])
+def test_kernel_plan(monkeypatch, lengths, H, d, expected):
+    from la_inputs import cu_seqlens
+
+    monkeypatch.delenv("LA_NDV", raising=False)
+    n, order = la.kernel_plan(cu_seqlens(lengths), H, d, compute_units=256)
+    assert n == expected
+    # the dispatch order is longest first (stable) for 2 to 512 sequences
+    if 2 <= len(lengths) <= 512:
+        assert order.tolist() == sorted(range(len(lengths)), key=lambda i: -lengths[i])
+    else:
+        assert order.tolist() == list(range(len(lengths)))
+
+
+def test_kernel_plan_override_and_errors(monkeypatch):
+    from la_inputs import cu_seqlens
+
+    cu = cu_seqlens([8192] * 5)
+    monkeypatch.setenv("LA_NDV", "1")
+    assert la.kernel_plan(cu, 64, compute_units=256)[0] == 5
+    monkeypatch.setenv("LA_NDV", "4")
+    assert la.kernel_plan(cu, 64, compute_units=256)[0] == 0
+    monkeypatch.setenv("LA_NDV", "3")
+    with pytest.raises(la.LAError, match="LA_NDV"):
+        la.kernel_plan(cu, 64, compute_units=256)
+    monkeypatch.delenv("LA_NDV")
+    for args, code in (((5, cu.ctypes.data, 64, 128, -1), la.LA_ERR_INVALID_ARG),
+                       ((-1, cu.ctypes.data, 64, 128, 256), la.LA_ERR_INVALID_ARG),
+                       ((5, None, 64, 128, 256), la.LA_ERR_INVALID_ARG),
+                       ((5, cu.ctypes.data, 0, 128, 256), la.LA_ERR_INVALID_ARG),
+                       ((5, cu.ctypes.data, 64, 96, 256), la.LA_ERR_UNSUPPORTED)):
+        st, _ = la.la_prefill_kernel_plan(*args, None)
+        assert st == code, (args, st, la.la_last_error())
+    bad = np.array([0, 10, 5], np.int32)
+    st, _ = la.la_prefill_kernel_plan(2, bad.ctypes.data, 64, 128, 256, None)
+    assert st == la.LA_ERR_INVALID_ARG

@@ -90,9 +90,9 @@ def test_random_kernel_choice(dev, monkeypatch, case):
     """la_prefill at d = 128 over 32 to 1280 (sequence, head) chains, equal or
     mixed lengths: the library picks the 32-column kernel, one workgroup per
     chain, or whole waves of the latter with the remaining sequences in
-    slices.  Whatever it picks, every sequence's rows and final state equal,
-    bit for bit, those of one of the two kernels forced for the whole call
-    (LA_NDV), and the call matches the oracle."""
+    slices.  Every sequence's rows and final state equal, bit for bit, those
+    of the kernel that la_prefill_kernel_plan names for it, forced for the
+    whole call (LA_NDV), and the call matches the oracle."""
     import torch
     import linear_attention_la_amd as la
 
@@ -126,10 +126,12 @@ def test_random_kernel_choice(dev, monkeypatch, case):
     o, kv = run(None)
     forced = [run("1"), run("4")]
     monkeypatch.delenv("LA_NDV")
-    for s in range(S):
+    n_wide, order = la.kernel_plan(cu, H, 128)  # the plan for this device
+    for pos, s in enumerate(order.tolist()):
         rows = slice(int(cu[s]), int(cu[s + 1]))
-        assert any(torch.equal(o[rows], fo[rows]) and torch.equal(kv[s], fkv[s])
-                   for fo, fkv in forced), f"sequence {s} matches neither kernel"
+        fo, fkv = forced[0] if pos < n_wide else forced[1]
+        assert torch.equal(o[rows], fo[rows]) and torch.equal(kv[s], fkv[s]), \
+            f"sequence {s} did not run on the kernel la_prefill_kernel_plan names"
     o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0)
     s1 = parity.check(to_np(o), o_ref, 1, 1e-2, what=f"case {case} o")
     s2 = parity.check(to_np(kv), kv_ref, 1, 1e-2, what=f"case {case} kv")

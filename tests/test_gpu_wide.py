@@ -324,6 +324,8 @@ def test_split_launch(dev, monkeypatch, lengths, wide_seqs):
     o_wide, kv_wide = run("1")
     o_slices, kv_slices = run("4")
     monkeypatch.delenv("LA_NDV")
+    n_wide, order = la.kernel_plan(cu, H, D)
+    assert n_wide == len(wide_seqs) and sorted(order[:n_wide].tolist()) == wide_seqs
     for s in range(S):
         rows = slice(int(cu[s]), int(cu[s + 1]))
         ref_o, ref_kv = (o_wide, kv_wide) if s in wide_seqs else (o_slices, kv_slices)
