@@ -37,7 +37,9 @@ One JSON line is printed with the contract fields plus:
                 the 32-column kernel on the fifth sequence) and for a packed
                 varlen batch (that kernel as well): back-to-back
                 launches over input sets that together exceed 1 GiB;
-                sweep_flatness gives max/min tokens/s over 1K ... 1M.
+                sweep_flatness gives max/min tokens/s over 1K ... 1M; each entry's
+                wide_seqs (la_prefill_kernel_plan) counts the sequences run one
+                workgroup per chain, the rest in 32-column slices.
 """
 
 import argparse
@@ -597,11 +599,13 @@ def bench_sweep(dev, reps=20, names=SWEEP, footprint=1 << 30):
         t = e0.elapsed_time(e1) / n / 1e3
         ts = sorted(launch_times(run, n, s, flush=lambda: scratch.zero_()))
         by = prefill_bytes(T, S)
+        wide_seqs = la.kernel_plan(cu, H, D)[0]  # sequences on the one-workgroup-per-chain kernel
         res[name] = {"tokens": T, "seqs": S, "us": round(t * 1e6, 1),
                      "us_single": round(ts[len(ts) // 2] * 1e6, 1), "input_sets": n_sets,
                      "tokens_per_s": round(T / t, 0), "GB_per_s": round(by / t / 1e9, 1),
                      "frac_of_8TBs": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
-                     "tflops_beta64": round(prefill_flops(T) / t / 1e12, 1)}
+                     "tflops_beta64": round(prefill_flops(T) / t / 1e12, 1),
+                     "wide_seqs": int(wide_seqs)}
         del sets, o, kvf
         torch.cuda.empty_cache()
     return res
