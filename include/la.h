@@ -498,13 +498,16 @@ typedef struct la_norm {
  * Arguments as la_prefill, plus norm, workspace and workspace_bytes.
  * in_dtype must be LA_BF16 and head_dim 128 (else LA_ERR_UNSUPPORTED).
  * With more (sequence, head) pairs than half the compute units of the
- * current device, one workgroup per pair runs the chain (as la_prefill) and
- * the workspace is unused (may be NULL).  With fewer, the sequences are cut
- * into segments (as la_prefill_segmented's chained scan, with a segment
- * length the library chooses so that segments x heads reaches the compute
- * units), which needs a workspace of la_prefill_normed_workspace_size
- * bytes (16-byte aligned, overlapping no other buffer; contents ignored and
- * left undefined).  o must not overlap the weight or the gate.  Errors as
+ * current device, one workgroup per pair runs the chain (as la_prefill).
+ * With fewer, the sequences are cut into segments (as la_prefill_segmented's
+ * chained scan, with a segment length the library chooses so that segments
+ * x heads reaches the compute units).  When the pairs past whole waves of
+ * the first kind fill at most half the compute units and their sequences
+ * are consecutive, those sequences may run through the chained scan after
+ * the wave (as la_prefill's split, decided by a model of both plans).  The
+ * scan needs a workspace of la_prefill_normed_workspace_size bytes (16-byte
+ * aligned, overlapping no other buffer; contents ignored and left
+ * undefined); when that size is 0 the workspace is unused (may be NULL).  o must not overlap the weight or the gate.  Errors as
  * la_prefill, plus LA_ERR_INVALID_ARG for a NULL norm or weight, a bad eps,
  * a misaligned or overlapping weight or gate, or a missing or short
  * workspace.  Nothing synchronises.

@@ -195,6 +195,43 @@ constexpr double kLaunchUs = 8.0;
 // than kPlanSeqs sequences, or whose remainder is larger, run on the wide
 // kernel alone.
 constexpr int32_t kPlanSeqs = 128;
+
+// Blocks of the i-th sequence in dispatch order.
+double seq_blocks(const la::PrefillArgs& a, const int32_t* cu_host, int32_t i) {
+  const int32_t s = a.ordered ? a.seq_order[i] : i;
+  return (double)((cu_host[s + 1] - cu_host[s] + 63) / 64);
+}
+
+// Time (us) of a launch of `per` workgroups for each sequence at dispatch
+// positions [from, to) on `cus` compute units, each lasting its sequence's
+// blocks x block_us, the GPU handing every workgroup in turn to the compute
+// unit that frees first.  The units are kept as groups (time they free, how
+// many), in order of time: the workgroups of one sequence take the earliest
+// groups.
+double launch_us(const la::PrefillArgs& a, const int32_t* cu_host, int cus, int32_t from,
+                 int32_t to, int64_t per, double block_us) {
+  std::vector<std::pair<double, int64_t>> groups(1, {0.0, (int64_t)cus});
+  double last = 0.0;
+  for (int32_t i = from; i < to; ++i) {
+    const double d = seq_blocks(a, cu_host, i) * block_us;
+    int64_t left = per;
+    while (left > 0) {
+      const double t = groups.front().first;
+      const int64_t take = std::min(left, groups.front().second);
+      if ((groups.front().second -= take) == 0) groups.erase(groups.begin());
+      left -= take;
+      last = std::max(last, t + d);
+      auto at = std::lower_bound(groups.begin(), groups.end(), t + d,
+                                 [](const std::pair<double, int64_t>& g, double x) {
+                                   return g.first < x;
+                                 });
+      if (at != groups.end() && at->first == t + d) at->second += take;
+      else groups.insert(at, {t + d, take});
+    }
+  }
+  return last;
+}
+
 int32_t wide_sequences(const la::PrefillArgs& a, const int32_t* cu_host, int cus) {
   const int32_t S = a.num_seqs, H = a.num_heads;
   const int64_t chains = (int64_t)S * H;
@@ -202,41 +239,9 @@ int32_t wide_sequences(const la::PrefillArgs& a, const int32_t* cu_host, int cus
   const int32_t seqs = (int32_t)(chains / cus * cus / H);  // whole sequences in whole waves
   const int64_t rest = chains - (int64_t)seqs * H;
   if (seqs == 0 || rest == 0 || 2 * rest > cus) return S;
-  auto blocks = [&](int32_t i) {  // blocks of the i-th sequence in dispatch order
-    const int32_t s = a.ordered ? a.seq_order[i] : i;
-    return (double)((cu_host[s + 1] - cu_host[s] + 63) / 64);
-  };
-  // Time of a launch of `per` workgroups for each sequence at dispatch
-  // positions [from, to), each lasting its sequence's blocks x block_us, the
-  // GPU handing every workgroup in turn to the compute unit that frees
-  // first.  The units are kept as groups (time they free, how many), in
-  // order of time: the workgroups of one sequence take the earliest groups.
-  std::vector<std::pair<double, int64_t>> groups;
-  auto launch_us = [&](int32_t from, int32_t to, int64_t per, double block_us) {
-    groups.assign(1, {0.0, (int64_t)cus});
-    double last = 0.0;
-    for (int32_t i = from; i < to; ++i) {
-      const double d = blocks(i) * block_us;
-      int64_t left = per;
-      while (left > 0) {
-        const double t = groups.front().first;
-        const int64_t take = std::min(left, groups.front().second);
-        if ((groups.front().second -= take) == 0) groups.erase(groups.begin());
-        left -= take;
-        last = std::max(last, t + d);
-        auto at = std::lower_bound(groups.begin(), groups.end(), t + d,
-                                   [](const std::pair<double, int64_t>& g, double x) {
-                                     return g.first < x;
-                                   });
-        if (at != groups.end() && at->first == t + d) at->second += take;
-        else groups.insert(at, {t + d, take});
-      }
-    }
-    return last;
-  };
-  const double split = launch_us(0, seqs, H, kWideBlockUs) + kLaunchUs +
-                       launch_us(seqs, S, 128 / la::kBf16Cols * H, kSliceBlockUs);
-  return split < launch_us(0, S, H, kWideBlockUs) ? seqs : S;
+  const double split = launch_us(a, cu_host, cus, 0, seqs, H, kWideBlockUs) + kLaunchUs +
+                       launch_us(a, cu_host, cus, seqs, S, 128 / la::kBf16Cols * H, kSliceBlockUs);
+  return split < launch_us(a, cu_host, cus, 0, S, H, kWideBlockUs) ? seqs : S;
 }
 
 // The kernels of a bf16 la_prefill or la_prefill_pool call, as the number of
@@ -916,6 +921,55 @@ bool normed_wide(int32_t num_seqs, int32_t num_heads) {
   return 2 * (int64_t)num_seqs * num_heads > cus;
 }
 
+// How la_prefill_normed runs a call with one workgroup per pair: the first
+// wide_seqs sequences of the dispatch order on that kernel, and the others,
+// sequences [tail_lo, tail_lo + tail_n) of the index order, through the
+// chained scan in segments of tail_seg tokens (tail_n = 0: no second part).
+// As for la_prefill, the pairs beyond whole waves of the wide kernel would
+// take an extra wave a whole chain long; when they fill at most half the
+// compute units and their sequences are consecutive in the index order (so
+// that the scan takes cu_seqlens from an offset), a model of the two plans
+// decides: the wide kernel's waves as in wide_sequences, the scan as its
+// waves of items (a local-state pass of 0.44 and an output pass of one
+// block-time per block) plus one ~3 us hop per segment boundary.
+struct NormedPlan {
+  int32_t wide_seqs, tail_lo, tail_n, tail_seg;
+};
+constexpr double kScanHopUs = 3.0;
+
+NormedPlan normed_plan(const la::PrefillArgs& a, const int32_t* cu_host) {
+  const int32_t S = a.num_seqs, H = a.num_heads;
+  NormedPlan p{S, 0, 0, 0};
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t chains = (int64_t)S * H;
+  if (chains > 16 * (int64_t)cus || S > kPlanSeqs) return p;
+  const int32_t seqs = (int32_t)(chains / cus * cus / H);
+  const int64_t rest = chains - (int64_t)seqs * H;
+  if (seqs == 0 || rest == 0 || 2 * rest > cus) return p;
+  int32_t lo = S, hi = -1;
+  int64_t tail_tokens = 0;
+  for (int32_t i = seqs; i < S; ++i) {
+    const int32_t s = a.ordered ? a.seq_order[i] : i;
+    lo = std::min(lo, s);
+    hi = std::max(hi, s);
+    tail_tokens += cu_host[s + 1] - cu_host[s];
+  }
+  if (hi - lo + 1 != S - seqs) return p;  // not consecutive
+  const int32_t seg = normed_segment_len(tail_tokens, H);
+  int64_t items = 0, most = 1;
+  for (int32_t s = lo; s <= hi; ++s) {
+    const int64_t len = cu_host[s + 1] - cu_host[s];
+    const int64_t n = len <= 0 ? 1 : (len + seg - 1) / seg;
+    items += n * H;
+    most = std::max(most, n);
+  }
+  const double scan = (double)((items + cus - 1) / cus) * ((seg + 63) / 64) * kWideBlockUs * 1.44 +
+                      kScanHopUs * (double)(most - 1);
+  const double split = launch_us(a, cu_host, cus, 0, seqs, H, kWideBlockUs) + kLaunchUs + scan;
+  if (split < launch_us(a, cu_host, cus, 0, S, H, kWideBlockUs)) p = {seqs, lo, S - seqs, seg};
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -931,8 +985,23 @@ la_status la_prefill_normed_workspace_size(int32_t num_seqs, const int32_t* cu_s
     return fail(LA_ERR_UNSUPPORTED, "the normed prefill takes head_dim 128 only");
   if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
   if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
-  if (num_seqs == 0 || normed_wide(num_seqs, num_heads)) return ok();
+  if (num_seqs == 0) return ok();
   SegmentLayout lay;
+  if (normed_wide(num_seqs, num_heads)) {
+    // the scan over the sequences past whole waves, if the plan has one
+    la::PrefillArgs a;
+    memset(&a, 0, sizeof(a));
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    set_order(a, cu_seqlens_host, num_seqs);
+    const NormedPlan p = normed_plan(a, cu_seqlens_host);
+    if (p.tail_n == 0) return ok();
+    if ((st = segment_layout(cu_seqlens_host + p.tail_lo, p.tail_n, num_heads, head_dim,
+                             p.tail_seg, true, &lay)) != LA_OK)
+      return st;
+    *bytes = lay.total;
+    return ok();
+  }
   const int32_t seg = normed_segment_len(cu_seqlens_host[num_seqs], num_heads);
   if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, seg, true, &lay)) !=
       LA_OK)
@@ -968,38 +1037,40 @@ la_status la_prefill_normed(const void* q, const void* k, const void* v,
   }
   if (num_seqs == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (normed_wide(num_seqs, num_heads)) {
-    la::PrefillArgs a;
-    memset(&a, 0, sizeof(a));
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.cu_seqlens = cu_seqlens_dev;
-    a.kv_init = kv_init;
-    a.o = o;
-    a.kv_final = kv_final;
-    a.num_seqs = num_seqs;
-    a.num_heads = num_heads;
-    a.num_items = num_seqs * num_heads;
-    for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
-    set_order(a, cu_seqlens_host, num_seqs);
-    a.norm_weight = norm->weight;
-    a.gate = norm->gate;
-    a.norm_eps = norm->eps;
-    return hip_status(la::launch_prefill_wide_normed(a, out_dtype, s), "la_prefill_normed launch");
-  }
-  // fewer pairs than compute units: the chained scan over segments
-  const int32_t seg = normed_segment_len(total_tokens, num_heads);
+  la::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_seqlens = cu_seqlens_dev;
+  a.kv_init = kv_init;
+  a.o = o;
+  a.kv_final = kv_final;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  for (int32_t h = 0; h < num_heads; ++h) a.log2_decay[h] = (float)log2((double)decay[h]);
+  set_order(a, cu_seqlens_host, num_seqs);
+  a.norm_weight = norm->weight;
+  a.gate = norm->gate;
+  a.norm_eps = norm->eps;
+  // One workgroup per pair with more pairs than half the compute units (the
+  // sequences past whole waves possibly through the scan, normed_plan),
+  // else the chained scan over segments for every sequence.
+  const bool wide = normed_wide(num_seqs, num_heads);
+  const NormedPlan plan = wide ? normed_plan(a, cu_seqlens_host) : NormedPlan{0, 0, num_seqs, 0};
+  const int32_t scan_lo = plan.tail_lo, scan_n = plan.tail_n;
+  const int32_t seg = wide ? plan.tail_seg : normed_segment_len(total_tokens, num_heads);
   SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, seg, true, &lay)) !=
-      LA_OK)
-    return st;
-  if (!workspace) return fail(LA_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", lay.total);
-  if (!aligned16(workspace)) return fail(LA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  if (workspace_bytes < lay.total)
-    return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes,
-                lay.total);
-  {
+  if (scan_n > 0) {
+    if ((st = segment_layout(cu_seqlens_host + scan_lo, scan_n, num_heads, head_dim, seg, true,
+                             &lay)) != LA_OK)
+      return st;
+    if (!workspace)
+      return fail(LA_ERR_INVALID_ARG, "workspace is NULL (%zu bytes needed)", lay.total);
+    if (!aligned16(workspace)) return fail(LA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < lay.total)
+      return fail(LA_ERR_INVALID_ARG, "workspace_bytes = %zu < %zu required", workspace_bytes,
+                  lay.total);
     const size_t tok = (size_t)total_tokens * num_heads * head_dim;
     const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
     const Range rw = range("workspace", workspace, lay.total);
@@ -1012,11 +1083,18 @@ la_status la_prefill_normed(const void* q, const void* k, const void* v,
     for (const Range& r : others)
       if (overlap(rw, r)) return fail(LA_ERR_INVALID_ARG, "workspace overlaps %s", r.name);
   }
-  float l2[LA_MAX_HEADS];
-  for (int32_t h = 0; h < num_heads; ++h) l2[h] = (float)log2((double)decay[h]);
-  return segmented_chain(q, k, v, cu_seqlens_dev, num_seqs, num_heads, head_dim, out_dtype, l2,
-                         kv_init, o, kv_final, lay, static_cast<char*>(workspace), false, s,
-                         false, norm);
+  if (wide) {
+    a.num_items = plan.wide_seqs * num_heads;
+    const hipError_t e = la::launch_prefill_wide_normed(a, out_dtype, s);
+    if (e != hipSuccess || scan_n == 0) return hip_status(e, "la_prefill_normed launch");
+  }
+  // sequences [scan_lo, scan_lo + scan_n) of the index order: their states
+  // from that offset of kv_init / kv_final, their rows where they are
+  const int64_t state_off = (int64_t)scan_lo * num_heads * head_dim * head_dim;
+  return segmented_chain(q, k, v, cu_seqlens_dev + scan_lo, scan_n, num_heads, head_dim,
+                         out_dtype, a.log2_decay, kv_init ? kv_init + state_off : nullptr, o,
+                         kv_final ? kv_final + state_off : nullptr, lay,
+                         static_cast<char*>(workspace), false, s, false, norm);
 }
 
 la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads,

@@ -215,3 +215,60 @@ def test_gate_limits_bitwise(dev, name):
     torch.cuda.synchronize()
     assert torch.equal(yz, y0 * 0.5), "gate 0"
     assert torch.equal(y1, y0), "gate 64"
+
+
+@pytest.mark.parametrize("lengths,H,tail", [([640] * 5, 64, [4]),
+                                            ([600, 700, 640, 640, 640], 64, [0]),
+                                            ([3072] * 33, 8, [32])])
+def test_prefill_normed_split(dev, lengths, H, tail):
+    """Pairs past one whole wave of the one-workgroup-per-pair kernel (320 or
+    264 pairs on 256 compute units): the sequences of the wave run on that
+    kernel, the remaining ones (consecutive in the index order) through the
+    chained scan.  Every sequence's output and final state equal, bit for
+    bit, those of a call on its own part alone (the wave's sequences: one
+    workgroup per pair; the rest: the scan, with the same segments), and the
+    call matches the oracle on four heads."""
+    import torch
+    import linear_attention_la_amd as la
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip(f"the split planned here assumes 256 compute units, not {cus}")
+    d = 128
+    say(f"case normed split lengths={lengths[:6]} H={H} tail={tail}")
+    T, S = int(sum(lengths)), len(lengths)
+    cu = cu_seqlens(lengths)
+    q, k, v = host_qkv(T, H, d, 411, "bf16")
+    g = host_qkv(T, H, d, 412, "bf16")[0] * 20.0
+    kv0 = random_states(S, H, d, 413, scale=0.1)
+    w = _weights(H, d, 414)
+    decay = np.exp(-np.linspace(0.001, 0.1, H)).astype(np.float32)
+    qd, kd, vd, gd = (to_dev(x, torch.bfloat16, dev) for x in (q, k, v, g))
+    kv0d = to_dev(kv0, torch.float32, dev)
+    wd = to_dev(w, torch.float32, dev)
+    assert la.prefill_normed_workspace_size(cu, H, d) > 0, "no scan part planned"
+    y, kv = la.prefill_normed(qd, kd, vd, cu, decay, wd, 1e-5, gd, kv_init=kv0d,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+
+    def alone(seqs):
+        rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in seqs])
+        idx = torch.from_numpy(rows).to(dev)
+        part = [lengths[s] for s in seqs]
+        yp, kvp = la.prefill_normed(qd[idx].contiguous(), kd[idx].contiguous(),
+                                    vd[idx].contiguous(), cu_seqlens(part), decay, wd, 1e-5,
+                                    gd[idx].contiguous(), kv_init=kv0d[seqs].contiguous(),
+                                    out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return idx, yp, kvp
+
+    for seqs in ([s for s in range(S) if s not in tail], tail):
+        idx, yp, kvp = alone(seqs)
+        assert torch.equal(y[idx], yp), f"sequences {seqs[:4]}...: rows"
+        assert torch.equal(kv[seqs], kvp), f"sequences {seqs[:4]}...: final states"
+    heads = [0, 1, H // 2, H - 1]
+    o_ref, kv_ref = oracle.prefill_varlen(q[:, heads], k[:, heads], v[:, heads], cu,
+                                          decay[heads], kv_init=kv0[:, heads])
+    y_ref = oracle.norm_gate(o_ref, w[heads], 1e-5, to_np(gd)[:, heads])
+    parity.check(to_np(y)[:, heads], y_ref, 1, 1e-2, what="normed split y")
+    parity.check(to_np(kv)[:, heads], kv_ref, 1, 1e-2, what="normed split kv")
