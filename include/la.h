@@ -521,9 +521,11 @@ la_status la_prefill_normed(const void* q, const void* k, const void* v,
                             void* stream);
 
 /* Bytes of workspace la_prefill_normed needs for these sequences and heads
- * on the current device (0 when there are enough (sequence, head) pairs
- * for one workgroup each).  Host only apart from reading the device's
- * compute-unit count.  Errors as la_prefill_segmented_workspace_size. */
+ * on the current device: 0 when every (sequence, head) pair runs one
+ * workgroup each, else the chained scan's workspace for the sequences it
+ * takes.  The plan is the call's own, so the size is exact for it.  Host
+ * only apart from reading the device's compute-unit count.  Errors as
+ * la_prefill_segmented_workspace_size. */
 la_status la_prefill_normed_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
                                            int32_t num_heads, int32_t head_dim, size_t* bytes);
 
