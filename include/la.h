@@ -223,6 +223,11 @@ la_status la_prefill_kernel_plan(int32_t num_seqs, const int32_t* cu_seqlens_hos
  *   segment_len      tokens per segment, a positive multiple of 64; the last
  *                    segment of a sequence may be shorter.  A sequence of L
  *                    tokens gives max(1, ceil(L / segment_len)) segments.
+ *                    0: the library's choice, about one (segment, head) item
+ *                    per compute unit of the current device (256 without
+ *                    one): ceil(T x num_heads / CUs) rounded up to a
+ *                    multiple of 64 -- the length that first fills the
+ *                    compute units, which measured fastest.
  *   workspace        device scratch of at least the size that
  *                    la_prefill_segmented_workspace_size reports for the same
  *                    num_seqs, cu_seqlens_host, num_heads, head_dim and
@@ -304,8 +309,10 @@ la_status la_prefill_segmented_noalloc(const void* q, const void* k, const void*
 /*
  * la_prefill_segmented_workspace_size -- bytes of workspace that
  * la_prefill_segmented needs for these arguments (host only, no device
- * call).  *bytes is 0 on error.  Errors: LA_ERR_INVALID_ARG (NULL bytes or
- * cu_seqlens_host, bad cu_seqlens, num_seqs < 0, bad segment_len),
+ * call apart from reading the current device's compute-unit count when
+ * segment_len is 0).  *bytes is 0 on error.  Errors: LA_ERR_INVALID_ARG
+ * (NULL bytes or cu_seqlens_host, bad cu_seqlens, num_seqs < 0, bad
+ * segment_len),
  * LA_ERR_UNSUPPORTED (heads or head_dim as la_prefill, too many segments).
  */
 la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* cu_seqlens_host,
@@ -387,7 +394,8 @@ la_status la_prefill_backward_workspace_size(int32_t num_seqs, int32_t num_heads
  * fp32 sums.
  *
  * Arguments as la_prefill_backward, except:
- *   segment_len      tokens per segment, a positive multiple of 64.
+ *   segment_len      tokens per segment, a positive multiple of 64, or 0
+ *                    for the library's choice (as in la_prefill_segmented).
  *   workspace        device scratch of at least
  *                    la_prefill_backward_segmented_workspace_size bytes
  *                    (always needed), 16-byte aligned, overlapping no other

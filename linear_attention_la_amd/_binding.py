@@ -474,9 +474,10 @@ def prefill_segmented(q, k, v, cu_seqlens, decay, segment_len, kv_init=None, out
                       stream=None, final_state=True, out=None, kv_final=None,
                       cu_seqlens_host=None, workspace=None):
     """prefill() with every sequence cut into segments of ``segment_len``
-    tokens (a multiple of 64) processed as parallel chains.  ``workspace``: a
-    device tensor of at least prefill_segmented_workspace_size() bytes, or
-    None to allocate one.  Same returns as prefill()."""
+    tokens (a multiple of 64, or 0 for the library's choice) processed as
+    parallel chains.  ``workspace``: a device tensor of at least
+    prefill_segmented_workspace_size() bytes, or None to allocate one.  Same
+    returns as prefill()."""
     torch = _torch()
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
                          out, kv_final, cu_seqlens_host)
@@ -753,7 +754,8 @@ def prefill_backward_segmented(q, k, v, d_o, cu_seqlens, decay, segment_len, kv_
                                cu_seqlens_host=None, workspace=None, dq=None, dk=None, dv=None,
                                dkv_init=None):
     """prefill_backward() with every sequence cut into segments of
-    ``segment_len`` tokens (a multiple of 64) processed as parallel chains.
+    ``segment_len`` tokens (a multiple of 64, or 0 for the library's choice)
+    processed as parallel chains.
     ``workspace``: a device tensor of at least
     prefill_backward_segmented_workspace_size() bytes, or None to allocate
     one.  Same returns as prefill_backward()."""

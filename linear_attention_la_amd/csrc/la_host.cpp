@@ -322,11 +322,32 @@ int32_t batch_stride(int32_t batch) {
   return (int32_t)step;
 }
 
+// segment_len of the segmented entry points: a positive multiple of 64, or 0
+// for the library's choice (resolve_segment_len).
 la_status check_segment_len(int32_t segment_len) {
-  if (segment_len <= 0 || segment_len % 64 != 0)
-    return fail(LA_ERR_INVALID_ARG, "segment_len = %d is not a positive multiple of 64",
-                segment_len);
+  if (segment_len < 0 || segment_len % 64 != 0)
+    return fail(LA_ERR_INVALID_ARG,
+                "segment_len = %d is neither 0 nor a positive multiple of 64", segment_len);
   return LA_OK;
+}
+
+// A segment length for `total_tokens` tokens and `num_heads` heads: about
+// one (segment, head) item per compute unit of the current device (256, the
+// MI355X, without one), a multiple of 64 tokens -- the length that first
+// gives one chain per compute unit, which measured fastest for the forward
+// scan and the backward alike.
+int32_t auto_segment_len(int64_t total_tokens, int32_t num_heads) {
+  const int cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t per = (total_tokens * num_heads + cus - 1) / cus;
+  const int64_t len = ((per + 63) / 64) * 64;
+  return (int32_t)std::min<int64_t>(std::max<int64_t>(len, 64), (int64_t)1 << 30);
+}
+
+// The segment length a call uses: segment_len, or for 0 the library's
+// choice over all the call's tokens (cu_host validated).
+int32_t resolve_segment_len(int32_t segment_len, const int32_t* cu_host, int32_t num_seqs,
+                            int32_t num_heads) {
+  return segment_len > 0 ? segment_len : auto_segment_len(cu_host[num_seqs], num_heads);
 }
 
 // Byte offsets of the segmented-prefill workspace sections (each 256 B
@@ -641,7 +662,8 @@ la_status la_prefill_segmented_workspace_size(int32_t num_seqs, const int32_t* c
   if (!cu_seqlens_host) return fail(LA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
   if ((st = check_cu(cu_seqlens_host, num_seqs)) != LA_OK) return st;
   SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len,
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim,
+                           resolve_segment_len(segment_len, cu_seqlens_host, num_seqs, num_heads),
                            scan_path(head_dim), &lay)) != LA_OK)
     return st;
   *bytes = lay.total;
@@ -810,7 +832,8 @@ la_status segmented_args(const void* q, const void* k, const void* v,
     *done = true;
     return ok();
   }
-  return segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len,
+  return segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim,
+                        resolve_segment_len(segment_len, cu_seqlens_host, num_seqs, num_heads),
                         scan_path(head_dim), lay);
 }
 
@@ -901,17 +924,6 @@ la_status la_prefill_segmented_noalloc(const void* q, const void* k, const void*
 
 namespace {
 
-// la_prefill_normed with fewer (sequence, head) pairs than compute units cuts
-// the sequences into segments of this length: about one segment per compute
-// unit over all heads, at least one block.  Without a device to ask, the
-// compute units are taken as 256 (MI355X).
-int32_t normed_segment_len(int64_t total_tokens, int32_t num_heads) {
-  const int cus = device_cus() > 0 ? device_cus() : 256;
-  const int64_t per = (total_tokens * num_heads + cus - 1) / cus;
-  const int64_t len = ((per + 63) / 64) * 64;
-  return (int32_t)std::min<int64_t>(std::max<int64_t>(len, 64), (int64_t)1 << 30);
-}
-
 // Whether la_prefill_normed runs one workgroup per (sequence, head) pair
 // (else the chained scan over segments): with more pairs than half the
 // compute units, where the one wave of whole chains is faster than the
@@ -955,7 +967,7 @@ NormedPlan normed_plan(const la::PrefillArgs& a, const int32_t* cu_host) {
     tail_tokens += cu_host[s + 1] - cu_host[s];
   }
   if (hi - lo + 1 != S - seqs) return p;  // not consecutive
-  const int32_t seg = normed_segment_len(tail_tokens, H);
+  const int32_t seg = auto_segment_len(tail_tokens, H);
   int64_t items = 0, most = 1;
   for (int32_t s = lo; s <= hi; ++s) {
     const int64_t len = cu_host[s + 1] - cu_host[s];
@@ -1002,7 +1014,7 @@ la_status la_prefill_normed_workspace_size(int32_t num_seqs, const int32_t* cu_s
     *bytes = lay.total;
     return ok();
   }
-  const int32_t seg = normed_segment_len(cu_seqlens_host[num_seqs], num_heads);
+  const int32_t seg = auto_segment_len(cu_seqlens_host[num_seqs], num_heads);
   if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, seg, true, &lay)) !=
       LA_OK)
     return st;
@@ -1059,7 +1071,7 @@ la_status la_prefill_normed(const void* q, const void* k, const void* v,
   const bool wide = normed_wide(num_seqs, num_heads);
   const NormedPlan plan = wide ? normed_plan(a, cu_seqlens_host) : NormedPlan{0, 0, num_seqs, 0};
   const int32_t scan_lo = plan.tail_lo, scan_n = plan.tail_n;
-  const int32_t seg = wide ? plan.tail_seg : normed_segment_len(total_tokens, num_heads);
+  const int32_t seg = wide ? plan.tail_seg : auto_segment_len(total_tokens, num_heads);
   SegmentLayout lay;
   if (scan_n > 0) {
     if ((st = segment_layout(cu_seqlens_host + scan_lo, scan_n, num_heads, head_dim, seg, true,
@@ -1317,8 +1329,9 @@ la_status la_prefill_backward_segmented_workspace_size(int32_t num_seqs,
   // the four-kernel layout (the reverse-time chains need a state per segment
   // boundary), then one set of S initial states
   SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, false,
-                           &lay)) != LA_OK)
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim,
+                           resolve_segment_len(segment_len, cu_seqlens_host, num_seqs, num_heads),
+                           false, &lay)) != LA_OK)
     return st;
   *bytes = align256(lay.total) + (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
   return ok();
@@ -1337,8 +1350,9 @@ la_status la_prefill_backward_segmented(
     return st;
   if (num_seqs == 0) return ok();
   SegmentLayout lay;
-  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim, segment_len, false,
-                           &lay)) != LA_OK)
+  if ((st = segment_layout(cu_seqlens_host, num_seqs, num_heads, head_dim,
+                           resolve_segment_len(segment_len, cu_seqlens_host, num_seqs, num_heads),
+                           false, &lay)) != LA_OK)
     return st;
   const size_t sb = (size_t)num_seqs * num_heads * head_dim * head_dim * 4;
   const size_t init_off = align256(lay.total);

@@ -99,6 +99,10 @@ int main(void) {
            la_prefill_segmented_workspace_size(S, cub, 2, 64, 64, &bytes), LA_OK);
     expect("backward segmented workspace",
            la_prefill_backward_segmented_workspace_size(S, cub, 2, 128, 64, &bytes), LA_OK);
+    expect("segmented workspace, library's segment length",
+           la_prefill_segmented_workspace_size(S, cub, 2, 128, 0, &bytes), LA_OK);
+    expect("backward segmented workspace, library's segment length",
+           la_prefill_backward_segmented_workspace_size(S, cub, 2, 64, 0, &bytes), LA_OK);
     free(cub);
   }
 

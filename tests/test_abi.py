@@ -219,7 +219,22 @@ def test_segmented_workspace_size_layout():
     assert n == 2 * 512 + 2 * 256 + 33024 + 2 * 64 * 64 * 128 * 128 * 4
 
 
-@pytest.mark.parametrize("seg", [0, -64, 100, 63])
+def test_segmented_auto_segment_len():
+    """segment_len 0 lets the library pick about one (segment, head) item per
+    compute unit (256 without a device), in multiples of 64 tokens: 1M
+    tokens x 8 heads -> 32768, 8192 x 64 -> 2048, 100 x 4 -> 64."""
+    for cu, H, seg in (([0, 1 << 20], 8, 32768), ([0, 8192], 64, 2048), ([0, 100], 4, 64),
+                       ([0, 5000, 5000, 9000], 16, 576)):
+        for d in (64, 128):
+            assert _ws_size(cu, H=H, d=d, seg=0) == _ws_size(cu, H=H, d=d, seg=seg)
+            c = np.asarray(cu, np.int32)
+            assert la.la_prefill_backward_segmented_workspace_size(c.shape[0] - 1, c.ctypes.data,
+                                                                   H, d, 0) == \
+                la.la_prefill_backward_segmented_workspace_size(c.shape[0] - 1, c.ctypes.data,
+                                                                H, d, seg)
+
+
+@pytest.mark.parametrize("seg", [-64, 100, 63, -1])
 def test_segmented_workspace_size_rejects_segment_len(seg):
     st, n = _ws_size([0, 100], seg=seg)
     assert st == la.LA_ERR_INVALID_ARG and n == 0
@@ -251,7 +266,7 @@ def _seg(**kw):
 
 
 BAD_SEGMENTED = [
-    ("segment_len_zero", dict(seg=0), la.LA_ERR_INVALID_ARG),
+    ("segment_len_negative", dict(seg=-64), la.LA_ERR_INVALID_ARG),
     ("segment_len_not_multiple", dict(seg=96), la.LA_ERR_INVALID_ARG),
     ("fp32_input", dict(in_dt=la.LA_FP32, out_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
     ("workspace_null", dict(ws=None), la.LA_ERR_INVALID_ARG),
@@ -615,7 +630,7 @@ def test_backward_segmented_workspace_size():
 
 BAD_BACKWARD_SEGMENTED = [
     ("segment_len_not_multiple", dict(seg=96), la.LA_ERR_INVALID_ARG),
-    ("segment_len_zero", dict(seg=0), la.LA_ERR_INVALID_ARG),
+    ("segment_len_negative", dict(seg=-128), la.LA_ERR_INVALID_ARG),
     ("fp32_inputs", dict(in_dt=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
     ("tiny_decay_with_final_grad", dict(decay=np.array([0.9, 1e-30, 0.9, 0.9], np.float32)),
      la.LA_ERR_UNSUPPORTED),

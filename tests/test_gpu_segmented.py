@@ -155,3 +155,37 @@ def test_bench_config_one_million_tokens(dev):
         say("segmented 1M head", h, s1, s2)
     del qd, kd, vd, o, kv
     torch.cuda.empty_cache()
+
+
+def test_auto_segment_len_bitwise(dev):
+    """segment_len 0 lets the library choose about one (segment, head) item per
+    compute unit: the forward (the chained scan) and the segmented backward
+    then equal, bit for bit, the calls with that length given explicitly."""
+    import torch
+    import linear_attention_la_amd as la
+    from la_inputs import device_qkv, device_states
+
+    lengths, H = [5000, 0, 2304, 640], 8
+    cu_h = cu_seqlens(lengths)
+    T, S = int(cu_h[-1]), len(lengths)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    seg = max(64, -(-(-(-T * H // cus)) // 64) * 64)
+    say(f"case auto segment_len lengths={lengths} H={H} -> {seg}")
+    q, k, v = device_qkv(T, H, 128, 531, dev)
+    do = device_qkv(T, H, 128, 532, dev)[0]
+    kv0 = device_states(S, H, 128, 533, dev, scale=0.1)
+    g = device_states(S, H, 128, 534, dev, scale=0.1)
+    cu = torch.from_numpy(cu_h).to(dev)
+    decay = np.exp(-np.linspace(0.001, 0.1, H)).astype(np.float32)
+    assert la.prefill_segmented_workspace_size(cu_h, H, 128, 0) == \
+        la.prefill_segmented_workspace_size(cu_h, H, 128, seg)
+    o0, s0 = la.prefill_segmented(q, k, v, cu, decay, 0, kv_init=kv0, cu_seqlens_host=cu_h)
+    o1, s1 = la.prefill_segmented(q, k, v, cu, decay, seg, kv_init=kv0, cu_seqlens_host=cu_h)
+    b0 = la.prefill_backward_segmented(q, k, v, do, cu, decay, 0, kv_init=kv0, dkv_final=g,
+                                       cu_seqlens_host=cu_h)
+    b1 = la.prefill_backward_segmented(q, k, v, do, cu, decay, seg, kv_init=kv0, dkv_final=g,
+                                       cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(s0, s1), "forward"
+    for name, x0, x1 in zip(("dq", "dk", "dv", "dkv_init"), b0, b1):
+        assert torch.equal(x0, x1), name
