@@ -473,8 +473,9 @@ def bench_normed(dev, reps=10):
     """The output normalisation fused into the kernels that write O
     (la_prefill_normed, la_decode_normed; weight [H, d], eps 1e-6, a bf16
     gate) against the same result unfused: la_prefill / la_decode, then the
-    normalisation and gate as torch operations on the written output.  Two
-    prefill shapes: eight 8K sequences (one workgroup per chain) and the
+    normalisation and gate as torch operations on the written output.  Three
+    prefill shapes: eight 8K sequences (one workgroup per chain), five (one
+    wave of that kernel, then the chained scan for the fifth) and the
     headline B=1, N=8192 (fused: the chained scan; unfused: the 32-column
     kernel); and the 256 x 64 decode batch.  Algorithmic bytes of the fused
     prefill: the plain prefill's plus the gate read (2 B per element); the
@@ -495,7 +496,8 @@ def bench_normed(dev, reps=10):
         return y.to(o.dtype)
 
     res = {}
-    for name in ("batch8_n8k", "n8k"):
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    for name in ("batch8_n8k", "batch5_n8k", "n8k"):
         wl = workload(name)
         cu = cu_seqlens(wl["lengths"])
         T, S = int(cu[-1]), len(wl["lengths"])
@@ -521,8 +523,10 @@ def bench_normed(dev, reps=10):
         med = lambda fn: sorted(launch_times(fn, reps, s, flush=lambda: scratch.zero_()))[reps // 2]  # noqa
         tf, tu, tn, tp = med(fused), med(unfused), med(fused_ng), med(plain)
         by = prefill_bytes(T, S) + T * H * D * 2
-        res[name] = {"tokens": T, "seqs": S, "path": "one workgroup per chain" if need == 0
-                     else "chained scan", "fused_us": round(tf * 1e6, 1),
+        path = ("one workgroup per chain" if need == 0 else
+                "one workgroup per chain, then the chained scan" if 2 * S * H > cus else
+                "chained scan")
+        res[name] = {"tokens": T, "seqs": S, "path": path, "fused_us": round(tf * 1e6, 1),
                      "fused_no_gate_us": round(tn * 1e6, 1), "plain_prefill_us": round(tp * 1e6, 1),
                      "unfused_us": round(tu * 1e6, 1), "speedup": round(tu / tf, 3),
                      "fused_frac_of_8TBs": round(by / tf / 1e9 / HBM_PEAK_GBS, 4)}
