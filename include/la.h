@@ -32,10 +32,15 @@
  * Ownership.  The caller allocates and owns every buffer.  The library
  * allocates no device memory, keeps no pointer after a call returns and
  * holds no global state (apart from the static device scratch of
- * la_prefill_segmented_noalloc); calls on different streams with disjoint
- * outputs may run concurrently (la_prefill_segmented_noalloc excepted).  Work is enqueued on `stream` (a hipStream_t passed
- * as void*, NULL = the default stream) and is asynchronous: device buffers
- * must stay valid until the stream has passed the kernel.  Host arrays
+ * la_prefill_segmented_noalloc and per-device caches of the compute-unit
+ * count and that scratch's address); calls on different streams with
+ * disjoint outputs may run concurrently (la_prefill_segmented_noalloc
+ * excepted).  Results depend only on the arguments; which kernels run
+ * depends on them, on the device's compute-unit count and on the LA_NDV
+ * sweep override (see la_prefill).  Work is enqueued on `stream` (a
+ * hipStream_t passed as void*, NULL = the default stream) and is
+ * asynchronous: device buffers must stay valid until the stream has passed
+ * the kernel.  Host arrays
  * (decay, cu_seqlens_host) are read only during the call.  The device that
  * owns the buffers must be the calling thread's current HIP device.
  *
