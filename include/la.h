@@ -35,9 +35,10 @@
  * la_prefill_segmented_noalloc and per-device caches of the compute-unit
  * count and that scratch's address); calls on different streams with
  * disjoint outputs may run concurrently (la_prefill_segmented_noalloc
- * excepted).  Results depend only on the arguments; which kernels run
- * depends on them, on the device's compute-unit count and on the LA_NDV
- * sweep override (see la_prefill).  Work is enqueued on `stream` (a
+ * excepted).  Which kernels run -- and so the last bits of the results, all
+ * within the same tolerance -- depends on the arguments, the device's
+ * compute-unit count and the LA_NDV sweep override (see la_prefill); given
+ * those, every call is deterministic.  Work is enqueued on `stream` (a
  * hipStream_t passed as void*, NULL = the default stream) and is
  * asynchronous: device buffers must stay valid until the stream has passed
  * the kernel.  Host arrays
