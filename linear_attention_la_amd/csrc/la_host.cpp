@@ -6,6 +6,7 @@
 #include <math.h>
 #include <algorithm>
 #include <atomic>
+#include <new>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -413,6 +414,25 @@ la_status segment_layout(const int32_t* cu, int32_t num_seqs, int32_t num_heads,
   return LA_OK;
 }
 
+// Every slot in [0, pool_size) and used at most once (two sequences on one
+// state would race).  Duplicates are found on a sorted copy, so the host
+// memory the check takes follows the number of slots, not the pool size.
+la_status check_slots(const int32_t* slots, int32_t n, int32_t pool_size) {
+  for (int32_t i = 0; i < n; ++i)
+    if (slots[i] < 0 || slots[i] >= pool_size)
+      return fail(LA_ERR_INVALID_ARG, "slots[%d] = %d is outside [0, %d)", i, slots[i], pool_size);
+  std::vector<int32_t> sorted;
+  try {
+    sorted.assign(slots, slots + n);
+  } catch (const std::bad_alloc&) {
+    return fail(LA_ERR_UNSUPPORTED, "no host memory to check %d slots", n);
+  }
+  std::sort(sorted.begin(), sorted.end());
+  for (int32_t i = 1; i < n; ++i)
+    if (sorted[i] == sorted[i - 1]) return fail(LA_ERR_INVALID_ARG, "slot %d is used twice", sorted[i]);
+  return LA_OK;
+}
+
 // Decode with num_states states in kv; sequence b uses state slots[b] (or b
 // when slots is NULL).  The slot array has been validated by the caller.
 la_status decode_common(const void* q, const void* k, const void* v, float* kv,
@@ -584,15 +604,7 @@ la_status la_prefill_pool(const void* q, const void* k, const void* v,
   if (!aligned16(kv_pool)) return fail(LA_ERR_INVALID_ARG, "kv_pool is not 16-byte aligned");
   if (!slots_dev || !slots_host)
     return fail(LA_ERR_INVALID_ARG, "slots_dev and slots_host must be non-NULL");
-  // every slot in range and used once (two sequences on one state would race)
-  std::vector<uint8_t> used((size_t)pool_size, 0);
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t x = slots_host[s];
-    if (x < 0 || x >= pool_size)
-      return fail(LA_ERR_INVALID_ARG, "slots[%d] = %d is outside [0, %d)", s, x, pool_size);
-    if (used[(size_t)x]) return fail(LA_ERR_INVALID_ARG, "slot %d is used twice", x);
-    used[(size_t)x] = 1;
-  }
+  if ((st = check_slots(slots_host, num_seqs, pool_size)) != LA_OK) return st;
   const size_t tok = (size_t)total_tokens * num_heads * head_dim;
   const Range rp = range("kv_pool", kv_pool, (size_t)pool_size * num_heads * head_dim * head_dim * 4);
   const Range others[] = {range("q", q, tok * 2), range("k", k, tok * 2), range("v", v, tok * 2),
@@ -1468,15 +1480,8 @@ la_status la_decode_pool(const void* q, const void* k, const void* v, float* kv_
   if (batch > 0) {
     if (!slots_dev || !slots_host)
       return fail(LA_ERR_INVALID_ARG, "slots_dev and slots_host must be non-NULL");
-    // every slot in range and used once (two sequences on one state would race)
-    std::vector<uint8_t> used((size_t)pool_size, 0);
-    for (int32_t b = 0; b < batch; ++b) {
-      const int32_t x = slots_host[b];
-      if (x < 0 || x >= pool_size)
-        return fail(LA_ERR_INVALID_ARG, "slots[%d] = %d is outside [0, %d)", b, x, pool_size);
-      if (used[(size_t)x]) return fail(LA_ERR_INVALID_ARG, "slot %d is used twice", x);
-      used[(size_t)x] = 1;
-    }
+    const la_status st = check_slots(slots_host, batch, pool_size);
+    if (st != LA_OK) return st;
   }
   return decode_common(q, k, v, kv_pool, pool_size, slots_dev, slots_host, decay, batch,
                        num_heads, head_dim, in_dtype, o, stream);

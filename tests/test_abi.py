@@ -458,6 +458,18 @@ def test_decode_pool_rejects(name, kw, code):
     assert msg
 
 
+def test_pool_slot_checks_scale_with_the_slots():
+    # A repeated slot in a pool of 2^31 - 1 states is found by sorting the
+    # slots, not by a table of the pool's size (that would take 2 GiB).
+    big = 2**31 - 1
+    st, msg = _pool(P=big, slots=np.array([5, big - 1, 5], np.int32))
+    assert st == la.LA_ERR_INVALID_ARG and "slot 5 is used twice" in msg, msg
+    st, msg = _prefill_pool(P=big, slots=np.array([big - 1, big - 1], np.int32))
+    assert st == la.LA_ERR_INVALID_ARG and "used twice" in msg, msg
+    st, msg = _pool(slots=np.array([3, 9, 10], np.int32))
+    assert st == la.LA_ERR_INVALID_ARG and "slots[2] = 10" in msg, msg
+
+
 def test_decode_pool_zero_batch_is_noop():
     st, msg = _pool(B=0, slots=None, slots_dev=None, q=None, k=None, v=None, o=None)
     assert st == la.LA_OK, msg
