@@ -9,6 +9,7 @@ Two layers:
   current (or given) stream handle.
 """
 
+import contextlib
 import ctypes
 import os
 
@@ -272,6 +273,20 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _on(device):
+    """Context in which ``device`` is the calling thread's current HIP device:
+    the library takes the device that owns a call's buffers to be the current
+    one (its compute units, its static scratch), so every wrapper calls it
+    inside this.  Switches only when another device is current."""
+    torch = _torch()
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _SAME_DEVICE
+    return torch.cuda.device(device)
+
+
 _hip = None
 
 
@@ -443,7 +458,8 @@ def prefill(q, k, v, cu_seqlens, decay, kv_init=None, out_dtype=None, stream=Non
     synchronise the stream on every call."""
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
                          out, kv_final, cu_seqlens_host)
-    _check(la_prefill(*m.args, m.stream))
+    with _on(m.dev):
+        _check(la_prefill(*m.args, m.stream))
     return m.out, m.kv_final
 
 
@@ -481,17 +497,19 @@ def prefill_segmented(q, k, v, cu_seqlens, decay, segment_len, kv_init=None, out
     torch = _torch()
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
                          out, kv_final, cu_seqlens_host)
-    st, need = la_prefill_segmented_workspace_size(m.S, m.cu_host.data_ptr(), m.H, m.d,
-                                                   segment_len)
-    _check(st)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
-        if stream is not None:
-            workspace.record_stream(stream)
-    else:
-        _check_device_buffer("workspace", workspace, m.dev)
-    nbytes = workspace.numel() * workspace.element_size()
-    _check(la_prefill_segmented(*m.args, segment_len, workspace.data_ptr(), nbytes, m.stream))
+    with _on(m.dev):
+        st, need = la_prefill_segmented_workspace_size(m.S, m.cu_host.data_ptr(), m.H, m.d,
+                                                       segment_len)
+        _check(st)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=m.dev)
+            if stream is not None:
+                workspace.record_stream(stream)
+        else:
+            _check_device_buffer("workspace", workspace, m.dev)
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(la_prefill_segmented(*m.args, segment_len, workspace.data_ptr(), nbytes,
+                                    m.stream))
     return m.out, m.kv_final
 
 
@@ -505,7 +523,8 @@ def prefill_segmented_noalloc(q, k, v, cu_seqlens, decay, segment_len, kv_init=N
     Same returns as prefill()."""
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
                          out, kv_final, cu_seqlens_host)
-    _check(la_prefill_segmented_noalloc(*m.args, segment_len, m.stream))
+    with _on(m.dev):
+        _check(la_prefill_segmented_noalloc(*m.args, segment_len, m.stream))
     return m.out, m.kv_final
 
 
@@ -540,25 +559,26 @@ def prefill_normed(q, k, v, cu_seqlens, decay, weight, eps=1e-6, gate=None, kv_i
     m = _marshal_prefill(q, k, v, cu_seqlens, decay, kv_init, out_dtype, stream, final_state,
                          out, kv_final, cu_seqlens_host)
     nm, keep = _marshal_norm(weight, eps, gate, m.H, m.d, m.dev, q)
-    st, need = la_prefill_normed_workspace_size(m.S, m.cu_host.data_ptr(), m.H, m.d)
-    _check(st)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=m.dev)
-        if stream is not None:
-            workspace.record_stream(stream)
-    elif workspace is not None:
-        _check_device_buffer("workspace", workspace, m.dev)
-    wp = 0 if workspace is None else workspace.data_ptr()
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    a = m.args
-    _check(la_prefill_normed(*a[:13], nm, a[13], a[14], wp or None, nbytes, m.stream))
+    with _on(m.dev):
+        st, need = la_prefill_normed_workspace_size(m.S, m.cu_host.data_ptr(), m.H, m.d)
+        _check(st)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=m.dev)
+            if stream is not None:
+                workspace.record_stream(stream)
+        elif workspace is not None:
+            _check_device_buffer("workspace", workspace, m.dev)
+        wp = 0 if workspace is None else workspace.data_ptr()
+        nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        a = m.args
+        _check(la_prefill_normed(*a[:13], nm, a[13], a[14], wp or None, nbytes, m.stream))
     del keep
     return m.out, m.kv_final
 
 
 def prefill_normed_workspace_size(cu_seqlens_host, num_heads, head_dim):
     """Bytes of device workspace prefill_normed needs on the current device."""
-    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens_host, dtype=np.int32).reshape(-1))
     st, n = la_prefill_normed_workspace_size(cu.shape[0] - 1, cu.ctypes.data, num_heads,
                                              head_dim)
     _check(st)
@@ -608,10 +628,12 @@ def prefill_pool(q, k, v, cu_seqlens, decay, kv_pool, slots, out_dtype=None, str
             or kv_pool.dim() != 4 or tuple(kv_pool.shape[1:]) != (m.H, m.d, m.d)):
         raise ValueError("kv_pool must be a contiguous fp32 device tensor [P, H, d, d]")
     sl_dev, sl_host = _marshal_slots(slots, slots_host, m.S, m.dev, stream)
-    _check(la_prefill_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.cu_dev.data_ptr(),
-                           m.cu_host.data_ptr(), m.S, m.T, m.H, m.d, m.in_code, m.out_code,
-                           m.dec.ctypes.data, kv_pool.data_ptr(), kv_pool.shape[0],
-                           sl_dev.data_ptr(), sl_host.ctypes.data, m.out.data_ptr(), m.stream))
+    with _on(m.dev):
+        _check(la_prefill_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), m.cu_dev.data_ptr(),
+                               m.cu_host.data_ptr(), m.S, m.T, m.H, m.d, m.in_code, m.out_code,
+                               m.dec.ctypes.data, kv_pool.data_ptr(), kv_pool.shape[0],
+                               sl_dev.data_ptr(), sl_host.ctypes.data, m.out.data_ptr(),
+                               m.stream))
     return m.out
 
 
@@ -630,9 +652,10 @@ def decode(q, k, v, kv, decay, stream=None, out=None):
     _check_out("kv", kv, (B, H, d, d), torch.float32, q.device)
     dec = _host_decay(decay, H)
     out = torch.empty_like(q) if out is None else _check_out("out", out, q.shape, q.dtype, q.device)
-    st = la_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(), dec.ctypes.data,
-                   B, H, d, _dtype_code(q), out.data_ptr(), _stream_handle(stream, q.device))
-    _check(st)
+    with _on(q.device):
+        _check(la_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(),
+                         dec.ctypes.data, B, H, d, _dtype_code(q), out.data_ptr(),
+                         _stream_handle(stream, q.device)))
     return out
 
 
@@ -653,10 +676,10 @@ def decode_normed(q, k, v, kv, decay, weight, eps=1e-6, gate=None, stream=None, 
     dec = _host_decay(decay, H)
     nm, keep = _marshal_norm(weight, eps, gate, H, d, q.device, q)
     out = torch.empty_like(q) if out is None else _check_out("out", out, q.shape, q.dtype, q.device)
-    st = la_decode_normed(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(),
-                          dec.ctypes.data, B, H, d, _dtype_code(q), nm, out.data_ptr(),
-                          _stream_handle(stream, q.device))
-    _check(st)
+    with _on(q.device):
+        _check(la_decode_normed(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv.data_ptr(),
+                                dec.ctypes.data, B, H, d, _dtype_code(q), nm, out.data_ptr(),
+                                _stream_handle(stream, q.device)))
     del keep
     return out
 
@@ -686,10 +709,10 @@ def decode_pool(q, k, v, kv_pool, slots, decay, stream=None, out=None, slots_hos
     sl_dev, sl_host = _marshal_slots(slots, slots_host, B, dev, stream)
     dec = _host_decay(decay, H)
     out = torch.empty_like(q) if out is None else _check_out("out", out, q.shape, q.dtype, dev)
-    st = la_decode_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_pool.data_ptr(), P,
-                        sl_dev.data_ptr(), sl_host.ctypes.data, dec.ctypes.data, B, H, d,
-                        _dtype_code(q), out.data_ptr(), _stream_handle(stream, dev))
-    _check(st)
+    with _on(dev):
+        _check(la_decode_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_pool.data_ptr(), P,
+                              sl_dev.data_ptr(), sl_host.ctypes.data, dec.ctypes.data, B, H, d,
+                              _dtype_code(q), out.data_ptr(), _stream_handle(stream, dev)))
     return out
 
 
@@ -712,6 +735,14 @@ def _backward(q, k, v, d_o, cu_seqlens, decay, kv_init, dkv_final, grad_dtype, s
         dkv_init = torch.empty((m.S, m.H, m.d, m.d), dtype=torch.float32, device=m.dev)
     else:
         _check_out("dkv_init", dkv_init, (m.S, m.H, m.d, m.d), torch.float32, m.dev)
+    with _on(m.dev):
+        return _backward_call(m, d_o, kv_init, dkv_final, stream, workspace, dk, dv, dkv_init,
+                              segment_len)
+
+
+def _backward_call(m, d_o, kv_init, dkv_final, stream, workspace, dk, dv, dkv_init,
+                   segment_len):
+    torch = _torch()
     if segment_len is None:
         st, need = la_prefill_backward_workspace_size(m.S, m.H, m.d)
         needed = kv_init is not None or dkv_final is not None
