@@ -28,9 +28,11 @@ One JSON line is printed with the contract fields plus:
   decode        la_decode alone on 256 sequences x 64 heads: GB/s vs 8 TB/s.
   mixed         decode on one stream concurrent with a packed prefill of 8
                 sequences (lengths U[1K, 32K]) on another.
-  peaks         measured on the GPU: a 1 GiB read+write stream (HBM) and an 8192^3
-                bf16 matmul; roofline.frac_of_measured_stream relates the
-                prefill kernel to that stream.
+  peaks         measured on the GPU: a 1 GiB read+write stream (HBM), an 8192^3
+                bf16 matmul, and an MFMA-only loop on random and on zero
+                operands with the shader clock it ran at;
+                roofline.frac_of_measured_stream relates the prefill kernel
+                to that stream.
   sweep         tokens/s at N = 1K ... 1M, for three, five and eight 8K
                 sequences in one call (192, 320 and 512 chains: the
                 one-workgroup-per-chain kernel, for 320 chains followed by
@@ -169,12 +171,63 @@ def settle(fn, seconds=None):
     return i
 
 
+PEAK_LIB = os.path.join(ROOT, "linear_attention_la_amd", "_lib", "libla_peak.so")
+
+
+def mfma_loop_peak(dev, iters=10000, reps=10):
+    """bf16 MFMA rate of an MFMA-only loop (libla_peak.so: no memory traffic,
+    8 independent accumulators a wave, 16 waves on every compute unit), on
+    N(0,1) operands and on zero operands: TFLOP/s (region time of `reps`
+    launches after a settle) and the shader clock the waves ran at (their
+    shader-clock count over the 100 MHz constant clock, median over
+    waves).  The operands decide how much the matrix cores switch, hence
+    the power the loop draws and the clock the board's power limit allows.
+    None if the library was not built."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(PEAK_LIB):
+        return None
+    L = ctypes.CDLL(PEAK_LIB)
+    L.la_peak_mfma_bf16.restype = ctypes.c_int
+    L.la_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    threads, waves = cus * 1024, cus * 16
+    s = torch.cuda.current_stream()
+    sums = torch.empty(threads, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * waves, dtype=torch.int64, device=dev)
+    flops = waves * iters * 8 * 16 * 16 * 32 * 2
+    res = {}
+    for name in ("random", "zeros"):
+        g = torch.Generator(device=dev).manual_seed(7)
+        ops = (torch.randn(threads * 128, generator=g, device=dev) if name == "random"
+               else torch.zeros(threads * 128, device=dev)).to(torch.bfloat16)
+
+        def run(i):
+            st = L.la_peak_mfma_bf16(ops.data_ptr(), sums.data_ptr(), clocks.data_ptr(), cus,
+                                     iters, ctypes.c_void_p(s.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"la_peak_mfma_bf16: HIP error {st}")
+        settle(run)
+        t = region_time(run, reps, s)
+        c = clocks.view(waves, 2).cpu().numpy()
+        ghz = float(np.median(c[:, 0] / np.maximum(c[:, 1], 1))) * 0.1
+        res[name] = {"TFLOP_per_s": round(flops / t / 1e12, 1),
+                     "frac_of_2500": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4),
+                     "clock_GHz": round(ghz, 3), "us_per_launch": round(t * 1e6, 1)}
+        del ops
+    del sums, clocks
+    return res
+
+
 def measured_peaks(dev):
     """Peaks measured on this GPU: HBM GB/s of a 1 GiB fp32 stream that reads
     and writes every element once (torch.mul with out=, the fastest of the
-    torch streaming kernels here; copy_ reaches less) and bf16 TFLOP/s of an
-    8192^3 torch matmul (hipBLASLt); both medians of 10 launches after
-    warm-up."""
+    torch streaming kernels here; copy_ reaches less), bf16 TFLOP/s of an
+    8192^3 torch matmul (hipBLASLt), both medians of 10 launches (the
+    matmul's after a settle), and the MFMA-only loop of mfma_loop_peak."""
     import torch
 
     s = torch.cuda.current_stream()
@@ -188,8 +241,7 @@ def measured_peaks(dev):
     n = 8192
     a = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
     b = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        torch.matmul(a, b)
+    settle(lambda i: torch.matmul(a, b))
     t = sorted(launch_times(lambda i: torch.matmul(a, b), 10, s))[5]
     gemm_tflops = 2 * n ** 3 / t / 1e12
     del a, b
@@ -197,7 +249,9 @@ def measured_peaks(dev):
     return {"stream_GB_per_s": round(stream_gbs, 1), "stream_frac_of_8TBs": round(stream_gbs / HBM_PEAK_GBS, 4),
             "bf16_gemm_TFLOP_per_s": round(gemm_tflops, 1),
             "bf16_gemm_frac_of_2500": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
-            "note": "1 GiB fp32 read+write stream (torch.mul out=); 8192^3 bf16 matmul (hipBLASLt)"}
+            "mfma_loop_bf16": mfma_loop_peak(dev),
+            "note": "1 GiB fp32 read+write stream (torch.mul out=); 8192^3 bf16 matmul (hipBLASLt); "
+                    "MFMA-only loop on N(0,1) and on zero operands (libla_peak.so)"}
 
 
 def _host_info():
@@ -779,6 +833,8 @@ def main():
                     help="only run a plain 1 GiB device copy 3 times (scale for HBM counters)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time la_decode on the 256 x 64-head serving batch")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only the measured HBM stream, GEMM and MFMA-loop peaks")
     ap.add_argument("--normed-only", action="store_true",
                     help="only time the fused output normalisation against the unfused one")
     ap.add_argument("--mixed-only", action="store_true",
@@ -827,6 +883,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}))
+        return
+    if args.peaks_only:
+        print(json.dumps({"peaks": measured_peaks(dev)}), flush=True)
         return
     if args.normed_only:
         la.lib()

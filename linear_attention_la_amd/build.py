@@ -32,6 +32,11 @@ FLAGS = [
 ]
 SOURCES = ["la_host.cpp", "la_prefill_bf16.hip", "la_prefill_wide.hip", "la_prefill_f32.hip",
            "la_decode.hip", "la_segment.hip", "la_state.hip"]
+# A separate library with the MFMA-only loop that the benchmark uses to
+# measure the GPU's matrix-core peak (not part of la.h, not linked into
+# libla.so).
+PEAK_SOURCE = os.path.join("probe", "la_peak.hip")
+PEAK_LIB = os.path.join(OUT_DIR, "libla_peak.so")
 
 
 def _compile(src):
@@ -48,23 +53,28 @@ def _compile(src):
     return obj, errs
 
 
-def build(verbose=False):
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    for obj, msgs in results:
-        if msgs.strip() and verbose:
-            print(msgs, file=sys.stderr)
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     # --no-undefined: a kernel whose host stub was not emitted (clang can drop
     # it without a diagnostic) fails here instead of at load time.
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp] + \
-        [o for o, _ in results]
+        list(objs)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(OUT_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(_compile, SOURCES + [PEAK_SOURCE]))
+    for obj, msgs in results:
+        if msgs.strip() and verbose:
+            print(msgs, file=sys.stderr)
+    _link([o for o, _ in results[:len(SOURCES)]], LIB)
+    _link([results[-1][0]], PEAK_LIB)
     return LIB
 
 

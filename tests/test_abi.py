@@ -55,6 +55,19 @@ def test_library_exports_only_the_c_abi():
     assert not [n for n in names if "launch_" in n or "segmented_chain" in n or "check_" in n]
 
 
+def test_peak_probe_library_is_separate():
+    """The benchmark's MFMA-loop probe is its own library: it exports only its
+    entry point, and libla.so does not contain it."""
+    import subprocess
+
+    path = os.path.join(os.path.dirname(la.lib_path()), "libla_peak.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert {n for n in names if n.startswith("la_")} == {"la_peak_mfma_bf16"}
+    assert not hasattr(la.lib(), "la_peak_mfma_bf16")
+
+
 def test_status_strings():
     assert la.la_status_str(la.LA_OK) == "LA_OK"
     assert la.la_status_str(la.LA_ERR_INVALID_ARG) == "LA_ERR_INVALID_ARG"
