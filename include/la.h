@@ -184,7 +184,9 @@ la_status la_prefill(const void* q, const void* k, const void* v,
  * A zero-length sequence leaves its slot unchanged.  Kernels, and the
  * LA_NDV override, as in la_prefill.  Errors as la_prefill, plus
  * LA_ERR_INVALID_ARG for a NULL pool or slot array, a slot out of range or a
- * repeated slot, and LA_ERR_UNSUPPORTED for fp32 inputs.
+ * repeated slot, and LA_ERR_UNSUPPORTED for fp32 inputs.  Repeated slots are
+ * found on a sorted host copy of slots_host (S entries, whatever pool_size);
+ * if it cannot be allocated the call returns LA_ERR_UNSUPPORTED.
  */
 la_status la_prefill_pool(const void* q, const void* k, const void* v,
                           const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -466,7 +468,9 @@ la_status la_decode(const void* q, const void* k, const void* v, float* kv,
  *               la_decode; o must not overlap the pool.
  *
  * Errors as la_decode, plus LA_ERR_INVALID_ARG for a NULL slot array, a slot
- * out of range or a repeated slot.
+ * out of range or a repeated slot.  Repeated slots are found on a sorted host
+ * copy of slots_host (batch entries, whatever pool_size); if it cannot be
+ * allocated the call returns LA_ERR_UNSUPPORTED.
  */
 la_status la_decode_pool(const void* q, const void* k, const void* v, float* kv_pool,
                          int32_t pool_size, const int32_t* slots_dev, const int32_t* slots_host,
