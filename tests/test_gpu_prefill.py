@@ -330,3 +330,52 @@ def test_binding_rejects_mismatched_outputs(dev):
     o, kv_f = la.prefill(q, k, v, cu, decay)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(kv_f).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_size_variants_agree(dev, d, monkeypatch):
+    """The compiled block sizes agree with one another, not only each with the
+    oracle: the fp32 kernel (beta = 32), the 32-column bf16 kernel and, for
+    d = 128, the one-workgroup-per-chain kernel (beta = 64 both, forced by
+    LA_NDV) on the same bf16-valued inputs, fp32 outputs, ragged lengths
+    across block edges, with initial states.  Each pair within 1e-4 relative
+    L2 per head (both sit within ~3e-5 of the exact result), and each
+    against the oracle at a block size none of them uses (beta = 100)."""
+    import torch
+    import linear_attention_la_amd as la
+
+    lengths = [1, 63, 64, 65, 200, 0, 333]
+    H = 3
+    decay = np.array([1.0, 0.97, 0.6], np.float32)
+    say(f"case block-size variants lengths={lengths} H={H} d={d}")
+    T = int(sum(lengths))
+    q, k, v = host_qkv(T, H, d, 51 + d, "bf16")  # bf16-representable fp32 arrays
+    cu = cu_seqlens(lengths)
+    kv0 = random_states(len(lengths), H, d, 58 + d, scale=0.1)
+    kv0d = to_dev(kv0, torch.float32, dev)
+    runs = {}
+    for name, dt, ndv in (("fp32 beta=32", torch.float32, None),
+                          ("32-column beta=64", torch.bfloat16, str(d // 32)),
+                          ("one workgroup per chain beta=64", torch.bfloat16, "1")):
+        if ndv == "1" and d != 128:
+            continue
+        if ndv is None:
+            monkeypatch.delenv("LA_NDV", raising=False)
+        else:
+            monkeypatch.setenv("LA_NDV", ndv)
+        qd, kd, vd = (to_dev(x, dt, dev) for x in (q, k, v))
+        o, kv = la.prefill(qd, kd, vd, cu, decay, kv_init=kv0d, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        runs[name] = (to_np(o), to_np(kv))
+    monkeypatch.delenv("LA_NDV", raising=False)
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0, beta=100)
+    names = list(runs)
+    for name in names:
+        parity.check(runs[name][0], o_ref, 1, 1e-2, what=f"{name} o vs oracle")
+        parity.check(runs[name][1], kv_ref, 1, 1e-2, what=f"{name} kv vs oracle")
+    for i in range(len(names)):
+        for j in range(i + 1, len(names)):
+            a, b = runs[names[i]], runs[names[j]]
+            s1 = parity.check(a[0], b[0], 1, 1e-4, what=f"{names[i]} vs {names[j]} o")
+            s2 = parity.check(a[1], b[1], 1, 1e-4, what=f"{names[i]} vs {names[j]} kv")
+            say(f"{names[i]} vs {names[j]}", s1, s2)
