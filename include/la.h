@@ -149,9 +149,10 @@ typedef enum la_dtype LA_ENUM_BASE { LA_BF16 = 0, LA_FP32 = 1 } la_dtype;
  * Sweep override (bf16 inputs): the environment variable LA_NDV, read on
  * every call that has sequences, forces one kernel for every pair -- "1"
  * one workgroup per pair (d = 128 only), "4" (d = 128) or "2" (d = 64) the
- * 32-column slices.  Unset or empty: the choice above.  Any other value is LA_ERR_UNSUPPORTED
- * (after the argument checks, before anything is enqueued).  The block
- * length is not an option: both kernels tile by 64 tokens.
+ * 32-column slices.  Unset or empty: the choice above.  Any other value is
+ * LA_ERR_UNSUPPORTED (after the argument checks, before anything is
+ * enqueued).  The block length is not an option: both kernels tile by 64
+ * tokens.
  */
 la_status la_prefill(const void* q, const void* k, const void* v,
                      const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -265,9 +266,10 @@ la_status la_prefill_kernel_plan(int32_t num_seqs, const int32_t* cu_seqlens_hos
  * correct run needs); a wait that reached it would end the remaining waits
  * at once and leave the outputs undefined -- it exists so that a fault
  * cannot hang the GPU, and no correct call reaches it.  The workspace holds
- * 2 states per (sequence, head) whatever the segment count.  d = 64: four kernels (plan, a state-only pass
- * over all segments, the prefix over them, the output pass); the workspace
- * holds one state per segment and per sequence.
+ * 2 states per (sequence, head) whatever the segment count.  d = 64: four
+ * kernels (plan, a state-only pass over all segments, the prefix over them,
+ * the output pass); the workspace holds one state per segment and per
+ * sequence.
  */
 la_status la_prefill_segmented(const void* q, const void* k, const void* v,
                                const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -525,8 +527,9 @@ typedef struct la_norm {
  * the wave (as la_prefill's split, decided by a model of both plans).  The
  * scan needs a workspace of la_prefill_normed_workspace_size bytes (16-byte
  * aligned, overlapping no other buffer; contents ignored and left
- * undefined); when that size is 0 the workspace is unused (may be NULL).  o must not overlap the weight or the gate.  Errors as
- * la_prefill, plus LA_ERR_INVALID_ARG for a NULL norm or weight, a bad eps,
+ * undefined); when that size is 0 the workspace is unused (may be NULL).
+ * o must not overlap the weight or the gate.  Errors as la_prefill, plus
+ * LA_ERR_INVALID_ARG for a NULL norm or weight, a bad eps,
  * a misaligned or overlapping weight or gate, or a missing or short
  * workspace.  Nothing synchronises.
  */
