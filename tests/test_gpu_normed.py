@@ -226,8 +226,9 @@ def test_prefill_normed_split(dev, lengths, H, tail):
     kernel, the remaining ones (consecutive in the index order) through the
     chained scan.  Every sequence's output and final state equal, bit for
     bit, those of a call on its own part alone (the wave's sequences: one
-    workgroup per pair; the rest: the scan, with the same segments), and the
-    call matches the oracle on four heads."""
+    workgroup per pair; the rest: the scan, with the same segments) and
+    those of the same call in place, and the call matches the oracle on
+    four heads."""
     import torch
     import linear_attention_la_amd as la
 
@@ -266,6 +267,14 @@ def test_prefill_normed_split(dev, lengths, H, tail):
         idx, yp, kvp = alone(seqs)
         assert torch.equal(y[idx], yp), f"sequences {seqs[:4]}...: rows"
         assert torch.equal(kv[seqs], kvp), f"sequences {seqs[:4]}...: final states"
+    # in place (kv_final is kv_init): both parts read their initial states
+    # before writing the final ones
+    kv_ip = kv0d.clone()
+    y_ip, _ = la.prefill_normed(qd, kd, vd, cu, decay, wd, 1e-5, gd, kv_init=kv_ip,
+                                kv_final=kv_ip, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ip, y), "in place: rows"
+    assert torch.equal(kv_ip, kv), "in place: final states"
     heads = [0, 1, H // 2, H - 1]
     o_ref, kv_ref = oracle.prefill_varlen(q[:, heads], k[:, heads], v[:, heads], cu,
                                           decay[heads], kv_init=kv0[:, heads])
