@@ -287,7 +287,8 @@ def test_ndv_override_forces_either_kernel(dev, monkeypatch):
 
 
 @pytest.mark.parametrize("lengths,wide_seqs", [([640] * 5, [0, 1, 2, 3]),
-                                               ([576, 640, 640, 640, 640], [1, 2, 3, 4])])
+                                               ([576, 640, 640, 640, 640], [1, 2, 3, 4]),
+                                               ([640, 640, 640, 640, 320, 0], [0, 1, 2, 3])])
 def test_split_launch(dev, monkeypatch, lengths, wide_seqs):
     """Five sequences x 64 heads (320 chains on 256 compute units): the four
     longest sequences fill one wave of the one-workgroup-per-chain kernel and
@@ -295,7 +296,9 @@ def test_split_launch(dev, monkeypatch, lengths, wide_seqs):
     an extra wave of the wide kernel.  Each sequence's rows and final state
     equal, bit for bit, those of the kernel it was given (forced for the
     whole call with LA_NDV), also on a state pool; the call matches the
-    oracle.  The second case dispatches the sequences out of index order."""
+    oracle.  The second case dispatches the sequences out of index order; the
+    third (384 chains) sends a shorter and a zero-length sequence to the
+    slices."""
     import torch
     import linear_attention_la_amd as la
 
@@ -337,7 +340,7 @@ def test_split_launch(dev, monkeypatch, lengths, wide_seqs):
     parity.check(to_np(kv), kv_ref, 1, 1e-2, what="split kv")
 
     pool = torch.zeros((7, H, D, D), dtype=torch.float32, device=dev)
-    slots = [6, 0, 3, 5, 1]
+    slots = [6, 0, 3, 5, 1, 2][:S]
     pool[slots] = kv0d
     o_pool = la.prefill_pool(qd, kd, vd, cu, decay, pool, slots, out_dtype=torch.float32)
     torch.cuda.synchronize()
