@@ -162,6 +162,16 @@ int main(void) {
          la_prefill_pool(Q, K, V, CUD, cu, 2, 100, H, D, LA_BF16, LA_BF16, decay, KVF, 10, CUD, dup,
                          O, NULL),
          LA_ERR_INVALID_ARG);
+  /* the repeated-slot check sorts a copy of the slots: its memory follows
+     the batch, not a pool of 2^31 - 1 states */
+  int32_t far_dup[3] = {5, 2147483646, 5}, last_twice[2] = {2147483646, 2147483646};
+  expect("decode pool repeated slot, largest pool",
+         la_decode_pool(Q, K, V, KVF, 2147483647, CUD, far_dup, decay, 3, H, D, LA_BF16, O, NULL),
+         LA_ERR_INVALID_ARG);
+  expect("decode pool last slot of the largest pool twice",
+         la_decode_pool(Q, K, V, KVF, 2147483647, CUD, last_twice, decay, 2, H, D, LA_BF16, O,
+                        NULL),
+         LA_ERR_INVALID_ARG);
 
   /* dtype arguments outside the enumerators (a C caller may pass any int):
      rejected, and never read as the enum type before they are checked */
