@@ -16,6 +16,7 @@ library is missing, every call raises.
     o = prefill_pool(q, k, v, cu_seqlens, decay, pool, slots)   # continues from pool[slots]
     s = cu_masked_stream(mask)   # a stream restricted to some compute units (two-stream serving)
     n, order = kernel_plan(cu_seqlens, num_heads)   # which prefill kernels a call would run
+    o, kv = attention(q, k, v, cu_seqlens, decay, kv_init)   # differentiable (torch autograd)
 """
 
 from ._binding import (  # noqa: F401
@@ -62,4 +63,5 @@ from ._binding import (  # noqa: F401
     prefill_normed_workspace_size,
     decode_pool,
     prefill_pool,
+    attention,
 )

@@ -801,3 +801,85 @@ def prefill_backward_segmented_workspace_size(cu_seqlens_host, num_heads, head_d
                                                          num_heads, head_dim, segment_len)
     _check(st)
     return n
+
+
+# ---- autograd ----
+
+_attention_fn = None
+
+
+def _attention_function():
+    """The torch.autograd.Function behind attention(), defined on first use
+    (torch is imported lazily by this module)."""
+    global _attention_fn
+    if _attention_fn is not None:
+        return _attention_fn
+    torch = _torch()
+
+    class LightningAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, kv_init, cu_dev, cu_host, decay, segment_len):
+            ctx.set_materialize_grads(False)
+            if segment_len is None:
+                o, kv = prefill(q, k, v, cu_dev, decay, kv_init=kv_init,
+                                cu_seqlens_host=cu_host)
+            else:
+                o, kv = prefill_segmented(q, k, v, cu_dev, decay, segment_len, kv_init=kv_init,
+                                          cu_seqlens_host=cu_host)
+            ctx.save_for_backward(q, k, v, kv_init)
+            ctx.cu = (cu_dev, cu_host)
+            ctx.decay, ctx.segment_len = decay, segment_len
+            return o, kv
+
+        @staticmethod
+        def backward(ctx, d_o, dkv_final):
+            q, k, v, kv_init = ctx.saved_tensors
+            needs = ctx.needs_input_grad
+            if d_o is None and dkv_final is None:
+                return (None,) * 8
+            # an unused output's gradient is zero (the library needs d_o)
+            d_o = torch.zeros_like(q) if d_o is None else d_o.contiguous()
+            if dkv_final is not None:
+                dkv_final = dkv_final.contiguous()
+            cu_dev, cu_host = ctx.cu
+            init_grad = kv_init is not None and needs[3]
+            common = dict(kv_init=kv_init, dkv_final=dkv_final, init_grad=init_grad,
+                          cu_seqlens_host=cu_host)
+            if ctx.segment_len is None:
+                dq, dk, dv, dkv0 = prefill_backward(q, k, v, d_o, cu_dev, ctx.decay, **common)
+            else:
+                dq, dk, dv, dkv0 = prefill_backward_segmented(q, k, v, d_o, cu_dev, ctx.decay,
+                                                              ctx.segment_len, **common)
+            return (dq if needs[0] else None, dk if needs[1] else None,
+                    dv if needs[2] else None, dkv0 if init_grad else None,
+                    None, None, None, None)
+
+    _attention_fn = LightningAttention
+    return _attention_fn
+
+
+def attention(q, k, v, cu_seqlens, decay, kv_init=None, segment_len=None):
+    """Differentiable prefill: (o, kv_final) = prefill(...) with gradients for
+    q, k, v and kv_init through prefill_backward (segment_len given: through
+    prefill_segmented and prefill_backward_segmented).  q, k, v: device bf16
+    [T, H, d]; decay: host [H], not differentiated; kv_init: device fp32
+    [S, H, d, d] or None.  Gradients have the dtype of their input.
+    cu_seqlens is copied to the host once, here, and both copies are reused
+    by the backward."""
+    torch = _torch()
+    if not isinstance(q, torch.Tensor) or not q.is_cuda:
+        raise TypeError("q must be a device tensor")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("attention() takes bf16 q, k, v (the backward is bf16-only)")
+    if q.dim() != 3:
+        raise ValueError("q must be a [T, H, d] tensor")
+    dev = q.device
+    if isinstance(cu_seqlens, torch.Tensor):
+        cu_host = cu_seqlens.detach().to("cpu", torch.int32).contiguous()
+        cu_dev = cu_seqlens if (cu_seqlens.device == dev and cu_seqlens.dtype == torch.int32
+                                and cu_seqlens.is_contiguous()) else cu_host.to(dev)
+    else:
+        cu_host = torch.from_numpy(np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32)))
+        cu_dev = cu_host.to(dev)
+    decay = _host_decay(decay, q.shape[1])
+    return _attention_function().apply(q, k, v, kv_init, cu_dev, cu_host, decay, segment_len)
