@@ -26,6 +26,9 @@ One JSON line is printed with the contract fields plus:
                 over heads of the same workload.
   mfma          algorithmic TFLOP/s at beta=64 against 2.5 PFLOP/s bf16.
   decode        la_decode alone on 256 sequences x 64 heads: GB/s vs 8 TB/s.
+  fp32_prefill  la_prefill with fp32 inputs and output on the n8k shape (the
+                fp32 kernel): TFLOP/s at beta=32 against the 157.3 TFLOP/s
+                fp32 matrix peak, and GB/s against 8 TB/s.
   mixed         decode on one stream concurrent with a packed prefill of 8
                 sequences (lengths U[1K, 32K]) on another.
   peaks         measured on the GPU: a 1 GiB read+write stream (HBM), an 8192^3
@@ -59,6 +62,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s + MFMA TFLOP/s (H=64,d=128,N=8K..1M); decode HBM GB/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix peak
 H, D, BETA = 64, 128, 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n8k_hbm_traffic.txt")
 KERNEL_SOURCES = ["linear_attention_la_amd/csrc/la_prefill_bf16.hip",
@@ -77,6 +81,12 @@ def prefill_flops(tokens, heads=H, d=D, beta=BETA):
     """Algorithmic flops at block size beta: 4 d^2 (Q S and K^T V) plus
     2 d (beta + 1) (causal halves of Q K^T and P V) per token per head."""
     return tokens * heads * (4 * d * d + 2 * d * (beta + 1))
+
+
+def prefill_fp32_bytes(tokens, seqs, heads=H, d=D):
+    """Algorithmic HBM bytes of an fp32-in, fp32-out prefill: Q, K, V read and
+    O written once (4 B each), plus the fp32 final state."""
+    return tokens * heads * d * 16 + seqs * heads * d * d * 4
 
 
 def decode_bytes(batch, heads=H, d=D):
@@ -724,6 +734,45 @@ def bench_backward(dev, reps=10, name="n8k"):
             "algorithmic_bytes": by}
 
 
+def bench_prefill_fp32(dev, reps=10):
+    """la_prefill with fp32 inputs and fp32 output on the n8k shape (B=1,
+    H=64, N=8192, d=128): the fp32 kernel (fp32 matrix cores, beta = 32, 256
+    workgroups); settled, then `reps` calls back to back in one event pair.
+    Algorithmic flops at beta = 32: 4 d^2 + 2 d (beta + 1) per token and head;
+    algorithmic bytes: q, k, v read and o written in fp32 plus the final
+    state."""
+    import torch
+
+    import linear_attention_la_amd as la
+    from la_inputs import cu_seqlens, device_qkv, workload
+
+    w = workload("n8k")
+    cu = cu_seqlens(w["lengths"])
+    N = int(cu[-1])
+    q, k, v = device_qkv(N, H, D, w["seed"], dev, dtype="fp32")
+    cu_dev = torch.from_numpy(cu).to(dev)
+    o = torch.empty_like(q)
+    kv = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    run = lambda i: la.prefill(q, k, v, cu_dev, w["decay"], cu_seqlens_host=cu, out=o,  # noqa
+                               kv_final=kv)
+    for _ in range(3):
+        run(0)
+    settle(run)
+    t = region_time(run, reps, torch.cuda.current_stream())
+    flops = prefill_flops(N, beta=32)
+    by = prefill_fp32_bytes(N, 1)
+    del q, k, v, o, kv
+    torch.cuda.empty_cache()
+    return {"workload": f"la_prefill B=1 H={H} N={N} d={D} fp32 in/out, fp32 state",
+            "kernel": "prefill_f32_kernel<128, float>",
+            "us": round(t * 1e6, 1), "tokens_per_s": round(N / t, 0),
+            "TFLOP_per_s": round(flops / t / 1e12, 2),
+            "frac_of_fp32_mfma_peak": round(flops / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            "GB_per_s": round(by / t / 1e9, 1),
+            "frac_of_8TBs": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_flops": flops, "algorithmic_bytes": by}
+
+
 SEG_H, SEG_N, SEG_LEN = 8, 1 << 20, 1 << 15
 
 
@@ -843,6 +892,8 @@ def main():
                     help="only time la_decode_pool (256 sequences on a pool of 1024)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time la_prefill_backward on n8k and batch8_n8k")
+    ap.add_argument("--fp32-only", action="store_true",
+                    help="only time la_prefill with fp32 inputs on the n8k shape")
     ap.add_argument("--sweep-only", choices=SWEEP,
                     help="only time one workload of the length / batch sweep")
     ap.add_argument("--segmented-only", action="store_true",
@@ -875,6 +926,9 @@ def main():
         return
     if args.sweep_only:
         print(json.dumps({"sweep": bench_sweep(dev, names=(args.sweep_only,))}), flush=True)
+        return
+    if args.fp32_only:
+        print(json.dumps({"fp32_prefill": bench_prefill_fp32(dev)}), flush=True)
         return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -982,6 +1036,7 @@ def main():
         line["backward_segmented"] = bench_backward_segmented(dev)
         line["backward"] = bench_backward(dev)
         line["backward_batch8"] = bench_backward(dev, name="batch8_n8k")
+        line["fp32_prefill"] = bench_prefill_fp32(dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline()
     else:

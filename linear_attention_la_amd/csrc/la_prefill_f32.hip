@@ -1,17 +1,23 @@
 // fp32 prefill kernel: blockwise causal linear attention with per-head decay,
-// all arithmetic in fp32 FMA (no reduced-precision products).
+// every product and sum in fp32 (no reduced-precision operands).
 //
 // This is the path for fp32 inputs, whose results must stay within ~1e-5
-// relative of the exact value; it favours plain, exact-order fp32 over speed.
-// The bf16 path (la_prefill_bf16.hip) is the fast one.
+// relative of the exact value.  Its contractions run on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation), which
+// keep fp32 precision at twice the rate of unpacked fp32 FMA.  The bf16 path
+// (la_prefill_bf16.hip) is the fast one.
 //
 // Method: per (sequence, head) the tokens are cut into blocks of BETA; inside
 // a block the masked, decayed left product (Q K^T .* M) V is formed, and the
 // carried d x d state contributes Q S (right product) before being advanced
 // by K^T V (emonzhong.com "MiniMax-01: Scaling Foundation Models with
 // Lightning Attention" 方法要点; mizuki blog "MiniMax-01：4M 上下文破局"
-// 关键概念清单).  One workgroup owns one (sequence, head, 32-column slice of
-// the state) chain and walks its blocks in order.
+// 关键概念清单).  One workgroup of four waves owns one (sequence, head,
+// 32-column slice of the state) chain and walks its blocks in order; the
+// next block's rows load into registers while the current block computes.
+//
+// MFMA operand layout (16 x 16 x 4, wave64): lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16] and receives D[4 (l / 16) + r][l % 16], r = 0..3.
 
 #include "la_device.h"
 #include "la_internal.h"
@@ -20,7 +26,12 @@ namespace la {
 namespace {
 
 constexpr int kBeta = 32;
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // four waves
+constexpr int kPad = 4;        // LDS row padding (floats); keeps rows 16 B aligned
+
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <typename OutT>
 __device__ __forceinline__ void store_out(OutT* p, float x);
@@ -35,11 +46,20 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   constexpr int DV = kF32Cols;
   constexpr int NDV = D / DV;
-  __shared__ float Qs[kBeta][D + 1];
-  __shared__ float Ks[kBeta][D + 1];
-  __shared__ float Vs[kBeta][DV + 1];
-  __shared__ float Ps[kBeta][kBeta + 1];
-  __shared__ float St[D][DV + 1];
+  constexpr int QF = kBeta * D / 4 / kThreads;   // float4 of Q (and of K) per thread
+  constexpr int VF = kBeta * DV / 4 / kThreads;  // float4 of V per thread
+  static_assert(QF >= 1 && VF == 1 && DV == 32 && kBeta == 32, "tile shapes");
+  // Q and K rows as loaded; V and the state slice transposed (row = value
+  // column), so that every MFMA operand is a 16-byte read along the
+  // reduction index.  Reductions take their index in the order
+  // 16 c + 4 (l / 16) + e for element e of lane l's 16-byte piece of chunk c:
+  // a permutation of the index, the same for A and B, so each product sum
+  // is unchanged.
+  __shared__ __attribute__((aligned(16))) float Qs[kBeta][D + kPad];
+  __shared__ __attribute__((aligned(16))) float Ks[kBeta][D + kPad];
+  __shared__ __attribute__((aligned(16))) float Vt[DV][kBeta + kPad];
+  __shared__ __attribute__((aligned(16))) float Ps[kBeta][kBeta + kPad];
+  __shared__ __attribute__((aligned(16))) float St[DV][D + kPad];  // S^T slice
   __shared__ float pw[kBeta + 1];  // lambda^n, n = 0..kBeta
 
   const int item = xcd_remap(blockIdx.x, a.num_items, NDV);
@@ -48,6 +68,9 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   const int h = sh % a.num_heads;
   const int s = seq_of(a, sh / a.num_heads);
   const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lr = t & 15;         // operand row (A) / column (B, D) within a tile
+  const int lk = (t >> 4) & 3;   // operand reduction lane group; D rows 4 lk .. 4 lk + 3
   const int H = a.num_heads;
   const int c0 = cs * DV;
   const int64_t start = a.cu_seqlens[s];
@@ -61,65 +84,132 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   if (t <= kBeta) pw[t] = exp2f((float)t * a.log2_decay[h]);
   for (int idx = t; idx < D * DV; idx += kThreads) {
     const int r = idx / DV, c = idx % DV;
-    St[r][c] = a.kv_init ? a.kv_init[state_off + (int64_t)r * D + c0 + c] : 0.0f;
+    St[c][r] = a.kv_init ? a.kv_init[state_off + (int64_t)r * D + c0 + c] : 0.0f;
   }
-  __syncthreads();
+
+  // Rows of one block in registers: thread t holds float4 number t + n kThreads
+  // of the block's Q and K rows (row-major, D / 4 per row) and float4 t of its
+  // V slice (8 per row).  Rows past the sequence end are zero.
+  float4 rq[QF], rk[QF], rv;
+  auto load = [&](int64_t b0) {
+    const int ell = (int)((end - b0) < kBeta ? (end - b0) : kBeta);
+#pragma unroll
+    for (int n = 0; n < QF; ++n) {
+      const int f = t + n * kThreads, row = f / (D / 4), c4 = f % (D / 4);
+      const int64_t off = ((b0 + row) * H + h) * (int64_t)D + 4 * c4;
+      rq[n] = row < ell ? *reinterpret_cast<const float4*>(q + off) : make_float4(0, 0, 0, 0);
+      rk[n] = row < ell ? *reinterpret_cast<const float4*>(k + off) : make_float4(0, 0, 0, 0);
+    }
+    const int row = t / (DV / 4), c4 = t % (DV / 4);
+    const int64_t off = ((b0 + row) * H + h) * (int64_t)D + c0 + 4 * c4;
+    rv = row < ell ? *reinterpret_cast<const float4*>(v + off) : make_float4(0, 0, 0, 0);
+  };
+  if (start < end) load(start);
 
   for (int64_t b0 = start; b0 < end; b0 += kBeta) {
     const int ell = (int)((end - b0) < kBeta ? (end - b0) : kBeta);
-    // Stage the block (rows past the end of the sequence are zero).
-    for (int idx = t; idx < kBeta * D; idx += kThreads) {
-      const int row = idx / D, col = idx % D;
-      float qv = 0.0f, kv = 0.0f;
-      if (row < ell) {
-        const int64_t off = ((b0 + row) * H + h) * (int64_t)D + col;
-        qv = q[off];
-        kv = k[off];
-      }
-      Qs[row][col] = qv;
-      Ks[row][col] = kv;
+#pragma unroll
+    for (int n = 0; n < QF; ++n) {
+      const int f = t + n * kThreads, row = f / (D / 4), c4 = f % (D / 4);
+      *reinterpret_cast<float4*>(&Qs[row][4 * c4]) = rq[n];
+      *reinterpret_cast<float4*>(&Ks[row][4 * c4]) = rk[n];
     }
-    for (int idx = t; idx < kBeta * DV; idx += kThreads) {
-      const int row = idx / DV, col = idx % DV;
-      Vs[row][col] = row < ell ? v[((b0 + row) * H + h) * (int64_t)D + c0 + col] : 0.0f;
+    {
+      const int row = t / (DV / 4), c4 = t % (DV / 4);
+      Vt[4 * c4 + 0][row] = rv.x;
+      Vt[4 * c4 + 1][row] = rv.y;
+      Vt[4 * c4 + 2][row] = rv.z;
+      Vt[4 * c4 + 3][row] = rv.w;
     }
     __syncthreads();
+    if (b0 + kBeta < end) load(b0 + kBeta);
 
-    // Intra-block scores with the causal decay mask.
-    for (int idx = t; idx < kBeta * kBeta; idx += kThreads) {
-      const int i = idx / kBeta, j = idx % kBeta;
-      float p = 0.0f;
-      if (j <= i) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < D; ++r) acc = fmaf(Qs[i][r], Ks[j][r], acc);
-        p = acc * pw[i - j];
+    // Intra-block scores with the causal decay mask, one 16 x 16 tile per
+    // wave for the three tiles on or below the diagonal (the tile above it
+    // is never read).
+    if (wave < 3) {
+      const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
+      floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int kc = 0; kc < D; kc += 16) {
+        const float4 x = *reinterpret_cast<const float4*>(&Qs[16 * ti + lr][kc + 4 * lk]);
+        const float4 y = *reinterpret_cast<const float4*>(&Ks[16 * tj + lr][kc + 4 * lk]);
+        acc0 = mfma4(x.x, y.x, acc0);
+        acc1 = mfma4(x.y, y.y, acc1);
+        acc0 = mfma4(x.z, y.z, acc0);
+        acc1 = mfma4(x.w, y.w, acc1);
       }
-      Ps[i][j] = p;
-    }
-    __syncthreads();
-
-    // Output: intra (P V) + lambda^(i+1) * inter (Q S).
-    for (int idx = t; idx < kBeta * DV; idx += kThreads) {
-      const int i = idx / DV, c = idx % DV;
-      if (i < ell) {
-        float intra = 0.0f;
-        for (int j = 0; j <= i; ++j) intra = fmaf(Ps[i][j], Vs[j][c], intra);
-        float inter = 0.0f;
-#pragma unroll 8
-        for (int r = 0; r < D; ++r) inter = fmaf(Qs[i][r], St[r][c], inter);
-        store_out(o + ((b0 + i) * H + h) * (int64_t)D + c0 + c, fmaf(pw[i + 1], inter, intra));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * lk + r, j = 16 * tj + lr;
+        const float f = pw[max(i - j, 0)];
+        Ps[i][j] = j <= i ? (acc0[r] + acc1[r]) * f : 0.0f;
       }
     }
     __syncthreads();
 
-    // State: S <- lambda^ell S + (diag(lambda^(ell-1-j)) K)^T V.
+    // Output: intra (P V) + lambda^(i+1) * inter (Q S), one 16 x 16 tile of
+    // (query rows, value columns) per wave.
+    {
+      const int ti = wave >> 1, tc = wave & 1;
+      floatx4 oi = {0, 0, 0, 0}, oe0 = {0, 0, 0, 0}, oe1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int jc = 0; jc < 32; jc += 16) {
+        if (jc > 16 * ti) break;
+        const float4 x = *reinterpret_cast<const float4*>(&Ps[16 * ti + lr][jc + 4 * lk]);
+        const float4 y = *reinterpret_cast<const float4*>(&Vt[16 * tc + lr][jc + 4 * lk]);
+        oi = mfma4(x.x, y.x, oi);
+        oi = mfma4(x.y, y.y, oi);
+        oi = mfma4(x.z, y.z, oi);
+        oi = mfma4(x.w, y.w, oi);
+      }
+#pragma unroll
+      for (int kc = 0; kc < D; kc += 16) {
+        const float4 x = *reinterpret_cast<const float4*>(&Qs[16 * ti + lr][kc + 4 * lk]);
+        const float4 y = *reinterpret_cast<const float4*>(&St[16 * tc + lr][kc + 4 * lk]);
+        oe0 = mfma4(x.x, y.x, oe0);
+        oe1 = mfma4(x.y, y.y, oe1);
+        oe0 = mfma4(x.z, y.z, oe0);
+        oe1 = mfma4(x.w, y.w, oe1);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ti + 4 * lk + r;
+        if (i < ell)
+          store_out(o + ((b0 + i) * H + h) * (int64_t)D + c0 + 16 * tc + lr,
+                    fmaf(pw[i + 1], oe0[r] + oe1[r], oi[r]));
+      }
+    }
+    __syncthreads();
+
+    // State: S <- lambda^ell S + (diag(lambda^(ell-1-j)) K)^T V; wave w owns
+    // the 16 x 16 tiles w, w + 4, ... of the D x 32 slice.
     const float fl = pw[ell];
-    for (int idx = t; idx < D * DV; idx += kThreads) {
-      const int r = idx / DV, c = idx % DV;
-      float acc = 0.0f;
-      for (int j = 0; j < ell; ++j) acc = fmaf(Ks[j][r] * pw[ell - 1 - j], Vs[j][c], acc);
-      St[r][c] = fmaf(fl, St[r][c], acc);
+    // This lane's weights lambda^(ell-1-j) for its eight reduction indices j
+    // (rows j >= ell of K are zero, so their weight only has to be finite).
+    float wj[kBeta / 4];
+#pragma unroll
+    for (int n = 0; n < kBeta / 4; ++n)
+      wj[n] = pw[max(ell - 1 - (16 * (n / 4) + 4 * lk + n % 4), 0)];
+#pragma unroll
+    for (int tile = wave; tile < (D / 16) * 2; tile += 4) {
+      const int tr = tile >> 1, tc = tile & 1;
+      floatx4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int jc = 0; jc < kBeta; jc += 16) {
+        const float4 y = *reinterpret_cast<const float4*>(&Vt[16 * tc + lr][jc + 4 * lk]);
+        const float yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc = mfma4(Ks[jc + 4 * lk + e][16 * tr + lr] * wj[jc / 4 + e], yv[e], acc);
+      }
+      float4* p = reinterpret_cast<float4*>(&St[16 * tc + lr][16 * tr + 4 * lk]);
+      float4 x = *p;
+      x.x = fmaf(fl, x.x, acc[0]);
+      x.y = fmaf(fl, x.y, acc[1]);
+      x.z = fmaf(fl, x.z, acc[2]);
+      x.w = fmaf(fl, x.w, acc[3]);
+      *p = x;
     }
     __syncthreads();
   }
@@ -127,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   if (a.kv_final) {
     for (int idx = t; idx < D * DV; idx += kThreads) {
       const int r = idx / DV, c = idx % DV;
-      a.kv_final[state_off + (int64_t)r * D + c0 + c] = St[r][c];
+      a.kv_final[state_off + (int64_t)r * D + c0 + c] = St[c][r];
     }
   }
 }

@@ -39,6 +39,14 @@ def test_prefill_flops_at_beta_64():
     assert bench.prefill_flops(8192) / bench.prefill_bytes(8192, 1) == pytest.approx(79.6, abs=0.1)
 
 
+def test_fp32_prefill_units():
+    # fp32 in/out: 16 d B per token and head plus the state; beta = 32 flops
+    assert bench.prefill_fp32_bytes(8192, 1) == 8192 * 64 * 128 * 16 + 64 * 128 * 128 * 4
+    assert bench.prefill_fp32_bytes(8192, 1) == 2 * bench.prefill_bytes(8192, 1) - 64 * 128 * 128 * 4
+    # 4 d^2 + 2 d (32 + 1) = 73,984 per token and head at d = 128
+    assert bench.prefill_flops(1, heads=1, beta=32) == 73_984
+
+
 def test_decode_bytes_of_the_serving_batch():
     # 256 sequences x 64 heads x (8 d^2 + 8 d) at d = 128
     assert bench.decode_bytes(256) == 2_164_260_864

@@ -17,7 +17,8 @@ def dev():
     return device()
 
 
-def _run(dev, lengths, H, d, dtype, decay, seed, kv_init=False, out_f32=False, beta=64):
+def _run(dev, lengths, H, d, dtype, decay, seed, kv_init=False, out_f32=False, beta=64,
+         heads=None):
     import torch
     import linear_attention_la_amd as la
 
@@ -33,7 +34,8 @@ def _run(dev, lengths, H, d, dtype, decay, seed, kv_init=False, out_f32=False, b
     o, kv = la.prefill(qd, kd, vd, cu, decay, kv_init=kv0d,
                        out_dtype=torch.float32 if out_f32 else None)
     torch.cuda.synchronize()
-    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0, beta=beta)
+    o_ref, kv_ref = oracle.prefill_varlen(q, k, v, cu, decay, kv_init=kv0, beta=beta,
+                                          heads=heads)
     return to_np(o), to_np(kv), o_ref, kv_ref
 
 
@@ -56,6 +58,20 @@ def test_fp32_ragged(dev, d, kv_init):
                                 out_f32=True)
     parity.check(o, o_ref, 1, 1e-5, what="fp32 ragged o")
     parity.check(kv, kv_ref, 1, 1e-5, what="fp32 ragged kv")
+
+
+def test_fp32_n8k_sampled_heads(dev):
+    """fp32 inputs at the 8K shape (B=1, H=64, N=8192, d=128, seeded decays,
+    initial state): 256 blocks of 32 tokens per chain on the fp32 kernel;
+    head 0 and the weakest and strongest decays against the oracle at 1e-5."""
+    w = workload("n8k")
+    heads = [0, int(np.argmin(w["decay"])), int(np.argmax(w["decay"]))]
+    o, kv, o_ref, kv_ref = _run(dev, w["lengths"], w["H"], w["d"], "fp32", w["decay"],
+                                w["seed"] + 100, kv_init=True, out_f32=True, beta=32,
+                                heads=heads)
+    s1 = parity.check(o[:, heads], o_ref[:, heads], 1, 1e-5, what="fp32 n8k o")
+    s2 = parity.check(kv[:, heads], kv_ref[:, heads], 1, 1e-5, what="fp32 n8k kv")
+    say("fp32 n8k", s1, s2)
 
 
 @pytest.mark.parametrize("d", [64, 128])
