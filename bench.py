@@ -232,6 +232,45 @@ def mfma_loop_peak(dev, iters=10000, reps=10):
     return res
 
 
+def mfma_loop_peak_f32(dev, iters=2500, reps=10):
+    """fp32 MFMA rate of the MFMA-only loop on v_mfma_f32_16x16x4_f32
+    (libla_peak.so, as mfma_loop_peak) on N(0,1) operands: TFLOP/s against
+    the 157.3 TFLOP/s fp32 matrix peak and the shader clock.  None if the
+    library was not built."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(PEAK_LIB):
+        return None
+    L = ctypes.CDLL(PEAK_LIB)
+    L.la_peak_mfma_f32.restype = ctypes.c_int
+    L.la_peak_mfma_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    threads, waves = cus * 1024, cus * 16
+    s = torch.cuda.current_stream()
+    sums = torch.empty(threads, dtype=torch.float32, device=dev)
+    clocks = torch.zeros(2 * waves, dtype=torch.int64, device=dev)
+    g = torch.Generator(device=dev).manual_seed(7)
+    ops = torch.randn(threads * 16, generator=g, device=dev)
+    flops = waves * iters * 8 * 16 * 16 * 4 * 2
+
+    def run(i):
+        st = L.la_peak_mfma_f32(ops.data_ptr(), sums.data_ptr(), clocks.data_ptr(), cus, iters,
+                                ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"la_peak_mfma_f32: HIP error {st}")
+    settle(run)
+    t = region_time(run, reps, s)
+    c = clocks.view(waves, 2).cpu().numpy()
+    ghz = float(np.median(c[:, 0] / np.maximum(c[:, 1], 1))) * 0.1
+    del ops, sums, clocks
+    return {"TFLOP_per_s": round(flops / t / 1e12, 1),
+            "frac_of_157_3": round(flops / t / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+            "clock_GHz": round(ghz, 3), "us_per_launch": round(t * 1e6, 1)}
+
+
 def measured_peaks(dev):
     """Peaks measured on this GPU: HBM GB/s of a 1 GiB fp32 stream that reads
     and writes every element once (torch.mul with out=, the fastest of the
@@ -260,6 +299,7 @@ def measured_peaks(dev):
             "bf16_gemm_TFLOP_per_s": round(gemm_tflops, 1),
             "bf16_gemm_frac_of_2500": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
             "mfma_loop_bf16": mfma_loop_peak(dev),
+            "mfma_loop_f32": mfma_loop_peak_f32(dev),
             "note": "1 GiB fp32 read+write stream (torch.mul out=); 8192^3 bf16 matmul (hipBLASLt); "
                     "MFMA-only loop on N(0,1) and on zero operands (libla_peak.so)"}
 
@@ -928,7 +968,8 @@ def main():
         print(json.dumps({"sweep": bench_sweep(dev, names=(args.sweep_only,))}), flush=True)
         return
     if args.fp32_only:
-        print(json.dumps({"fp32_prefill": bench_prefill_fp32(dev)}), flush=True)
+        print(json.dumps({"fp32_prefill": bench_prefill_fp32(dev),
+                          "mfma_loop_f32": mfma_loop_peak_f32(dev)}), flush=True)
         return
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)

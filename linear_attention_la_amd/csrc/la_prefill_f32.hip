@@ -19,6 +19,8 @@
 // MFMA operand layout (16 x 16 x 4, wave64): lane l supplies A[l % 16][l / 16]
 // and B[l / 16][l % 16] and receives D[4 (l / 16) + r][l % 16], r = 0..3.
 
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -106,8 +108,63 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
   };
   if (start < end) load(start);
 
+  // The state update of a block, S <- lambda^ell S + (diag(lambda^(ell-1-j))
+  // K)^T V, is accumulated in registers while the block's scores and
+  // outputs are formed (wave 3, idle for the scores, takes the first four
+  // 16 x 16 tiles of the D x 32 slice then; every wave takes NB more with
+  // the outputs), and written back to LDS with the next block's rows, so a
+  // block needs three barriers.
+  constexpr int NT = (D / 16) * 2;  // state tiles of the slice
+  constexpr int NB = (NT - 4) / 4;  // tiles per wave with the outputs
+  floatx4 accA[4], accB[NB];
+  float fl = 1.0f;
+  bool pending = false;
+  // Accumulate the updates of N tiles (tile -> key-row tile tr = tile / 2,
+  // value-column tile tc = tile % 2) together, so that consecutive MFMAs
+  // are independent.
+  auto state_tiles = [&](auto n_tiles, int first, floatx4* acc, const float* wj) {
+    constexpr int N = decltype(n_tiles)::value;
+#pragma unroll
+    for (int n = 0; n < N; ++n) acc[n] = floatx4{0, 0, 0, 0};
+#pragma unroll
+    for (int jc = 0; jc < kBeta; jc += 16) {
+      float4 y[2];
+      y[0] = *reinterpret_cast<const float4*>(&Vt[lr][jc + 4 * lk]);
+      y[1] = *reinterpret_cast<const float4*>(&Vt[16 + lr][jc + 4 * lk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float* kr = &Ks[jc + 4 * lk + e][0];
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          const int tile = first + n, tr = tile >> 1, tc = tile & 1;
+          const float ye = e == 0 ? y[tc].x : e == 1 ? y[tc].y : e == 2 ? y[tc].z : y[tc].w;
+          acc[n] = mfma4(kr[16 * tr + lr] * wj[jc / 4 + e], ye, acc[n]);
+        }
+      }
+    }
+  };
+  auto write_tile = [&](int tile, const floatx4& acc) {
+    const int tr = tile >> 1, tc = tile & 1;
+    float4* p = reinterpret_cast<float4*>(&St[16 * tc + lr][16 * tr + 4 * lk]);
+    float4 x = *p;
+    x.x = fmaf(fl, x.x, acc[0]);
+    x.y = fmaf(fl, x.y, acc[1]);
+    x.z = fmaf(fl, x.z, acc[2]);
+    x.w = fmaf(fl, x.w, acc[3]);
+    *p = x;
+  };
+  auto write_state = [&]() {
+    if (wave == 3) {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) write_tile(n, accA[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) write_tile(4 + wave * NB + n, accB[n]);
+  };
+
   for (int64_t b0 = start; b0 < end; b0 += kBeta) {
     const int ell = (int)((end - b0) < kBeta ? (end - b0) : kBeta);
+    if (pending) write_state();  // the previous block's update
 #pragma unroll
     for (int n = 0; n < QF; ++n) {
       const int f = t + n * kThreads, row = f / (D / 4), c4 = f % (D / 4);
@@ -124,93 +181,81 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(PrefillArgs a) {
     __syncthreads();
     if (b0 + kBeta < end) load(b0 + kBeta);
 
+    // This lane's weights lambda^(ell-1-j) for its eight reduction indices j
+    // of the state update (rows j >= ell of K are zero, so their weight only
+    // has to be finite).
+    float wj[kBeta / 4];
+#pragma unroll
+    for (int n = 0; n < kBeta / 4; ++n)
+      wj[n] = pw[max(ell - 1 - (16 * (n / 4) + 4 * lk + n % 4), 0)];
+
     // Intra-block scores with the causal decay mask, one 16 x 16 tile per
     // wave for the three tiles on or below the diagonal (the tile above it
-    // is never read).
+    // is never read); wave 3 meanwhile accumulates four state tiles.
     if (wave < 3) {
       const int ti = wave == 0 ? 0 : 1, tj = wave == 2 ? 1 : 0;
-      floatx4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+      floatx4 a0 = {0, 0, 0, 0}, a1 = a0, a2 = a0, a3 = a0;
 #pragma unroll
       for (int kc = 0; kc < D; kc += 16) {
         const float4 x = *reinterpret_cast<const float4*>(&Qs[16 * ti + lr][kc + 4 * lk]);
         const float4 y = *reinterpret_cast<const float4*>(&Ks[16 * tj + lr][kc + 4 * lk]);
-        acc0 = mfma4(x.x, y.x, acc0);
-        acc1 = mfma4(x.y, y.y, acc1);
-        acc0 = mfma4(x.z, y.z, acc0);
-        acc1 = mfma4(x.w, y.w, acc1);
+        a0 = mfma4(x.x, y.x, a0);
+        a1 = mfma4(x.y, y.y, a1);
+        a2 = mfma4(x.z, y.z, a2);
+        a3 = mfma4(x.w, y.w, a3);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ti + 4 * lk + r, j = 16 * tj + lr;
         const float f = pw[max(i - j, 0)];
-        Ps[i][j] = j <= i ? (acc0[r] + acc1[r]) * f : 0.0f;
+        Ps[i][j] = j <= i ? ((a0[r] + a1[r]) + (a2[r] + a3[r])) * f : 0.0f;
       }
+    } else {
+      state_tiles(std::integral_constant<int, 4>(), 0, accA, wj);
     }
     __syncthreads();
 
     // Output: intra (P V) + lambda^(i+1) * inter (Q S), one 16 x 16 tile of
-    // (query rows, value columns) per wave.
+    // (query rows, value columns) per wave; then this wave's NB state tiles.
     {
       const int ti = wave >> 1, tc = wave & 1;
-      floatx4 oi = {0, 0, 0, 0}, oe0 = {0, 0, 0, 0}, oe1 = {0, 0, 0, 0};
+      const floatx4 z = {0, 0, 0, 0};
+      floatx4 oi[4] = {z, z, z, z}, oe[4] = {z, z, z, z};
 #pragma unroll
       for (int jc = 0; jc < 32; jc += 16) {
         if (jc > 16 * ti) break;
         const float4 x = *reinterpret_cast<const float4*>(&Ps[16 * ti + lr][jc + 4 * lk]);
         const float4 y = *reinterpret_cast<const float4*>(&Vt[16 * tc + lr][jc + 4 * lk]);
-        oi = mfma4(x.x, y.x, oi);
-        oi = mfma4(x.y, y.y, oi);
-        oi = mfma4(x.z, y.z, oi);
-        oi = mfma4(x.w, y.w, oi);
+        oi[0] = mfma4(x.x, y.x, oi[0]);
+        oi[1] = mfma4(x.y, y.y, oi[1]);
+        oi[2] = mfma4(x.z, y.z, oi[2]);
+        oi[3] = mfma4(x.w, y.w, oi[3]);
       }
 #pragma unroll
       for (int kc = 0; kc < D; kc += 16) {
         const float4 x = *reinterpret_cast<const float4*>(&Qs[16 * ti + lr][kc + 4 * lk]);
         const float4 y = *reinterpret_cast<const float4*>(&St[16 * tc + lr][kc + 4 * lk]);
-        oe0 = mfma4(x.x, y.x, oe0);
-        oe1 = mfma4(x.y, y.y, oe1);
-        oe0 = mfma4(x.z, y.z, oe0);
-        oe1 = mfma4(x.w, y.w, oe1);
+        oe[0] = mfma4(x.x, y.x, oe[0]);
+        oe[1] = mfma4(x.y, y.y, oe[1]);
+        oe[2] = mfma4(x.z, y.z, oe[2]);
+        oe[3] = mfma4(x.w, y.w, oe[3]);
       }
+      state_tiles(std::integral_constant<int, NB>(), 4 + wave * NB, accB, wj);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ti + 4 * lk + r;
         if (i < ell)
           store_out(o + ((b0 + i) * H + h) * (int64_t)D + c0 + 16 * tc + lr,
-                    fmaf(pw[i + 1], oe0[r] + oe1[r], oi[r]));
+                    fmaf(pw[i + 1], (oe[0][r] + oe[1][r]) + (oe[2][r] + oe[3][r]),
+                         (oi[0][r] + oi[1][r]) + (oi[2][r] + oi[3][r])));
       }
     }
+    fl = pw[ell];
+    pending = true;
     __syncthreads();
-
-    // State: S <- lambda^ell S + (diag(lambda^(ell-1-j)) K)^T V; wave w owns
-    // the 16 x 16 tiles w, w + 4, ... of the D x 32 slice.
-    const float fl = pw[ell];
-    // This lane's weights lambda^(ell-1-j) for its eight reduction indices j
-    // (rows j >= ell of K are zero, so their weight only has to be finite).
-    float wj[kBeta / 4];
-#pragma unroll
-    for (int n = 0; n < kBeta / 4; ++n)
-      wj[n] = pw[max(ell - 1 - (16 * (n / 4) + 4 * lk + n % 4), 0)];
-#pragma unroll
-    for (int tile = wave; tile < (D / 16) * 2; tile += 4) {
-      const int tr = tile >> 1, tc = tile & 1;
-      floatx4 acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int jc = 0; jc < kBeta; jc += 16) {
-        const float4 y = *reinterpret_cast<const float4*>(&Vt[16 * tc + lr][jc + 4 * lk]);
-        const float yv[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc = mfma4(Ks[jc + 4 * lk + e][16 * tr + lr] * wj[jc / 4 + e], yv[e], acc);
-      }
-      float4* p = reinterpret_cast<float4*>(&St[16 * tc + lr][16 * tr + 4 * lk]);
-      float4 x = *p;
-      x.x = fmaf(fl, x.x, acc[0]);
-      x.y = fmaf(fl, x.y, acc[1]);
-      x.z = fmaf(fl, x.z, acc[2]);
-      x.w = fmaf(fl, x.w, acc[3]);
-      *p = x;
-    }
+  }
+  if (pending) {
+    write_state();
     __syncthreads();
   }
 

@@ -57,15 +57,16 @@ def test_library_exports_only_the_c_abi():
 
 def test_peak_probe_library_is_separate():
     """The benchmark's MFMA-loop probe is its own library: it exports only its
-    entry point, and libla.so does not contain it."""
+    entry points (the bf16 and fp32 loops), and libla.so contains neither."""
     import subprocess
 
     path = os.path.join(os.path.dirname(la.lib_path()), "libla_peak.so")
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     names = {line.split()[-1] for line in out.splitlines() if line.strip()}
-    assert {n for n in names if n.startswith("la_")} == {"la_peak_mfma_bf16"}
+    assert {n for n in names if n.startswith("la_")} == {"la_peak_mfma_bf16", "la_peak_mfma_f32"}
     assert not hasattr(la.lib(), "la_peak_mfma_bf16")
+    assert not hasattr(la.lib(), "la_peak_mfma_f32")
 
 
 def test_status_strings():
